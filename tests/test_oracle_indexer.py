@@ -1,0 +1,239 @@
+"""Pins of the oracle's indexer, pool and Top-K steps.
+
+Each pin rests on something other than the oracle's own code: exact integer
+arithmetic on E4M3 values decoded by PyTorch, a hand-worked example
+(tests/golden/worked_scores.txt), the ordering characterisation of a Top-k set,
+a different sorting routine (Python's ``sorted``), the block-prefilter lemma,
+and the invariants the pages state (Reindex picks inside the pool; a position
+outside the pool cannot be picked by a Reindex layer)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import csa2 as O
+from oracle import formats as F
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def torch_e4m3_int(codes):
+    """E4M3 bytes -> exact integers in units of 2^-9 (decoded by PyTorch)."""
+    v = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    x = v.to(torch.float64).numpy() * 512.0
+    assert np.all(x == np.round(x))
+    return x.astype(np.int64)
+
+
+def torch_q8(q_bf16):
+    t = torch.from_numpy(np.ascontiguousarray(q_bf16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def rand_case(rng, n=300):
+    k8 = workloads.to_e4m3_bytes(rng.standard_normal((n, 128), dtype=np.float32))
+    q = workloads.to_bf16_bits(rng.standard_normal((32, 128), dtype=np.float32))
+    return k8, q
+
+
+def test_worked_example_scores():
+    rows = []
+    with open(os.path.join(GOLDEN, "worked_scores.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                r, c0, c1, s = line.split()
+                rows.append((int(r), int(c0, 16), int(c1, 16), float(s)))
+    k8 = np.zeros((len(rows), 128), np.uint8)
+    for r, c0, c1, _ in rows:
+        k8[r, 0], k8[r, 1] = c0, c1
+    qf = np.zeros((32, 128), np.float32)
+    qf[0, 0], qf[1, 1] = 1.0, 2.0
+    w = np.ones(32, np.float32)
+    w[0], w[1] = 0.5, 0.25
+    s = O.indexer_scores(k8, O.quantize_query(workloads.to_bf16_bits(qf)), w)
+    assert list(s) == [r[3] for r in rows]
+
+
+def test_quantize_query_matches_torch():
+    rng = np.random.default_rng(1)
+    q = workloads.to_bf16_bits(rng.standard_normal((32, 128), dtype=np.float32) * 3)
+    assert np.array_equal(O.quantize_query(q), torch_q8(q))
+
+
+@pytest.mark.parametrize("h", [0, 7, 31])
+def test_single_head_score_is_exact_integer_dot(h):
+    rng = np.random.default_rng(10 + h)
+    k8, q = rand_case(rng)
+    w = np.zeros(32, np.float32)
+    w[h] = 1.0
+    s = O.indexer_scores(k8, O.quantize_query(q), w)
+    d = torch_e4m3_int(k8) @ torch_e4m3_int(torch_q8(q))[h]   # exact, units of 2^-18
+    expect = np.maximum(d, 0).astype(np.float64) * 2.0 ** -18
+    assert np.array_equal(s, expect)
+    assert (d < 0).any() and (d > 0).any()
+
+
+def test_two_head_weighted_sum_exact():
+    rng = np.random.default_rng(3)
+    k8, q = rand_case(rng)
+    w = np.zeros(32, np.float32)
+    w[4], w[19] = 0.5, 0.25
+    s = O.indexer_scores(k8, O.quantize_query(q), w)
+    qi = torch_e4m3_int(torch_q8(q))
+    ki = torch_e4m3_int(k8)
+    d4, d19 = ki @ qi[4], ki @ qi[19]
+    expect = (2 * np.maximum(d4, 0) + np.maximum(d19, 0)).astype(np.float64) * 2.0 ** -20
+    assert np.array_equal(s, expect)
+
+
+def test_head_permutation_and_weight_scaling():
+    rng = np.random.default_rng(4)
+    k8, q = rand_case(rng)
+    w = rng.random(32, dtype=np.float32)
+    s = O.indexer_scores(k8, O.quantize_query(q), w)
+    perm = rng.permutation(32)
+    sp = O.indexer_scores(k8, O.quantize_query(q[perm]), w[perm])
+    assert np.allclose(s, sp, rtol=1e-14, atol=0)
+    s2 = O.indexer_scores(k8, O.quantize_query(q), 2 * w)
+    assert np.array_equal(s2, 2 * s)
+    assert np.all(s >= 0)
+
+
+def topk_by_sorted(keys, ids, k):
+    """Reference ranking with Python's sorted on (-key, id) tuples."""
+    order = sorted(zip((-float(x) for x in keys), (int(i) for i in ids)))
+    return sorted(i for _, i in order[:k])
+
+
+def check_topk_characterisation(cand, s, k, sel):
+    sel = [int(x) for x in sel if x >= 0]
+    assert len(sel) == min(k, len(cand))
+    assert sel == sorted(sel)
+    sc = dict(zip([int(c) for c in cand], [float(x) for x in s]))
+    chosen = set(sel)
+    rest = [int(p) for p in cand if int(p) not in chosen]
+    if chosen and rest:
+        # every chosen (score, position) ranks before every unchosen one
+        assert max((-sc[c], c) for c in chosen) < min((-sc[p], p) for p in rest)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_topk_selection_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 400))
+    cand = np.sort(rng.choice(1000, size=n, replace=False)).astype(np.int32)
+    s = rng.integers(0, 6, size=n).astype(np.float32)      # heavy ties
+    k = int(rng.integers(1, 80))
+    got = O.top_k(cand, s, k)
+    assert got.shape == (k,)
+    assert np.all(got[min(k, n):] == -1)
+    assert list(got[got >= 0]) == topk_by_sorted(s, cand, k)
+    check_topk_characterisation(cand, s, k, got)
+
+
+def brute_pool(blk, n_vis, block, P):
+    nb = len(blk)
+    order = sorted(range(nb), key=lambda j: (-float(blk[j]), j))
+    chosen = sorted(order[:P])
+    return [p for j in chosen for p in range(j * block, min((j + 1) * block, n_vis))]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pool_is_top_blocks_and_contains_dense_topk(seed):
+    rng = np.random.default_rng(100 + seed)
+    n_vis = int(rng.integers(1, 700))
+    block = 8
+    s32 = rng.integers(0, 9, size=n_vis).astype(np.float32)   # ties within and across blocks
+    P = int(rng.integers(1, 40))
+    k = int(rng.integers(1, P * block + 1))
+    blk = O.block_scores(s32, n_vis, block)
+    nb = -(-n_vis // block)
+    assert len(blk) == nb
+    for j in range(nb):
+        assert blk[j] == s32[j * block:(j + 1) * block].max()
+    pool = O.candidate_pool(blk, n_vis, block, P)
+    assert list(pool) == brute_pool(blk, n_vis, block, P)
+    # whole blocks, ascending, min(P, nb) of them
+    blocks = sorted(set(int(p) // block for p in pool))
+    assert len(blocks) == min(P, nb)
+    assert list(pool) == sorted(pool)
+    # lemma: the dense Top-k (every visible position) lies inside the pool, so the
+    # Top-k over the pool equals the dense Top-k, tie-breaks included (k <= P*block)
+    k = min(k, P)
+    dense = topk_by_sorted(s32, np.arange(n_vis), k)
+    assert set(dense) <= set(int(p) for p in pool)
+    assert list(O.top_k(pool, s32[pool], k)[:len(dense)]) == dense
+
+
+def test_full_layer_no_pool_and_degenerate_visibility():
+    rng = np.random.default_rng(7)
+    k8 = workloads.to_e4m3_bytes(rng.standard_normal((50, 128), dtype=np.float32))
+    q = workloads.to_bf16_bits(rng.standard_normal((32, 128), dtype=np.float32))
+    w = rng.random(32, dtype=np.float32)
+    # n_vis = 0: empty pool, all -1
+    f0 = O.full_layer(k8, q, w, 0, 8, 4, 16)
+    assert f0["pool"].shape == (0,) and np.all(f0["topk"] == -1)
+    # n_vis < k: every visible position selected, ragged last block
+    f1 = O.full_layer(k8, q, w, 13, 8, 4, 16)
+    assert list(f1["pool"]) == list(range(13))
+    assert list(f1["topk"][:13]) == list(range(13)) and np.all(f1["topk"][13:] == -1)
+    # no pool: dense Top-k
+    f2 = O.full_layer(k8, q, w, 50, 8, 0, 10)
+    assert f2["pool"] is None
+    assert list(f2["topk"]) == topk_by_sorted(f2["scores32"], np.arange(50), 10)
+
+
+def small_decode(seed=5, N=2000, P=16, k=32):
+    return workloads.Workload("t", seed, B=1, T=1, N=N, H=4, layer_set=(0, 1, 1, 2),
+                              n_reindex=2, pool_blocks=P, top_k=k)
+
+
+def test_reindex_inside_pool_and_reproduces_full():
+    w = small_decode()
+    inp = workloads.make_inputs(w, with_attention=False)
+    out = O.query_chain(inp, w, 0, 0, with_attention=False)
+    pool = set(int(p) for p in out["full"]["pool"])
+    for ri in out["reindex"]:
+        sel = [int(p) for p in ri["topk"] if p >= 0]
+        assert len(sel) == w.top_k and set(sel) <= pool
+    # a Reindex layer given the Full layer's own query and weights picks the Full Top-k
+    same = O.reindex_layer(inp["idx_k"][0], inp["idx_q"][0, 0], inp["head_w"][0, 0],
+                           out["full"]["pool"], w.top_k)
+    assert np.array_equal(same["topk"], out["full"]["topk"])
+    assert np.array_equal(same["topk_score"], out["full"]["topk_score"])
+    # a position outside the pool cannot be picked, even if it scores highest
+    outside = next(p for p in range(w.N) if p not in pool)
+    s_all = O.indexer_scores(inp["idx_k"][0], O.quantize_query(inp["ri_q"][0, 0, 0]), inp["ri_w"][0, 0, 0])
+    assert outside not in set(out["reindex"][0]["topk"].tolist())
+    assert s_all.shape == (w.N,)
+
+
+def test_prefill_visibility_readings():
+    w = workloads.WORKLOADS["prefill_4k_64k"]
+    nv = w.n_visible()
+    # the chunk is the last 4096 tokens of 65536 (p = 61440 .. 65535), m = 2 tokens per entry,
+    # only complete entries are visible
+    assert nv[0, 0] == 30720 and nv[0, -1] == 32768 and nv[0, 1] == 30721 and nv[0, 2] == 30721
+    se = w.swa_end()
+    assert se[0, 0] == 128 and se[0, -1] == 4096 + 127 and w.swa_rows == 4223
+
+
+def test_planted_cluster_recall_small():
+    w = workloads.small_variant(workloads.WORKLOADS["decode_1m"], N=65536, seed=77)
+    inp = workloads.make_inputs(w, with_attention=False)
+    out = O.query_chain(inp, w, 0, 0, with_attention=False)
+    assert np.isin(inp["planted_pos"], out["full"]["topk"]).all()
+
+
+def test_workload_shapes_match_page_figures():
+    from tests.test_oracle_formats import page_figures
+    figs = page_figures()
+    for name in ("decode_b8_128k", "decode_1m"):
+        w = workloads.WORKLOADS[name]
+        assert w.pool_blocks == figs["pool_blocks"] and w.block == figs["pool_block_size"]
+        assert w.pool_cap == figs["pool_positions"] and w.top_k == figs["top_k"]
+    assert workloads.IDX_HEADS == figs["indexer_heads"] and workloads.IDX_DIM == figs["indexer_head_dim"]
+    assert workloads.KV_DIM // workloads.KV_SCALE_BYTES == figs["scale_group"]
