@@ -1,0 +1,281 @@
+// C ABI of the CSA2 hot path: argument checks, workspace carving and kernel dispatch.
+// The operations and their readings are documented in include/csa2.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "csa2.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+csa2_status fail(csa2_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+csa2_status fail(csa2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+csa2_status ok() {
+  g_err.clear();
+  return CSA2_OK;
+}
+
+csa2_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return CSA2_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, st, ...) \
+  do {                          \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p) \
+  REQUIRE((p) != nullptr && aligned16(p), CSA2_ERR_INVALID_ARG, "%s must be a non-null 16-byte aligned device pointer", #p)
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carving: a running offset, 256-byte aligned pieces.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+struct FullPlan {
+  int Q, nb_max, chunk, n_wg, P, cap;
+  bool internal_pool;
+};
+
+FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
+  FullPlan p;
+  p.Q = B * T;
+  p.nb_max = (n_max + csa2::kBlock - 1) / csa2::kBlock;
+  p.chunk = csa2::scan_chunk_positions(n_max, p.Q);
+  p.n_wg = n_max > 0 ? (n_max + p.chunk - 1) / p.chunk : 1;
+  p.internal_pool = pool_blocks == 0;
+  p.P = p.internal_pool ? top_k : pool_blocks;
+  p.cap = p.P * csa2::kBlock;
+  return p;
+}
+
+// Pieces of the Full-layer workspace, in order.
+struct FullWs {
+  float* scores;
+  uint32_t* blkkey;
+  uint32_t* wg_minmax;
+  int32_t* pool_pos;
+  int32_t* pool_len;
+};
+
+size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
+  Carver c{(char*)ws};
+  FullWs w;
+  w.scores = c.take<float>((size_t)p.Q * (n_max > 0 ? n_max : 1));
+  w.blkkey = c.take<uint32_t>((size_t)p.Q * (p.nb_max > 0 ? p.nb_max : 1));
+  w.wg_minmax = c.take<uint32_t>((size_t)p.Q * p.n_wg * 2);
+  w.pool_pos = p.internal_pool ? c.take<int32_t>((size_t)p.Q * p.cap) : nullptr;
+  w.pool_len = p.internal_pool ? c.take<int32_t>((size_t)p.Q) : nullptr;
+  if (out) *out = w;
+  return c.off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_last_error(void) { return g_err.c_str(); }
+
+csa2_status csa2_quantize_query(const uint16_t* in_bf16, uint8_t* out_e4m3, int64_t n, void* stream) {
+  REQUIRE(n >= 0, CSA2_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return ok();
+  REQUIRE(in_bf16 != nullptr && out_e4m3 != nullptr, CSA2_ERR_INVALID_ARG, "null pointer");
+  csa2_status st = hip_check(csa2::launch_quantize_query(in_bf16, out_e4m3, n, (hipStream_t)stream),
+                             "quantize_query launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
+static csa2_status check_index_common(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
+                                      const float* head_w, const int32_t* n_visible, int B, int T,
+                                      int n_max) {
+  REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  REQUIRE((int64_t)B * T <= 65535, CSA2_ERR_UNSUPPORTED, "B*T must be <= 65535");
+  REQUIRE(n_max >= 0, CSA2_ERR_INVALID_ARG, "n_max must be >= 0");
+  REQUIRE(k_rows >= n_max && k_rows < ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "need n_max <= k_rows_per_seq < 2^31 (n_max %d, k_rows %lld)", n_max, (long long)k_rows);
+  REQUIRE_PTR(idx_k);
+  REQUIRE_PTR(idx_q);
+  REQUIRE_PTR(head_w);
+  REQUIRE_PTR(n_visible);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                              const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                              float* scores, void* stream) {
+  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  if (st != CSA2_OK) return st;
+  REQUIRE_PTR(scores);
+  if (n_max == 0) return ok();
+  const FullPlan p = plan_full(B, T, n_max, 1, 1);
+  st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+                                       scores, nullptr, p.nb_max, nullptr, p.chunk, p.n_wg, (hipStream_t)stream),
+                 "index scan launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
+size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k) {
+  (void)block_size;
+  if (B < 1 || T < 1 || n_max < 0 || pool_blocks < 0 || top_k < 1) return 0;
+  return carve_full(nullptr, plan_full(B, T, n_max, pool_blocks, top_k), n_max, nullptr);
+}
+
+csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k, int32_t* pool_pos,
+                            int32_t* pool_len, int32_t* topk_idx, float* topk_score, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  if (st != CSA2_OK) return st;
+  REQUIRE(block_size == csa2::kBlock, CSA2_ERR_UNSUPPORTED, "block_size must be 8 (got %d)", block_size);
+  REQUIRE(top_k >= 1 && top_k <= csa2::kMaxTopK, CSA2_ERR_UNSUPPORTED, "top_k must be in [1, %d]", csa2::kMaxTopK);
+  REQUIRE(pool_blocks >= 0 && (int64_t)pool_blocks * block_size <= csa2::kMaxPool, CSA2_ERR_UNSUPPORTED,
+          "pool_blocks * block_size must be <= %d", csa2::kMaxPool);
+  REQUIRE(pool_blocks == 0 || top_k <= pool_blocks * block_size, CSA2_ERR_INVALID_ARG,
+          "top_k (%d) exceeds the pool capacity (%d)", top_k, pool_blocks * block_size);
+  if (pool_blocks > 0) {
+    REQUIRE_PTR(pool_pos);
+    REQUIRE_PTR(pool_len);
+  }
+  REQUIRE_PTR(topk_idx);
+  REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
+  const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  const size_t need = carve_full(nullptr, p, n_max, nullptr);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  FullWs w;
+  carve_full(workspace, p, n_max, &w);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* pp = p.internal_pool ? w.pool_pos : pool_pos;
+  int32_t* pl = p.internal_pool ? w.pool_len : pool_len;
+  if (n_max > 0) {
+    st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+                                         w.scores, w.blkkey, p.nb_max, w.wg_minmax, p.chunk, p.n_wg, s),
+                   "index scan launch");
+    if (st != CSA2_OK) return st;
+  }
+  st = hip_check(csa2::launch_pool_select(w.blkkey, p.nb_max, n_visible, n_max, p.P, w.wg_minmax, p.n_wg,
+                                          pp, p.cap, pl, p.Q, s),
+                 "pool select launch");
+  if (st != CSA2_OK) return st;
+  st = hip_check(csa2::launch_topk(pp, pl, p.cap, n_max, w.scores, n_max > 0 ? n_max : 1, true, p.Q, p.Q,
+                                   top_k, topk_idx, topk_score, s),
+                 "top-k launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
+size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k) {
+  (void)top_k;
+  if (L < 1 || B < 1 || T < 1 || pool_cap < 1) return 0;
+  return align_up((size_t)L * B * T * pool_cap * sizeof(float));
+}
+
+csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                         const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
+                         int pool_cap, int L, int B, int T, int top_k, int32_t* topk_idx,
+                         float* topk_score, void* workspace, size_t ws_bytes, void* stream) {
+  REQUIRE(L >= 1 && B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "L, B and T must be >= 1");
+  REQUIRE((int64_t)L * B * T <= 65535, CSA2_ERR_UNSUPPORTED, "L*B*T must be <= 65535");
+  REQUIRE(k_rows_per_seq >= 1 && k_rows_per_seq < ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+          "k_rows_per_seq must be in [1, 2^31)");
+  REQUIRE(pool_cap >= 1 && pool_cap <= csa2::kMaxPool, CSA2_ERR_UNSUPPORTED, "pool_cap must be in [1, %d]", csa2::kMaxPool);
+  REQUIRE(top_k >= 1 && top_k <= csa2::kMaxTopK, CSA2_ERR_UNSUPPORTED, "top_k must be in [1, %d]", csa2::kMaxTopK);
+  REQUIRE(top_k <= pool_cap, CSA2_ERR_INVALID_ARG, "top_k (%d) exceeds pool_cap (%d)", top_k, pool_cap);
+  REQUIRE_PTR(idx_k);
+  REQUIRE_PTR(idx_q);
+  REQUIRE_PTR(head_w);
+  REQUIRE_PTR(pool_pos);
+  REQUIRE_PTR(pool_len);
+  REQUIRE_PTR(topk_idx);
+  REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
+  const size_t need = csa2_reindex_workspace(L, B, T, pool_cap, top_k);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  const int Q = B * T;
+  hipStream_t s = (hipStream_t)stream;
+  float* ri = (float*)workspace;
+  const int chunk = csa2::ri_chunk_slots(pool_cap, L * Q);
+  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, k_rows_per_seq, idx_q, head_w, pool_pos, pool_len,
+                                                   pool_cap, L, Q, T, ri, chunk, s),
+                             "reindex score launch");
+  if (st != CSA2_OK) return st;
+  st = hip_check(csa2::launch_topk(pool_pos, pool_len, pool_cap, k_rows_per_seq, ri, pool_cap, false, L * Q, Q,
+                                   top_k, topk_idx, topk_score, s),
+                 "top-k launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
+size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int S) {
+  (void)L; (void)B; (void)T; (void)H; (void)top_k; (void)S;
+  return 0;
+}
+
+csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t kv_rows_per_seq,
+                             const uint16_t* q, const int32_t* idx_sets, const int32_t* layer_set, int S,
+                             const uint8_t* swa_kv, int swa_rows, const int32_t* swa_end, int swa_window,
+                             int L, int B, int T, int H, int top_k, float softmax_scale, uint16_t* out,
+                             float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  REQUIRE(L >= 1 && L <= csa2::kMaxLayers, CSA2_ERR_UNSUPPORTED, "L must be in [1, %d]", csa2::kMaxLayers);
+  REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1");
+  REQUIRE((int64_t)L * B * T <= 65535, CSA2_ERR_UNSUPPORTED, "L*B*T must be <= 65535");
+  REQUIRE(H >= 16 && H % 16 == 0 && H <= 1024, CSA2_ERR_UNSUPPORTED, "H must be a multiple of 16 in [16, 1024]");
+  REQUIRE(top_k >= 1 && top_k <= csa2::kMaxTopK, CSA2_ERR_UNSUPPORTED, "top_k must be in [1, %d]", csa2::kMaxTopK);
+  REQUIRE(S >= 1, CSA2_ERR_INVALID_ARG, "S must be >= 1");
+  REQUIRE(swa_window >= 0 && swa_window <= 4096, CSA2_ERR_UNSUPPORTED, "swa_window must be in [0, 4096]");
+  REQUIRE(swa_rows >= 0, CSA2_ERR_INVALID_ARG, "swa_rows must be >= 0");
+  REQUIRE(kv_rows_per_seq >= 1, CSA2_ERR_INVALID_ARG, "kv_rows_per_seq must be >= 1");
+  REQUIRE(layer_set != nullptr, CSA2_ERR_INVALID_ARG, "layer_set (host array) must be non-null");
+  REQUIRE(softmax_scale > 0.f, CSA2_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  REQUIRE_PTR(kv_codes);
+  REQUIRE_PTR(kv_scales);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(idx_sets);
+  REQUIRE_PTR(swa_end);
+  REQUIRE_PTR(out);
+  REQUIRE(swa_rows == 0 || (swa_kv != nullptr && aligned16(swa_kv)), CSA2_ERR_INVALID_ARG,
+          "swa_kv must be a 16-byte aligned device pointer");
+  REQUIRE(lse == nullptr || aligned16(lse), CSA2_ERR_INVALID_ARG, "lse must be 16-byte aligned");
+  csa2::LayerSets sets;
+  for (int l = 0; l < L; ++l) {
+    REQUIRE(layer_set[l] >= 0 && layer_set[l] < S, CSA2_ERR_INVALID_ARG, "layer_set[%d] = %d is not in [0, %d)",
+            l, layer_set[l], S);
+    sets.set[l] = layer_set[l];
+  }
+  csa2_status st = hip_check(csa2::launch_sparse_attn(kv_codes, kv_scales, kv_rows_per_seq, q, idx_sets, sets,
+                                                      swa_rows ? swa_kv : kv_codes, swa_rows, swa_end,
+                                                      swa_window, L, B, T, H, top_k, softmax_scale, out, lse,
+                                                      (hipStream_t)stream),
+                             "sparse attention launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// Device-side building blocks shared by the CSA2 kernels (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+constexpr int kIdxHeads = 32;
+constexpr int kIdxDim = 128;
+constexpr int kKvDim = 512;
+constexpr int kKvCodeBytes = 256;
+constexpr int kKvScaleBytes = 32;
+constexpr int kBlock = 8;          // positions per pool block
+constexpr int kMaxPool = 16384;    // largest pool (2048 blocks x 8 positions)
+constexpr int kMaxTopK = 2048;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// D = A(16x32) * B(32x16) + C, bf16 inputs, fp32 accumulate.
+// Lane l holds A row (l % 16), k = 8*(l/16) .. +7; B column (l % 16), same k;
+// C column (l % 16), rows 4*(l/16) .. +3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two E4M3 bytes (the low or high 16 bits of `w`) -> two bf16 (exact: E4M3 has 4 significant
+// bits and its exponent range lies inside bf16's).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 E4M3 bytes (two dwords) -> 8 bf16 (one MFMA operand), byte order preserved.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t d0, uint32_t d1) {
+  u32x4 r;
+  r.x = e4m3x2_to_bf16x2<false>(d0);
+  r.y = e4m3x2_to_bf16x2<true>(d0);
+  r.z = e4m3x2_to_bf16x2<false>(d1);
+  r.w = e4m3x2_to_bf16x2<true>(d1);
+  return r;
+}
+
+// Two E2M1 codes (byte SEL of `w`, low nibble first) times an E4M3 scale -> two bf16.
+// The hardware conversion is used with a unit scale only: its scale operand contributes just
+// its power-of-two exponent.  The fp32 product code * scale is exact (at most 6 significant
+// bits, magnitude within [2^-10, 2688]), so its upper 16 bits are the exact bf16 value.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_scaled_to_bf16x2(uint32_t w, float scale) {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  const uint32_t a = __float_as_uint(v.x * scale), b = __float_as_uint(v.y * scale);
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+// E4M3 byte -> float, exact (software decode; used for scales and the query path).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c >> 7) & 1u, e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 0) v = (float)m * 0.001953125f;                 // m/8 * 2^-6 = m * 2^-9
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20)); // (1 + m/8) * 2^(e-7)
+  if (e == 15 && m == 7) v = __uint_as_float(0x7fc00000u);
+  return s ? -v : v;
+}
+
+// float -> E4M3 byte: round to nearest even, saturate to +-448, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                       // NaN
+  float fa = __uint_as_float(a);
+  if (fa >= 448.0f) return sign | 0x7eu;                    // saturate (includes +-inf)
+  if (fa < 0.015625f) {                                     // below 2^-6: subnormal grid 2^-9
+    float q = __builtin_rintf(fa * 512.0f);                 // exact scaling, round half even
+    return sign | (uint32_t)q;                              // q == 8 is the code of 2^-6
+  }
+  uint32_t exp = (a >> 23) - 127u + 7u;                     // E4M3 exponent field (1..15)
+  uint32_t mant = a & 0x7fffffu;
+  uint32_t m3 = mant >> 20, rem = mant & 0xfffffu;
+  uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (m3 & 1u));
+  uint32_t code = (exp << 3) + m3 + up;                     // a carry moves into the exponent
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving 32-bit key of a float score (larger score -> larger key; -0 counts as +0).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Ranking key of (score key, index): larger key first, then smaller index first.
+__device__ __forceinline__ uint64_t rank_key(uint32_t key, uint32_t idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t rank_key_index(uint64_t rk) {
+  return 0xffffffffu - (uint32_t)(rk & 0xffffffffu);
+}
+
+__device__ __forceinline__ int bitlen64(uint64_t x) { return x ? 64 - __clzll(x) : 0; }
+
+}  // namespace csa2

@@ -1,0 +1,142 @@
+/*
+ * csa2.h -- C ABI of the CSA2 decode hot path on MI355X (gfx950).
+ *
+ * The operations follow the DeepSeek-V4.1-Flash pages:
+ *   - blog.4sapi.com, section 2 "CSA2" and its mode table: a Full layer computes its own
+ *     indexer scores and Top-K; a Reindex layer reuses the Full layer's indexer K and main KV
+ *     but re-scores with its own indexer query; a Reuse layer inherits the Top-K indices
+ *     (so it has no entry point here: the caller passes its leader's index set).
+ *   - readance.app, section 4.3, and blog.4sapi.com, section 4 "Hierarchical Sparse Indexer":
+ *     the first Full indexer scans every visible position, filters by block into a shared
+ *     candidate pool (2048 blocks x 8 positions = 16384), Reindex layers pick their Top-512
+ *     inside the pool; the indexer has 32 query heads of dim 128.
+ *   - blog.4sapi.com, section 5 "FP4 KV", and the animattoys.com FP4 section: the main KV is
+ *     FP4 E2M1 with one E4M3 scale per 16 channels and no second-level scale; the sliding
+ *     window (SWA) KV stays FP8.
+ *
+ * Readings fixed by this library where the pages are silent:
+ *   - indexer score s[p] = sum_h w[h] * ReLU(q8[h] . k[p]), one 128-dim E4M3 key per position
+ *     shared by the 32 heads; q8 = the bf16 query rounded to E4M3 (nearest even, saturating
+ *     to +-448, unit scale);
+ *   - block = 8 consecutive positions aligned at 0 (the last may be partial), block score =
+ *     max of its scores; ranking ties go to the lower block / position index; scores rank as
+ *     float32 with -0 equal to +0;
+ *   - index outputs list positions in ascending order with -1 padding;
+ *   - attention: one softmax over the selected main-KV rows and the window's SWA rows,
+ *     keys = values (a shared 512-wide latent), no sink, no bias.
+ *
+ * Conventions for every call:
+ *   - tensor arguments are DEVICE pointers owned by the caller (except where marked host),
+ *     row-major and contiguous; they must be 16-byte aligned;
+ *   - bf16 tensors are passed as uint16_t bit patterns;
+ *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued asynchronously;
+ *   - argument checks run on the host, never read device memory, and return
+ *     CSA2_ERR_INVALID_ARG / CSA2_ERR_UNSUPPORTED / CSA2_ERR_WORKSPACE before anything is
+ *     enqueued; a failed launch returns CSA2_ERR_HIP; csa2_last_error() then describes it;
+ *   - the library keeps no state between calls; concurrent calls need distinct workspaces;
+ *   - device-side data outside its documented range (n_visible beyond n_max, positions
+ *     outside the cache, NaN codes) is clamped or ignored, never read out of bounds, and
+ *     otherwise gives unspecified results.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, misaligned pointer */
+  CSA2_ERR_UNSUPPORTED = 2,   /* a shape this build does not implement */
+  CSA2_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace() size */
+  CSA2_ERR_HIP = 4            /* a HIP launch failed */
+} csa2_status;
+
+#define CSA2_IDX_HEADS 32   /* indexer query heads */
+#define CSA2_IDX_DIM 128    /* indexer head dim = indexer-K row bytes (E4M3) */
+#define CSA2_KV_DIM 512     /* main-KV latent width (keys = values) */
+#define CSA2_KV_CODE_BYTES 256
+#define CSA2_KV_SCALE_BYTES 32
+
+/* Message of the last non-OK status returned on the calling thread ("" if none). */
+const char* csa2_last_error(void);
+
+/* Step A1 on its own: indexer query prep. in_bf16[n] -> out_e4m3[n], round to nearest even,
+ * saturating to +-448, NaN -> 0x7F. csa2_index_full / csa2_reindex apply the same rounding
+ * internally; this entry exists to verify it and for callers that keep E4M3 queries. */
+csa2_status csa2_quantize_query(const uint16_t* in_bf16, uint8_t* out_e4m3, int64_t n, void* stream);
+
+/* Steps A1-A2 on their own: the Full scan's scores without any selection.
+ *   idx_k      [B][k_rows_per_seq][128] E4M3 indexer keys
+ *   idx_q      [B][T][32][128] bf16 indexer queries
+ *   head_w     [B][T][32] float head weights
+ *   n_visible  [B][T] int32 visible positions of each query (clamped to [0, n_max])
+ *   scores     [B][T][n_max] float out; entries at or beyond n_visible are left untouched
+ * Requires n_max <= k_rows_per_seq. */
+csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                              const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                              float* scores, void* stream);
+
+/* Full layer (blog.4sapi.com sec.4; readance.app sec.4.2/4.3): score every visible position,
+ * keep the top `pool_blocks` blocks of `block_size` positions by block score as the candidate
+ * pool, and take the Top-`top_k` positions of the pool.  With pool_blocks == 0 there is no
+ * pool and the Top-K runs over every visible position (an encoder Full layer).
+ *   pool_pos   [B][T][pool_blocks*block_size] int32 out (ascending, -1 after pool_len), or NULL
+ *              when pool_blocks == 0
+ *   pool_len   [B][T] int32 out (pool entries), or NULL when pool_blocks == 0
+ *   topk_idx   [B][T][top_k] int32 out (ascending positions, -1 padded)
+ *   topk_score [B][T][top_k] float out aligned with topk_idx (0 for padding), or NULL
+ *   workspace  device scratch of at least csa2_index_full_workspace(...) bytes
+ * Supported: block_size == 8, 1 <= top_k <= 2048, top_k <= pool_blocks*block_size when
+ * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= k_rows_per_seq < 2^31. */
+size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k);
+csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k,
+                            int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Reindex layers (blog.4sapi.com sec.2 mode table and sec.4; alphalab.site sec."2. CSA2"):
+ * for each of L layers, re-score only the pool positions with the layer's own indexer query
+ * and weights, then take its own Top-`top_k`.  Positions outside the pool are never picked.
+ *   idx_q      [L][B][T][32][128] bf16;  head_w [L][B][T][32] float
+ *   pool_pos   [B][T][pool_cap] int32 positions (entries >= pool_len and negative or
+ *              out-of-range entries are ignored); pool_len [B][T] int32
+ *   topk_idx   [L][B][T][top_k] int32 out; topk_score [L][B][T][top_k] float out or NULL
+ * Supported: 1 <= top_k <= 2048, top_k <= pool_cap <= 16384. */
+size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k);
+csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                         const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
+                         int pool_cap, int L, int B, int T, int top_k,
+                         int32_t* topk_idx, float* topk_score,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Sparse attention of L layers (blog.4sapi.com sec.2 and sec.5; alphalab.site sec."3. FP4"):
+ * layer l attends, per query and head, over the main-KV rows of index set layer_set[l]
+ * (FP4 E2M1 codes x E4M3 per-16-channel scales, dequantised exactly) followed by its own SWA
+ * rows [max(0, swa_end - swa_window), swa_end), with one softmax over both segments.
+ *   kv_codes   [B][kv_rows_per_seq][256] uint8, channel 2i in the low nibble of byte i
+ *   kv_scales  [B][kv_rows_per_seq][32]  uint8 E4M3, scale g covers channels 16g..16g+15
+ *   q          [L][B][T][H][512] bf16 (already rotated)
+ *   idx_sets   [S][B][T][top_k] int32 positions (negative / out-of-range entries are empty)
+ *   layer_set  HOST [L] int32 set id of each layer (a Reuse layer names its leader's set)
+ *   swa_kv     [L][B][swa_rows][512] E4M3 (unit scale)
+ *   swa_end    [B][T] int32 exclusive end row of each query's window (clamped to [0, swa_rows])
+ *   out        [L][B][T][H][512] bf16 out;  lse [L][B][T][H] float out (natural log) or NULL;
+ *              a query with no rows at all gets out = 0 and lse = -inf
+ * Supported: H % 16 == 0, 1 <= top_k <= 2048, 0 <= swa_window <= 4096. */
+size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int S);
+csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t kv_rows_per_seq,
+                             const uint16_t* q, const int32_t* idx_sets, const int32_t* layer_set, int S,
+                             const uint8_t* swa_kv, int swa_rows, const int32_t* swa_end, int swa_window,
+                             int L, int B, int T, int H, int top_k, float softmax_scale,
+                             uint16_t* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,83 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point include/csa2.h
+declares, and rejects bad arguments on the host before anything is enqueued."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def H():
+    import hierarchical_kv_indexer_amd as H
+    if not os.path.exists(H.LIB_PATH):
+        from hierarchical_kv_indexer_amd import build
+        build.build()
+    H.lib()
+    return H
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(H):
+    names = declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(H.lib(), n), n
+    assert set(names) == {e[0] for e in H.EXPORTS}
+
+
+def test_workspace_sizes(H):
+    assert H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512) >= (1 << 20) * 4 + (1 << 17) * 4
+    assert H.csa2_reindex_workspace(4, 1, 1, 16384, 512) >= 4 * 16384 * 4
+    assert H.csa2_index_full_workspace(0, 1, 10, 8, 4, 4) == 0
+
+
+FAKE = 1 << 20   # a 16-byte aligned non-null value; validation fails before it is used
+
+
+def expect(H, status, fn, *args):
+    with pytest.raises(H.Csa2Error) as e:
+        fn(*args)
+    assert e.value.status == status, str(e.value)
+
+
+def test_index_full_rejects(H):
+    ok = [FAKE, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30]
+    def call(**ch):
+        a = list(ok)
+        names = ["idx_k", "k_rows", "idx_q", "head_w", "nvis", "B", "T", "n_max", "block", "P", "K",
+                 "pool_pos", "pool_len", "topk_idx", "topk_score", "ws", "ws_bytes"]
+        for k, v in ch.items():
+            a[names.index(k)] = v
+        return lambda: H.csa2_index_full(*a)
+    expect(H, 1, call(idx_k=None))
+    expect(H, 1, call(idx_q=FAKE + 4))                 # misaligned
+    expect(H, 2, call(block=16))
+    expect(H, 1, call(K=600))                          # top_k > pool capacity
+    expect(H, 2, call(K=4096))
+    expect(H, 2, call(P=4096))                         # pool > 16384 positions
+    expect(H, 1, call(n_max=5000))                     # n_max > k_rows
+    expect(H, 3, call(ws_bytes=16))
+    expect(H, 3, call(ws=None))
+    expect(H, 1, call(B=0))
+
+
+def test_reindex_and_attention_reject(H):
+    expect(H, 1, lambda: H.csa2_reindex(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 512, 1, 1, 1, 1024, FAKE, None, FAKE, 1 << 30))
+    expect(H, 2, lambda: H.csa2_reindex(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 20000, 1, 1, 1, 512, FAKE, None, FAKE, 1 << 30))
+    expect(H, 3, lambda: H.csa2_reindex(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 1024, 1, 1, 1, 512, FAKE, None, FAKE, 8))
+    base = [FAKE, FAKE, 100, FAKE, FAKE, [0, 0], 1, FAKE, 128, FAKE, 128, 2, 1, 1, 16, 512, 0.04, FAKE, None, None, 0]
+    a = list(base); a[14] = 24                                       # H not a multiple of 16
+    expect(H, 2, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[5] = [0, 3]                                    # layer_set out of range
+    expect(H, 1, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[16] = 0.0
+    expect(H, 1, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[11] = 65; a[5] = [0] * 65
+    expect(H, 2, lambda: H.csa2_sparse_attn(*a))

@@ -1,0 +1,276 @@
+"""GPU parity of the HIP library (through its C ABI) against the CPU oracle, stage by stage,
+on seeded inputs that span several tiles with ragged tails, plus exhaustive format checks
+and edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import csa2 as O
+from oracle import formats as F
+from tests import gpu_chain as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import hierarchical_kv_indexer_amd as H
+    H.lib()
+
+
+def small(name="tiny_4k", **kw):
+    return workloads.small_variant(workloads.WORKLOADS[name], **kw)
+
+
+# ------------------------------------------------------------------ formats
+
+def test_quantize_query_all_bf16_bit_exact():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    out = G.empty((65536,), torch.uint8)
+    import hierarchical_kv_indexer_amd as H
+    H.csa2_quantize_query(G.dev(bits), out, 65536)
+    got = G.host(out)
+    ref = F.e4m3_from_value(F.bf16_value(bits))
+    nan = np.isnan(F.bf16_value(bits))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7F) == 0x7F)
+
+
+def test_scan_every_e4m3_code_exact():
+    # rows r = 0..255 hold code r in channel 0; query t=0 has +1 and t=1 has -1 there (head 0)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    k8 = np.zeros((1, 256, 128), np.uint8)
+    k8[0, :, 0] = codes
+    qf = np.zeros((1, 2, 32, 128), np.float32)
+    qf[0, 0, 0, 0], qf[0, 1, 0, 0] = 1.0, -1.0
+    w = np.zeros((1, 2, 32), np.float32)
+    w[:, :, 0] = 1.0
+    inp = {"idx_k": k8, "idx_q": workloads.to_bf16_bits(qf), "head_w": w,
+           "n_visible": np.full((1, 2), 256, np.int32)}
+    s = G.gpu_index_scores(inp, 1, 2, 256)
+    v = F.e4m3_value(codes)
+    assert np.array_equal(s[0, 0], np.maximum(v, 0).astype(np.float32))
+    assert np.array_equal(s[0, 1], np.maximum(-v, 0).astype(np.float32))
+
+
+def test_fp4_dequant_every_code_and_scale_exact():
+    # one main row per query, no window: the output is the dequantised row itself
+    rows = 8
+    codes = np.zeros((1, rows, 256), np.uint8)
+    ch = np.arange(512)
+    nib = (ch % 16).astype(np.uint8)
+    codes[0, :] = nib[0::2] | (nib[1::2] << 4)
+    sc = (np.arange(rows * 32) % 256).astype(np.uint8).reshape(1, rows, 32)
+    sc[(sc & 0x7F) == 0x7F] = 0x38
+    w = workloads.Workload("dq", 1, B=1, T=rows, N=rows, H=16, layer_set=(0,), n_reindex=0,
+                           top_k=1, swa_window=0)
+    inp = {"kv_codes": codes, "kv_scales": sc,
+           "q": workloads.to_bf16_bits(np.random.default_rng(0).standard_normal((1, 1, rows, 16, 512), dtype=np.float32)),
+           "swa": np.zeros((1, 1, 1, 512), np.uint8), "swa_end": np.zeros((1, rows), np.int32)}
+    idx = np.arange(rows, dtype=np.int32).reshape(1, 1, rows, 1)
+    out, lse = G.gpu_attention(inp, w, idx)
+    ref = F.kv_row_values(codes[0], sc[0])
+    got = F.bf16_value(out[0, 0])          # [rows][16][512]
+    for r in range(rows):
+        assert np.array_equal(got[r], np.broadcast_to(ref[r], (16, 512))), f"row {r}"
+
+
+# ------------------------------------------------------------------ indexer stages
+
+@pytest.mark.parametrize("B,T,N,nv", [(1, 1, 4096, None), (2, 3, 4093, [4093, 4000, 17, 0, 8, 1])])
+def test_index_scores_parity(B, T, N, nv):
+    w = small(B=B, T=T, N=N, seed=2000 + N)
+    inp = workloads.make_inputs(w, with_attention=False)
+    if nv is not None:
+        inp["n_visible"] = np.array(nv, np.int32).reshape(B, T)
+    s = G.gpu_index_scores(inp, B, T, N)
+    for b in range(B):
+        for t in range(T):
+            n = int(inp["n_visible"][b, t])
+            q8 = O.quantize_query(inp["idx_q"][b, t])
+            ref = O.indexer_scores(inp["idx_k"][b, :n], q8, inp["head_w"][b, t])
+            bound = G.score_abs_bound(inp["idx_k"][b, :n], inp["idx_q"][b, t], inp["head_w"][b, t])
+            G.assert_scores_close(s[b, t, :n], ref, bound, f"b{b} t{t}")
+            assert np.all(np.isnan(s[b, t, n:])), "scores beyond n_visible must be untouched"
+
+
+def check_full(w, inp, gpu, b, t):
+    n = int(inp["n_visible"][b, t])
+    ref = O.full_layer(inp["idx_k"][b], inp["idx_q"][b, t], inp["head_w"][b, t], n, w.block,
+                       w.pool_blocks, w.top_k)
+    s = ref["scores"]
+    nd = 0
+    if w.pool_blocks:
+        nd += G.assert_pool_equiv(gpu["pool_pos"][b, t], int(gpu["pool_len"][b, t]), ref["pool"],
+                                  ref["scores32"], n, w.block, w.pool_blocks, f"pool b{b} t{t}")
+    nd += G.assert_topk_equiv(gpu["topk"][b, t], ref["topk"], lambda p: s[p], f"topk b{b} t{t}")
+    g = gpu["topk"][b, t]
+    sel = g[g >= 0]
+    bound = G.score_abs_bound(inp["idx_k"][b][sel], inp["idx_q"][b, t], inp["head_w"][b, t])
+    G.assert_scores_close(gpu["topk_score"][b, t][:len(sel)], s[sel], bound, "topk_score")
+    assert np.all(gpu["topk_score"][b, t][len(sel):] == 0)
+    return ref, nd
+
+
+@pytest.mark.parametrize("N,P,K,nv", [
+    (4096, 64, 64, None),            # tiny decode workload
+    (20003, 128, 256, None),         # ragged, several scan WGs
+    (5000, 64, 512, [5000, 300, 511, 0]),   # n_vis < K, n_vis = 0, pool larger than nb
+])
+def test_index_full_parity(N, P, K, nv):
+    T = 1 if nv is None else len(nv)
+    w = small(T=T, N=N, pool_blocks=P, top_k=K, seed=3000 + N)
+    inp = workloads.make_inputs(w, with_attention=False)
+    if nv is not None:
+        inp["n_visible"] = np.array(nv, np.int32).reshape(1, T)
+    gpu = G.gpu_index_full(inp, 1, T, N, P, K)
+    for t in range(T):
+        check_full(w, inp, gpu, 0, t)
+
+
+def test_index_full_no_pool_dense_topk():
+    w = small(T=3, N=9000, pool_blocks=0, top_k=200, seed=31)
+    inp = workloads.make_inputs(w, with_attention=False)
+    inp["n_visible"] = np.array([[9000, 4321, 100]], np.int32)
+    gpu = G.gpu_index_full(inp, 1, 3, 9000, 0, 200)
+    for t in range(3):
+        check_full(w, inp, gpu, 0, t)
+
+
+def test_index_full_ties():
+    # many equal keys: identical rows -> identical scores; ranking must fall back to index order
+    w = small(N=3000, pool_blocks=40, top_k=100, seed=41)
+    inp = workloads.make_inputs(w, with_attention=False)
+    k = inp["idx_k"]
+    k[0, 1000:2000] = k[0, 5]            # 1000 identical keys
+    gpu = G.gpu_index_full(inp, 1, 1, 3000, 40, 100)
+    ref, nd = check_full(w, inp, gpu, 0, 0)
+    assert np.array_equal(gpu["topk"][0, 0], ref["topk"])   # exact ties resolve identically
+
+
+def test_reindex_parity_on_oracle_pool():
+    w = small(T=2, N=30000, pool_blocks=256, top_k=300, n_reindex=3, seed=51)
+    inp = workloads.make_inputs(w, with_attention=False)
+    cap = w.pool_cap
+    pool_pos = np.full((1, 2, cap), -1, np.int32)
+    pool_len = np.zeros((1, 2), np.int32)
+    refs = []
+    for t in range(2):
+        f = O.full_layer(inp["idx_k"][0], inp["idx_q"][0, t], inp["head_w"][0, t], w.N, w.block,
+                         w.pool_blocks, w.top_k)
+        pool_pos[0, t, :len(f["pool"])] = f["pool"]
+        pool_len[0, t] = len(f["pool"])
+        refs.append(f["pool"])
+    gpu = G.gpu_reindex(inp, 1, 2, pool_pos, pool_len, w.top_k)
+    for l in range(3):
+        for t in range(2):
+            r = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][l, 0, t], inp["ri_w"][l, 0, t], refs[t], w.top_k)
+            sc = dict(zip(refs[t].tolist(), r["scores"].tolist()))
+            G.assert_topk_equiv(gpu["topk"][l, 0, t], r["topk"], lambda p: sc[p], f"ri l{l} t{t}")
+            sel = gpu["topk"][l, 0, t]
+            assert set(sel[sel >= 0].tolist()) <= set(refs[t].tolist())
+
+
+def test_reindex_user_pools_with_invalid_entries():
+    w = small("reindex_pool_256k", T=4, N=50000, user_pool=3000, top_k=512, seed=61)
+    inp = workloads.make_inputs(w, with_attention=False)
+    pp = inp["pool_pos"].copy()
+    pl = inp["pool_len"].copy()
+    pp[0, 1, 10] = -5
+    pp[0, 1, 11] = 10 ** 7            # out of range: ignored
+    pl[0, 2] = 400                    # fewer than top_k
+    pl[0, 3] = 0
+    gpu = G.gpu_reindex(inp, 1, 4, pp, pl, 512)
+    for t in range(4):
+        pool = pp[0, t, :pl[0, t]]
+        pool = pool[(pool >= 0) & (pool < w.N)]
+        r = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][0, 0, t], inp["ri_w"][0, 0, t], pool, 512)
+        sc = dict(zip(pool.tolist(), r["scores"].tolist()))
+        G.assert_topk_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"user pool t{t}")
+
+
+# ------------------------------------------------------------------ attention
+
+def test_attention_parity_on_oracle_sets():
+    w = small(B=2, T=2, N=3000, H=32, layer_set=(0, 0, 1), n_reindex=1, pool_blocks=64, top_k=200, seed=71)
+    inp = workloads.make_inputs(w)
+    sets = np.full((2, 2, 2, 200), -1, np.int32)
+    rng = np.random.default_rng(5)
+    for s in range(2):
+        for b in range(2):
+            for t in range(2):
+                n = [200, 137, 0, 64][(s + 2 * b + t) % 4]     # ragged and empty sets
+                sets[s, b, t, :n] = np.sort(rng.choice(w.N, n, replace=False))
+    inp["swa_end"] = np.array([[128, 50], [0, 128]], np.int32)   # partial and empty windows
+    out, lse = G.gpu_attention(inp, w, sets)
+    worst = 0.0
+    for l in range(w.L):
+        for b in range(2):
+            for t in range(2):
+                rows = O.attention_rows(inp["kv_codes"][b], inp["kv_scales"][b], sets[w.layer_set[l], b, t],
+                                        inp["swa"][l, b], int(inp["swa_end"][b, t]), w.swa_window)
+                o, ls = O.attention(inp["q"][l, b, t], rows, 1 / math.sqrt(512))
+                worst = max(worst, G.assert_attention_close(out[l, b, t], o, f"l{l} b{b} t{t}"))
+                if rows.shape[0] == 0:
+                    assert np.all(np.isneginf(lse[l, b, t]))
+                else:
+                    assert np.allclose(lse[l, b, t], ls, rtol=1e-3, atol=1e-3)
+    print(f"attention worst rel err {worst:.3g}")
+    assert worst < 1e-2
+
+
+# ------------------------------------------------------------------ whole chain
+
+def run_chain_and_check(w, inp, queries):
+    B, T = w.B, w.T
+    gpu_full = G.gpu_index_full(inp, B, T, w.N, w.pool_blocks, w.top_k) if w.has_full else None
+    if not w.has_full:
+        pool_pos, pool_len = inp["pool_pos"], inp["pool_len"]
+    elif w.pool_blocks:
+        pool_pos, pool_len = gpu_full["pool_pos"], gpu_full["pool_len"]
+    else:
+        pool_pos = pool_len = None
+    gpu_ri = G.gpu_reindex(inp, B, T, pool_pos, pool_len, w.top_k) if w.n_reindex else None
+    sets = []
+    if w.has_full:
+        sets.append(gpu_full["topk"])
+    if w.n_reindex:
+        sets += [gpu_ri["topk"][r] for r in range(w.n_reindex)]
+    sets = np.stack(sets)
+    out, lse = G.gpu_attention(inp, w, sets)
+    for (b, t) in queries:
+        if w.has_full:
+            check_full(w, inp, gpu_full, b, t)
+        gp = pool_pos[b, t, :pool_len[b, t]] if pool_pos is not None else None
+        ref = O.query_chain(inp, w, b, t, pool_override=gp, idx_sets_override=sets[:, b, t])
+        for r in range(w.n_reindex):
+            sc = dict(zip(gp.tolist(), ref["reindex"][r]["scores"].tolist()))
+            G.assert_topk_equiv(gpu_ri["topk"][r, b, t], ref["reindex"][r]["topk"], lambda p: sc[p], f"ri{r}")
+        for l in range(w.L):
+            G.assert_attention_close(out[l, b, t], ref["attn_out"][l], f"attn l{l} b{b} t{t}")
+    return out
+
+
+def test_chain_tiny_decode():
+    w = workloads.WORKLOADS["tiny_4k"]
+    inp = workloads.make_inputs(w)
+    run_chain_and_check(w, inp, [(0, 0)])
+
+
+def test_chain_planted_64k():
+    w = small("decode_1m", N=65536, seed=81)
+    inp = workloads.make_inputs(w)
+    run_chain_and_check(w, inp, [(0, 0)])
+    g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
+    assert np.isin(inp["planted_pos"], g["topk"][0, 0]).all()
+
+
+def test_chain_prefill_small():
+    w = small("prefill_4k_64k", T=64, N=4096, prefill_tokens=8192, seed=91)
+    inp = workloads.make_inputs(w)
+    run_chain_and_check(w, inp, [(0, 0), (0, 31), (0, 63)])
