@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Throughput of the CSA2 decode hot path on one MI355X.
+
+One step = one pass of the whole path for one batch of synthetic input: the Full indexer scan
+over every visible position, the block candidate pool and Top-K, every Reindex layer (re-score
+the pool with its own query, Top-K) and sparse attention for every attention layer (FP4 main
+KV rows of the layer's index set merged with its FP8 window).  Reuse layers run attention on
+their leader's index set.  Default workload: batch 1 decode over a 1M-entry context
+(Full + 4 Reindex + 15 Reuse layers, 16 attention heads).
+
+Inputs are resident in HBM before timing.  The context (indexer K and main KV) is replicated
+``--replicas`` times at distinct addresses and steps rotate over the replicas, so the 256 MB
+Infinity Cache cannot serve the 128 MiB indexer-K stream from one step to the next.  Each step
+is replayed from HIP graphs captured once per replica (the scan in one graph, the rest in a
+second one, with timing events between them).
+
+Prints one JSON line (metric, value in queries/s, roofline of the scan kernel, CPU oracle
+baseline) on stdout; a per-stage breakdown goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode queries/s at 1M ctx (Full+Reindex+attn); achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+SCAN_SOURCES = ("hierarchical_kv_indexer_amd/csrc/scan.hip", "hierarchical_kv_indexer_amd/csrc/common.hpp")
+PMC_FILE = os.path.join(ROOT, "profiles", "k_idx_scan_decode_1m_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha1()
+    for p in SCAN_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def scan_algorithmic_bytes(w) -> int:
+    """Bytes the Full scan must move per launch: every visible indexer-K row (128 B), the
+    indexer queries (32x128 bf16), head weights (32 fp32) and n_visible of each query."""
+    q = w.B * w.T
+    rows = int(w.n_visible().astype("int64").sum())
+    return rows * 128 + q * (32 * 128 * 2 + 32 * 4 + 4)
+
+
+def step_algorithmic_bytes(w) -> int:
+    """Bytes one whole step must move (documented per term in the design notes)."""
+    q = w.B * w.T
+    K = w.top_k
+    b = scan_algorithmic_bytes(w) if w.has_full else 0
+    if w.has_full and w.pool_blocks:
+        b += q * (w.pool_cap * 4 + 4)                      # pool written
+    b += (q * K * 4) if w.has_full else 0                  # Full Top-K written
+    for _ in range(w.n_reindex):
+        b += q * (w.pool_cap * 4 + w.pool_cap * 128 + 32 * 128 * 2 + 32 * 4 + K * 4)
+    sets = w.n_sets
+    b += q * sets * K * (4 + 288)                          # each index set: indices + gathered FP4 rows
+    b += q * w.L * (w.swa_window * 512 + 2 * w.H * 512 * 2)  # window rows, q in, out
+    return b
+
+
+def traffic_from_profile():
+    """HBM bytes per scan launch from the committed rocprofv3 counter summary, or None when the
+    scan kernel's sources changed since the counters were taken."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha1") != scan_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds: float):
+    """The oracle, as it stands, on this host: the whole chain for query (0, 0), repeated."""
+    from oracle import csa2 as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.query_chain(inp, w, 0, 0)
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and n >= 2) or n >= 50:
+            break
+    return {"value": n / el, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} runs of the full chain (Full scan of {w.N} positions, pool, Top-{w.top_k}, "
+                      f"{w.n_reindex} Reindex layers, {w.L} attention layers) for one query of "
+                      f"{w.name}, {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_1m")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding plan is written up with the design notes).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import hierarchical_kv_indexer_amd as H
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if not w.has_full:
+        print("bench.py times workloads with a Full layer", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H.lib()
+    t_gen = time.perf_counter()
+    inp = workloads.make_inputs(w)
+    log(f"[bench] generated {w.name} inputs in {time.perf_counter() - t_gen:.1f} s")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    B, T, N, K, L, Hh, R = w.B, w.T, w.N, w.top_k, w.L, w.H, args.replicas
+    Q = B * T
+    k_rep = [up(inp["idx_k"]) for _ in range(R)]
+    codes_rep = [up(inp["kv_codes"]) for _ in range(R)]
+    scales_rep = [up(inp["kv_scales"]) for _ in range(R)]
+    idx_q, head_w, n_vis = up(inp["idx_q"]), up(inp["head_w"]), up(inp["n_visible"])
+    ri_q, ri_w = up(inp["ri_q"]), up(inp["ri_w"])
+    qa, swa, swa_end = up(inp["q"]), up(inp["swa"]), up(inp["swa_end"])
+    S = w.n_sets
+    sets = torch.full((S, B, T, K), -1, dtype=torch.int32, device=dev)
+    pool_pos = torch.empty((B, T, w.pool_cap), dtype=torch.int32, device=dev)
+    pool_len = torch.empty((B, T), dtype=torch.int32, device=dev)
+    out = torch.empty((L, B, T, Hh, 512), dtype=torch.int16, device=dev)
+    lse = torch.empty((L, B, T, Hh), dtype=torch.float32, device=dev)
+    ws_full_b = H.csa2_index_full_workspace(B, T, N, w.block, w.pool_blocks, K)
+    ws_ri_b = H.csa2_reindex_workspace(max(w.n_reindex, 1), B, T, w.pool_cap, K)
+    ws_attn_b = H.csa2_sparse_attn_workspace(L, B, T, Hh, K, w.swa_window)
+    ws_full = torch.empty((ws_full_b,), dtype=torch.uint8, device=dev)
+    ws_attn = torch.empty((max(ws_attn_b, 1),), dtype=torch.uint8, device=dev)
+    ws_ri = torch.empty((ws_ri_b,), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(512)
+
+    def scan(r):
+        H.csa2_index_scan(k_rep[r], N, idx_q, head_w, n_vis, B, T, N, w.block, w.pool_blocks, K,
+                          ws_full, ws_full_b)
+
+    def select():
+        H.csa2_index_select(n_vis, B, T, N, w.block, w.pool_blocks, K, pool_pos, pool_len, sets[0],
+                            None, ws_full, ws_full_b)
+
+    def reindex(r):
+        if w.n_reindex:
+            H.csa2_reindex(k_rep[r], N, ri_q, ri_w, pool_pos, pool_len, w.pool_cap, w.n_reindex, B, T, K,
+                           sets[1:], None, ws_ri, ws_ri_b)
+
+    def attend(r):
+        H.csa2_sparse_attn(codes_rep[r], scales_rep[r], N, qa, sets, list(w.layer_set), S, swa, w.swa_rows,
+                           swa_end, w.swa_window, L, B, T, Hh, K, scale, out, lse, ws_attn, ws_attn_b)
+
+    def rest(r):
+        select()
+        reindex(r)
+        attend(r)
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        # eager warm-up and a per-stage breakdown (events on the launch stream)
+        for r in range(R):
+            scan(r); rest(r)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        stage_ms = np.zeros(4)
+        reps = 10
+        for i in range(reps):
+            r = i % R
+            ev[0].record(); scan(r); ev[1].record(); select(); ev[2].record(); reindex(r); ev[3].record()
+            attend(r); ev[4].record()
+            ev[4].synchronize()
+            stage_ms += [ev[j].elapsed_time(ev[j + 1]) for j in range(4)]
+        stage_ms /= reps
+        log("[bench] eager stage ms: scan %.4f  select %.4f  reindex %.4f  attention %.4f" % tuple(stage_ms))
+
+        graphs = None
+        if not args.no_graph:
+            graphs = []
+            for r in range(R):
+                g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g1, stream=stream):
+                    scan(r)
+                with torch.cuda.graph(g2, stream=stream):
+                    rest(r)
+                graphs.append((g1, g2))
+
+        def run_step(i, e0=None, e1=None):
+            r = i % R
+            if e0 is not None:
+                e0.record()
+            if graphs:
+                graphs[r][0].replay()
+            else:
+                scan(r)
+            if e1 is not None:
+                e1.record()
+            if graphs:
+                graphs[r][1].replay()
+            else:
+                rest(r)
+
+        for i in range(args.warmup):
+            run_step(i)
+        e_scan = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            run_step(i, *e_scan[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall = t1 - t0
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in e_scan]))
+    ms_per_step = wall * 1e3 / args.steps
+
+    # parity spot check of the timed outputs against the oracle on this query (cheap: C3 is B=1)
+    value = args.steps * Q / wall
+    scan_bytes = scan_algorithmic_bytes(w)
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    step_bytes = step_algorithmic_bytes(w)
+    log(f"[bench] {args.steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.2f} us/step, scan {scan_ms * 1e3:.2f} us "
+        f"({achieved:.0f} GB/s algorithmic), whole step {step_bytes / (ms_per_step * 1e-3) / 1e9:.0f} GB/s algorithmic")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "query_tokens": T, "context_entries": N,
+                   "pool": f"{w.pool_blocks}x{w.block}", "top_k": K, "reindex_layers": w.n_reindex,
+                   "attention_layers": L, "attention_heads": Hh, "indexer_heads": 32, "indexer_dim": 128,
+                   "swa_window": w.swa_window, "context_replicas": R,
+                   "launch": "eager" if args.no_graph else "hipgraph",
+                   "step_algorithmic_bytes": step_bytes,
+                   "step_algorithmic_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "kernel": "k_idx_scan", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
+                     "avg_launch_us": round(scan_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

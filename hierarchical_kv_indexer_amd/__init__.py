@@ -25,6 +25,8 @@ EXPORTS = (
     ("csa2_quantize_query", _I, (_P, _P, _I64, _P)),
     ("csa2_index_scores", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
     ("csa2_index_full_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
+    ("csa2_index_scan", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
+    ("csa2_index_select", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_full", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_reindex_workspace", _SZ, (_I, _I, _I, _I, _I)),
     ("csa2_reindex", _I, (_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
@@ -110,6 +112,22 @@ def csa2_index_full(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int
                                  _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
 
 
+def csa2_index_scan(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
+                    n_max: int, block_size: int, pool_blocks: int, top_k: int, workspace,
+                    ws_bytes: int, stream=None) -> None:
+    _check(lib().csa2_index_scan(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
+                                 _ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
+                                 _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
+
+
+def csa2_index_select(n_visible, B: int, T: int, n_max: int, block_size: int, pool_blocks: int,
+                      top_k: int, pool_pos, pool_len, topk_idx, topk_score, workspace,
+                      ws_bytes: int, stream=None) -> None:
+    _check(lib().csa2_index_select(_ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
+                                   _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
+                                   _ptr(workspace), ws_bytes, _stream(stream, n_visible)))
+
+
 def csa2_reindex_workspace(L: int, B: int, T: int, pool_cap: int, top_k: int) -> int:
     return lib().csa2_reindex_workspace(L, B, T, pool_cap, top_k)
 
@@ -123,8 +141,8 @@ def csa2_reindex(idx_k, k_rows_per_seq: int, idx_q, head_w, pool_pos, pool_len, 
                               _stream(stream, idx_k)))
 
 
-def csa2_sparse_attn_workspace(L: int, B: int, T: int, H: int, top_k: int, S: int) -> int:
-    return lib().csa2_sparse_attn_workspace(L, B, T, H, top_k, S)
+def csa2_sparse_attn_workspace(L: int, B: int, T: int, H: int, top_k: int, swa_window: int) -> int:
+    return lib().csa2_sparse_attn_workspace(L, B, T, H, top_k, swa_window)
 
 
 def csa2_sparse_attn(kv_codes, kv_scales, kv_rows_per_seq: int, q, idx_sets,

@@ -61,16 +61,21 @@ struct Carver {
 };
 
 struct FullPlan {
-  int Q, nb_max, chunk, n_wg, P, cap;
+  int Q, nb_max, nb_stride, chunk, n_wg, n_units, blocks_per_unit, P, cap;
   bool internal_pool;
 };
+
+constexpr int kMaxPositions = 1 << 23;   // n_wg <= 1024 with chunks of at most 8192 positions
 
 FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
   FullPlan p;
   p.Q = B * T;
   p.nb_max = (n_max + csa2::kBlock - 1) / csa2::kBlock;
+  p.nb_stride = (p.nb_max + 63) / 64 * 64;                 // 256-byte rows of block keys
   p.chunk = csa2::scan_chunk_positions(n_max, p.Q);
   p.n_wg = n_max > 0 ? (n_max + p.chunk - 1) / p.chunk : 1;
+  p.n_units = p.n_wg * csa2::kScanUnitsPerWg;
+  p.blocks_per_unit = p.chunk / (csa2::kBlock * csa2::kScanUnitsPerWg);
   p.internal_pool = pool_blocks == 0;
   p.P = p.internal_pool ? top_k : pool_blocks;
   p.cap = p.P * csa2::kBlock;
@@ -81,19 +86,17 @@ FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
 struct FullWs {
   float* scores;
   uint32_t* blkkey;
-  uint32_t* wg_minmax;
-  int32_t* pool_pos;
-  int32_t* pool_len;
+  uint64_t* lists;
+  uint64_t* cuts;
 };
 
 size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
   Carver c{(char*)ws};
   FullWs w;
   w.scores = c.take<float>((size_t)p.Q * (n_max > 0 ? n_max : 1));
-  w.blkkey = c.take<uint32_t>((size_t)p.Q * (p.nb_max > 0 ? p.nb_max : 1));
-  w.wg_minmax = c.take<uint32_t>((size_t)p.Q * p.n_wg * 2);
-  w.pool_pos = p.internal_pool ? c.take<int32_t>((size_t)p.Q * p.cap) : nullptr;
-  w.pool_len = p.internal_pool ? c.take<int32_t>((size_t)p.Q) : nullptr;
+  w.blkkey = c.take<uint32_t>((size_t)p.Q * p.nb_stride + 64);   // + tail read by unit batches
+  w.lists = c.take<uint64_t>((size_t)p.Q * p.n_units * 4);
+  w.cuts = c.take<uint64_t>((size_t)p.Q * p.n_units);
   if (out) *out = w;
   return c.off;
 }
@@ -119,6 +122,7 @@ static csa2_status check_index_common(const uint8_t* idx_k, int64_t k_rows, cons
   REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
   REQUIRE((int64_t)B * T <= 65535, CSA2_ERR_UNSUPPORTED, "B*T must be <= 65535");
   REQUIRE(n_max >= 0, CSA2_ERR_INVALID_ARG, "n_max must be >= 0");
+  REQUIRE(n_max <= kMaxPositions, CSA2_ERR_UNSUPPORTED, "n_max must be <= %d", kMaxPositions);
   REQUIRE(k_rows >= n_max && k_rows < ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
           "need n_max <= k_rows_per_seq < 2^31 (n_max %d, k_rows %lld)", n_max, (long long)k_rows);
   REQUIRE_PTR(idx_k);
@@ -137,7 +141,8 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, cons
   if (n_max == 0) return ok();
   const FullPlan p = plan_full(B, T, n_max, 1, 1);
   st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                       scores, nullptr, p.nb_max, nullptr, p.chunk, p.n_wg, (hipStream_t)stream),
+                                       scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg,
+                                       (hipStream_t)stream),
                  "index scan launch");
   return st == CSA2_OK ? ok() : st;
 }
@@ -148,19 +153,54 @@ size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int po
   return carve_full(nullptr, plan_full(B, T, n_max, pool_blocks, top_k), n_max, nullptr);
 }
 
-csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
-                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
-                            int block_size, int pool_blocks, int top_k, int32_t* pool_pos,
-                            int32_t* pool_len, int32_t* topk_idx, float* topk_score, void* workspace,
-                            size_t ws_bytes, void* stream) {
-  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
-  if (st != CSA2_OK) return st;
+static csa2_status check_full_shape(int B, int T, int n_max, int block_size, int pool_blocks, int top_k) {
+  REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
+  REQUIRE((int64_t)B * T <= 65535, CSA2_ERR_UNSUPPORTED, "B*T must be <= 65535");
+  REQUIRE(n_max >= 0, CSA2_ERR_INVALID_ARG, "n_max must be >= 0");
   REQUIRE(block_size == csa2::kBlock, CSA2_ERR_UNSUPPORTED, "block_size must be 8 (got %d)", block_size);
   REQUIRE(top_k >= 1 && top_k <= csa2::kMaxTopK, CSA2_ERR_UNSUPPORTED, "top_k must be in [1, %d]", csa2::kMaxTopK);
   REQUIRE(pool_blocks >= 0 && (int64_t)pool_blocks * block_size <= csa2::kMaxPool, CSA2_ERR_UNSUPPORTED,
           "pool_blocks * block_size must be <= %d", csa2::kMaxPool);
   REQUIRE(pool_blocks == 0 || top_k <= pool_blocks * block_size, CSA2_ERR_INVALID_ARG,
           "top_k (%d) exceeds the pool capacity (%d)", top_k, pool_blocks * block_size);
+  return CSA2_OK;
+}
+
+static csa2_status check_workspace(const FullPlan& p, int n_max, void* workspace, size_t ws_bytes) {
+  const size_t need = carve_full(nullptr, p, n_max, nullptr);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  if (st != CSA2_OK) return st;
+  if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
+  const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
+  FullWs w;
+  carve_full(workspace, p, n_max, &w);
+  if (n_max > 0) {
+    st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg,
+                                         (hipStream_t)stream),
+                   "index scan launch");
+    if (st != CSA2_OK) return st;
+  }
+  return ok();
+}
+
+csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max, int block_size,
+                              int pool_blocks, int top_k, int32_t* pool_pos, int32_t* pool_len,
+                              int32_t* topk_idx, float* topk_score, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  csa2_status st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k);
+  if (st != CSA2_OK) return st;
+  REQUIRE_PTR(n_visible);
   if (pool_blocks > 0) {
     REQUIRE_PTR(pool_pos);
     REQUIRE_PTR(pool_len);
@@ -168,28 +208,40 @@ csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const 
   REQUIRE_PTR(topk_idx);
   REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
   const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
-  const size_t need = carve_full(nullptr, p, n_max, nullptr);
-  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
-          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
   FullWs w;
   carve_full(workspace, p, n_max, &w);
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* pp = p.internal_pool ? w.pool_pos : pool_pos;
-  int32_t* pl = p.internal_pool ? w.pool_len : pool_len;
-  if (n_max > 0) {
-    st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                         w.scores, w.blkkey, p.nb_max, w.wg_minmax, p.chunk, p.n_wg, s),
-                   "index scan launch");
-    if (st != CSA2_OK) return st;
-  }
-  st = hip_check(csa2::launch_pool_select(w.blkkey, p.nb_max, n_visible, n_max, p.P, w.wg_minmax, p.n_wg,
-                                          pp, p.cap, pl, p.Q, s),
-                 "pool select launch");
-  if (st != CSA2_OK) return st;
-  st = hip_check(csa2::launch_topk(pp, pl, p.cap, n_max, w.scores, n_max > 0 ? n_max : 1, true, p.Q, p.Q,
-                                   top_k, topk_idx, topk_score, s),
-                 "top-k launch");
+  st = hip_check(csa2::launch_pool_topk(w.lists, w.cuts, p.n_units, p.blocks_per_unit, w.blkkey, p.nb_stride,
+                                        n_visible, n_max, w.scores, p.P, top_k,
+                                        p.internal_pool ? nullptr : pool_pos, p.cap,
+                                        p.internal_pool ? nullptr : pool_len, topk_idx, topk_score, p.Q,
+                                        (hipStream_t)stream),
+                 "pool/top-k launch");
   return st == CSA2_OK ? ok() : st;
+}
+
+csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k, int32_t* pool_pos,
+                            int32_t* pool_len, int32_t* topk_idx, float* topk_score, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  // check everything (both stages) before enqueueing anything
+  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  if (st != CSA2_OK) return st;
+  if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
+  if (pool_blocks > 0) {
+    REQUIRE_PTR(pool_pos);
+    REQUIRE_PTR(pool_len);
+  }
+  REQUIRE_PTR(topk_idx);
+  REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
+  if ((st = check_workspace(plan_full(B, T, n_max, pool_blocks, top_k), n_max, workspace, ws_bytes)) != CSA2_OK)
+    return st;
+  st = csa2_index_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
+                       top_k, workspace, ws_bytes, stream);
+  if (st != CSA2_OK) return st;
+  return csa2_index_select(n_visible, B, T, n_max, block_size, pool_blocks, top_k, pool_pos, pool_len, topk_idx,
+                           topk_score, workspace, ws_bytes, stream);
 }
 
 size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k) {
@@ -222,9 +274,8 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
   const int Q = B * T;
   hipStream_t s = (hipStream_t)stream;
   float* ri = (float*)workspace;
-  const int chunk = csa2::ri_chunk_slots(pool_cap, L * Q);
   csa2_status st = hip_check(csa2::launch_ri_score(idx_k, k_rows_per_seq, idx_q, head_w, pool_pos, pool_len,
-                                                   pool_cap, L, Q, T, ri, chunk, s),
+                                                   pool_cap, L, Q, T, ri, s),
                              "reindex score launch");
   if (st != CSA2_OK) return st;
   st = hip_check(csa2::launch_topk(pool_pos, pool_len, pool_cap, k_rows_per_seq, ri, pool_cap, false, L * Q, Q,
@@ -233,9 +284,9 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
   return st == CSA2_OK ? ok() : st;
 }
 
-size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int S) {
-  (void)L; (void)B; (void)T; (void)H; (void)top_k; (void)S;
-  return 0;
+size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int swa_window) {
+  if (L < 1 || B < 1 || T < 1 || H < 16 || H % 16 != 0 || top_k < 1 || swa_window < 0) return 0;
+  return csa2::plan_attn(L, B, T, H, top_k, swa_window).ws_bytes;
 }
 
 csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t kv_rows_per_seq,
@@ -243,7 +294,6 @@ csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, 
                              const uint8_t* swa_kv, int swa_rows, const int32_t* swa_end, int swa_window,
                              int L, int B, int T, int H, int top_k, float softmax_scale, uint16_t* out,
                              float* lse, void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   REQUIRE(L >= 1 && L <= csa2::kMaxLayers, CSA2_ERR_UNSUPPORTED, "L must be in [1, %d]", csa2::kMaxLayers);
   REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1");
   REQUIRE((int64_t)L * B * T <= 65535, CSA2_ERR_UNSUPPORTED, "L*B*T must be <= 65535");
@@ -270,10 +320,13 @@ csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, 
             l, layer_set[l], S);
     sets.set[l] = layer_set[l];
   }
+  const size_t need = csa2_sparse_attn_workspace(L, B, T, H, top_k, swa_window);
+  REQUIRE(need == 0 || (workspace != nullptr && aligned16(workspace) && ws_bytes >= need), CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
   csa2_status st = hip_check(csa2::launch_sparse_attn(kv_codes, kv_scales, kv_rows_per_seq, q, idx_sets, sets,
                                                       swa_rows ? swa_kv : kv_codes, swa_rows, swa_end,
                                                       swa_window, L, B, T, H, top_k, softmax_scale, out, lse,
-                                                      (hipStream_t)stream),
+                                                      need ? workspace : nullptr, (hipStream_t)stream),
                              "sparse attention launch");
   return st == CSA2_OK ? ok() : st;
 }

@@ -7,10 +7,12 @@
 // A main row is 256 bytes of E2M1 codes plus 32 E4M3 scales (one per 16 channels); the
 // dequantised value code * scale is exact in bf16, and so is an E4M3 SWA value.
 //
-// One workgroup (4 waves) handles 16 heads of one (layer, query) and streams the rows in
-// chunks of 64: rows are gathered and dequantised into LDS as bf16, S = Q X^T and O += P X run
-// on bf16 MFMA (16x16x32) with an online softmax in fp32; the next chunk's raw bytes are
-// loaded into registers while the current chunk is computed.
+// A workgroup (4 waves) handles 16 heads of one (layer, query) over one split of its rows and
+// streams them in chunks of 64: rows are gathered and dequantised into LDS as bf16, S = Q X^T
+// and O += P X run on bf16 MFMA (16x16x32) with an online softmax in fp32, and the next chunk's
+// raw bytes are loaded into registers while the current chunk is computed.  When the (layer,
+// query, head group) count alone cannot fill the GPU, the rows are split across workgroups and
+// k_attn_combine merges the partial softmax states (max, sum, weighted rows).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,38 +21,13 @@ namespace csa2 {
 constexpr int kRows = 64;                    // rows per chunk
 constexpr int kXStride = kKvDim + 8;         // bf16 elements per LDS row (pad: 16 bytes)
 constexpr int kPStride = kRows + 8;          // bf16 elements per P row
+constexpr int kMaxSplitRows = 4096 + kMaxTopK;   // a split never exceeds k + window rows
 
 struct RawRow {          // this thread's quarter (128 channels) of one chunk row
   u32x4 d[8];            // main: d[0..3] = 64 code bytes; SWA: d[0..7] = 128 E4M3 bytes
   u32x2 sc;              // main: 8 scale bytes
   int kind;              // 0 empty, 1 main, 2 SWA
 };
-
-__device__ __forceinline__ void load_raw(RawRow& r, int slot, int k, const int32_t* __restrict__ idx,
-                                         int64_t kv_rows, const uint8_t* __restrict__ codes_seq,
-                                         const uint8_t* __restrict__ scales_seq,
-                                         const uint8_t* __restrict__ swa_seq, int ws, int we,
-                                         int quarter) {
-  r.kind = 0;
-  if (slot < k) {
-    const int pos = idx[slot];
-    if (pos >= 0 && (int64_t)pos < kv_rows) {
-      const u32x4* c = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 64 * quarter);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r.d[i] = c[i];
-      r.sc = *(const u32x2*)(scales_seq + (size_t)pos * kKvScaleBytes + 8 * quarter);
-      r.kind = 1;
-    }
-  } else {
-    const int row = ws + (slot - k);
-    if (row < we) {
-      const u32x4* c = (const u32x4*)(swa_seq + (size_t)row * kKvDim + 128 * quarter);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r.d[i] = c[i];
-      r.kind = 2;
-    }
-  }
-}
 
 // Dequantise this thread's quarter row into LDS (128 bf16 = 16 x 16 bytes).
 __device__ __forceinline__ void store_row(const RawRow& r, uint16_t* xrow, int quarter) {
@@ -91,18 +68,24 @@ __device__ __forceinline__ void store_row(const RawRow& r, uint16_t* xrow, int q
   }
 }
 
-// grid (H/16, L*Q), 256 threads.
+// Rows of a (layer, query) are numbered: main slots 0 .. k-1 (index set order), then the window's
+// SWA rows.  grid (n_splits, H/16, L*Q): split s covers row slots [s*split_rows, (s+1)*split_rows)
+// for 16 heads.  With one split the normalised bf16 output and lse are written directly;
+// otherwise the split writes its partial state (running max m and sum l in log2 units, and the
+// unnormalised sum of p*x) for k_attn_combine.
 __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t kv_rows,
     const uint16_t* __restrict__ qg, const int32_t* __restrict__ idx_sets, LayerSets sets,
     const uint8_t* __restrict__ swa, int swa_rows, const int32_t* __restrict__ swa_end, int window,
-    int Q, int B, int T, int H, int k, float scale_log2, uint16_t* __restrict__ out,
+    int Q, int B, int T, int H, int k, float scale_log2, int split_rows, int n_splits,
+    float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t X[kRows * kXStride];
   __shared__ __attribute__((aligned(16))) uint16_t P[16 * kPStride];
   __shared__ float red[4][16];
+  __shared__ int32_t rowok[kRows];
 
-  const int hg = blockIdx.x, lq = blockIdx.y;
+  const int split = blockIdx.x, hg = blockIdx.y, lq = blockIdx.z;
   const int l = lq / Q, q = lq % Q, b = q / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -111,10 +94,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   we = we < 0 ? 0 : (we > swa_rows ? swa_rows : we);
   const int ws = max(0, we - window);
   const int nslots = k + (we - ws);
-  const int nchunks = (nslots + kRows - 1) / kRows;
+  const int s0 = split * split_rows, s1 = min(nslots, s0 + split_rows);
+  const int nchunks = s1 > s0 ? (s1 - s0 + kRows - 1) / kRows : 0;
   const uint8_t* codes_seq = kv_codes + (size_t)b * kv_rows * kKvCodeBytes;
   const uint8_t* scales_seq = kv_scales + (size_t)b * kv_rows * kKvScaleBytes;
   const uint8_t* swa_seq = swa + ((size_t)l * B + b) * (size_t)swa_rows * kKvDim;
+
+  const int my_row = tid >> 2, quarter = tid & 3;
+  // main-row index of this thread's row in chunk c (-1: none), prefetched one chunk ahead
+  auto row_index = [&](int c) {
+    const int slot = s0 + c * kRows + my_row;
+    if (slot >= s1 || slot >= k) return -1;
+    const int pos = idx[slot];
+    return (pos >= 0 && (int64_t)pos < kv_rows) ? pos : -1;
+  };
+  int pos_cur = nchunks > 0 ? row_index(0) : -1;
+  int pos_next = nchunks > 1 ? row_index(1) : -1;
 
   // query of 16 heads as MFMA A operands: head j, channels 32c + 8g .. +7
   const uint16_t* qh = qg + (((size_t)l * Q + q) * H + 16 * hg) * kKvDim;
@@ -129,30 +124,44 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
 
-  const int my_row = tid >> 2, quarter = tid & 3;
+  auto load_chunk = [&](RawRow& r, int c, int pos) {
+    const int slot = s0 + c * kRows + my_row;
+    r.kind = 0;
+    if (slot < s1) {
+      if (slot < k) {
+        if (pos >= 0) {
+          const u32x4* cp = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 64 * quarter);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r.d[i] = cp[i];
+          r.sc = *(const u32x2*)(scales_seq + (size_t)pos * kKvScaleBytes + 8 * quarter);
+          r.kind = 1;
+        }
+      } else {
+        const u32x4* cp = (const u32x4*)(swa_seq + (size_t)(ws + slot - k) * kKvDim + 128 * quarter);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.d[i] = cp[i];
+        r.kind = 2;
+      }
+    }
+  };
   RawRow raw;
-  load_raw(raw, my_row, k, idx, kv_rows, codes_seq, scales_seq, swa_seq, ws, we, quarter);
+  if (nchunks > 0) load_chunk(raw, 0, pos_cur);
 
   for (int c = 0; c < nchunks; ++c) {
     store_row(raw, X + my_row * kXStride, quarter);
+    if (quarter == 0) rowok[my_row] = raw.kind != 0;
     __syncthreads();
-    if (c + 1 < nchunks)
-      load_raw(raw, (c + 1) * kRows + my_row, k, idx, kv_rows, codes_seq, scales_seq, swa_seq, ws,
-               we, quarter);
+    if (c + 1 < nchunks) {
+      load_chunk(raw, c + 1, pos_next);
+      pos_next = c + 2 < nchunks ? row_index(c + 2) : -1;
+    }
 
     // S[head 4g+v][row 16*wave + j]
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     const uint16_t* xr = X + (16 * wave + j) * kXStride + 8 * g;
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc) s = mfma16x16x32(qa[cc], *(const u32x4*)(xr + 32 * cc), s);
-    const int slot = c * kRows + 16 * wave + j;
-    bool row_ok;
-    if (slot < k) {
-      const int pos = idx[slot];
-      row_ok = pos >= 0 && (int64_t)pos < kv_rows;
-    } else {
-      row_ok = slot < nslots;
-    }
+    const bool row_ok = rowok[16 * wave + j] != 0;
     float sv[4], mx[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
-      float mc = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+      const float mc = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
       mnew[v] = fmaxf(m_run[v], mc);
       alpha[v] = mnew[v] == -INFINITY ? 1.f : exp2f(m_run[v] - mnew[v]);
       const float p = mnew[v] == -INFINITY ? 0.f : exp2f(sv[v] - mnew[v]);
@@ -221,31 +230,120 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     __syncthreads();   // X, P and red[] are rewritten by the next chunk
   }
 
-  // out[l][q][16*hg + 4g+v][dim], lse
-  uint16_t* oh = out + (((size_t)l * Q + q) * H + 16 * hg) * kKvDim;
+  const size_t hrow = (size_t)lq * H + 16 * hg;      // (layer, query, first head of the group)
+  if (n_splits == 1) {
+    uint16_t* oh = out + hrow * kKvDim;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int h = 4 * g + v;
-    const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * g + v;
+      const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) oh[(size_t)h * kKvDim + 128 * wave + 16 * t + j] = (uint16_t)f32_to_bf16_rne(o[t][v] * inv);
-    if (lse && wave == 0 && j == 0) {
-      lse[((size_t)l * Q + q) * H + 16 * hg + h] =
-          l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * 0.69314718055994531f : -INFINITY;
+      for (int t = 0; t < 8; ++t)
+        oh[(size_t)h * kKvDim + 128 * wave + 16 * t + j] = (uint16_t)f32_to_bf16_rne(o[t][v] * inv);
+      if (lse && wave == 0 && j == 0)
+        lse[hrow + h] = l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * 0.69314718055994531f : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * g + v;
+      const size_t pr = (hrow + h) * n_splits + split;
+      float* po = part_o + pr * kKvDim;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) po[128 * wave + 16 * t + j] = o[t][v];
+      if (wave == 0 && j == 0) {
+        part_ml[pr * 2] = m_run[v];
+        part_ml[pr * 2 + 1] = l_run[v];
+      }
     }
   }
+}
+
+// grid (H/16, L*Q), 256 threads: merges the n_splits partial states of 16 heads; wave w handles
+// heads 4w .. 4w+3, each lane 8 dims of a head.  All splits of a head are loaded together.
+constexpr int kMaxSplits = 16;
+__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int n_splits, int H,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int hg = blockIdx.x, lq = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    const size_t hrow = (size_t)lq * H + 16 * hg + 4 * wave + hh;
+    const float* ml = part_ml + hrow * n_splits * 2;
+    float m[kMaxSplits], l[kMaxSplits];
+    f32x4 a[kMaxSplits], c[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < n_splits) {
+        m[s] = ml[2 * s];
+        l[s] = ml[2 * s + 1];
+        const f32x4* po = (const f32x4*)(part_o + (hrow * n_splits + s) * kKvDim + 8 * lane);
+        a[s] = po[0];
+        c[s] = po[1];
+      }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+      if (s < n_splits) M = fmaxf(M, m[s]);
+    float L = 0.f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < n_splits && m[s] != -INFINITY) {
+        const float w = exp2f(m[s] - M);
+        L += w * l[s];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { acc[i] += w * a[s][i]; acc[4 + i] += w * c[s][i]; }
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pk[i] = f32_to_bf16_rne(acc[2 * i] * inv) | (f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
+    *(u32x4*)(out + hrow * kKvDim + 8 * lane) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    if (lse && lane == 0) lse[hrow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+AttnPlan plan_attn(int L, int B, int T, int H, int k, int window) {
+  AttnPlan p;
+  const long long groups = (long long)L * B * T * (H / 16);
+  const int rows_max = k + window;
+  const int max_chunks = (rows_max + kRows - 1) / kRows;
+  long long want = (512 + groups - 1) / groups;         // splits to reach ~512 workgroups
+  int splits = (int)(want < max_chunks ? want : max_chunks);
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits < 1) splits = 1;
+  int chunks_per = (max_chunks + splits - 1) / splits;
+  p.split_rows = chunks_per * kRows;
+  if (p.split_rows > kMaxSplitRows) p.split_rows = kMaxSplitRows;
+  p.n_splits = (rows_max + p.split_rows - 1) / p.split_rows;
+  if (p.n_splits < 1) p.n_splits = 1;
+  const size_t heads = (size_t)L * B * T * H;
+  p.ws_bytes = p.n_splits > 1 ? heads * p.n_splits * (kKvDim + 2) * sizeof(float) : 0;
+  return p;
 }
 
 hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t kv_rows,
                               const uint16_t* q, const int32_t* idx_sets, const LayerSets& sets,
                               const uint8_t* swa, int swa_rows, const int32_t* swa_end, int window,
                               int L, int B, int T, int H, int k, float scale, uint16_t* out,
-                              float* lse, hipStream_t s) {
+                              float* lse, void* workspace, hipStream_t s) {
   const int Q = B * T;
   const float scale_log2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(k_sparse_attn, dim3(H / 16, L * Q), dim3(kAttnThreads), 0, s, kv_codes,
-                     kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q, B, T,
-                     H, k, scale_log2, out, lse);
+  const AttnPlan p = plan_attn(L, B, T, H, k, window);
+  float* part_o = (float*)workspace;
+  float* part_ml = part_o ? part_o + (size_t)L * Q * H * p.n_splits * kKvDim : nullptr;
+  hipLaunchKernelGGL(k_sparse_attn, dim3(p.n_splits, H / 16, L * Q), dim3(kAttnThreads), 0, s, kv_codes,
+                     kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q, B, T, H, k,
+                     scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_splits == 1) return e;
+  hipLaunchKernelGGL(k_attn_combine, dim3(H / 16, L * Q), dim3(kAttnThreads), 0, s, part_o, part_ml,
+                     p.n_splits, H, out, lse);
   return hipGetLastError();
 }
 

@@ -120,4 +120,92 @@ __device__ __forceinline__ uint32_t rank_key_index(uint64_t rk) {
 
 __device__ __forceinline__ int bitlen64(uint64_t x) { return x ? 64 - __clzll(x) : 0; }
 
+// ---- cross-lane helpers (wave64)
+
+// Sum of x over lane pairs l, l^16, combined in the same order on both lanes.
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Sum of x over lane pairs l, l^32, combined in the same order on both lanes.
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Max of x over the aligned group of 8 lanes containing this lane (result in every lane).
+__device__ __forceinline__ uint32_t max8_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  return x;
+}
+// DPP wave64 primitives (no LDS traffic).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t swap16(uint32_t x) {   // value of lane l ^ 16
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t swap32(uint32_t x) {   // value of lane l ^ 32
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+}
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += dpp_or_zero<0x111>(x);          // row_shr:1
+  x += dpp_or_zero<0x112>(x);          // row_shr:2
+  x += dpp_or_zero<0x114>(x);          // row_shr:4
+  x += dpp_or_zero<0x118>(x);          // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);     // row_bcast:15 into rows 1, 3
+  x += dpp_or_zero<0x143, 0xc>(x);     // row_bcast:31 into rows 2, 3
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_mov<0xB1>(x));        // quad_perm [1,0,3,2]
+  x = max(x, dpp_mov<0x4E>(x));        // quad_perm [2,3,0,1]
+  x = max(x, dpp_mov<0x141>(x));       // row_half_mirror
+  x = max(x, dpp_mov<0x140>(x));       // row_mirror
+  x = max(x, swap16(x));
+  x = max(x, swap32(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_mov<0xB1>(x));
+  x = min(x, dpp_mov<0x4E>(x));
+  x = min(x, dpp_mov<0x141>(x));
+  x = min(x, dpp_mov<0x140>(x));
+  x = min(x, swap16(x));
+  x = min(x, swap32(x));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  x += swap16(x);
+  x += swap32(x);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t w = shfl_xor_u64(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
 }  // namespace csa2

@@ -15,21 +15,22 @@ struct LayerSets { int32_t set[kMaxLayers]; };
 // scan.hip
 hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hipStream_t s);
 int scan_chunk_positions(int n_max, int queries);
+constexpr int kScanUnitsPerWg = kScanThreads / 64;   // one unit per wave
 hipError_t launch_idx_scan(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
-                           float* scores, uint32_t* blkkey, int nb_max, uint32_t* wg_minmax,
-                           int chunk, int n_wg, hipStream_t s);
-int ri_chunk_slots(int pool_cap, int items);
+                           float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
+                           uint64_t* cuts, int chunk, int n_wg, hipStream_t s);
 hipError_t launch_ri_score(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
-                           int pool_cap, int L, int Q, int T, float* ri_scores, int chunk,
-                           hipStream_t s);
+                           int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s);
 
 // select.hip
-hipError_t launch_pool_select(const uint32_t* blkkey, int nb_max, const int32_t* n_visible,
-                              int n_max, int pool_blocks, const uint32_t* wg_minmax, int n_wg,
-                              int32_t* pool_pos, int pool_cap_out, int32_t* pool_len, int Q,
-                              hipStream_t s);
+// Pool of the top P blocks plus the Top-K of the pool, one WG per query (pool_pos / pool_len
+// may be null).
+hipError_t launch_pool_topk(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
+                            const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max,
+                            const float* scores, int P, int K, int32_t* pool_pos, int cap_out,
+                            int32_t* pool_len, int32_t* topk_idx, float* topk_score, int Q, hipStream_t s);
 // Top-K over candidate lists.  Candidate slot i of item it has position cand_pos[(it % Q)*cap + i]
 // (slots >= cand_len[it % Q] are empty).  by_position: the score of a candidate is
 // scores[(it % Q)*score_stride + pos]; otherwise scores[it*score_stride + slot].
@@ -38,10 +39,15 @@ hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap
                        int Q, int k, int32_t* out_idx, float* out_score, hipStream_t s);
 
 // attn.hip
+struct AttnPlan {
+  int split_rows, n_splits;
+  size_t ws_bytes;     // partial states when the rows are split over several workgroups
+};
+AttnPlan plan_attn(int L, int B, int T, int H, int k, int window);
 hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t kv_rows,
                               const uint16_t* q, const int32_t* idx_sets, const LayerSets& sets,
                               const uint8_t* swa, int swa_rows, const int32_t* swa_end, int window,
                               int L, int B, int T, int H, int k, float scale, uint16_t* out,
-                              float* lse, hipStream_t s);
+                              float* lse, void* workspace, hipStream_t s);
 
 }  // namespace csa2

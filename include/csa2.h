@@ -92,8 +92,23 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, cons
  *   topk_score [B][T][top_k] float out aligned with topk_idx (0 for padding), or NULL
  *   workspace  device scratch of at least csa2_index_full_workspace(...) bytes
  * Supported: block_size == 8, 1 <= top_k <= 2048, top_k <= pool_blocks*block_size when
- * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= k_rows_per_seq < 2^31. */
+ * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= 2^23, n_max <= k_rows_per_seq. */
 size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k);
+
+/* The two stages of csa2_index_full as separate calls (same arguments, same workspace, which
+ * carries the scan's scores and block keys from the first call to the second; the pair must
+ * be enqueued in order on one stream with identical shape arguments).
+ *   csa2_index_scan:   steps A1-A2 plus the block maxima (reads idx_k, idx_q, head_w, n_visible)
+ *   csa2_index_select: steps A3-A4 (pool and Top-K; reads n_visible and the workspace) */
+csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k,
+                            void* workspace, size_t ws_bytes, void* stream);
+csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max,
+                              int block_size, int pool_blocks, int top_k,
+                              int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k,
@@ -104,8 +119,9 @@ csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const 
  * for each of L layers, re-score only the pool positions with the layer's own indexer query
  * and weights, then take its own Top-`top_k`.  Positions outside the pool are never picked.
  *   idx_q      [L][B][T][32][128] bf16;  head_w [L][B][T][32] float
- *   pool_pos   [B][T][pool_cap] int32 positions (entries >= pool_len and negative or
- *              out-of-range entries are ignored); pool_len [B][T] int32
+ *   pool_pos   [B][T][pool_cap] int32 distinct positions in ascending order (as csa2_index_full
+ *              writes them; the Top-K output keeps the pool's order); entries >= pool_len and
+ *              negative or out-of-range entries are ignored; pool_len [B][T] int32
  *   topk_idx   [L][B][T][top_k] int32 out; topk_score [L][B][T][top_k] float out or NULL
  * Supported: 1 <= top_k <= 2048, top_k <= pool_cap <= 16384. */
 size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k);
@@ -128,8 +144,9 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
  *   swa_end    [B][T] int32 exclusive end row of each query's window (clamped to [0, swa_rows])
  *   out        [L][B][T][H][512] bf16 out;  lse [L][B][T][H] float out (natural log) or NULL;
  *              a query with no rows at all gets out = 0 and lse = -inf
- * Supported: H % 16 == 0, 1 <= top_k <= 2048, 0 <= swa_window <= 4096. */
-size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int S);
+ *   workspace  device scratch of csa2_sparse_attn_workspace(...) bytes (may be 0: then NULL is fine)
+ * Supported: H % 16 == 0, 1 <= top_k <= 2048, 0 <= swa_window <= 4096, L <= 64. */
+size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int swa_window);
 csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, int64_t kv_rows_per_seq,
                              const uint16_t* q, const int32_t* idx_sets, const int32_t* layer_set, int S,
                              const uint8_t* swa_kv, int swa_rows, const int32_t* swa_end, int swa_window,

@@ -92,7 +92,7 @@ def gpu_attention(inp, w, idx_sets: np.ndarray, layers: Optional[Sequence[int]] 
     S, k = idx_sets.shape[0], idx_sets.shape[-1]
     out = empty((L, B, T, Hh, 512), torch.int16)
     lse = empty((L, B, T, Hh), torch.float32)
-    ws_bytes = H.csa2_sparse_attn_workspace(L, B, T, Hh, k, S)
+    ws_bytes = H.csa2_sparse_attn_workspace(L, B, T, Hh, k, w.swa_window)
     ws = empty((max(ws_bytes, 1),), torch.uint8)
     swa = inp["swa"]
     H.csa2_sparse_attn(dev(inp["kv_codes"]), dev(inp["kv_scales"]), inp["kv_codes"].shape[1], dev(inp["q"]),

@@ -81,3 +81,5 @@ def test_reindex_and_attention_reject(H):
     expect(H, 1, lambda: H.csa2_sparse_attn(*a))
     a = list(base); a[11] = 65; a[5] = [0] * 65
     expect(H, 2, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[19] = None; a[20] = 0                          # split rows need a workspace
+    expect(H, 3, lambda: H.csa2_sparse_attn(*a))
