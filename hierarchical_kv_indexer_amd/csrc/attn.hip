@@ -23,6 +23,23 @@ constexpr int kXStride = kKvDim + 8;         // bf16 elements per LDS row (pad: 
 constexpr int kPStride = kRows + 8;          // bf16 elements per P row
 constexpr int kMaxSplitRows = 4096 + kMaxTopK;   // a split never exceeds k + window rows
 
+// Max / sum over the 16 lanes of a DPP row; every lane of the row gets the same value (the
+// pairwise steps are symmetric, so the sum is rounded identically in each lane).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(x))));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(x))));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, __uint_as_float(dpp_mov<0x141>(__float_as_uint(x))));   // row_half_mirror
+  x = fmaxf(x, __uint_as_float(dpp_mov<0x140>(__float_as_uint(x))));   // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __uint_as_float(dpp_mov<0xB1>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<0x4E>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<0x141>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<0x140>(__float_as_uint(x)));
+  return x;
+}
+
 struct RawRow {          // this thread's quarter (128 channels) of one chunk row
   u32x4 d[8];            // main: d[0..3] = 64 code bytes; SWA: d[0..7] = 128 E4M3 bytes
   u32x2 sc;              // main: 8 scale bytes
@@ -82,7 +99,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t X[kRows * kXStride];
   __shared__ __attribute__((aligned(16))) uint16_t P[16 * kPStride];
-  __shared__ float red[4][16];
+  __shared__ float red_m[4][16], red_l[4][16];
   __shared__ int32_t rowok[kRows];
 
   const int split = blockIdx.x, hg = blockIdx.y, lq = blockIdx.z;
@@ -166,47 +183,40 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       sv[v] = row_ok ? s[v] * scale_log2 : -INFINITY;
-      mx[v] = sv[v];
+      mx[v] = row16_max(sv[v]);
     }
-#pragma unroll
-    for (int o2 = 1; o2 < 16; o2 <<= 1)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mx[v] = fmaxf(mx[v], __shfl_xor(mx[v], o2));
     if (j == 0) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][4 * g + v] = mx[v];
+      for (int v = 0; v < 4; ++v) red_m[wave][4 * g + v] = mx[v];
     }
     __syncthreads();
     float alpha[4], mnew[4], psum[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
-      const float mc = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+      const float mc = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
       mnew[v] = fmaxf(m_run[v], mc);
       alpha[v] = mnew[v] == -INFINITY ? 1.f : exp2f(m_run[v] - mnew[v]);
       const float p = mnew[v] == -INFINITY ? 0.f : exp2f(sv[v] - mnew[v]);
       const uint32_t pb = f32_to_bf16_rne(p);
       P[h * kPStride + 16 * wave + j] = (uint16_t)pb;
-      psum[v] = bf16_bits_to_f32(pb);
+      psum[v] = row16_sum(bf16_bits_to_f32(pb));
     }
-#pragma unroll
-    for (int o2 = 1; o2 < 16; o2 <<= 1)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) psum[v] += __shfl_xor(psum[v], o2);
-    __syncthreads();   // red[] reads done, P written
     if (j == 0) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][4 * g + v] = psum[v];
+      for (int v = 0; v < 4; ++v) red_l[wave][4 * g + v] = psum[v];
     }
-    __syncthreads();
+    __syncthreads();   // P and red_l written
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
-      const float ps = (red[0][h] + red[1][h]) + (red[2][h] + red[3][h]);
+      const float ps = (red_l[0][h] + red_l[1][h]) + (red_l[2][h] + red_l[3][h]);
       l_run[v] = l_run[v] * alpha[v] + ps;
       m_run[v] = mnew[v];
     }
-    // O[head 4g+v][dim 128*wave + 16t + j] = alpha * O + sum_r P[head][r] X[r][dim]
+    // O[head 4g+v][dim 128*wave + 8j + t] = alpha * O + sum_r P[head][r] X[r][dim].  The B operand
+    // of tile t needs rows 8g .. 8g+7 of one dim; a lane reads its 8 dims of each row in one
+    // 16-byte LDS access and pairs the halves of two rows with byte permutes.
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -214,32 +224,36 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
     for (int kk = 0; kk < kRows / 32; ++kk) {
       const u32x4 pa = *(const u32x4*)(P + j * kPStride + 32 * kk + 8 * g);
-      const uint16_t* xc = X + (32 * kk + 8 * g) * kXStride + 128 * wave + j;
+      const uint16_t* xc = X + (32 * kk + 8 * g) * kXStride + 128 * wave + 8 * j;
+      u32x4 xv[8];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        u32x4 xb;
+      for (int e = 0; e < 8; ++e) xv[e] = *(const u32x4*)(xc + e * kXStride);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x4 lo, hi;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = xc[(2 * e) * kXStride + 16 * t];
-          const uint32_t hi = xc[(2 * e + 1) * kXStride + 16 * t];
-          xb[e] = lo | (hi << 16);
+          lo[e] = __builtin_amdgcn_perm(xv[2 * e + 1][i], xv[2 * e][i], 0x05040100u);
+          hi[e] = __builtin_amdgcn_perm(xv[2 * e + 1][i], xv[2 * e][i], 0x07060302u);
         }
-        o[t] = mfma16x16x32(pa, xb, o[t]);
+        o[2 * i] = mfma16x16x32(pa, lo, o[2 * i]);
+        o[2 * i + 1] = mfma16x16x32(pa, hi, o[2 * i + 1]);
       }
     }
-    __syncthreads();   // X, P and red[] are rewritten by the next chunk
+    if (c + 1 < nchunks) __syncthreads();   // X, P, red_m and red_l are rewritten by the next chunk
   }
 
   const size_t hrow = (size_t)lq * H + 16 * hg;      // (layer, query, first head of the group)
   if (n_splits == 1) {
-    uint16_t* oh = out + hrow * kKvDim;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
       const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
+      u32x4 pk;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        oh[(size_t)h * kKvDim + 128 * wave + 16 * t + j] = (uint16_t)f32_to_bf16_rne(o[t][v] * inv);
+      for (int i = 0; i < 4; ++i)
+        pk[i] = f32_to_bf16_rne(o[2 * i][v] * inv) | (f32_to_bf16_rne(o[2 * i + 1][v] * inv) << 16);
+      *(u32x4*)(out + (hrow + h) * kKvDim + 128 * wave + 8 * j) = pk;
       if (lse && wave == 0 && j == 0)
         lse[hrow + h] = l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * 0.69314718055994531f : -INFINITY;
     }
@@ -248,9 +262,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
       const size_t pr = (hrow + h) * n_splits + split;
-      float* po = part_o + pr * kKvDim;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) po[128 * wave + 16 * t + j] = o[t][v];
+      f32x4* po = (f32x4*)(part_o + pr * kKvDim + 128 * wave + 8 * j);
+      po[0] = f32x4{o[0][v], o[1][v], o[2][v], o[3][v]};
+      po[1] = f32x4{o[4][v], o[5][v], o[6][v], o[7][v]};
       if (wave == 0 && j == 0) {
         part_ml[pr * 2] = m_run[v];
         part_ml[pr * 2 + 1] = l_run[v];
@@ -259,53 +273,46 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   }
 }
 
-// grid (H/16, L*Q), 256 threads: merges the n_splits partial states of 16 heads; wave w handles
-// heads 4w .. 4w+3, each lane 8 dims of a head.  All splits of a head are loaded together.
+// grid (H, L*Q), one wave per head: lane i merges dims 8i .. 8i+7 over the head's n_splits
+// partial states.  Every split slot is loaded up front (indices past n_splits clamp to the last
+// split and get weight zero), so the loads of a lane are all in flight together.
 constexpr int kMaxSplits = 16;
-__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(
+__global__ __launch_bounds__(64) void k_attn_combine(
     const float* __restrict__ part_o, const float* __restrict__ part_ml, int n_splits, int H,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int hg = blockIdx.x, lq = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t hrow = (size_t)blockIdx.y * H + blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* ml = part_ml + hrow * n_splits * 2;
+  float m[kMaxSplits], l[kMaxSplits];
+  f32x4 a[kMaxSplits], c[kMaxSplits];
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    const size_t hrow = (size_t)lq * H + 16 * hg + 4 * wave + hh;
-    const float* ml = part_ml + hrow * n_splits * 2;
-    float m[kMaxSplits], l[kMaxSplits];
-    f32x4 a[kMaxSplits], c[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      if (s < n_splits) {
-        m[s] = ml[2 * s];
-        l[s] = ml[2 * s + 1];
-        const f32x4* po = (const f32x4*)(part_o + (hrow * n_splits + s) * kKvDim + 8 * lane);
-        a[s] = po[0];
-        c[s] = po[1];
-      }
-    }
-    float M = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-      if (s < n_splits) M = fmaxf(M, m[s]);
-    float L = 0.f;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      if (s < n_splits && m[s] != -INFINITY) {
-        const float w = exp2f(m[s] - M);
-        L += w * l[s];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { acc[i] += w * a[s][i]; acc[4 + i] += w * c[s][i]; }
-      }
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    uint32_t pk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pk[i] = f32_to_bf16_rne(acc[2 * i] * inv) | (f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
-    *(u32x4*)(out + hrow * kKvDim + 8 * lane) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-    if (lse && lane == 0) lse[hrow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int sc = s < n_splits ? s : n_splits - 1;
+    m[s] = ml[2 * sc];
+    l[s] = ml[2 * sc + 1];
+    const f32x4* po = (const f32x4*)(part_o + (hrow * n_splits + sc) * kKvDim + 8 * lane);
+    a[s] = po[0];
+    c[s] = po[1];
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, s < n_splits ? m[s] : -INFINITY);
+  float L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const float w = (s < n_splits && m[s] != -INFINITY) ? exp2f(m[s] - M) : 0.f;
+    L += w * l[s];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { acc[i] += w * a[s][i]; acc[4 + i] += w * c[s][i]; }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    pk[i] = f32_to_bf16_rne(acc[2 * i] * inv) | (f32_to_bf16_rne(acc[2 * i + 1] * inv) << 16);
+  *(u32x4*)(out + hrow * kKvDim + 8 * lane) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  if (lse && lane == 0) lse[hrow] = L > 0.f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
 AttnPlan plan_attn(int L, int B, int T, int H, int k, int window) {
@@ -342,7 +349,7 @@ hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales,
                      scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(H / 16, L * Q), dim3(kAttnThreads), 0, s, part_o, part_ml,
+  hipLaunchKernelGGL(k_attn_combine, dim3(H, L * Q), dim3(64), 0, s, part_o, part_ml,
                      p.n_splits, H, out, lse);
   return hipGetLastError();
 }
