@@ -26,6 +26,8 @@ EXPORTS = (
     ("csa2_index_scores", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
     ("csa2_index_full_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
     ("csa2_index_scan", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
+    ("csa2_index_pool", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
+    ("csa2_index_topk", _I, (_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_select", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_full", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_reindex_workspace", _SZ, (_I, _I, _I, _I, _I)),
@@ -118,6 +120,21 @@ def csa2_index_scan(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int
     _check(lib().csa2_index_scan(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
                                  _ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
                                  _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
+
+
+def csa2_index_pool(n_visible, B: int, T: int, n_max: int, block_size: int, pool_blocks: int,
+                    top_k: int, pool_pos, pool_len, workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().csa2_index_pool(_ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
+                                 _ptr(pool_pos), _ptr(pool_len), _ptr(workspace), ws_bytes,
+                                 _stream(stream, n_visible)))
+
+
+def csa2_index_topk(B: int, T: int, n_max: int, block_size: int, pool_blocks: int, top_k: int,
+                    pool_pos, pool_len, topk_idx, topk_score, workspace, ws_bytes: int,
+                    stream=None) -> None:
+    _check(lib().csa2_index_topk(B, T, n_max, block_size, pool_blocks, top_k, _ptr(pool_pos),
+                                 _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score), _ptr(workspace),
+                                 ws_bytes, _stream(stream, topk_idx)))
 
 
 def csa2_index_select(n_visible, B: int, T: int, n_max: int, block_size: int, pool_blocks: int,

@@ -88,6 +88,8 @@ struct FullWs {
   uint32_t* blkkey;
   uint64_t* lists;
   uint64_t* cuts;
+  int32_t* pool_pos;   // internal pool (pool_blocks == 0 only)
+  int32_t* pool_len;
 };
 
 size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
@@ -97,6 +99,8 @@ size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
   w.blkkey = c.take<uint32_t>((size_t)p.Q * p.nb_stride + 64);   // + tail read by unit batches
   w.lists = c.take<uint64_t>((size_t)p.Q * p.n_units * 4);
   w.cuts = c.take<uint64_t>((size_t)p.Q * p.n_units);
+  w.pool_pos = p.internal_pool ? c.take<int32_t>((size_t)p.Q * p.cap) : nullptr;
+  w.pool_len = p.internal_pool ? c.take<int32_t>((size_t)p.Q) : nullptr;
   if (out) *out = w;
   return c.off;
 }
@@ -194,6 +198,70 @@ csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const 
   return ok();
 }
 
+static csa2_status check_pool_args(const FullPlan& p, int32_t* pool_pos, int32_t* pool_len) {
+  if (!p.internal_pool) {
+    REQUIRE_PTR(pool_pos);
+    REQUIRE_PTR(pool_len);
+  }
+  return CSA2_OK;
+}
+
+static csa2_status check_topk_args(int32_t* topk_idx, float* topk_score) {
+  REQUIRE_PTR(topk_idx);
+  REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
+  return CSA2_OK;
+}
+
+// The pool; with topk_idx non-null the same kernel also takes the Top-K of the pool.
+static csa2_status launch_pool_stage(const FullPlan& p, const FullWs& w, const int32_t* n_visible, int n_max,
+                                     int32_t* pool_pos, int32_t* pool_len, int top_k, int32_t* topk_idx,
+                                     float* topk_score, hipStream_t s) {
+  return hip_check(csa2::launch_pool(w.lists, w.cuts, p.n_units, p.blocks_per_unit, w.blkkey, p.nb_stride,
+                                     n_visible, n_max, p.P, p.internal_pool ? w.pool_pos : pool_pos, p.cap,
+                                     p.internal_pool ? w.pool_len : pool_len, w.scores, topk_idx ? top_k : 0,
+                                     topk_idx, topk_score, p.Q, s),
+                   "pool launch");
+}
+
+static csa2_status launch_topk_stage(const FullPlan& p, const FullWs& w, int n_max, const int32_t* pool_pos,
+                                     const int32_t* pool_len, int top_k, int32_t* topk_idx, float* topk_score,
+                                     hipStream_t s) {
+  return hip_check(csa2::launch_topk(p.internal_pool ? w.pool_pos : pool_pos,
+                                     p.internal_pool ? w.pool_len : pool_len, p.cap, n_max > 0 ? n_max : 1,
+                                     w.scores, n_max, true, p.Q, p.Q, top_k, topk_idx, topk_score, s),
+                   "top-k launch");
+}
+
+csa2_status csa2_index_pool(const int32_t* n_visible, int B, int T, int n_max, int block_size, int pool_blocks,
+                            int top_k, int32_t* pool_pos, int32_t* pool_len, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  csa2_status st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k);
+  if (st != CSA2_OK) return st;
+  REQUIRE_PTR(n_visible);
+  const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  if ((st = check_pool_args(p, pool_pos, pool_len)) != CSA2_OK) return st;
+  if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
+  FullWs w;
+  carve_full(workspace, p, n_max, &w);
+  st = launch_pool_stage(p, w, n_visible, n_max, pool_pos, pool_len, top_k, nullptr, nullptr, (hipStream_t)stream);
+  return st == CSA2_OK ? ok() : st;
+}
+
+csa2_status csa2_index_topk(int B, int T, int n_max, int block_size, int pool_blocks, int top_k,
+                            const int32_t* pool_pos, const int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  csa2_status st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k);
+  if (st != CSA2_OK) return st;
+  const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  if ((st = check_pool_args(p, (int32_t*)pool_pos, (int32_t*)pool_len)) != CSA2_OK) return st;
+  if ((st = check_topk_args(topk_idx, topk_score)) != CSA2_OK) return st;
+  if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
+  FullWs w;
+  carve_full(workspace, p, n_max, &w);
+  st = launch_topk_stage(p, w, n_max, pool_pos, pool_len, top_k, topk_idx, topk_score, (hipStream_t)stream);
+  return st == CSA2_OK ? ok() : st;
+}
+
 csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max, int block_size,
                               int pool_blocks, int top_k, int32_t* pool_pos, int32_t* pool_len,
                               int32_t* topk_idx, float* topk_score, void* workspace, size_t ws_bytes,
@@ -201,22 +269,14 @@ csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max,
   csa2_status st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k);
   if (st != CSA2_OK) return st;
   REQUIRE_PTR(n_visible);
-  if (pool_blocks > 0) {
-    REQUIRE_PTR(pool_pos);
-    REQUIRE_PTR(pool_len);
-  }
-  REQUIRE_PTR(topk_idx);
-  REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
   const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  if ((st = check_pool_args(p, pool_pos, pool_len)) != CSA2_OK) return st;
+  if ((st = check_topk_args(topk_idx, topk_score)) != CSA2_OK) return st;
   if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
   FullWs w;
   carve_full(workspace, p, n_max, &w);
-  st = hip_check(csa2::launch_pool_topk(w.lists, w.cuts, p.n_units, p.blocks_per_unit, w.blkkey, p.nb_stride,
-                                        n_visible, n_max, w.scores, p.P, top_k,
-                                        p.internal_pool ? nullptr : pool_pos, p.cap,
-                                        p.internal_pool ? nullptr : pool_len, topk_idx, topk_score, p.Q,
-                                        (hipStream_t)stream),
-                 "pool/top-k launch");
+  st = launch_pool_stage(p, w, n_visible, n_max, pool_pos, pool_len, top_k, topk_idx, topk_score,
+                         (hipStream_t)stream);
   return st == CSA2_OK ? ok() : st;
 }
 
@@ -229,14 +289,10 @@ csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const 
   csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
   if (st != CSA2_OK) return st;
   if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
-  if (pool_blocks > 0) {
-    REQUIRE_PTR(pool_pos);
-    REQUIRE_PTR(pool_len);
-  }
-  REQUIRE_PTR(topk_idx);
-  REQUIRE(topk_score == nullptr || aligned16(topk_score), CSA2_ERR_INVALID_ARG, "topk_score must be 16-byte aligned");
-  if ((st = check_workspace(plan_full(B, T, n_max, pool_blocks, top_k), n_max, workspace, ws_bytes)) != CSA2_OK)
-    return st;
+  const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  if ((st = check_pool_args(p, pool_pos, pool_len)) != CSA2_OK) return st;
+  if ((st = check_topk_args(topk_idx, topk_score)) != CSA2_OK) return st;
+  if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
   st = csa2_index_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
                        top_k, workspace, ws_bytes, stream);
   if (st != CSA2_OK) return st;

@@ -25,12 +25,12 @@ hipError_t launch_ri_score(const uint8_t* idx_k, int64_t k_rows, const uint16_t*
                            int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s);
 
 // select.hip
-// Pool of the top P blocks plus the Top-K of the pool, one WG per query (pool_pos / pool_len
-// may be null).
-hipError_t launch_pool_topk(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
-                            const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max,
-                            const float* scores, int P, int K, int32_t* pool_pos, int cap_out,
-                            int32_t* pool_len, int32_t* topk_idx, float* topk_score, int Q, hipStream_t s);
+// Pool of the top P blocks (positions ascending, -1 padded to cap_out), one WG per query.
+// With K > 0 the same WG then takes the Top-K of the pool from the scan's scores.
+hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
+                       const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max, int P,
+                       int32_t* pool_pos, int cap_out, int32_t* pool_len, const float* scores, int K,
+                       int32_t* topk_idx, float* topk_score, int Q, hipStream_t s);
 // Top-K over candidate lists.  Candidate slot i of item it has position cand_pos[(it % Q)*cap + i]
 // (slots >= cand_len[it % Q] are empty).  by_position: the score of a candidate is
 // scores[(it % Q)*score_stride + pos]; otherwise scores[it*score_stride + slot].

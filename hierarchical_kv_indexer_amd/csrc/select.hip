@@ -27,24 +27,31 @@ constexpr int kBins = 4096;
 constexpr int kNT = kSelectThreads;      // 1024 threads
 constexpr int kWaves = kNT / 64;
 constexpr int kRankMax = 256;            // bins this small are resolved by direct ranking
-constexpr int kCandCap = 4096;           // LDS candidates (saturated units, slow-path compaction)
+constexpr int kCandCap = 4096;           // LDS candidates (re-read units, slow-path compaction)
 constexpr int kTopE = kMaxPool / kNT;    // slots per thread (16)
 constexpr int kUnitsPerThread = 4;       // units per thread in the pool kernel (<= 4096 units)
+static_assert(kBins == 4 * kNT, "find_bin gives each thread four bins");
+static_assert(kNT == 4 * kRankMax, "ranking splits the bin into four quarters");
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
-struct SelectSmem {
-  uint32_t hist[kBins];
+struct __attribute__((aligned(16))) SelectSmem {
+  uint32_t hist[kBins];                  // all zero between passes (find_bin clears what it reads)
   uint64_t rankbuf[kRankMax];
-  uint32_t rank[kRankMax];
-  uint32_t wsum[2][kWaves];
-  uint32_t wmin[2][kWaves];
-  uint32_t wmax[2][kWaves];
-  uint32_t ecnt[kTopE * kWaves];
+  uint32_t rankpart[3][kRankMax];        // partial ranks from quarters 1..3
+  u32x4 wred[2][kWaves];                 // per-wave partials of block reductions
+  uint32_t ecnt[2][kTopE * kWaves];      // per-(element, wave) counts of ordered_offsets
   uint64_t result;
   uint32_t found_bin, found_above, found_cnt, ncand, nrank, nsat;
 };
 
-// Block-wide collectives.  Each alternates between two LDS buffers, so one barrier per call
-// suffices: a buffer is rewritten only after the next call's barrier.
+// Clears the histogram and counters; the kernel's first barrier publishes it.
+__device__ __forceinline__ void smem_init(SelectSmem& sm) {
+  *(u32x4*)&sm.hist[4 * threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 0) { sm.nrank = 0; sm.ncand = 0; sm.nsat = 0; }
+}
+
+// Block-wide collectives with one barrier each.  Their LDS buffers alternate, so a buffer is
+// rewritten only after the next collective's barrier.
 struct Block {
   SelectSmem& sm;
   int parity = 0;
@@ -53,12 +60,12 @@ struct Block {
   __device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t inc = wave_incl_sum(v);
-    if (lane == 63) sm.wsum[parity][wave] = inc;
+    if (lane == 63) sm.wred[parity][wave].x = inc;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const uint32_t s = sm.wsum[parity][w];
+      const uint32_t s = sm.wred[parity][w].x;
       before += w < wave ? s : 0u;
       tot += s;
     }
@@ -66,50 +73,52 @@ struct Block {
     total = tot;
     return before + inc - v;
   }
-  __device__ __forceinline__ uint32_t sum(uint32_t v) {
-    uint32_t total;
-    (void)excl_scan(v, total);
-    return total;
-  }
-  __device__ __forceinline__ void minmax(uint32_t& mn, uint32_t& mx) {
+  // Block sum of cnt, min of mn and max of mx.
+  __device__ __forceinline__ void reduce(uint32_t& cnt, uint32_t& mn, uint32_t& mx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    cnt = wave_sum_u32(cnt);
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
-    if (lane == 0) { sm.wmin[parity][wave] = mn; sm.wmax[parity][wave] = mx; }
+    if (lane == 0) sm.wred[parity][wave] = u32x4{cnt, mn, mx, 0u};
     __syncthreads();
+    cnt = 0u;
+    mn = 0xffffffffu;
+    mx = 0u;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      mn = min(mn, sm.wmin[parity][w]);
-      mx = max(mx, sm.wmax[parity][w]);
+      const u32x4 r = sm.wred[parity][w];
+      cnt += r.x;
+      mn = min(mn, r.y);
+      mx = max(mx, r.z);
     }
     parity ^= 1;
   }
 };
 
-// Find b with above(b) < need <= above(b) + hist[b] (above(b): keys in bins > b).
-__device__ __forceinline__ void find_bin(int nbins, uint32_t need, Block& bk) {
+// Find b with above(b) < need <= above(b) + hist[b] (above(b): keys in bins > b) and clear the
+// histogram.  Thread t owns bins 4t .. 4t+3.
+__device__ __forceinline__ void find_bin(uint32_t need, Block& bk) {
   SelectSmem& sm = bk.sm;
   const int t = threadIdx.x;
-  uint32_t h[4], mine = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int bin = 4 * t + i;
-    h[i] = bin < nbins ? sm.hist[bin] : 0u;
-    mine += h[i];
-  }
+  u32x4* hp = (u32x4*)&sm.hist[4 * t];
+  const u32x4 h = *hp;
+  *hp = u32x4{0u, 0u, 0u, 0u};
+  const uint32_t mine = h.x + h.y + h.z + h.w;
   uint32_t total;
   const uint32_t below = bk.excl_scan(mine, total);
   uint32_t above = total - below - mine;
   if (above < need && need <= above + mine) {
+    const uint32_t hv[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
     for (int i = 3; i >= 0; --i) {
-      if (above < need && need <= above + h[i]) {
+      if (above < need && need <= above + hv[i]) {
         sm.found_bin = 4 * t + i;
         sm.found_above = above;
-        sm.found_cnt = h[i];
+        sm.found_cnt = hv[i];
       }
-      above += h[i];
+      above += hv[i];
     }
+    sm.nrank = 0u;
   }
   __syncthreads();
 }
@@ -122,6 +131,7 @@ __device__ __forceinline__ uint64_t key_hi(uint32_t mx32) { return ((uint64_t)mx
 // number of keys).  for_each(f) calls f(key) for every key this thread holds (keys outside
 // [lo, hi], e.g. 0 for "none", are ignored).  If `cand` is non-null, the keys of a bin with at
 // most kCandCap keys are copied there once and later passes read only the copy.
+// Requires a clear histogram (smem_init); leaves it clear.
 template <class ForEach>
 __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uint64_t hi, Block& bk,
                                uint64_t* cand) {
@@ -130,9 +140,6 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
   while (true) {
     if (lo == hi) return lo;
     const int shift = max(0, bitlen64(hi - lo) - 12);
-    const int nbins = (int)((hi - lo) >> shift) + 1;
-    for (int i = threadIdx.x; i < nbins; i += kNT) sm.hist[i] = 0u;
-    __syncthreads();
     auto count = [&](uint64_t k) {
       if (k >= lo && k <= hi) atomicAdd(&sm.hist[(uint32_t)((k - lo) >> shift)], 1u);
     };
@@ -143,7 +150,7 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
       for_each(count);
     }
     __syncthreads();
-    find_bin(nbins, need, bk);
+    find_bin(need, bk);
     const uint32_t bin = sm.found_bin, above = sm.found_above, cnt = sm.found_cnt;
     need -= above;
     const uint64_t nlo = lo + ((uint64_t)bin << shift);
@@ -152,9 +159,8 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
     hi = nhi;
     if (shift == 0) return lo;
     if (cnt <= (uint32_t)kRankMax) {
-      // rank the few keys of the bin directly
-      if (threadIdx.x == 0) sm.nrank = 0;
-      __syncthreads();
+      // rank the few keys of the bin directly: thread t compares key t % 256 with one quarter of
+      // the bin (the quarter is the same for a whole wave, so every LDS read is a broadcast)
       auto collect = [&](uint64_t k) {
         if (k >= lo && k <= hi) sm.rankbuf[atomicAdd(&sm.nrank, 1u)] = k;
       };
@@ -164,21 +170,23 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
       } else {
         for_each(collect);
       }
-      if (threadIdx.x < kRankMax) sm.rank[threadIdx.x] = 0u;
       __syncthreads();
-      {
-        // key i = t % kRankMax is compared with a quarter of the bin by each of 4 threads
-        const uint32_t i = threadIdx.x % kRankMax, part = threadIdx.x / kRankMax;
-        if (i < cnt) {
-          const uint64_t x = sm.rankbuf[i];
-          const uint32_t b0 = part * (kRankMax / 4), b1 = min(cnt, b0 + kRankMax / 4);
-          uint32_t r = 0;
-          for (uint32_t m = b0; m < b1; ++m) r += sm.rankbuf[m] > x ? 1u : 0u;
-          if (r) atomicAdd(&sm.rank[i], r);
-        }
+      constexpr uint32_t kPart = kRankMax / 4;
+      const uint32_t i = threadIdx.x % kRankMax, part = threadIdx.x / kRankMax;
+      const uint64_t x = sm.rankbuf[i];
+      const uint32_t m0 = part * kPart, m1 = min(cnt, m0 + kPart);
+      uint32_t r = 0, m = m0;
+      for (; m + 2 <= m1; m += 2) {
+        const u64x2 v = *(const u64x2*)(sm.rankbuf + m);
+        r += (v.x > x ? 1u : 0u) + (v.y > x ? 1u : 0u);
       }
+      if (m < m1) r += sm.rankbuf[m] > x ? 1u : 0u;
+      if (part) sm.rankpart[part - 1][i] = r;
       __syncthreads();
-      if (threadIdx.x < cnt && sm.rank[threadIdx.x] == need - 1) sm.result = sm.rankbuf[threadIdx.x];
+      if (part == 0 && i < cnt) {
+        r += sm.rankpart[0][i] + sm.rankpart[1][i] + sm.rankpart[2][i];
+        if (r == need - 1) sm.result = x;
+      }
       __syncthreads();
       return sm.result;
     }
@@ -189,8 +197,8 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
         if (k >= lo && k <= hi) cand[atomicAdd(&sm.ncand, 1u)] = k;
       });
       use_cand = true;
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
@@ -200,64 +208,79 @@ template <int N>
 __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&c)[N], uint32_t (&off)[N], Block& bk) {
   SelectSmem& sm = bk.sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* ec = sm.ecnt[bk.parity];
+  bk.parity ^= 1;
   uint32_t incl[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     incl[i] = wave_incl_sum(c[i]);
-    if (lane == 63) sm.ecnt[i * kWaves + wave] = incl[i];
+    if (lane == 63) ec[i * kWaves + wave] = incl[i];
   }
   __syncthreads();
-  // exclusive scan of the N*kWaves wave totals, in (i, wave) order
-  const uint32_t v = threadIdx.x < N * kWaves ? sm.ecnt[threadIdx.x] : 0u;
-  uint32_t total;
-  const uint32_t pre = bk.excl_scan(v, total);
-  __syncthreads();
-  if (threadIdx.x < N * kWaves) sm.ecnt[threadIdx.x] = pre;
-  __syncthreads();
+  // lane i < N: the total of element i over all waves and its part in waves before this one
+  uint32_t tot_i = 0u, pre_w = 0u;
+  if (lane < N) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) off[i] = sm.ecnt[i * kWaves + wave] + incl[i] - c[i];
-  return total;
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t v = ec[lane * kWaves + w];
+      tot_i += v;
+      pre_w += w < wave ? v : 0u;
+    }
+  }
+  const uint32_t inc_t = wave_incl_sum(tot_i);
+  const uint32_t base = inc_t - tot_i + pre_w;
+#pragma unroll
+  for (int i = 0; i < N; ++i) off[i] = (uint32_t)__builtin_amdgcn_readlane((int)base, i) + incl[i] - c[i];
+  return (uint32_t)__builtin_amdgcn_readlane((int)inc_t, N - 1);
 }
 
 // ------------------------------------------------------------------ pool + Full Top-K
 
-constexpr int kBitmapBlocks = 1 << 18;   // contexts up to 2M positions rank blocks with an LDS bitmap
+// Sort four block indices ascending (0xffffffff = none sorts last).
+__device__ __forceinline__ void sort4(uint32_t (&v)[4]) {
+  auto cx = [&](int a, int b) {
+    const uint32_t x = min(v[a], v[b]), y = max(v[a], v[b]);
+    v[a] = x;
+    v[b] = y;
+  };
+  cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+}
 
-// One WG per query.  Keeps the top P blocks by (block max desc, block asc) as the pool
-// (positions ascending; all blocks if there are at most P), then takes the Top-K positions of
-// the pool by (score desc, position asc), written in ascending order.
-// lists/cuts: per-unit five best blocks from the scan (see k_idx_scan), n_units <= 4096 with
-// blocks_per_unit blocks each.  blkkey rows are nb_max entries apart.
-// pool_pos / pool_len may be null (no pool output).
-__global__ __launch_bounds__(kNT) void k_pool_topk(
+// One WG per query: keeps the top P blocks by (block max desc, block asc) as the pool, written
+// as positions in ascending order (all blocks if there are at most P), -1 padded to cap_out.
+// With K > 0 it goes on to the Top-K positions of the pool by (score desc, position asc),
+// written in ascending order (-1 padded), from the pool held in LDS.
+// lists/cuts: per-unit five best blocks from the scan (see k_idx_scan); unit u covers blocks
+// [u*bpu, (u+1)*bpu), n_units <= 4096.  blkkey rows are nb_max entries apart.
+//
+// Pool order: thread t owns units i*kNT + t (i < 4).  Once the P-th best block key T* is
+// known, the selected blocks of a unit that was not re-read are its listed keys >= T*, sorted
+// by index; a re-read unit is counted and written by one wave, in index order, with ballots.
+// ordered_offsets places the units: unit order is block order.
+__global__ __launch_bounds__(kNT) void k_pool(
     const uint64_t* __restrict__ lists, const uint64_t* __restrict__ cuts, int n_units,
-    int blocks_per_unit, const uint32_t* __restrict__ blkkey, int nb_max,
-    const int32_t* __restrict__ n_visible, int n_max, const float* __restrict__ scores, int P, int K,
+    int bpu, const uint32_t* __restrict__ blkkey, int nb_max,
+    const int32_t* __restrict__ n_visible, int n_max, int P,
     int32_t* __restrict__ pool_pos, int cap_out, int32_t* __restrict__ pool_len,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+    const float* __restrict__ scores, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
   __shared__ SelectSmem sm;
-  __shared__ union {
-    uint64_t cand[kCandCap];                  // blocks of re-read units (before the pool is known)
-    uint32_t bitmap[kBitmapBlocks / 32];      // selected blocks (afterwards)
-  } u1;
-  __shared__ uint16_t wpre[kBitmapBlocks / 32];
-  __shared__ uint32_t sel[kMaxTopK];         // selected blocks, any order
+  __shared__ uint64_t cand[kCandCap];        // re-read units, bpu keys each (0 = below T0)
   __shared__ uint32_t byrank[kMaxTopK];      // selected blocks, ascending
-  __shared__ uint16_t satlist[kUnitsPerThread * kNT];
+  __shared__ uint16_t satunit[kUnitsPerThread * kNT];   // unit of each re-read slot
+  __shared__ uint32_t satcnt[kUnitsPerThread * kNT];    // its count, then its output offset
   Block bk{sm};
   const int q = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int nv = n_visible[q];
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   const int nb = (nv + kBlock - 1) / kBlock;
   const uint32_t* keys = blkkey + (size_t)q * nb_max;
-  uint64_t* cand = u1.cand;
+  smem_init(sm);
 
   const bool all = nb <= P;
   uint32_t nsel = 0;
   if (!all) {
     uint64_t e[kUnitsPerThread][4];
     uint64_t cut[kUnitsPerThread];
-    bool sat[kUnitsPerThread];
     uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i) {
@@ -285,156 +308,144 @@ __global__ __launch_bounds__(kNT) void k_pool_topk(
 #pragma unroll
         for (int r = 0; r < 4; ++r) f(e[i][r]);
     };
-    uint64_t t0 = 1ull;
-    const uint32_t n_listed = bk.sum(nvalid);
-    bk.minmax(mn, mx);
-    if (n_listed >= (uint32_t)P) t0 = select_kth(for_each_e, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
-    // units that may hold unlisted blocks >= t0: re-read them (one wave per unit)
-    if (t == 0) { sm.nsat = 0; sm.ncand = 0; }
-    __syncthreads();
+    bk.reduce(nvalid, mn, mx);
+    uint64_t t0 = 1ull;                       // T0 <= T*: the P-th best listed key
+    if (nvalid >= (uint32_t)P) t0 = select_kth(for_each_e, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
+
+    // units that may hold unlisted blocks >= T0 are re-read; sidx = their slot
+    int sidx[kUnitsPerThread];
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i) {
-      sat[i] = cut[i] != 0ull && cut[i] >= t0;
-      if (sat[i]) satlist[atomicAdd(&sm.nsat, 1u)] = (uint16_t)(i * kNT + t);
+      const bool sat = cut[i] != 0ull && cut[i] >= t0;
+      sidx[i] = sat ? (int)atomicAdd(&sm.nsat, 1u) : -1;
+      if (sat) satunit[sidx[i]] = (uint16_t)(i * kNT + t);
     }
     __syncthreads();
     const uint32_t nsat = sm.nsat;
-    for (uint32_t si = wave; si < nsat; si += kWaves) {
-      const int jb = satlist[si] * blocks_per_unit, je = min(nb, jb + blocks_per_unit);
-      for (int jj = jb + lane; jj < je; jj += 64) {
-        const uint64_t k = rank_key(keys[jj], (uint32_t)jj);
-        if (k >= t0) {
-          const uint32_t idx = atomicAdd(&sm.ncand, 1u);
-          if (idx < (uint32_t)kCandCap) cand[idx] = k;
+    const bool dense = nsat * (uint32_t)bpu <= (uint32_t)kCandCap;   // re-read keys fit in LDS
+    auto unit_key = [&](uint32_t si, int o) -> uint64_t {   // key of block o of re-read slot si
+      const int jj = satunit[si] * bpu + o;
+      return jj < nb ? rank_key(keys[jj], (uint32_t)jj) : 0ull;
+    };
+    if (dense) {
+      for (uint32_t si = wave; si < nsat; si += kWaves)
+        for (int o = lane; o < bpu; o += 64) {
+          const uint64_t k = unit_key(si, o);
+          cand[si * bpu + o] = k >= t0 ? k : 0ull;
         }
-      }
     }
-    __syncthreads();
-    const uint32_t ncand = sm.ncand;
-    const bool slow = ncand > (uint32_t)kCandCap;
-    uint64_t tstar;
-    // candidates: listed keys >= t0 of units not re-read, plus the re-read units' blocks >= t0
+    auto sat_key = [&](uint32_t si, int o) -> uint64_t {
+      return dense ? cand[si * bpu + o] : unit_key(si, o);
+    };
+    // listed keys that stay candidates: >= T0, in units that were not re-read
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (sat[i] || e[i][r] < t0) e[i][r] = 0ull;
-    if (nsat == 0) {
-      tstar = t0;                    // every block >= t0 is listed
-    } else if (!slow) {
+        if (sidx[i] >= 0 || e[i][r] < t0) e[i][r] = 0ull;
+    __syncthreads();
+
+    uint64_t tstar = t0;                      // no unit re-read: every block >= T0 is listed
+    if (nsat > 0) {
+      uint32_t dummy = 0;
       mn = 0xffffffffu;
       mx = 0u;
-#pragma unroll
-      for (int i = 0; i < kUnitsPerThread; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (e[i][r]) { mn = min(mn, (uint32_t)(e[i][r] >> 32)); mx = max(mx, (uint32_t)(e[i][r] >> 32)); }
-      for (uint32_t i = t; i < ncand; i += kNT) {
-        mn = min(mn, (uint32_t)(cand[i] >> 32));
-        mx = max(mx, (uint32_t)(cand[i] >> 32));
-      }
-      bk.minmax(mn, mx);
-      auto for_each_c = [&](auto f) {
+      if (dense) {
 #pragma unroll
         for (int i = 0; i < kUnitsPerThread; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) f(e[i][r]);
-        for (uint32_t i = threadIdx.x; i < ncand; i += kNT) f(cand[i]);
-      };
-      tstar = select_kth(for_each_c, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
-    } else {
-      // many units re-read (heavy ties): select over every block directly
-      mn = 0xffffffffu;
-      mx = 0u;
-      for (int jj = t; jj < nb; jj += kNT) { mn = min(mn, keys[jj]); mx = max(mx, keys[jj]); }
-      bk.minmax(mn, mx);
-      tstar = select_kth(
-          [&](auto f) {
-            constexpr int kB = 8;
-            for (int base = t; base < nb; base += kNT * kB) {
-              uint32_t kk[kB];
+          for (int r = 0; r < 4; ++r)
+            if (e[i][r]) { mn = min(mn, (uint32_t)(e[i][r] >> 32)); mx = max(mx, (uint32_t)(e[i][r] >> 32)); }
+        const uint32_t nc = nsat * (uint32_t)bpu;
+        for (uint32_t i = t; i < nc; i += kNT)
+          if (cand[i]) { mn = min(mn, (uint32_t)(cand[i] >> 32)); mx = max(mx, (uint32_t)(cand[i] >> 32)); }
+        bk.reduce(dummy, mn, mx);
+        auto for_each_c = [&](auto f) {
 #pragma unroll
-              for (int u = 0; u < kB; ++u) {
-                const int jj = base + u * kNT;
-                kk[u] = keys[jj < nb ? jj : 0];
-              }
+          for (int i = 0; i < kUnitsPerThread; ++i)
 #pragma unroll
-              for (int u = 0; u < kB; ++u) {
-                const int jj = base + u * kNT;
-                if (jj < nb) f(rank_key(kk[u], (uint32_t)jj));
+            for (int r = 0; r < 4; ++r) f(e[i][r]);
+          for (uint32_t i = threadIdx.x; i < nc; i += kNT) f(cand[i]);
+        };
+        tstar = select_kth(for_each_c, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
+      } else {
+        // many units re-read (heavy ties): select over every block directly
+        for (int jj = t; jj < nb; jj += kNT) { mn = min(mn, keys[jj]); mx = max(mx, keys[jj]); }
+        bk.reduce(dummy, mn, mx);
+        tstar = select_kth(
+            [&](auto f) {
+              constexpr int kB = 8;
+              for (int base = t; base < nb; base += kNT * kB) {
+                uint32_t kk[kB];
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                  const int jj = base + u * kNT;
+                  kk[u] = keys[jj < nb ? jj : 0];
+                }
+#pragma unroll
+                for (int u = 0; u < kB; ++u) {
+                  const int jj = base + u * kNT;
+                  if (jj < nb) f(rank_key(kk[u], (uint32_t)jj));
+                }
               }
-            }
-          },
-          (uint32_t)P, key_lo(mn), key_hi(mx), bk, cand);
+            },
+            (uint32_t)P, key_lo(mn), key_hi(mx), bk, cand);
+      }
     }
-    // the selected blocks, in any order
-    if (t == 0) sm.nrank = 0;
+
+    // selected blocks of each re-read unit, counted by one wave
+    for (uint32_t si = wave; si < nsat; si += kWaves) {
+      uint32_t c = 0;
+      for (int o0 = 0; o0 < bpu; o0 += 64) {
+        const int o = o0 + lane;
+        c += (uint32_t)__popcll(__ballot(o < bpu && sat_key(si, o) >= tstar));
+      }
+      if (lane == 0) satcnt[si] = c;
+    }
     __syncthreads();
-    if (!slow) {
+    uint32_t lb[kUnitsPerThread][4], cnt[kUnitsPerThread], off[kUnitsPerThread];
 #pragma unroll
-      for (int i = 0; i < kUnitsPerThread; ++i)
+    for (int i = 0; i < kUnitsPerThread; ++i) {
+      cnt[i] = 0u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lb[i][r] = 0xffffffffu;
+      if (sidx[i] < 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (e[i][r] && e[i][r] >= tstar) sel[atomicAdd(&sm.nrank, 1u)] = rank_key_index(e[i][r]);
-      for (uint32_t i = t; i < ncand; i += kNT)
-        if (cand[i] >= tstar) sel[atomicAdd(&sm.nrank, 1u)] = rank_key_index(cand[i]);
-    } else {
-      for (int jj = t; jj < nb; jj += kNT)
-        if (rank_key(keys[jj], (uint32_t)jj) >= tstar) sel[atomicAdd(&sm.nrank, 1u)] = (uint32_t)jj;
+          if (e[i][r] >= tstar) { lb[i][r] = rank_key_index(e[i][r]); ++cnt[i]; }
+        sort4(lb[i]);
+      } else {
+        cnt[i] = satcnt[sidx[i]];
+      }
+    }
+    nsel = min(ordered_offsets(cnt, off, bk), (uint32_t)P);
+#pragma unroll
+    for (int i = 0; i < kUnitsPerThread; ++i) {
+      if (sidx[i] < 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((uint32_t)r < cnt[i] && off[i] + r < (uint32_t)P) byrank[off[i] + r] = lb[i][r];
+      } else {
+        satcnt[sidx[i]] = off[i];
+      }
     }
     __syncthreads();
-    nsel = min(sm.nrank, (uint32_t)P);
-    // ascending order of the selected blocks
-    if (nb <= kBitmapBlocks) {
-      const int nw = (nb + 31) >> 5;
-      for (int w = t; w < nw; w += kNT) u1.bitmap[w] = 0u;
-      __syncthreads();
-      for (uint32_t i = t; i < nsel; i += kNT) atomicOr(&u1.bitmap[sel[i] >> 5], 1u << (sel[i] & 31));
-      __syncthreads();
-      constexpr int kWpt = kBitmapBlocks / 32 / kNT;   // words per thread (8)
-      uint32_t wc[kWpt], mine = 0;
-#pragma unroll
-      for (int i = 0; i < kWpt; ++i) {
-        const int w = kWpt * t + i;
-        wc[i] = w < nw ? (uint32_t)__popc(u1.bitmap[w]) : 0u;
-        mine += wc[i];
+    for (uint32_t si = wave; si < nsat; si += kWaves) {
+      uint32_t n = satcnt[si];
+      const int jb = satunit[si] * bpu;
+      for (int o0 = 0; o0 < bpu; o0 += 64) {
+        const int o = o0 + lane;
+        const bool sel = o < bpu && sat_key(si, o) >= tstar;
+        const uint64_t m = __ballot(sel);
+        const uint32_t at = n + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+        if (sel && at < (uint32_t)P) byrank[at] = (uint32_t)(jb + o);
+        n += (uint32_t)__popcll(m);
       }
-      uint32_t tot;
-      uint32_t pre = bk.excl_scan(mine, tot);
-#pragma unroll
-      for (int i = 0; i < kWpt; ++i) {
-        const int w = kWpt * t + i;
-        if (w < nw) wpre[w] = (uint16_t)pre;
-        pre += wc[i];
-      }
-      __syncthreads();
-      for (uint32_t i = t; i < nsel; i += kNT) {
-        const uint32_t jj = sel[i];
-        const uint32_t rk = wpre[jj >> 5] + (uint32_t)__popc(u1.bitmap[jj >> 5] & ((1u << (jj & 31)) - 1u));
-        byrank[rk] = jj;
-      }
-    } else {
-      // bitonic sort of the (padded) selection
-      constexpr int kS = kMaxTopK;
-      for (int i = t; i < kS; i += kNT) byrank[i] = i < (int)nsel ? sel[i] : 0xffffffffu;
-      __syncthreads();
-      for (int k2 = 2; k2 <= kS; k2 <<= 1)
-        for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
-          for (int i = t; i < kS; i += kNT) {
-            const int x = i ^ j2;
-            if (x > i) {
-              const uint32_t a = byrank[i], c = byrank[x];
-              const bool up = (i & k2) == 0;
-              if ((a > c) == up) { byrank[i] = c; byrank[x] = a; }
-            }
-          }
-          __syncthreads();
-        }
     }
     __syncthreads();
   }
 
-  // ---- pool positions: slot s holds block byrank[s / 8], or position s when all blocks are kept
+  // pool positions: slot s holds block byrank[s / 8], or position s when all blocks are kept
   int total;
   if (all) {
     total = nv;
@@ -443,13 +454,12 @@ __global__ __launch_bounds__(kNT) void k_pool_topk(
     if (nsel > 0 && (int)byrank[nsel - 1] == nb - 1) total -= kBlock - (nv - kBlock * (nb - 1));
   }
   auto slot_pos = [&](int sl) { return all ? sl : kBlock * (int)byrank[sl >> 3] + (sl & 7); };
-  if (pool_pos) {
-    int32_t* gp = pool_pos + (size_t)q * cap_out;
-    for (int sl = t; sl < cap_out; sl += kNT) gp[sl] = sl < total ? slot_pos(sl) : -1;
-  }
-  if (pool_len && t == 0) pool_len[q] = total;
+  int32_t* gp = pool_pos + (size_t)q * cap_out;
+  for (int sl = t; sl < cap_out; sl += kNT) gp[sl] = sl < total ? slot_pos(sl) : -1;
+  if (t == 0) pool_len[q] = total;
+  if (K == 0) return;
 
-  // ---- Top-K of the pool (slot = i*kNT + t)
+  // Top-K of the pool by (score desc, position asc), slot = i*kNT + t, written in slot order
   const float* sc = scores + (size_t)q * n_max;
   int32_t ps[kTopE];
   float sv[kTopE];
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(kNT) void k_pool_topk(
 #pragma unroll
   for (int i = 0; i < kTopE; ++i) sv[i] = sc[ps[i] >= 0 ? ps[i] : 0];
   uint64_t key[kTopE];
-  uint32_t mn = 0xffffffffu, mx = 0u;
+  uint32_t mn = 0xffffffffu, mx = 0u, dummy = 0u;
 #pragma unroll
   for (int i = 0; i < kTopE; ++i) {
     const uint32_t k32 = score_key(sv[i]);
@@ -470,7 +480,7 @@ __global__ __launch_bounds__(kNT) void k_pool_topk(
   }
   uint64_t thr = 1ull;
   if (total > K) {
-    bk.minmax(mn, mx);
+    bk.reduce(dummy, mn, mx);
     auto for_each_k = [&](auto f) {
 #pragma unroll
       for (int i = 0; i < kTopE; ++i) f(key[i]);
@@ -486,7 +496,7 @@ __global__ __launch_bounds__(kNT) void k_pool_topk(
 #pragma unroll
   for (int i = 0; i < kTopE; ++i) {
     if (c2[i] && o2[i] < (uint32_t)K) {
-      oi[o2[i]] = ps[i];
+      oi[o2[i]] = (int32_t)rank_key_index(key[i]);
       if (os) os[o2[i]] = key_score((uint32_t)(key[i] >> 32));
     }
   }
@@ -496,12 +506,12 @@ __global__ __launch_bounds__(kNT) void k_pool_topk(
   }
 }
 
-hipError_t launch_pool_topk(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
-                            const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max,
-                            const float* scores, int P, int K, int32_t* pool_pos, int cap_out,
-                            int32_t* pool_len, int32_t* topk_idx, float* topk_score, int Q, hipStream_t s) {
-  hipLaunchKernelGGL(k_pool_topk, dim3(Q), dim3(kNT), 0, s, lists, cuts, n_units, blocks_per_unit, blkkey,
-                     nb_max, n_visible, n_max, scores, P, K, pool_pos, cap_out, pool_len, topk_idx, topk_score);
+hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
+                       const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max, int P,
+                       int32_t* pool_pos, int cap_out, int32_t* pool_len, const float* scores, int K,
+                       int32_t* topk_idx, float* topk_score, int Q, hipStream_t s) {
+  hipLaunchKernelGGL(k_pool, dim3(Q), dim3(kNT), 0, s, lists, cuts, n_units, blocks_per_unit, blkkey,
+                     nb_max, n_visible, n_max, P, pool_pos, cap_out, pool_len, scores, K, topk_idx, topk_score);
   return hipGetLastError();
 }
 
@@ -519,6 +529,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
   __shared__ SelectSmem sm;
   Block bk{sm};
   const int it = blockIdx.x, q = it % Q, t = threadIdx.x;
+  smem_init(sm);
   int len = cand_len[q];
   len = len < 0 ? 0 : (len > cap ? cap : len);
   const int32_t* cp = cand_pos + (size_t)q * cap;
@@ -548,9 +559,8 @@ __global__ __launch_bounds__(kNT) void k_topk(
     if (ok[e]) { mn = min(mn, k32); mx = max(mx, k32); }
   }
   uint64_t thr = 1ull;
-  const uint32_t n_valid = bk.sum(nvalid);
-  if (n_valid > (uint32_t)k) {
-    bk.minmax(mn, mx);
+  bk.reduce(nvalid, mn, mx);
+  if (nvalid > (uint32_t)k) {
     auto for_each = [&](auto f) {
 #pragma unroll
       for (int e = 0; e < kTopE; ++e) f(key[e]);
@@ -566,7 +576,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
 #pragma unroll
   for (int e = 0; e < kTopE; ++e) {
     if (c[e] && off[e] < (uint32_t)k) {   // duplicate positions in a caller pool can tie
-      oi[off[e]] = pos[e];
+      oi[off[e]] = (int32_t)rank_key_index(key[e]);
       if (os) os[off[e]] = key_score((uint32_t)(key[e] >> 32));
     }
   }

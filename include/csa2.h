@@ -65,12 +65,12 @@ typedef enum {
 /* Message of the last non-OK status returned on the calling thread ("" if none). */
 const char* csa2_last_error(void);
 
-/* Step A1 on its own: indexer query prep. in_bf16[n] -> out_e4m3[n], round to nearest even,
+/* Indexer query preparation on its own. in_bf16[n] -> out_e4m3[n], round to nearest even,
  * saturating to +-448, NaN -> 0x7F. csa2_index_full / csa2_reindex apply the same rounding
  * internally; this entry exists to verify it and for callers that keep E4M3 queries. */
 csa2_status csa2_quantize_query(const uint16_t* in_bf16, uint8_t* out_e4m3, int64_t n, void* stream);
 
-/* Steps A1-A2 on their own: the Full scan's scores without any selection.
+/* Query preparation and the Full scan on their own: every visible position's score, no selection.
  *   idx_k      [B][k_rows_per_seq][128] E4M3 indexer keys
  *   idx_q      [B][T][32][128] bf16 indexer queries
  *   head_w     [B][T][32] float head weights
@@ -95,14 +95,30 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, cons
  * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= 2^23, n_max <= k_rows_per_seq. */
 size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k);
 
-/* The two stages of csa2_index_full as separate calls (same arguments, same workspace, which
- * carries the scan's scores and block keys from the first call to the second; the pair must
- * be enqueued in order on one stream with identical shape arguments).
- *   csa2_index_scan:   steps A1-A2 plus the block maxima (reads idx_k, idx_q, head_w, n_visible)
- *   csa2_index_select: steps A3-A4 (pool and Top-K; reads n_visible and the workspace) */
+/* The stages of csa2_index_full as separate calls.  They take the same arguments and the same
+ * workspace, which carries the scan's scores and block keys (and, with pool_blocks == 0, the
+ * internal pool) from one stage to the next; enqueue them in this order with identical shape
+ * arguments.  csa2_index_pool and csa2_index_topk may run on different streams as long as
+ * each starts after the previous stage has finished (e.g. the Top-K of the Full layer on one
+ * stream while csa2_reindex scores the same pool on another).
+ *   csa2_index_scan:   query preparation, the scan and the block maxima
+ *                      (reads idx_k, idx_q, head_w, n_visible)
+ *   csa2_index_pool:   the candidate pool (reads n_visible and the workspace; writes pool_pos
+ *                      and pool_len, which may be NULL only when pool_blocks == 0)
+ *   csa2_index_topk:   the Top-K over the pool (reads the workspace and the pool)
+ *   csa2_index_select: the pool and its Top-K in one pass (same results as csa2_index_pool
+ *                      followed by csa2_index_topk) */
 csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k,
+                            void* workspace, size_t ws_bytes, void* stream);
+csa2_status csa2_index_pool(const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k,
+                            int32_t* pool_pos, int32_t* pool_len,
+                            void* workspace, size_t ws_bytes, void* stream);
+csa2_status csa2_index_topk(int B, int T, int n_max, int block_size, int pool_blocks, int top_k,
+                            const int32_t* pool_pos, const int32_t* pool_len,
+                            int32_t* topk_idx, float* topk_score,
                             void* workspace, size_t ws_bytes, void* stream);
 csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max,
                               int block_size, int pool_blocks, int top_k,

@@ -83,3 +83,14 @@ def test_reindex_and_attention_reject(H):
     expect(H, 2, lambda: H.csa2_sparse_attn(*a))
     a = list(base); a[19] = None; a[20] = 0                          # split rows need a workspace
     expect(H, 3, lambda: H.csa2_sparse_attn(*a))
+
+
+def test_stage_entries_reject(H):
+    # pool stage: a caller pool is required when pool_blocks > 0
+    expect(H, 1, lambda: H.csa2_index_pool(FAKE, 1, 1, 4096, 8, 64, 64, None, FAKE, FAKE, 1 << 30))
+    expect(H, 2, lambda: H.csa2_index_pool(FAKE, 1, 1, 4096, 16, 64, 64, FAKE, FAKE, FAKE, 1 << 30))
+    expect(H, 3, lambda: H.csa2_index_pool(FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, FAKE, 64))
+    # top-k stage: output required, internal pool allowed when pool_blocks == 0
+    expect(H, 1, lambda: H.csa2_index_topk(1, 1, 4096, 8, 64, 64, FAKE, FAKE, None, None, FAKE, 1 << 30))
+    expect(H, 1, lambda: H.csa2_index_topk(1, 1, 4096, 8, 0, 64, None, None, FAKE, FAKE + 4, FAKE, 1 << 30))
+    expect(H, 3, lambda: H.csa2_index_topk(1, 1, 4096, 8, 0, 64, None, None, FAKE, None, FAKE, 8))

@@ -1,0 +1,80 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times: the
+whole chain runs for every query of the workload; the oracle checks sampled queries.
+
+  decode_1m        batch 1, 1M-entry context, Full + 4 Reindex + 15 Reuse (20 attention layers)
+  decode_b8_128k   batch 8, 128K entries each, Full + 4 Reindex + 5 Reuse, 64 heads
+  reindex_pool_256k  64 queries with their own 16384-position pools over a 256K context
+  prefill_4k_64k   4096 causal queries over 32768 entries, Full + 5 Reuse, 64 heads
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import gpu_chain as G
+from tests.test_gpu_parity import run_chain_and_check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    import hierarchical_kv_indexer_amd as H
+    H.lib()
+
+
+def _announce(name, queries):
+    print(f"\n[full-size] {name}: checking queries {queries}", flush=True)
+
+
+def test_decode_1m_whole_chain():
+    w = workloads.WORKLOADS["decode_1m"]
+    inp = workloads.make_inputs(w)
+    _announce(w.name, [(0, 0)])
+    run_chain_and_check(w, inp, [(0, 0)])
+    g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
+    assert np.isin(inp["planted_pos"], g["topk"][0, 0]).all(), "planted cluster not recalled"
+
+
+def test_decode_b8_128k_sampled():
+    w = workloads.WORKLOADS["decode_b8_128k"]
+    inp = workloads.make_inputs(w)
+    queries = [(0, 0), (5, 0), (7, 0)]
+    _announce(w.name, queries)
+    run_chain_and_check(w, inp, queries)
+
+
+def test_reindex_pool_256k_sampled():
+    w = workloads.WORKLOADS["reindex_pool_256k"]
+    inp = workloads.make_inputs(w)
+    queries = [(0, 0), (0, 17), (0, 63)]
+    _announce(w.name, queries)
+    run_chain_and_check(w, inp, queries)
+
+
+def test_prefill_4k_64k_sampled():
+    w = workloads.WORKLOADS["prefill_4k_64k"]
+    inp = workloads.make_inputs(w)
+    queries = [(0, 0), (0, 2047), (0, 4095)]
+    _announce(w.name, queries)
+    run_chain_and_check(w, inp, queries)
+
+
+def test_decode_1m_all_keys_equal():
+    """Every indexer key equal: all scores tie, so ranking falls to position order.  The pool is
+    the first P blocks, every Top-K (Full and Reindex) the first K positions.  Every unit of the
+    scan holds more than four pool blocks, so the whole-context selection path runs."""
+    w = workloads.small_variant(workloads.WORKLOADS["decode_1m"], seed=97)
+    inp = workloads.make_inputs(w, with_attention=False)
+    inp["idx_k"][0, :] = inp["idx_k"][0, 12345]
+    _announce("decode_1m, all keys equal", [(0, 0)])
+    g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
+    cap = w.pool_cap
+    assert int(g["pool_len"][0, 0]) == cap
+    assert np.array_equal(g["pool_pos"][0, 0], np.arange(cap, dtype=np.int32))
+    assert np.array_equal(g["topk"][0, 0], np.arange(w.top_k, dtype=np.int32))
+    assert np.all(g["topk_score"][0, 0] == g["topk_score"][0, 0, 0])
+    ri = G.gpu_reindex(inp, 1, 1, g["pool_pos"], g["pool_len"], w.top_k)
+    for r in range(w.n_reindex):
+        assert np.array_equal(ri["topk"][r, 0, 0], np.arange(w.top_k, dtype=np.int32))

@@ -133,6 +133,37 @@ def test_index_full_parity(N, P, K, nv):
         check_full(w, inp, gpu, 0, t)
 
 
+@pytest.mark.parametrize("P", [256, 0])
+def test_stage_entries_match_index_full(P):
+    """scan, pool and Top-K called as separate stages (the Top-K on a second stream) give the
+    same bits as csa2_index_full."""
+    import hierarchical_kv_indexer_amd as H
+    N, K, T = 20000, 300, 2
+    w = small(T=T, N=N, pool_blocks=P, top_k=K, seed=3100 + P)
+    inp = workloads.make_inputs(w, with_attention=False)
+    ref = G.gpu_index_full(inp, 1, T, N, P, K)
+    cap = max(P * 8, 1)
+    pool_pos = G.empty((1, T, cap), torch.int32) if P else None
+    pool_len = G.empty((1, T), torch.int32) if P else None
+    idx = G.empty((1, T, K), torch.int32)
+    sc = G.empty((1, T, K), torch.float32)
+    wsb = H.csa2_index_full_workspace(1, T, N, 8, P, K)
+    ws = G.empty((wsb,), torch.uint8)
+    k, q, hw, nv = G.dev(inp["idx_k"]), G.dev(inp["idx_q"]), G.dev(inp["head_w"]), G.dev(inp["n_visible"])
+    H.csa2_index_scan(k, N, q, hw, nv, 1, T, N, 8, P, K, ws, wsb)
+    H.csa2_index_pool(nv, 1, T, N, 8, P, K, pool_pos, pool_len, ws, wsb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        H.csa2_index_topk(1, T, N, 8, P, K, pool_pos, pool_len, idx, sc, ws, wsb)
+    torch.cuda.current_stream().wait_stream(side)
+    assert np.array_equal(G.host(idx), ref["topk"])
+    assert np.array_equal(G.host(sc).view(np.uint32), ref["topk_score"].view(np.uint32))
+    if P:
+        assert np.array_equal(G.host(pool_pos), ref["pool_pos"])
+        assert np.array_equal(G.host(pool_len), ref["pool_len"])
+
+
 def test_index_full_no_pool_dense_topk():
     w = small(T=3, N=9000, pool_blocks=0, top_k=200, seed=31)
     inp = workloads.make_inputs(w, with_attention=False)
