@@ -8,6 +8,8 @@
 // k-th largest key: a radix select whose digit width adapts to the live key range.  Each pass
 // histograms the keys inside [lo, hi] into at most 4096 bins of width 2^shift and keeps the bin
 // holding the k-th key; once that bin holds at most kRankMax keys they are ranked directly.
+// While the digit lies in the upper (score) half of the key, a pass works on 32-bit values and
+// sends out-of-range keys to spare bins instead of branching.
 //
 // Pool selection does not revisit every block: the scan leaves, for each unit (one wave's
 // contiguous range of blocks), its four best blocks and the fifth best key.  With T0 = the
@@ -16,8 +18,10 @@
 // whose fifth best key reaches T0 are re-read in full.  The P best of the surviving candidates
 // are exactly the P best blocks (and when no unit is re-read, T* = T0).
 //
-// Layout: element i of thread t is slot i*1024 + t, so every load instruction of a wave reads
-// consecutive addresses; outputs keep slot order through per-(element, wave) ballot counts.
+// A workgroup is 1024 threads (16 waves on one CU), so every per-thread instruction costs
+// about 16 cycles: the code keeps per-key work small.  Element i of thread t is slot i*1024 + t,
+// so every load instruction of a wave reads consecutive addresses; output in slot order takes
+// in-wave prefixes from ballots and one barrier for the per-wave totals.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,18 +32,18 @@ constexpr int kNT = kSelectThreads;      // 1024 threads
 constexpr int kWaves = kNT / 64;
 constexpr int kRankMax = 256;            // bins this small are resolved by direct ranking
 constexpr int kCandCap = 4096;           // LDS candidates (re-read units, slow-path compaction)
-constexpr int kTopE = kMaxPool / kNT;    // slots per thread (16)
+constexpr int kE = kMaxPool / kNT;       // slots per thread (16): slot i*kNT + t for i < kE
 constexpr int kUnitsPerThread = 4;       // units per thread in the pool kernel (<= 4096 units)
 static_assert(kBins == 4 * kNT, "find_bin gives each thread four bins");
 static_assert(kNT == 4 * kRankMax, "ranking splits the bin into four quarters");
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
 
 struct __attribute__((aligned(16))) SelectSmem {
-  uint32_t hist[kBins];                  // all zero between passes (find_bin clears what it reads)
+  uint32_t hist[kBins + 64];             // all zero between passes; bins kBins.. take strays
   uint64_t rankbuf[kRankMax];
   uint32_t rankpart[3][kRankMax];        // partial ranks from quarters 1..3
   u32x4 wred[2][kWaves];                 // per-wave partials of block reductions
-  uint32_t ecnt[2][kTopE * kWaves];      // per-(element, wave) counts of ordered_offsets
+  uint32_t ecnt[2][kE * kWaves];         // per-(element, wave) totals of ordered_offsets
   uint64_t result;
   uint32_t found_bin, found_above, found_cnt, ncand, nrank, nsat;
 };
@@ -95,6 +99,48 @@ struct Block {
   }
 };
 
+// Offsets that keep slot order (slot = i*kNT + t): off[i] = the sum of the counts c of every
+// earlier slot; returns the total.  Each element's in-wave prefix comes from a ballot (counts
+// 0/1, FLAGS) or a DPP scan (any counts); one barrier exchanges the per-(element, wave) totals,
+// and lane i of each wave then prefixes element i over the waves.  N <= kE.
+template <bool FLAGS, int N>
+__device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&c)[N], uint32_t (&off)[N], Block& bk) {
+  SelectSmem& sm = bk.sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* ec = sm.ecnt[bk.parity];
+  bk.parity ^= 1;
+  uint32_t pre[N], mine = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (FLAGS) {
+      const uint64_t m = __ballot(c[i] != 0u);
+      pre[i] = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (lane == i) mine = (uint32_t)__popcll(m);
+    } else {
+      const uint32_t inc = wave_incl_sum(c[i]);
+      pre[i] = inc - c[i];
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      if (lane == i) mine = tot;
+    }
+  }
+  if (lane < N) ec[lane * kWaves + wave] = mine;
+  __syncthreads();
+  uint32_t tot_i = 0u, pre_w = 0u;
+  if (lane < N) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t v = ec[lane * kWaves + w];
+      tot_i += v;
+      pre_w += w < wave ? v : 0u;
+    }
+  }
+  const uint32_t inc_t = wave_incl_sum(tot_i);
+  const uint32_t base = inc_t - tot_i + pre_w;
+#pragma unroll
+  for (int i = 0; i < N; ++i) off[i] = (uint32_t)__builtin_amdgcn_readlane((int)base, i) + pre[i];
+  return (uint32_t)__builtin_amdgcn_readlane((int)inc_t, N - 1);
+}
+
 // Find b with above(b) < need <= above(b) + hist[b] (above(b): keys in bins > b) and clear the
 // histogram.  Thread t owns bins 4t .. 4t+3.
 __device__ __forceinline__ void find_bin(uint32_t need, Block& bk) {
@@ -128,26 +174,40 @@ __device__ __forceinline__ uint64_t key_lo(uint32_t mn32) { return (uint64_t)mn3
 __device__ __forceinline__ uint64_t key_hi(uint32_t mx32) { return ((uint64_t)mx32 << 32) | 0xffffffffull; }
 
 // The need-th largest of a set of distinct 64-bit keys, all inside [lo, hi] (1 <= need <= the
-// number of keys).  for_each(f) calls f(key) for every key this thread holds (keys outside
-// [lo, hi], e.g. 0 for "none", are ignored).  If `cand` is non-null, the keys of a bin with at
-// most kCandCap keys are copied there once and later passes read only the copy.
+// number of keys).  for_each(f) calls f(key) for every key this thread holds (0 = none; keys
+// outside [lo, hi] are ignored).  If `cand` is non-null, the keys of a bin with at most
+// kCandCap keys are copied there once and later passes read only the copy.
 // Requires a clear histogram (smem_init); leaves it clear.
 template <class ForEach>
 __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uint64_t hi, Block& bk,
                                uint64_t* cand) {
   SelectSmem& sm = bk.sm;
   bool use_cand = false;
+  if (lo == 0ull) lo = 1ull;             // 0 marks "no key"
+  const uint32_t stray = (uint32_t)kBins + (threadIdx.x & 63);
   while (true) {
-    if (lo == hi) return lo;
+    if (lo >= hi) return lo;
     const int shift = max(0, bitlen64(hi - lo) - 12);
-    auto count = [&](uint64_t k) {
-      if (k >= lo && k <= hi) atomicAdd(&sm.hist[(uint32_t)((k - lo) >> shift)], 1u);
-    };
-    if (use_cand) {
-      const uint32_t n = sm.ncand;
-      for (uint32_t i = threadIdx.x; i < n; i += kNT) count(cand[i]);
+    // With the digit in the upper half and lo's lower half zero (hi's is then all ones), a key
+    // is in range iff its upper half is: one 32-bit subtract and compare per key.
+    const bool wide = shift >= 32 && (uint32_t)lo == 0u && !use_cand;
+    if (wide) {
+      const uint32_t lo32 = (uint32_t)(lo >> 32), span = (uint32_t)((hi - lo) >> 32);
+      const uint32_t sh = (uint32_t)(shift - 32);
+      for_each([&](uint64_t k) {
+        const uint32_t d = (uint32_t)(k >> 32) - lo32;
+        atomicAdd(&sm.hist[d <= span ? (d >> sh) : stray], 1u);
+      });
     } else {
-      for_each(count);
+      auto count = [&](uint64_t k) {
+        if (k >= lo && k <= hi) atomicAdd(&sm.hist[(uint32_t)((k - lo) >> shift)], 1u);
+      };
+      if (use_cand) {
+        const uint32_t n = sm.ncand;
+        for (uint32_t i = threadIdx.x; i < n; i += kNT) count(cand[i]);
+      } else {
+        for_each(count);
+      }
     }
     __syncthreads();
     find_bin(need, bk);
@@ -161,14 +221,21 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
     if (cnt <= (uint32_t)kRankMax) {
       // rank the few keys of the bin directly: thread t compares key t % 256 with one quarter of
       // the bin (the quarter is the same for a whole wave, so every LDS read is a broadcast)
-      auto collect = [&](uint64_t k) {
-        if (k >= lo && k <= hi) sm.rankbuf[atomicAdd(&sm.nrank, 1u)] = k;
-      };
-      if (use_cand) {
-        const uint32_t n = sm.ncand;
-        for (uint32_t i = threadIdx.x; i < n; i += kNT) collect(cand[i]);
+      if (wide) {
+        const uint32_t lo32 = (uint32_t)(lo >> 32), span = (uint32_t)((hi - lo) >> 32);
+        for_each([&](uint64_t k) {
+          if ((uint32_t)(k >> 32) - lo32 <= span) sm.rankbuf[atomicAdd(&sm.nrank, 1u)] = k;
+        });
       } else {
-        for_each(collect);
+        auto collect = [&](uint64_t k) {
+          if (k >= lo && k <= hi) sm.rankbuf[atomicAdd(&sm.nrank, 1u)] = k;
+        };
+        if (use_cand) {
+          const uint32_t n = sm.ncand;
+          for (uint32_t i = threadIdx.x; i < n; i += kNT) collect(cand[i]);
+        } else {
+          for_each(collect);
+        }
       }
       __syncthreads();
       constexpr uint32_t kPart = kRankMax / 4;
@@ -202,36 +269,34 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
   }
 }
 
-// Offsets that keep slot order (slot = i*kNT + t) for per-slot counts c[i]: returns in off[i]
-// the number of counted items in all earlier slots; total = their sum.  N <= kTopE.
-template <int N>
-__device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&c)[N], uint32_t (&off)[N], Block& bk) {
-  SelectSmem& sm = bk.sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t* ec = sm.ecnt[bk.parity];
-  bk.parity ^= 1;
-  uint32_t incl[N];
+// Top-K of a slot array (slot = e*kNT + t, keys 0 = none): the k best keys written in slot
+// order as indices (and scores), -1 / 0 padded.
+__device__ __forceinline__ void topk_out(const uint64_t (&key)[kE], uint32_t nvalid, uint32_t mn, uint32_t mx,
+                                         int k, int32_t* __restrict__ oi, float* __restrict__ os, Block& bk) {
+  bk.reduce(nvalid, mn, mx);
+  uint64_t thr = 1ull;
+  if (nvalid > (uint32_t)k) {
+    auto for_each = [&](auto f) {
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    incl[i] = wave_incl_sum(c[i]);
-    if (lane == 63) ec[i * kWaves + wave] = incl[i];
+      for (int e = 0; e < kE; ++e) f(key[e]);
+    };
+    thr = select_kth(for_each, (uint32_t)k, key_lo(mn), key_hi(mx), bk, nullptr);
   }
-  __syncthreads();
-  // lane i < N: the total of element i over all waves and its part in waves before this one
-  uint32_t tot_i = 0u, pre_w = 0u;
-  if (lane < N) {
+  uint32_t c[kE], off[kE];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const uint32_t v = ec[lane * kWaves + w];
-      tot_i += v;
-      pre_w += w < wave ? v : 0u;
+  for (int e = 0; e < kE; ++e) c[e] = key[e] >= thr ? 1u : 0u;
+  const uint32_t total = ordered_offsets<true>(c, off, bk);
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    if (c[e] && off[e] < (uint32_t)k) {   // duplicate positions in a caller pool can tie
+      oi[off[e]] = (int32_t)rank_key_index(key[e]);
+      if (os) os[off[e]] = key_score((uint32_t)(key[e] >> 32));
     }
   }
-  const uint32_t inc_t = wave_incl_sum(tot_i);
-  const uint32_t base = inc_t - tot_i + pre_w;
-#pragma unroll
-  for (int i = 0; i < N; ++i) off[i] = (uint32_t)__builtin_amdgcn_readlane((int)base, i) + incl[i] - c[i];
-  return (uint32_t)__builtin_amdgcn_readlane((int)inc_t, N - 1);
+  for (int i = (int)min(total, (uint32_t)k) + (int)threadIdx.x; i < k; i += kNT) {
+    oi[i] = -1;
+    if (os) os[i] = 0.f;
+  }
 }
 
 // ------------------------------------------------------------------ pool + Full Top-K
@@ -247,16 +312,16 @@ __device__ __forceinline__ void sort4(uint32_t (&v)[4]) {
 }
 
 // One WG per query: keeps the top P blocks by (block max desc, block asc) as the pool, written
-// as positions in ascending order (all blocks if there are at most P), -1 padded to cap_out.
-// With K > 0 it goes on to the Top-K positions of the pool by (score desc, position asc),
-// written in ascending order (-1 padded), from the pool held in LDS.
+// as positions in ascending order (all blocks if there are at most P), -1 padded to cap_out
+// (a multiple of 8).  With K > 0 it goes on to the Top-K positions of the pool by (score desc,
+// position asc), written in ascending order (-1 padded), from the pool it holds.
 // lists/cuts: per-unit five best blocks from the scan (see k_idx_scan); unit u covers blocks
 // [u*bpu, (u+1)*bpu), n_units <= 4096.  blkkey rows are nb_max entries apart.
 //
-// Pool order: thread t owns units i*kNT + t (i < 4).  Once the P-th best block key T* is
-// known, the selected blocks of a unit that was not re-read are its listed keys >= T*, sorted
-// by index; a re-read unit is counted and written by one wave, in index order, with ballots.
-// ordered_offsets places the units: unit order is block order.
+// Pool order: thread t owns units i*kNT + t (i < 4).  Once the P-th best block key T* is known,
+// the selected blocks of a unit that was not re-read are its listed keys >= T*, sorted by index;
+// a re-read unit is counted and written by one wave, in index order, with ballots.  Unit order
+// is block order, so ordered_offsets over the units' counts places every unit.
 __global__ __launch_bounds__(kNT) void k_pool(
     const uint64_t* __restrict__ lists, const uint64_t* __restrict__ cuts, int n_units,
     int bpu, const uint32_t* __restrict__ blkkey, int nb_max,
@@ -418,7 +483,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
         cnt[i] = satcnt[sidx[i]];
       }
     }
-    nsel = min(ordered_offsets(cnt, off, bk), (uint32_t)P);
+    nsel = min(ordered_offsets<false>(cnt, off, bk), (uint32_t)P);
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i) {
       if (sidx[i] < 0) {
@@ -453,57 +518,36 @@ __global__ __launch_bounds__(kNT) void k_pool(
     total = 8 * (int)nsel;
     if (nsel > 0 && (int)byrank[nsel - 1] == nb - 1) total -= kBlock - (nv - kBlock * (nb - 1));
   }
-  auto slot_pos = [&](int sl) { return all ? sl : kBlock * (int)byrank[sl >> 3] + (sl & 7); };
+  int32_t ps[kE];
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const int sl = i * kNT + t;
+    ps[i] = sl < total ? (all ? sl : kBlock * (int)byrank[sl >> 3] + (sl & 7)) : -1;
+  }
   int32_t* gp = pool_pos + (size_t)q * cap_out;
-  for (int sl = t; sl < cap_out; sl += kNT) gp[sl] = sl < total ? slot_pos(sl) : -1;
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const int sl = i * kNT + t;
+    if (sl < cap_out) gp[sl] = ps[i];
+  }
   if (t == 0) pool_len[q] = total;
   if (K == 0) return;
 
-  // Top-K of the pool by (score desc, position asc), slot = i*kNT + t, written in slot order
+  // Top-K of the pool by (score desc, position asc), written in slot (= position) order
   const float* sc = scores + (size_t)q * n_max;
-  int32_t ps[kTopE];
-  float sv[kTopE];
+  float sv[kE];
 #pragma unroll
-  for (int i = 0; i < kTopE; ++i) {
-    const int sl = i * kNT + t;
-    ps[i] = sl < total ? slot_pos(sl) : -1;
-  }
+  for (int i = 0; i < kE; ++i) sv[i] = sc[ps[i] >= 0 ? ps[i] : 0];
+  uint64_t key[kE];
+  uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-  for (int i = 0; i < kTopE; ++i) sv[i] = sc[ps[i] >= 0 ? ps[i] : 0];
-  uint64_t key[kTopE];
-  uint32_t mn = 0xffffffffu, mx = 0u, dummy = 0u;
-#pragma unroll
-  for (int i = 0; i < kTopE; ++i) {
+  for (int i = 0; i < kE; ++i) {
     const uint32_t k32 = score_key(sv[i]);
     key[i] = ps[i] >= 0 ? rank_key(k32, (uint32_t)ps[i]) : 0ull;
+    nvalid += ps[i] >= 0 ? 1u : 0u;
     if (ps[i] >= 0) { mn = min(mn, k32); mx = max(mx, k32); }
   }
-  uint64_t thr = 1ull;
-  if (total > K) {
-    bk.reduce(dummy, mn, mx);
-    auto for_each_k = [&](auto f) {
-#pragma unroll
-      for (int i = 0; i < kTopE; ++i) f(key[i]);
-    };
-    thr = select_kth(for_each_k, (uint32_t)K, key_lo(mn), key_hi(mx), bk, nullptr);
-  }
-  uint32_t c2[kTopE], o2[kTopE];
-#pragma unroll
-  for (int i = 0; i < kTopE; ++i) c2[i] = key[i] >= thr ? 1u : 0u;
-  const uint32_t tot2 = ordered_offsets(c2, o2, bk);
-  int32_t* oi = topk_idx + (size_t)q * K;
-  float* os = topk_score ? topk_score + (size_t)q * K : nullptr;
-#pragma unroll
-  for (int i = 0; i < kTopE; ++i) {
-    if (c2[i] && o2[i] < (uint32_t)K) {
-      oi[o2[i]] = (int32_t)rank_key_index(key[i]);
-      if (os) os[o2[i]] = key_score((uint32_t)(key[i] >> 32));
-    }
-  }
-  for (int i = (int)min(tot2, (uint32_t)K) + t; i < K; i += kNT) {
-    oi[i] = -1;
-    if (os) os[i] = 0.f;
-  }
+  topk_out(key, nvalid, mn, mx, K, topk_idx + (size_t)q * K, topk_score ? topk_score + (size_t)q * K : nullptr, bk);
 }
 
 hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
@@ -521,7 +565,8 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
 // position cand_pos[i] (ignored if negative or >= n_rows).  by_position: its score is
 // scores[q*score_stride + pos], otherwise scores[it*score_stride + slot].  Output: the k best
 // positions in slot order (ascending positions for an ascending pool) with their scores,
-// -1 / 0 padded.
+// -1 / 0 padded.  Slot i*kNT + t belongs to thread t, so each load instruction reads
+// consecutive slots.
 __global__ __launch_bounds__(kNT) void k_topk(
     const int32_t* __restrict__ cand_pos, const int32_t* __restrict__ cand_len, int cap,
     int64_t n_rows, const float* __restrict__ scores, int64_t score_stride, int by_position,
@@ -534,56 +579,30 @@ __global__ __launch_bounds__(kNT) void k_topk(
   len = len < 0 ? 0 : (len > cap ? cap : len);
   const int32_t* cp = cand_pos + (size_t)q * cap;
   const float* sc = scores + (size_t)(by_position ? q : it) * score_stride;
-
-  int32_t pos[kTopE];
+  int32_t pos[kE];
 #pragma unroll
-  for (int e = 0; e < kTopE; ++e) {
-    const int slot = e * kNT + t;
-    pos[e] = cp[slot < len ? slot : 0];
+  for (int i = 0; i < kE; ++i) {
+    const int slot = i * kNT + t;
+    pos[i] = cp[slot < len ? slot : 0];
   }
-  bool ok[kTopE];
-  float s[kTopE];
+  bool ok[kE];
+  float s[kE];
 #pragma unroll
-  for (int e = 0; e < kTopE; ++e) {
-    const int slot = e * kNT + t;
-    ok[e] = slot < len && pos[e] >= 0 && (int64_t)pos[e] < n_rows;
-    s[e] = sc[by_position ? (ok[e] ? pos[e] : 0) : (slot < len ? slot : 0)];
+  for (int i = 0; i < kE; ++i) {
+    const int slot = i * kNT + t;
+    ok[i] = slot < len && pos[i] >= 0 && (int64_t)pos[i] < n_rows;
+    s[i] = sc[by_position ? (ok[i] ? pos[i] : 0) : (slot < len ? slot : 0)];
   }
-  uint64_t key[kTopE];
+  uint64_t key[kE];
   uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-  for (int e = 0; e < kTopE; ++e) {
-    const uint32_t k32 = score_key(s[e]);
-    key[e] = ok[e] ? rank_key(k32, (uint32_t)pos[e]) : 0ull;
-    nvalid += ok[e] ? 1u : 0u;
-    if (ok[e]) { mn = min(mn, k32); mx = max(mx, k32); }
+  for (int i = 0; i < kE; ++i) {
+    const uint32_t k32 = score_key(s[i]);
+    key[i] = ok[i] ? rank_key(k32, (uint32_t)pos[i]) : 0ull;
+    nvalid += ok[i] ? 1u : 0u;
+    if (ok[i]) { mn = min(mn, k32); mx = max(mx, k32); }
   }
-  uint64_t thr = 1ull;
-  bk.reduce(nvalid, mn, mx);
-  if (nvalid > (uint32_t)k) {
-    auto for_each = [&](auto f) {
-#pragma unroll
-      for (int e = 0; e < kTopE; ++e) f(key[e]);
-    };
-    thr = select_kth(for_each, (uint32_t)k, key_lo(mn), key_hi(mx), bk, nullptr);
-  }
-  uint32_t c[kTopE], off[kTopE];
-#pragma unroll
-  for (int e = 0; e < kTopE; ++e) c[e] = key[e] >= thr ? 1u : 0u;
-  const uint32_t total = ordered_offsets(c, off, bk);
-  int32_t* oi = out_idx + (size_t)it * k;
-  float* os = out_score ? out_score + (size_t)it * k : nullptr;
-#pragma unroll
-  for (int e = 0; e < kTopE; ++e) {
-    if (c[e] && off[e] < (uint32_t)k) {   // duplicate positions in a caller pool can tie
-      oi[off[e]] = (int32_t)rank_key_index(key[e]);
-      if (os) os[off[e]] = key_score((uint32_t)(key[e] >> 32));
-    }
-  }
-  for (int i = (int)min(total, (uint32_t)k) + t; i < k; i += kNT) {
-    oi[i] = -1;
-    if (os) os[i] = 0.f;
-  }
+  topk_out(key, nvalid, mn, mx, k, out_idx + (size_t)it * k, out_score ? out_score + (size_t)it * k : nullptr, bk);
 }
 
 hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int64_t n_rows,
