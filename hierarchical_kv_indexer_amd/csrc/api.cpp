@@ -65,7 +65,7 @@ struct FullPlan {
   bool internal_pool;
 };
 
-constexpr int kMaxPositions = 1 << 23;   // n_wg <= 1024 with chunks of at most 8192 positions
+constexpr int kMaxPositions = 1 << 23;   // scores only: 1024 chunks of 8192 positions per query
 
 FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
   FullPlan p;
@@ -167,6 +167,8 @@ static csa2_status check_full_shape(int B, int T, int n_max, int block_size, int
           "pool_blocks * block_size must be <= %d", csa2::kMaxPool);
   REQUIRE(pool_blocks == 0 || top_k <= pool_blocks * block_size, CSA2_ERR_INVALID_ARG,
           "top_k (%d) exceeds the pool capacity (%d)", top_k, pool_blocks * block_size);
+  REQUIRE(n_max <= csa2::kMaxFullPositions, CSA2_ERR_UNSUPPORTED, "n_max must be <= %d for the Full layer",
+          csa2::kMaxFullPositions);
   return CSA2_OK;
 }
 

@@ -5,7 +5,8 @@
 
 namespace csa2 {
 
-constexpr int kScanThreads = 256;
+constexpr int kScanThreads = 256;      // Reindex scoring
+constexpr int kFullThreads = 1024;     // Full scan: one workgroup of 16 waves per chunk
 constexpr int kSelectThreads = 1024;
 constexpr int kAttnThreads = 256;
 constexpr int kMaxLayers = 64;
@@ -15,7 +16,8 @@ struct LayerSets { int32_t set[kMaxLayers]; };
 // scan.hip
 hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hipStream_t s);
 int scan_chunk_positions(int n_max, int queries);
-constexpr int kScanUnitsPerWg = kScanThreads / 64;   // one unit per wave
+constexpr int kScanUnitsPerWg = kFullThreads / 64;   // 16 units of chunk/16 positions per chunk
+constexpr int kMaxFullPositions = 1 << 21;           // 256 chunks of 8192 per query: 4096 units
 hipError_t launch_idx_scan(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,

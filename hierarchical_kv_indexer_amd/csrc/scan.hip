@@ -36,22 +36,34 @@ hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hi
 }
 
 // The 32x128 query of one indexer head set, rounded to E4M3 and held as bf16 in LDS.
-// 256 threads, 16 consecutive values each: two 16-byte loads issued together.
+// NT threads, 4096/NT consecutive values each, loaded with 16-byte (or 8-byte) loads.
+template <int NT>
 __device__ __forceinline__ void stage_query(const uint16_t* __restrict__ q, uint16_t* qlds) {
-  static_assert(kIdxHeads * kIdxDim == kScanThreads * 16, "query staging assumes 256 threads");
-  const int base = threadIdx.x * 16;
-  const u32x4 a = *(const u32x4*)(q + base);
-  const u32x4 b = *(const u32x4*)(q + base + 8);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t o[8];
+  constexpr int kPer = kIdxHeads * kIdxDim / NT;      // values per thread (16 or 4)
+  static_assert(kPer == 16 || kPer == 4, "query staging assumes 256 or 1024 threads");
+  const int base = threadIdx.x * kPer;
+  uint32_t w[kPer / 2];
+  if constexpr (kPer == 16) {
+    const u32x4 a = *(const u32x4*)(q + base);
+    const u32x4 b = *(const u32x4*)(q + base + 8);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  } else {
+    const u32x2 a = *(const u32x2*)(q + base);
+    w[0] = a.x; w[1] = a.y;
+  }
+  uint32_t o[kPer / 2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kPer / 2; ++i) {
     const float lo = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(w[i] & 0xffffu)));
     const float hi = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(w[i] >> 16)));
     o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
   }
-  *(u32x4*)(qlds + base) = u32x4{o[0], o[1], o[2], o[3]};
-  *(u32x4*)(qlds + base + 8) = u32x4{o[4], o[5], o[6], o[7]};
+  if constexpr (kPer == 16) {
+    *(u32x4*)(qlds + base) = u32x4{o[0], o[1], o[2], o[3]};
+    *(u32x4*)(qlds + base + 8) = u32x4{o[4], o[5], o[6], o[7]};
+  } else {
+    *(u32x2*)(qlds + base) = u32x2{o[0], o[1]};
+  }
 }
 
 // Per-wave state for scoring tiles: the query as MFMA A operands and this lane's head weights.
@@ -114,130 +126,133 @@ __device__ __forceinline__ void load_row(const uint8_t* __restrict__ row, int g,
 // ---------------------------------------------------------------------------- Full scan
 
 constexpr int kScanU = 3;                       // tiles per pipeline stage of a wave
-constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kMaxBlocksPerWave = 256;          // chunk <= 8192 positions per WG
+constexpr int kFullWaves = kFullThreads / 64;   // 16
+static_assert(kFullWaves == kScanUnitsPerWg, "one unit per wave in the epilogue");
 
 size_t scan_lds_bytes(int chunk) {
-  const int tpw = chunk >> 6;
-  return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)kScanWaves * tpw * 16 * 4 + (size_t)kScanWaves * 2 * tpw * 4;
+  return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)chunk * 4 + (size_t)(chunk / kBlock) * 4 + 16;
 }
 
-// Best ranking key (score key, block) of a wave's blocks, removed from the set.  Entries are
-// (key, block) with key 0 / block 0xffffffff meaning "none"; returns rank_key or 0.
-template <int E>
-__device__ __forceinline__ uint64_t wave_pop_best(uint32_t (&key)[E], uint32_t (&blk)[E]) {
-  uint32_t bk = 0u, bj = 0xffffffffu;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (key[e] > bk || (key[e] == bk && blk[e] < bj)) { bk = key[e]; bj = blk[e]; }
-  const uint32_t m = wave_max_u32(bk);
-  const uint32_t jm = wave_min_u32(bk == m ? bj : 0xffffffffu);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (key[e] == m && blk[e] == jm) { key[e] = 0u; blk[e] = 0xffffffffu; }
+// Best ranking key (score key, block) of a wave's blocks (one per lane), removed from the
+// set.  Entries are (key, block) with key 0 / block 0xffffffff meaning "none"; returns
+// rank_key or 0.
+__device__ __forceinline__ uint64_t wave_pop_best(uint32_t& key, uint32_t& blk) {
+  const uint32_t m = wave_max_u32(key);
+  const uint32_t jm = wave_min_u32(key == m ? blk : 0xffffffffu);
+  if (key == m && blk == jm) { key = 0u; blk = 0xffffffffu; }
   return (m == 0u && jm == 0xffffffffu) ? 0ull : rank_key(m, jm);
 }
 
-// grid (n_wg, Q).  WG x covers positions [x*chunk, (x+1)*chunk) of query q = b*T + t; wave v
-// covers the contiguous tiles [v*tpw, (v+1)*tpw) of that range (a "unit").  Loads run one
-// pipeline stage (kScanU tiles) ahead of the MFMA work; the loop issues no global stores, so
-// its loads stay in flight: scores and block keys are staged in LDS and stored afterwards.
+// grid (n_wg, Q), one workgroup of 16 waves per chunk of positions (sized so the grid is about
+// one workgroup per CU).  The waves take pipeline stages of kScanU tiles from an LDS counter,
+// so a wave that the CU's arbitration favours simply takes more stages and all waves finish
+// together.  Each wave keeps one stage of loads in flight while it scores the previous one;
+// the loop issues no global stores (scores and block keys are staged in LDS and stored once
+// every tile is done).
 //
 // Writes scores[q][p] for p < n_visible and, when `blkkey` is non-null, the order key of
-// each block's max score.  When `lists` is non-null, each unit also writes its five best
-// blocks as ranking keys (score key << 32 | ~block): lists[q][unit][0..3] = the four best
-// (0 = none) and cuts[q][unit] = the fifth best (0 = none), so every block of the unit that
-// is not listed ranks at or below cuts[q][unit].
-__global__ __launch_bounds__(kScanThreads, 4) void k_idx_scan(
+// each block's max score.  When `lists` is non-null, each of the chunk's 16 units (equal,
+// contiguous ranges of chunk/16 positions) writes its five best blocks as ranking keys
+// (score key << 32 | ~block): lists[q][unit][0..3] = the four best (0 = none) and
+// cuts[q][unit] = the fifth best (0 = none), so every block of the unit that is not listed
+// ranks at or below cuts[q][unit].  Requires chunk % 1024 == 0 and chunk <= 8192.
+__global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     const uint8_t* __restrict__ idx_k, int64_t k_rows, const uint16_t* __restrict__ idx_q,
     const float* __restrict__ head_w, const int32_t* __restrict__ n_visible, int T, int n_max,
     int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
     uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int tpw = chunk >> 6;                     // tiles per wave (chunk is a multiple of 256)
   uint16_t* qlds = (uint16_t*)lds;
+  float* sbuf = (float*)(lds + kIdxHeads * kIdxDim * 2);
+  uint32_t* wkeys = (uint32_t*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4);
+  int* ctr = (int*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4 + (chunk / kBlock) * 4);
   const int q = blockIdx.y, b = q / T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
-  float* sbuf = (float*)(lds + kIdxHeads * kIdxDim * 2) + wave * tpw * 16;
-  uint32_t* wkeys = (uint32_t*)(lds + kIdxHeads * kIdxDim * 2 + kScanWaves * tpw * 16 * 4) + wave * 2 * tpw;
   int nv = n_visible[q];
   nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
   const int p_begin = blockIdx.x * chunk;
   const int p_end = min(p_begin + chunk, nv);
-  const int ntiles = p_end > p_begin ? (p_end - p_begin + 15) >> 4 : 0;
-  const int tb = wave * tpw;
-  const int nt = max(0, min(tpw, ntiles - tb));   // tiles of this wave
-  const int pw = p_begin + 16 * tb;               // first position of this wave
+  const int npos = max(0, p_end - p_begin);
+  const int ntiles = (npos + 15) >> 4;
   const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * kIdxDim;
+  const int plast = npos > 0 ? p_end - 1 : 0;
+  // Workgroups start at different tiles of their chunk and wrap around, so workgroups that
+  // stream in lockstep touch different address offsets at a time.
+  const int rot = ntiles > 0 ? (int)((blockIdx.x * 5u + blockIdx.y) % (unsigned)ntiles) : 0;
+  auto phys = [&](int t) { return t + rot < ntiles ? t + rot : t + rot - ntiles; };
 
-  // Rows past this wave's range are clamped to its last row, so every stage loads and computes
-  // unconditionally (no branch around a load keeps the compiler's wait counts exact and the
-  // next stage's loads in flight); results of such padding tiles are never stored.
-  const int plast = min(p_end, pw + 16 * nt) - 1;
-  u32x4 lo0[kScanU], hi0[kScanU], lo1[kScanU], hi1[kScanU];
-  auto load_stage = [&](u32x4(&lo)[kScanU], u32x4(&hi)[kScanU], int st) {
+  // Rows of tiles past the chunk are clamped to its last row, so every stage loads and
+  // computes unconditionally; results of such tiles are never stored.
+  u32x4 loA[kScanU], hiA[kScanU], loB[kScanU], hiB[kScanU];
+  auto load_stage = [&](u32x4(&lo)[kScanU], u32x4(&hi)[kScanU], int t0) {
 #pragma unroll
     for (int u = 0; u < kScanU; ++u) {
-      const int p = min(pw + 16 * (st * kScanU + u) + j, plast);
+      const int t = t0 + u;
+      const int p = min(p_begin + 16 * (t < ntiles ? phys(t) : t) + j, plast);
       load_row(kseq + (size_t)p * kIdxDim, g, lo[u], hi[u]);
     }
   };
-  const int ns = (nt + kScanU - 1) / kScanU;
-  if (nt > 0) load_stage(lo0, hi0, 0);            // first rows in flight before the query prep
+  int tA = wave * kScanU;                          // first stage of each wave: static
+  if (tA < ntiles) load_stage(loA, hiA, tA);       // in flight during the query prep
 
   if (ntiles > 0) {
-    stage_query(idx_q + (size_t)q * kIdxHeads * kIdxDim, qlds);
+    stage_query<kFullThreads>(idx_q + (size_t)q * kIdxHeads * kIdxDim, qlds);
+    if (threadIdx.x == 0) *ctr = kFullWaves * kScanU;
     __syncthreads();
     TileCtx cx;
     load_ctx(cx, qlds, head_w + (size_t)q * kIdxHeads);
-    auto compute_stage = [&](const u32x4(&lo)[kScanU], const u32x4(&hi)[kScanU], int st) {
+    auto grab = [&]() {                            // next stage of this wave (monotonic)
+      int v = 0;
+      if (lane == 0) v = atomicAdd(ctr, kScanU);
+      return __builtin_amdgcn_readfirstlane(v);
+    };
+    auto compute_stage = [&](const u32x4(&lo)[kScanU], const u32x4(&hi)[kScanU], int t0) {
 #pragma unroll
       for (int u = 0; u < kScanU; ++u) {
-        const int t = st * kScanU + u;
+        const int t = t0 + u;
         const float sc = tile_score(cx, lo[u], hi[u]);
-        const bool valid = pw + 16 * t + j < p_end;
-        const uint32_t key = max8_u32(valid ? score_key(sc) : 0u);
-        if (t < nt) {
-          if (g == 0) sbuf[16 * t + j] = sc;
-          if ((lane & 0x37) == 0) wkeys[2 * t + (lane >> 3)] = key;   // lanes 0, 8
+        if (t < ntiles) {
+          const int tp = phys(t);
+          const bool valid = 16 * tp + j < npos;
+          const uint32_t key = max8_u32(valid ? score_key(sc) : 0u);
+          if (g == 0) sbuf[16 * tp + j] = sc;
+          if ((lane & 0x37) == 0) wkeys[2 * tp + (lane >> 3)] = key;   // lanes 0, 8
         }
       }
     };
-    for (int st = 0; st < ns; st += 2) {
-      load_stage(lo1, hi1, st + 1);
-      compute_stage(lo0, hi0, st);
-      load_stage(lo0, hi0, st + 2);
-      compute_stage(lo1, hi1, st + 1);
+    int tB = grab();
+    while (tA < ntiles) {
+      load_stage(loB, hiB, tB);
+      compute_stage(loA, hiA, tA);
+      tA = grab();
+      if (tB >= ntiles) break;                     // later grabs only go further
+      load_stage(loA, hiA, tA);
+      compute_stage(loB, hiB, tB);
+      tB = grab();
     }
-    // coalesced stores of this wave's scores and block keys
-    const int nsw = p_end > pw ? min(16 * tpw, p_end - pw) : 0;
-    float* srow = scores + (size_t)q * n_max + pw;
-    for (int i = lane; i < nsw; i += 64) srow[i] = sbuf[i];
-    if (blkkey) {
-      const int nbw = (nsw + 7) >> 3;
-      uint32_t* brow = blkkey + (size_t)q * nb_max + (pw >> 3);
-      for (int i = lane; i < nbw; i += 64) brow[i] = wkeys[i];
-    }
+  }
+  __syncthreads();
+  // coalesced stores of the chunk's scores and block keys
+  float* srow = scores + (size_t)q * n_max + p_begin;
+  for (int i = threadIdx.x; i < npos; i += kFullThreads) srow[i] = sbuf[i];
+  const int nblk = (npos + kBlock - 1) / kBlock;
+  if (blkkey) {
+    uint32_t* brow = blkkey + (size_t)q * nb_max + p_begin / kBlock;
+    for (int i = threadIdx.x; i < nblk; i += kFullThreads) brow[i] = wkeys[i];
   }
   if (!lists) return;
-  // five best blocks of this wave's unit
-  const int nblk = p_end > pw ? min(2 * tpw, (p_end - pw + 7) >> 3) : 0;
-  const uint32_t jb0 = (uint32_t)(pw >> 3);
-  constexpr int E = kMaxBlocksPerWave / 64;
-  uint32_t key[E], blk[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = lane + 64 * e;
-    const bool ok = i < nblk;
-    key[e] = ok ? wkeys[i] : 0u;
-    blk[e] = ok ? jb0 + (uint32_t)i : 0xffffffffu;
-  }
-  const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kScanWaves + wave;
+  // five best blocks of unit `wave` (bpu <= 64 blocks: one per lane)
+  const int bpu = chunk / (kBlock * kFullWaves);
+  const int ub = wave * bpu;
+  const bool ok = lane < bpu && ub + lane < nblk;
+  uint32_t key = ok ? wkeys[ub + lane] : 0u;
+  uint32_t blk = ok ? (uint32_t)(p_begin / kBlock + ub + lane) : 0xffffffffu;
   uint64_t best[5];
 #pragma unroll
   for (int r = 0; r < 5; ++r) best[r] = wave_pop_best(key, blk);
   if (lane == 0) {
+    const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kFullWaves + wave;
     u32x4* lp = (u32x4*)(lists + unit * 4);
     lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
     lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
@@ -246,14 +261,14 @@ __global__ __launch_bounds__(kScanThreads, 4) void k_idx_scan(
 }
 
 int scan_chunk_positions(int n_max, int queries) {
-  // >= ~1024 workgroups in total and at most 1024 per query; chunks are multiples of 256
-  // positions and at most 8192 (the per-wave block list holds 256 blocks)
+  // about one workgroup per CU (256) over all queries, at most 256 workgroups per query (the
+  // pool takes at most 4096 units); multiples of 1024 positions, at most 8192 (LDS staging)
   long long total = (long long)n_max * (queries > 0 ? queries : 1);
-  long long c = total / 1024;
-  long long per_query = ((long long)n_max + 1023) / 1024;
+  long long c = (total + 255) / 256;
+  long long per_query = ((long long)n_max + 255) / 256;
   if (c < per_query) c = per_query;
-  c = (c + 255) / 256 * 256;
-  if (c < 256) c = 256;
+  c = (c + 1023) / 1024 * 1024;
+  if (c < 1024) c = 1024;
   if (c > 8192) c = 8192;
   return (int)c;
 }
@@ -262,7 +277,7 @@ hipError_t launch_idx_scan(const uint8_t* idx_k, int64_t k_rows, const uint16_t*
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
                            uint64_t* cuts, int chunk, int n_wg, hipStream_t s) {
-  hipLaunchKernelGGL(k_idx_scan, dim3(n_wg, Q), dim3(kScanThreads), scan_lds_bytes(chunk), s, idx_k, k_rows,
+  hipLaunchKernelGGL(k_idx_scan, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k, k_rows,
                      idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
   return hipGetLastError();
 }
@@ -297,7 +312,7 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
     const int slot = sw + 16 * u + j;
     pos[u] = slot < s_end ? pp[slot] : -1;
   }
-  stage_query(idx_q + (size_t)it * kIdxHeads * kIdxDim, qlds);
+  stage_query<kScanThreads>(idx_q + (size_t)it * kIdxHeads * kIdxDim, qlds);
   const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * kIdxDim;
   u32x4 lo[kRiTilesPerWave], hi[kRiTilesPerWave];
   bool ok[kRiTilesPerWave];

@@ -92,7 +92,8 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, cons
  *   topk_score [B][T][top_k] float out aligned with topk_idx (0 for padding), or NULL
  *   workspace  device scratch of at least csa2_index_full_workspace(...) bytes
  * Supported: block_size == 8, 1 <= top_k <= 2048, top_k <= pool_blocks*block_size when
- * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= 2^23, n_max <= k_rows_per_seq. */
+ * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= 2^21 (2^23 for csa2_index_scores),
+ * n_max <= k_rows_per_seq. */
 size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k);
 
 /* The stages of csa2_index_full as separate calls.  They take the same arguments and the same
