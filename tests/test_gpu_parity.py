@@ -305,3 +305,46 @@ def test_chain_prefill_small():
     w = small("prefill_4k_64k", T=64, N=4096, prefill_tokens=8192, seed=91)
     inp = workloads.make_inputs(w)
     run_chain_and_check(w, inp, [(0, 0), (0, 31), (0, 63)])
+
+
+def test_attention_split_merge_repeats_and_graph_replays():
+    """Rows split over workgroups leave partial softmax states in the workspace for the merge.
+    Repeated calls on one workspace (starting from arbitrary bytes), and replays of a captured
+    call with other work in between, must all give the eager result."""
+    import hierarchical_kv_indexer_amd as H
+    w = small(B=1, T=1, N=5000, H=16, layer_set=(0, 0, 1, 1), n_reindex=1, pool_blocks=64, top_k=512, seed=77)
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(9)
+    sets = np.stack([np.sort(rng.choice(w.N, 512, replace=False)).astype(np.int32) for _ in range(2)]).reshape(2, 1, 1, 512)
+    L, K = w.L, 512
+    assert H.csa2_sparse_attn_workspace(L, 1, 1, 16, K, w.swa_window) > 0, "expected split rows"
+    out_ref, _ = G.gpu_attention(inp, w, sets)
+    args = dict(codes=G.dev(inp["kv_codes"]), scales=G.dev(inp["kv_scales"]), q=G.dev(inp["q"]), sets=G.dev(sets),
+                swa=G.dev(inp["swa"]), end=G.dev(inp["swa_end"]))
+    out = G.empty((L, 1, 1, 16, 512), torch.int16)
+    wsb = H.csa2_sparse_attn_workspace(L, 1, 1, 16, K, w.swa_window)
+    ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device=G.DEV)     # arbitrary initial bytes
+
+    def call():
+        H.csa2_sparse_attn(args["codes"], args["scales"], w.N, args["q"], args["sets"], list(w.layer_set), 2,
+                           args["swa"], w.swa_rows, args["end"], w.swa_window, L, 1, 1, 16, K,
+                           1.0 / math.sqrt(512), out, None, ws, wsb)
+
+    for _ in range(3):
+        out.zero_()
+        call()
+        assert np.array_equal(G.host(out), out_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(G.host(out), out_ref), f"replay {i}"
+        call()                                                            # eager work between replays
+        assert np.array_equal(G.host(out), out_ref)
