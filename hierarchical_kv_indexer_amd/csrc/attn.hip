@@ -273,6 +273,191 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   }
 }
 
+// The same computation for 64 heads per workgroup (H % 64 == 0): wave w owns heads
+// 64*blockIdx.y + 16w .. +15 over every row of the chunk, so each gathered row is dequantised
+// once for all 64 heads.  A wave's softmax state, P tile and output (16 heads x 512 dims) are
+// its own: S = Q X^T takes 4 row tiles x 16 MFMAs and O += P X 32 dim tiles x 2 MFMAs per chunk,
+// with no cross-wave reduction.  grid (n_splits, H/64, L*Q); outputs as k_sparse_attn.
+__global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
+    const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t kv_rows,
+    const uint16_t* __restrict__ qg, const int32_t* __restrict__ idx_sets, LayerSets sets,
+    const uint8_t* __restrict__ swa, int swa_rows, const int32_t* __restrict__ swa_end, int window,
+    int Q, int B, int T, int H, int k, float scale_log2, int split_rows, int n_splits,
+    float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t X[kRows * kXStride];
+  __shared__ __attribute__((aligned(16))) uint16_t P[4 * 16 * kPStride];
+  __shared__ int32_t rowok[kRows];
+
+  const int split = blockIdx.x, hq = blockIdx.y, lq = blockIdx.z;
+  const int l = lq / Q, q = lq % Q, b = q / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, g = lane >> 4;
+  const int32_t* idx = idx_sets + ((size_t)sets.set[l] * Q + q) * k;
+  int we = swa_end[q];
+  we = we < 0 ? 0 : (we > swa_rows ? swa_rows : we);
+  const int ws = max(0, we - window);
+  const int nslots = k + (we - ws);
+  const int s0 = split * split_rows, s1 = min(nslots, s0 + split_rows);
+  const int nchunks = s1 > s0 ? (s1 - s0 + kRows - 1) / kRows : 0;
+  const uint8_t* codes_seq = kv_codes + (size_t)b * kv_rows * kKvCodeBytes;
+  const uint8_t* scales_seq = kv_scales + (size_t)b * kv_rows * kKvScaleBytes;
+  const uint8_t* swa_seq = swa + ((size_t)l * B + b) * (size_t)swa_rows * kKvDim;
+
+  const int my_row = tid >> 2, quarter = tid & 3;
+  auto row_index = [&](int c) {
+    const int slot = s0 + c * kRows + my_row;
+    if (slot >= s1 || slot >= k) return -1;
+    const int pos = idx[slot];
+    return (pos >= 0 && (int64_t)pos < kv_rows) ? pos : -1;
+  };
+  int pos_cur = nchunks > 0 ? row_index(0) : -1;
+  int pos_next = nchunks > 1 ? row_index(1) : -1;
+
+  const int hbase = 64 * hq + 16 * wave;           // this wave's first head
+  const uint16_t* qh = qg + (((size_t)l * Q + q) * H + hbase) * kKvDim;
+  u32x4 qa[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) qa[c] = *(const u32x4*)(qh + (size_t)j * kKvDim + 32 * c + 8 * g);
+
+  f32x4 o[32];                                     // tile 8*blk + t: dims 128*blk + 8j + t
+#pragma unroll
+  for (int t = 0; t < 32; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
+  uint16_t* Pw = P + wave * 16 * kPStride;
+
+  auto load_chunk = [&](RawRow& r, int c, int pos) {
+    const int slot = s0 + c * kRows + my_row;
+    r.kind = 0;
+    if (slot < s1) {
+      if (slot < k) {
+        if (pos >= 0) {
+          const u32x4* cp = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 64 * quarter);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r.d[i] = cp[i];
+          r.sc = *(const u32x2*)(scales_seq + (size_t)pos * kKvScaleBytes + 8 * quarter);
+          r.kind = 1;
+        }
+      } else {
+        const u32x4* cp = (const u32x4*)(swa_seq + (size_t)(ws + slot - k) * kKvDim + 128 * quarter);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r.d[i] = cp[i];
+        r.kind = 2;
+      }
+    }
+  };
+  RawRow raw;
+  if (nchunks > 0) load_chunk(raw, 0, pos_cur);
+
+  for (int c = 0; c < nchunks; ++c) {
+    store_row(raw, X + my_row * kXStride, quarter);
+    if (quarter == 0) rowok[my_row] = raw.kind != 0;
+    __syncthreads();
+    if (c + 1 < nchunks) {
+      load_chunk(raw, c + 1, pos_next);
+      pos_next = c + 2 < nchunks ? row_index(c + 2) : -1;
+    }
+
+    // S[head 4g+v][row 16r + j]
+    f32x4 s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s[r] = mfma16x16x32(qa[cc], *(const u32x4*)(X + (16 * r + j) * kXStride + 32 * cc + 8 * g), s[r]);
+    bool ok[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ok[r] = rowok[16 * r + j] != 0;
+    float alpha[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float sv[4], m = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = ok[r] ? s[r][v] * scale_log2 : -INFINITY;
+        m = fmaxf(m, sv[r]);
+      }
+      const float mnew = fmaxf(m_run[v], row16_max(m));
+      alpha[v] = mnew == -INFINITY ? 1.f : exp2f(m_run[v] - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = mnew == -INFINITY ? 0.f : exp2f(sv[r] - mnew);
+        const uint32_t pb = f32_to_bf16_rne(p);
+        Pw[(4 * g + v) * kPStride + 16 * r + j] = (uint16_t)pb;
+        ps += bf16_bits_to_f32(pb);
+      }
+      l_run[v] = l_run[v] * alpha[v] + row16_sum(ps);
+      m_run[v] = mnew;
+    }
+#pragma unroll
+    for (int t = 0; t < 32; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[t][v] *= alpha[v];
+    // O[head 4g+v][dim 128*blk + 8j + t] += sum_r P[head][r] X[r][dim]; the P tile is this
+    // wave's own, so it is read back without a barrier (a wave's LDS accesses are ordered).
+#pragma unroll
+    for (int kk = 0; kk < kRows / 32; ++kk) {
+      const u32x4 pa = *(const u32x4*)(Pw + j * kPStride + 32 * kk + 8 * g);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const uint16_t* xc = X + (32 * kk + 8 * g) * kXStride + 128 * blk + 8 * j;
+        u32x4 xv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = *(const u32x4*)(xc + e * kXStride);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = __builtin_amdgcn_perm(xv[2 * e + 1][i], xv[2 * e][i], 0x05040100u);
+            hi[e] = __builtin_amdgcn_perm(xv[2 * e + 1][i], xv[2 * e][i], 0x07060302u);
+          }
+          o[8 * blk + 2 * i] = mfma16x16x32(pa, lo, o[8 * blk + 2 * i]);
+          o[8 * blk + 2 * i + 1] = mfma16x16x32(pa, hi, o[8 * blk + 2 * i + 1]);
+        }
+      }
+    }
+    if (c + 1 < nchunks) __syncthreads();   // X and rowok are rewritten by the next chunk
+  }
+
+  const size_t hrow = (size_t)lq * H;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int h = hbase + 4 * g + v;
+    if (n_splits == 1) {
+      const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        u32x4 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pk[i] = f32_to_bf16_rne(o[8 * blk + 2 * i][v] * inv) |
+                  (f32_to_bf16_rne(o[8 * blk + 2 * i + 1][v] * inv) << 16);
+        *(u32x4*)(out + (hrow + h) * kKvDim + 128 * blk + 8 * j) = pk;
+      }
+      if (lse && j == 0)
+        lse[hrow + h] = l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * 0.69314718055994531f : -INFINITY;
+    } else {
+      const size_t pr = (hrow + h) * n_splits + split;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        f32x4* po = (f32x4*)(part_o + pr * kKvDim + 128 * blk + 8 * j);
+        po[0] = f32x4{o[8 * blk][v], o[8 * blk + 1][v], o[8 * blk + 2][v], o[8 * blk + 3][v]};
+        po[1] = f32x4{o[8 * blk + 4][v], o[8 * blk + 5][v], o[8 * blk + 6][v], o[8 * blk + 7][v]};
+      }
+      if (j == 0) {
+        part_ml[pr * 2] = m_run[v];
+        part_ml[pr * 2 + 1] = l_run[v];
+      }
+    }
+  }
+}
+
 // grid (H, L*Q), one wave per head: lane i merges dims 8i .. 8i+7 over the head's n_splits
 // partial states.  Every split slot is loaded up front (indices past n_splits clamp to the last
 // split and get weight zero), so the loads of a lane are all in flight together.
@@ -317,7 +502,8 @@ __global__ __launch_bounds__(64) void k_attn_combine(
 
 AttnPlan plan_attn(int L, int B, int T, int H, int k, int window) {
   AttnPlan p;
-  const long long groups = (long long)L * B * T * (H / 16);
+  p.heads_per_wg = H % 64 == 0 ? 64 : 16;
+  const long long groups = (long long)L * B * T * (H / p.heads_per_wg);
   const int rows_max = k + window;
   const int max_chunks = (rows_max + kRows - 1) / kRows;
   long long want = (512 + groups - 1) / groups;         // splits to reach ~512 workgroups
@@ -344,9 +530,14 @@ hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales,
   const AttnPlan p = plan_attn(L, B, T, H, k, window);
   float* part_o = (float*)workspace;
   float* part_ml = part_o ? part_o + (size_t)L * Q * H * p.n_splits * kKvDim : nullptr;
-  hipLaunchKernelGGL(k_sparse_attn, dim3(p.n_splits, H / 16, L * Q), dim3(kAttnThreads), 0, s, kv_codes,
-                     kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q, B, T, H, k,
-                     scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
+  if (p.heads_per_wg == 64)
+    hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.n_splits, H / 64, L * Q), dim3(kAttnThreads), 0, s,
+                       kv_codes, kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q,
+                       B, T, H, k, scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
+  else
+    hipLaunchKernelGGL(k_sparse_attn, dim3(p.n_splits, H / 16, L * Q), dim3(kAttnThreads), 0, s, kv_codes,
+                       kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q, B, T, H, k,
+                       scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(H, L * Q), dim3(64), 0, s, part_o, part_ml,

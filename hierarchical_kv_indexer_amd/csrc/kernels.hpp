@@ -42,6 +42,7 @@ hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap
 
 // attn.hip
 struct AttnPlan {
+  int heads_per_wg;    // 64 (k_sparse_attn_wide) when H % 64 == 0, else 16
   int split_rows, n_splits;
   size_t ws_bytes;     // partial states when the rows are split over several workgroups
 };

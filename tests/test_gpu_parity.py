@@ -227,8 +227,10 @@ def test_reindex_user_pools_with_invalid_entries():
 
 # ------------------------------------------------------------------ attention
 
-def test_attention_parity_on_oracle_sets():
-    w = small(B=2, T=2, N=3000, H=32, layer_set=(0, 0, 1), n_reindex=1, pool_blocks=64, top_k=200, seed=71)
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_attention_parity_on_oracle_sets(H):
+    """H = 32 runs 16 heads per workgroup; H = 64 and 128 run 64 heads per workgroup."""
+    w = small(B=2, T=2, N=3000, H=H, layer_set=(0, 0, 1), n_reindex=1, pool_blocks=64, top_k=200, seed=71)
     inp = workloads.make_inputs(w)
     sets = np.full((2, 2, 2, 200), -1, np.int32)
     rng = np.random.default_rng(5)
@@ -307,27 +309,28 @@ def test_chain_prefill_small():
     run_chain_and_check(w, inp, [(0, 0), (0, 31), (0, 63)])
 
 
-def test_attention_split_merge_repeats_and_graph_replays():
+@pytest.mark.parametrize("NH", [16, 64])
+def test_attention_split_merge_repeats_and_graph_replays(NH):
     """Rows split over workgroups leave partial softmax states in the workspace for the merge.
     Repeated calls on one workspace (starting from arbitrary bytes), and replays of a captured
     call with other work in between, must all give the eager result."""
     import hierarchical_kv_indexer_amd as H
-    w = small(B=1, T=1, N=5000, H=16, layer_set=(0, 0, 1, 1), n_reindex=1, pool_blocks=64, top_k=512, seed=77)
+    w = small(B=1, T=1, N=5000, H=NH, layer_set=(0, 0, 1, 1), n_reindex=1, pool_blocks=64, top_k=512, seed=77)
     inp = workloads.make_inputs(w)
     rng = np.random.default_rng(9)
     sets = np.stack([np.sort(rng.choice(w.N, 512, replace=False)).astype(np.int32) for _ in range(2)]).reshape(2, 1, 1, 512)
     L, K = w.L, 512
-    assert H.csa2_sparse_attn_workspace(L, 1, 1, 16, K, w.swa_window) > 0, "expected split rows"
+    assert H.csa2_sparse_attn_workspace(L, 1, 1, NH, K, w.swa_window) > 0, "expected split rows"
     out_ref, _ = G.gpu_attention(inp, w, sets)
     args = dict(codes=G.dev(inp["kv_codes"]), scales=G.dev(inp["kv_scales"]), q=G.dev(inp["q"]), sets=G.dev(sets),
                 swa=G.dev(inp["swa"]), end=G.dev(inp["swa_end"]))
-    out = G.empty((L, 1, 1, 16, 512), torch.int16)
-    wsb = H.csa2_sparse_attn_workspace(L, 1, 1, 16, K, w.swa_window)
+    out = G.empty((L, 1, 1, NH, 512), torch.int16)
+    wsb = H.csa2_sparse_attn_workspace(L, 1, 1, NH, K, w.swa_window)
     ws = torch.full((wsb,), 0x5A, dtype=torch.uint8, device=G.DEV)     # arbitrary initial bytes
 
     def call():
         H.csa2_sparse_attn(args["codes"], args["scales"], w.N, args["q"], args["sets"], list(w.layer_set), 2,
-                           args["swa"], w.swa_rows, args["end"], w.swa_window, L, 1, 1, 16, K,
+                           args["swa"], w.swa_rows, args["end"], w.swa_window, L, 1, 1, NH, K,
                            1.0 / math.sqrt(512), out, None, ws, wsb)
 
     for _ in range(3):
