@@ -22,6 +22,7 @@ constexpr int kRows = 64;                    // rows per chunk
 constexpr int kXStride = kKvDim + 8;         // bf16 elements per LDS row (pad: 16 bytes)
 constexpr int kPStride = kRows + 8;          // bf16 elements per P row
 constexpr int kMaxSplitRows = 4096 + kMaxTopK;   // a split never exceeds k + window rows
+constexpr float kLazyLog2 = 8.f;             // slack of the softmax reference point (log2 units)
 
 // Max / sum over the 16 lanes of a DPP row; every lane of the row gets the same value (the
 // pairwise steps are symmetric, so the sum is rounded identically in each lane).
@@ -372,7 +373,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
     bool ok[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ok[r] = rowok[16 * r + j] != 0;
+    // The reference point m_run of a head moves only when the chunk's max exceeds it by more
+    // than kLazyLog2, so P <= 2^kLazyLog2 and O is rescaled only on such a move (numerator
+    // and denominator share the reference point: the softmax is unchanged).
     float alpha[4];
+    bool moved = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       float sv[4], m = -INFINITY;
@@ -381,8 +386,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
         sv[r] = ok[r] ? s[r][v] * scale_log2 : -INFINITY;
         m = fmaxf(m, sv[r]);
       }
-      const float mnew = fmaxf(m_run[v], row16_max(m));
-      alpha[v] = mnew == -INFINITY ? 1.f : exp2f(m_run[v] - mnew);
+      m = row16_max(m);
+      const bool mv = m > m_run[v] + kLazyLog2;              // true from -inf to finite
+      const float mnew = mv ? m : m_run[v];
+      alpha[v] = (mv && m_run[v] != -INFINITY) ? exp2f(m_run[v] - mnew) : 1.f;
+      moved |= mv && m_run[v] != -INFINITY;
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -394,10 +402,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
       l_run[v] = l_run[v] * alpha[v] + row16_sum(ps);
       m_run[v] = mnew;
     }
+    if (__ballot(moved) != 0) {                              // wave-uniform, rare
 #pragma unroll
-    for (int t = 0; t < 32; ++t)
+      for (int t = 0; t < 32; ++t)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[t][v] *= alpha[v];
+        for (int v = 0; v < 4; ++v) o[t][v] *= alpha[v];
+    }
     // O[head 4g+v][dim 128*blk + 8j + t] += sum_r P[head][r] X[r][dim]; the P tile is this
     // wave's own, so it is read back without a barrier (a wave's LDS accesses are ordered).
 #pragma unroll
