@@ -235,7 +235,11 @@ def main() -> int:
         pool_pos, pool_len = up(inp["pool_pos"]), up(inp["pool_len"])
     out = torch.empty((L, B, T, Hh, 512), dtype=torch.int16, device=dev)
     lse = torch.empty((L, B, T, Hh), dtype=torch.float32, device=dev)
-    ws_full_b = H.csa2_index_full_workspace(B, T, N, w.block, w.pool_blocks, K) if w.has_full else 0
+    chain = w.has_full and w.pool_blocks > 0          # pool, Full Top-K and Reindex in one call
+    if chain:
+        ws_full_b = H.csa2_index_chain_workspace(B, T, N, w.block, w.pool_blocks, K, w.n_reindex)
+    else:
+        ws_full_b = H.csa2_index_full_workspace(B, T, N, w.block, w.pool_blocks, K) if w.has_full else 0
     ws_ri_b = H.csa2_reindex_workspace(max(w.n_reindex, 1), B, T, w.pool_cap, K)
     ws_attn_b = H.csa2_sparse_attn_workspace(L, B, T, Hh, K, w.swa_window)
     ws_full = torch.empty((max(ws_full_b, 1),), dtype=torch.uint8, device=dev)
@@ -252,6 +256,12 @@ def main() -> int:
         H.csa2_index_select(n_vis, B, T, N, w.block, w.pool_blocks, K, pool_pos, pool_len, sets[0], None,
                             ws_full, ws_full_b)
 
+    def select_reindex(r):
+        n = w.n_reindex
+        H.csa2_index_select_reindex(k_rep[r], N, n_vis, B, T, N, w.block, w.pool_blocks, K,
+                                    ri_q if n else None, ri_w if n else None, n, pool_pos, pool_len,
+                                    sets[0], None, ri_sets if n else None, None, ws_full, ws_full_b)
+
     def reindex(r):
         if w.n_reindex:
             H.csa2_reindex(k_rep[r], N, ri_q, ri_w, pool_pos, pool_len, w.pool_cap, w.n_reindex, B, T, K,
@@ -262,7 +272,9 @@ def main() -> int:
                            swa_end, w.swa_window, L, B, T, Hh, K, scale, out, lse, ws_attn, ws_attn_b)
 
     # The first stage is launched directly (and timed on its own); the others replay a graph.
-    if w.has_full:
+    if chain:
+        stages = (("scan", scan), ("pool, Full+Reindex top-k", select_reindex), ("attention", attend))
+    elif w.has_full:
         stages = (("scan", scan), ("pool+top-k", select), ("reindex", reindex), ("attention", attend))
     else:
         stages = (("reindex", reindex), ("attention", attend))

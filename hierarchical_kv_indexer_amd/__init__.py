@@ -30,6 +30,11 @@ EXPORTS = (
     ("csa2_index_topk", _I, (_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_select", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_full", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
+    ("csa2_index_chain_workspace", _SZ, (_I, _I, _I, _I, _I, _I, _I)),
+    ("csa2_index_chain", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                              _P, _SZ, _P)),
+    ("csa2_index_select_reindex", _I, (_P, _I64, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+                                       _P, _SZ, _P)),
     ("csa2_reindex_workspace", _SZ, (_I, _I, _I, _I, _I)),
     ("csa2_reindex", _I, (_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
     ("csa2_sparse_attn_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
@@ -143,6 +148,33 @@ def csa2_index_select(n_visible, B: int, T: int, n_max: int, block_size: int, po
     _check(lib().csa2_index_select(_ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
                                    _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
                                    _ptr(workspace), ws_bytes, _stream(stream, n_visible)))
+
+
+def csa2_index_chain_workspace(B: int, T: int, n_max: int, block_size: int, pool_blocks: int,
+                               top_k: int, L: int) -> int:
+    return lib().csa2_index_chain_workspace(B, T, n_max, block_size, pool_blocks, top_k, L)
+
+
+def csa2_index_chain(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int, n_max: int,
+                     block_size: int, pool_blocks: int, top_k: int, ri_q, ri_w, L: int, pool_pos, pool_len,
+                     topk_idx, topk_score, ri_topk_idx, ri_topk_score, workspace, ws_bytes: int,
+                     stream=None) -> None:
+    _check(lib().csa2_index_chain(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w), _ptr(n_visible),
+                                  B, T, n_max, block_size, pool_blocks, top_k, _ptr(ri_q), _ptr(ri_w), L,
+                                  _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
+                                  _ptr(ri_topk_idx), _ptr(ri_topk_score), _ptr(workspace), ws_bytes,
+                                  _stream(stream, idx_k)))
+
+
+def csa2_index_select_reindex(idx_k, k_rows_per_seq: int, n_visible, B: int, T: int, n_max: int,
+                              block_size: int, pool_blocks: int, top_k: int, ri_q, ri_w, L: int,
+                              pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx, ri_topk_score,
+                              workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().csa2_index_select_reindex(_ptr(idx_k), k_rows_per_seq, _ptr(n_visible), B, T, n_max,
+                                           block_size, pool_blocks, top_k, _ptr(ri_q), _ptr(ri_w), L,
+                                           _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
+                                           _ptr(ri_topk_idx), _ptr(ri_topk_score), _ptr(workspace), ws_bytes,
+                                           _stream(stream, idx_k)))
 
 
 def csa2_reindex_workspace(L: int, B: int, T: int, pool_cap: int, top_k: int) -> int:

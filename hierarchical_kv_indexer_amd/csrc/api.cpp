@@ -225,12 +225,26 @@ static csa2_status launch_pool_stage(const FullPlan& p, const FullWs& w, const i
                    "pool launch");
 }
 
+// The Full layer's Top-K over its pool, by position in the scan's scores.
+static csa2::TopkJob full_topk_job(const FullPlan& p, const FullWs& w, int n_max, int32_t* topk_idx,
+                                   float* topk_score) {
+  csa2::TopkJob j{};
+  j.scores = w.scores;
+  j.score_stride = n_max;
+  j.n_rows = n_max > 0 ? n_max : 1;
+  j.by_position = 1;
+  j.items = p.Q;
+  j.out_idx = topk_idx;
+  j.out_score = topk_score;
+  return j;
+}
+
 static csa2_status launch_topk_stage(const FullPlan& p, const FullWs& w, int n_max, const int32_t* pool_pos,
                                      const int32_t* pool_len, int top_k, int32_t* topk_idx, float* topk_score,
                                      hipStream_t s) {
   return hip_check(csa2::launch_topk(p.internal_pool ? w.pool_pos : pool_pos,
-                                     p.internal_pool ? w.pool_len : pool_len, p.cap, n_max > 0 ? n_max : 1,
-                                     w.scores, n_max, true, p.Q, p.Q, top_k, topk_idx, topk_score, s),
+                                     p.internal_pool ? w.pool_len : pool_len, p.cap, p.Q, top_k,
+                                     full_topk_job(p, w, n_max, topk_idx, topk_score), csa2::TopkJob{}, s),
                    "top-k launch");
 }
 
@@ -336,10 +350,114 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
                                                    pool_cap, L, Q, T, ri, s),
                              "reindex score launch");
   if (st != CSA2_OK) return st;
-  st = hip_check(csa2::launch_topk(pool_pos, pool_len, pool_cap, k_rows_per_seq, ri, pool_cap, false, L * Q, Q,
-                                   top_k, topk_idx, topk_score, s),
+  csa2::TopkJob j{};
+  j.scores = ri;
+  j.score_stride = pool_cap;
+  j.n_rows = k_rows_per_seq;
+  j.by_position = 0;
+  j.items = L * Q;
+  j.out_idx = topk_idx;
+  j.out_score = topk_score;
+  st = hip_check(csa2::launch_topk(pool_pos, pool_len, pool_cap, Q, top_k, j, csa2::TopkJob{}, s), "top-k launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
+// Full layer plus L Reindex layers over its pool: the Full workspace, then the Reindex scores.
+static size_t carve_chain(void* ws, const FullPlan& p, int n_max, int L, FullWs* fw, float** ri) {
+  const size_t full = carve_full(ws, p, n_max, fw);
+  if (ri) *ri = ws ? (float*)((char*)ws + full) : nullptr;
+  return full + (L > 0 ? align_up((size_t)L * p.Q * p.cap * sizeof(float)) : 0);
+}
+
+size_t csa2_index_chain_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k, int L) {
+  (void)block_size;
+  if (B < 1 || T < 1 || n_max < 0 || pool_blocks < 1 || top_k < 1 || L < 0) return 0;
+  return carve_chain(nullptr, plan_full(B, T, n_max, pool_blocks, top_k), n_max, L, nullptr, nullptr);
+}
+
+static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                               const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                               int block_size, int pool_blocks, int top_k, const uint16_t* ri_q,
+                               const float* ri_w, int L, int32_t* pool_pos, int32_t* pool_len,
+                               int32_t* topk_idx, float* topk_score, int32_t* ri_topk_idx,
+                               float* ri_topk_score, void* workspace, size_t ws_bytes, void* stream) {
+  csa2_status st;
+  if (do_scan) {
+    st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+    if (st != CSA2_OK) return st;
+  } else {
+    REQUIRE(k_rows_per_seq >= n_max && k_rows_per_seq < ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
+            "need n_max <= k_rows_per_seq < 2^31");
+    REQUIRE_PTR(idx_k);
+    REQUIRE_PTR(n_visible);
+  }
+  if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
+  REQUIRE(pool_blocks >= 1, CSA2_ERR_INVALID_ARG, "the chain needs a pool (pool_blocks >= 1)");
+  REQUIRE(L >= 0 && (int64_t)(L + 1) * B * T <= 65535, CSA2_ERR_UNSUPPORTED, "need L >= 0 and (L+1)*B*T <= 65535");
+  const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
+  if ((st = check_pool_args(p, pool_pos, pool_len)) != CSA2_OK) return st;
+  if ((st = check_topk_args(topk_idx, topk_score)) != CSA2_OK) return st;
+  if (L > 0) {
+    REQUIRE_PTR(ri_q);
+    REQUIRE_PTR(ri_w);
+    if ((st = check_topk_args(ri_topk_idx, ri_topk_score)) != CSA2_OK) return st;
+  }
+  const size_t need = carve_chain(nullptr, p, n_max, L, nullptr, nullptr);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  FullWs w;
+  float* ri = nullptr;
+  carve_chain(workspace, p, n_max, L, &w, &ri);
+  hipStream_t s = (hipStream_t)stream;
+  if (do_scan && n_max > 0) {
+    st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, s),
+                   "index scan launch");
+    if (st != CSA2_OK) return st;
+  }
+  st = launch_pool_stage(p, w, n_visible, n_max, pool_pos, pool_len, top_k, nullptr, nullptr, s);
+  if (st != CSA2_OK) return st;
+  csa2::TopkJob rj{};
+  if (L > 0) {
+    st = hip_check(csa2::launch_ri_score(idx_k, k_rows_per_seq, ri_q, ri_w, pool_pos, pool_len, p.cap, L, p.Q, T,
+                                         ri, s),
+                   "reindex score launch");
+    if (st != CSA2_OK) return st;
+    rj.scores = ri;
+    rj.score_stride = p.cap;
+    rj.n_rows = k_rows_per_seq;
+    rj.by_position = 0;
+    rj.items = L * p.Q;
+    rj.out_idx = ri_topk_idx;
+    rj.out_score = ri_topk_score;
+  }
+  // the Reindex layers' Top-K and the Full layer's Top-K in one launch
+  st = hip_check(csa2::launch_topk(pool_pos, pool_len, p.cap, p.Q, top_k, rj,
+                                   full_topk_job(p, w, n_max, topk_idx, topk_score), s),
                  "top-k launch");
   return st == CSA2_OK ? ok() : st;
+}
+
+csa2_status csa2_index_chain(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                             int block_size, int pool_blocks, int top_k, const uint16_t* ri_q, const float* ri_w,
+                             int L, int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                             int32_t* ri_topk_idx, float* ri_topk_score, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  return index_chain(true, idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
+                     top_k, ri_q, ri_w, L, pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx, ri_topk_score,
+                     workspace, ws_bytes, stream);
+}
+
+csa2_status csa2_index_select_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const int32_t* n_visible,
+                                      int B, int T, int n_max, int block_size, int pool_blocks, int top_k,
+                                      const uint16_t* ri_q, const float* ri_w, int L, int32_t* pool_pos,
+                                      int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                                      int32_t* ri_topk_idx, float* ri_topk_score, void* workspace,
+                                      size_t ws_bytes, void* stream) {
+  return index_chain(false, idx_k, k_rows_per_seq, nullptr, nullptr, n_visible, B, T, n_max, block_size,
+                     pool_blocks, top_k, ri_q, ri_w, L, pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx,
+                     ri_topk_score, workspace, ws_bytes, stream);
 }
 
 size_t csa2_sparse_attn_workspace(int L, int B, int T, int H, int top_k, int swa_window) {

@@ -36,9 +36,19 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
 // Top-K over candidate lists.  Candidate slot i of item it has position cand_pos[(it % Q)*cap + i]
 // (slots >= cand_len[it % Q] are empty).  by_position: the score of a candidate is
 // scores[(it % Q)*score_stride + pos]; otherwise scores[it*score_stride + slot].
-hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int64_t n_rows,
-                       const float* scores, int64_t score_stride, bool by_position, int items,
-                       int Q, int k, int32_t* out_idx, float* out_score, hipStream_t s);
+// One kind of Top-K item over the pools cand_pos/cand_len: `items` items (it = l*Q + q); by
+// position, the score of a candidate at position p is scores[q*score_stride + p], otherwise that
+// of slot i is scores[it*score_stride + i]; positions >= n_rows are ignored.
+struct TopkJob {
+  const float* scores;
+  int64_t score_stride, n_rows;
+  int by_position, items;
+  int32_t* out_idx;      // [items][k]
+  float* out_score;      // [items][k] or null
+};
+// Items of job a, then items of job b (b.items may be 0), in one launch.
+hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
+                       const TopkJob& a, const TopkJob& b, hipStream_t s);
 
 // attn.hip
 struct AttnPlan {

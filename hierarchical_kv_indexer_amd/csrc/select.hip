@@ -561,24 +561,26 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
 
 // ------------------------------------------------------------------ Top-K over given pools
 
-// One WG per item (it = l*Q + q).  Candidates: slots [0, len) of the item's query; slot i has
-// position cand_pos[i] (ignored if negative or >= n_rows).  by_position: its score is
-// scores[q*score_stride + pos], otherwise scores[it*score_stride + slot].  Output: the k best
-// positions in slot order (ascending positions for an ascending pool) with their scores,
-// -1 / 0 padded.  Slot i*kNT + t belongs to thread t, so each load instruction reads
-// consecutive slots.
-__global__ __launch_bounds__(kNT) void k_topk(
-    const int32_t* __restrict__ cand_pos, const int32_t* __restrict__ cand_len, int cap,
-    int64_t n_rows, const float* __restrict__ scores, int64_t score_stride, int by_position,
-    int Q, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+// One WG per item: the items of job a, then those of job b (it = l*Q + q within its job).
+// Candidates: slots [0, len) of the item's query; slot i has position cand_pos[i] (ignored if
+// negative or >= the job's n_rows); its score as TopkJob states.  Output: the k best positions
+// in slot order (ascending positions for an ascending pool) with their scores, -1 / 0 padded.
+// Slot i*kNT + t belongs to thread t, so each load instruction reads consecutive slots.
+__global__ __launch_bounds__(kNT) void k_topk(const int32_t* __restrict__ cand_pos,
+                                              const int32_t* __restrict__ cand_len, int cap, int Q, int k,
+                                              TopkJob a, TopkJob b) {
   __shared__ SelectSmem sm;
   Block bk{sm};
-  const int it = blockIdx.x, q = it % Q, t = threadIdx.x;
+  const bool in_a = (int)blockIdx.x < a.items;
+  const TopkJob& job = in_a ? a : b;
+  const int it = in_a ? (int)blockIdx.x : (int)blockIdx.x - a.items;
+  const int q = it % Q, t = threadIdx.x;
   smem_init(sm);
   int len = cand_len[q];
   len = len < 0 ? 0 : (len > cap ? cap : len);
   const int32_t* cp = cand_pos + (size_t)q * cap;
-  const float* sc = scores + (size_t)(by_position ? q : it) * score_stride;
+  const bool by_position = job.by_position != 0;
+  const float* sc = job.scores + (size_t)(by_position ? q : it) * job.score_stride;
   int32_t pos[kE];
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
@@ -590,7 +592,7 @@ __global__ __launch_bounds__(kNT) void k_topk(
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
     const int slot = i * kNT + t;
-    ok[i] = slot < len && pos[i] >= 0 && (int64_t)pos[i] < n_rows;
+    ok[i] = slot < len && pos[i] >= 0 && (int64_t)pos[i] < job.n_rows;
     s[i] = sc[by_position ? (ok[i] ? pos[i] : 0) : (slot < len ? slot : 0)];
   }
   uint64_t key[kE];
@@ -602,14 +604,15 @@ __global__ __launch_bounds__(kNT) void k_topk(
     nvalid += ok[i] ? 1u : 0u;
     if (ok[i]) { mn = min(mn, k32); mx = max(mx, k32); }
   }
-  topk_out(key, nvalid, mn, mx, k, out_idx + (size_t)it * k, out_score ? out_score + (size_t)it * k : nullptr, bk);
+  topk_out(key, nvalid, mn, mx, k, job.out_idx + (size_t)it * k,
+           job.out_score ? job.out_score + (size_t)it * k : nullptr, bk);
 }
 
-hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int64_t n_rows,
-                       const float* scores, int64_t score_stride, bool by_position, int items,
-                       int Q, int k, int32_t* out_idx, float* out_score, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(items), dim3(kNT), 0, s, cand_pos, cand_len, cap, n_rows, scores,
-                     score_stride, by_position ? 1 : 0, Q, k, out_idx, out_score);
+hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
+                       const TopkJob& a, const TopkJob& b, hipStream_t s) {
+  const int items = a.items + b.items;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_topk, dim3(items), dim3(kNT), 0, s, cand_pos, cand_len, cap, Q, k, a, b);
   return hipGetLastError();
 }
 

@@ -148,6 +148,35 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
                          int32_t* topk_idx, float* topk_score,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/* The indexer of one decode step (blog.4sapi.com sec.2 mode table and sec.4; readance.app
+ * sec.4.2/4.3): the Full layer (scan, candidate pool, its Top-K) followed by L Reindex layers over
+ * that pool, with the results csa2_index_full followed by csa2_reindex on its pool would give.
+ * The Full layer's Top-K is taken in the same launch as the Reindex layers' Top-K, since both
+ * only need the pool.  Arguments as for csa2_index_full and csa2_reindex:
+ *   idx_q, head_w        the Full layer's indexer query [B][T][32][128] bf16 and weights [B][T][32]
+ *   ri_q, ri_w           [L][B][T][32][128] bf16 and [L][B][T][32] float (unused when L == 0)
+ *   pool_pos, pool_len   the pool, out ([B][T][pool_blocks*8] and [B][T])
+ *   topk_idx, topk_score the Full layer's Top-K, out ([B][T][top_k]; topk_score may be NULL)
+ *   ri_topk_idx, ri_topk_score  the Reindex layers' Top-K, out ([L][B][T][top_k]; score may be NULL)
+ *   workspace            at least csa2_index_chain_workspace(...) bytes; it starts with the
+ *                        csa2_index_full workspace, so csa2_index_scan accepts it too
+ * csa2_index_select_reindex is csa2_index_chain without the scan: call it after csa2_index_scan
+ * on the same workspace (it reads the scan's results from there).
+ * Supported: as csa2_index_full with pool_blocks >= 1, L >= 0 and (L+1)*B*T <= 65535. */
+size_t csa2_index_chain_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k, int L);
+csa2_status csa2_index_chain(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                             int block_size, int pool_blocks, int top_k, const uint16_t* ri_q, const float* ri_w,
+                             int L, int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                             int32_t* ri_topk_idx, float* ri_topk_score, void* workspace, size_t ws_bytes,
+                             void* stream);
+csa2_status csa2_index_select_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const int32_t* n_visible,
+                                      int B, int T, int n_max, int block_size, int pool_blocks, int top_k,
+                                      const uint16_t* ri_q, const float* ri_w, int L, int32_t* pool_pos,
+                                      int32_t* pool_len, int32_t* topk_idx, float* topk_score,
+                                      int32_t* ri_topk_idx, float* ri_topk_score, void* workspace,
+                                      size_t ws_bytes, void* stream);
+
 /* Sparse attention of L layers (blog.4sapi.com sec.2 and sec.5; alphalab.site sec."3. FP4"):
  * layer l attends, per query and head, over the main-KV rows of index set layer_set[l]
  * (FP4 E2M1 codes x E4M3 per-16-channel scales, dequantised exactly) followed by its own SWA

@@ -86,6 +86,32 @@ def gpu_reindex(inp, B, T, pool_pos, pool_len, top_k, L=None):
     return {"topk": host(idx), "topk_score": host(sc)}
 
 
+def gpu_index_chain(inp, B, T, n_max, pool_blocks, top_k, L, split=False, block=8):
+    """csa2_index_chain (or csa2_index_scan + csa2_index_select_reindex with split=True)."""
+    cap = pool_blocks * block
+    pool_pos, pool_len = empty((B, T, cap), torch.int32), empty((B, T), torch.int32)
+    idx, sc = empty((B, T, top_k), torch.int32), empty((B, T, top_k), torch.float32)
+    ri_idx = empty((max(L, 1), B, T, top_k), torch.int32)
+    ri_sc = empty((max(L, 1), B, T, top_k), torch.float32)
+    ws_bytes = H.csa2_index_chain_workspace(B, T, n_max, block, pool_blocks, top_k, L)
+    ws = empty((ws_bytes,), torch.uint8)
+    k, q, hw, nv = dev(inp["idx_k"]), dev(inp["idx_q"]), dev(inp["head_w"]), dev(inp["n_visible"])
+    rq = dev(inp["ri_q"][:L]) if L else None
+    rw = dev(inp["ri_w"][:L]) if L else None
+    rows = inp["idx_k"].shape[1]
+    if split:
+        H.csa2_index_scan(k, rows, q, hw, nv, B, T, n_max, block, pool_blocks, top_k, ws, ws_bytes)
+        H.csa2_index_select_reindex(k, rows, nv, B, T, n_max, block, pool_blocks, top_k, rq, rw, L, pool_pos,
+                                    pool_len, idx, sc, ri_idx if L else None, ri_sc if L else None, ws, ws_bytes)
+    else:
+        H.csa2_index_chain(k, rows, q, hw, nv, B, T, n_max, block, pool_blocks, top_k, rq, rw, L, pool_pos,
+                           pool_len, idx, sc, ri_idx if L else None, ri_sc if L else None, ws, ws_bytes)
+    out = {"topk": host(idx), "topk_score": host(sc), "pool_pos": host(pool_pos), "pool_len": host(pool_len)}
+    if L:
+        out["ri_topk"], out["ri_topk_score"] = host(ri_idx), host(ri_sc)
+    return out
+
+
 def gpu_attention(inp, w, idx_sets: np.ndarray, layers: Optional[Sequence[int]] = None):
     """idx_sets [S][B][T][k]; returns out [L][B][T][H][512] (bf16 bits) and lse."""
     L, B, T, Hh = w.L, w.B, w.T, w.H

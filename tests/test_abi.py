@@ -36,6 +36,10 @@ def test_workspace_sizes(H):
     assert H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512) >= (1 << 20) * 4 + (1 << 17) * 4
     assert H.csa2_reindex_workspace(4, 1, 1, 16384, 512) >= 4 * 16384 * 4
     assert H.csa2_index_full_workspace(0, 1, 10, 8, 4, 4) == 0
+    full = H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512)
+    assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 2048, 512, 0) == full
+    assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 2048, 512, 4) >= full + 4 * 16384 * 4
+    assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 0, 512, 4) == 0     # the chain needs a pool
 
 
 FAKE = 1 << 20   # a 16-byte aligned non-null value; validation fails before it is used
@@ -94,3 +98,26 @@ def test_stage_entries_reject(H):
     expect(H, 1, lambda: H.csa2_index_topk(1, 1, 4096, 8, 64, 64, FAKE, FAKE, None, None, FAKE, 1 << 30))
     expect(H, 1, lambda: H.csa2_index_topk(1, 1, 4096, 8, 0, 64, None, None, FAKE, FAKE + 4, FAKE, 1 << 30))
     expect(H, 3, lambda: H.csa2_index_topk(1, 1, 4096, 8, 0, 64, None, None, FAKE, None, FAKE, 8))
+
+
+def test_chain_entries_reject(H):
+    ws = H.csa2_index_chain_workspace(1, 1, 4096, 8, 64, 64, 2)
+    ok = dict(pool_pos=FAKE, pool_len=FAKE, topk_idx=FAKE, topk_score=None, ri_topk_idx=FAKE, ri_topk_score=None)
+
+    def chain(pool_blocks=64, L=2, ri_q=FAKE, ws_bytes=ws, **kw):
+        a = dict(ok, **kw)
+        H.csa2_index_chain(FAKE, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, pool_blocks, 64, ri_q, FAKE, L,
+                           a["pool_pos"], a["pool_len"], a["topk_idx"], a["topk_score"], a["ri_topk_idx"],
+                           a["ri_topk_score"], FAKE, ws_bytes)
+
+    expect(H, 1, lambda: chain(pool_blocks=0))                 # no pool
+    expect(H, 1, lambda: chain(ri_q=None))                     # Reindex query missing
+    expect(H, 1, lambda: chain(ri_topk_idx=None))              # Reindex output missing
+    expect(H, 1, lambda: chain(pool_len=None))
+    expect(H, 2, lambda: chain(L=70000))
+    expect(H, 3, lambda: chain(ws_bytes=ws - 256))
+    # without the scan: the Full query is not needed, the keys and the pool still are
+    expect(H, 1, lambda: H.csa2_index_select_reindex(None, 4096, FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, 2, FAKE,
+                                                     FAKE, FAKE, None, FAKE, None, FAKE, ws))
+    expect(H, 3, lambda: H.csa2_index_select_reindex(FAKE, 4096, FAKE, 1, 1, 4096, 8, 64, 64, None, None, 0, FAKE,
+                                                     FAKE, FAKE, None, None, None, FAKE, 64))

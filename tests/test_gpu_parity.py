@@ -164,6 +164,26 @@ def test_stage_entries_match_index_full(P):
         assert np.array_equal(G.host(pool_len), ref["pool_len"])
 
 
+@pytest.mark.parametrize("L,split", [(2, False), (2, True), (0, False)])
+def test_index_chain_matches_full_then_reindex(L, split):
+    """The one-call indexer (Full Top-K launched with the Reindex Top-K) gives the same bits as
+    csa2_index_full followed by csa2_reindex on its pool; ragged n_visible per query."""
+    B, T, N, P, K = 2, 2, 20000, 256, 300
+    w = small(B=B, T=T, N=N, pool_blocks=P, top_k=K, n_reindex=max(L, 1), seed=3200 + L)
+    inp = workloads.make_inputs(w, with_attention=False)
+    inp["n_visible"] = np.array([[20000, 13001], [2047, 19999]], np.int32)
+    ref = G.gpu_index_full(inp, B, T, N, P, K)
+    got = G.gpu_index_chain(inp, B, T, N, P, K, L, split=split)
+    for key in ("topk", "pool_pos", "pool_len"):
+        assert np.array_equal(got[key], ref[key]), key
+    assert np.array_equal(got["topk_score"].view(np.uint32), ref["topk_score"].view(np.uint32))
+    if L:
+        ri = G.gpu_reindex(inp, B, T, ref["pool_pos"], ref["pool_len"], K, L=L)
+        assert np.array_equal(got["ri_topk"], ri["topk"])
+        assert np.array_equal(got["ri_topk_score"].view(np.uint32), ri["topk_score"].view(np.uint32))
+    check_full(w, inp, got, 1, 1)
+
+
 def test_index_full_no_pool_dense_topk():
     w = small(T=3, N=9000, pool_blocks=0, top_k=200, seed=31)
     inp = workloads.make_inputs(w, with_attention=False)
