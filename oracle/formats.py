@@ -23,6 +23,21 @@ animattoys.com section on the FP4 main KV cache):
 
 Encoders round to nearest, ties to the code with an even mantissa (which is the
 even code), and saturate to the largest finite magnitude.
+
+Main-KV quantisation (the producer of the cache; blog.4sapi.com section 5 and the
+animattoys.com FP4 section give the format and that it is applied to the rotated
+latent, not the rule for choosing a scale).  The reading taken here, per group of 16
+channels of a bf16 row:
+  amax  = max |x_c|;
+  scale = E4M3(amax / 6), the quotient rounded to binary32 first (6 = the largest E2M1
+          magnitude, so amax maps to the top of the FP4 range);
+  code_c = E2M1(x_c / scale), the quotient rounded to binary32 first, ties to even,
+          saturating at +-6, sign kept (-0 gives the negative-zero code);
+  a group whose scale byte is 0 (amax / 6 rounds to zero) stores code 0 everywhere.
+Both quotients are IEEE binary32 divisions, the precision in which the GPU kernel takes
+the same integer decisions.  Parity: pinned by the round trip of exactly representable
+rows, the error bound of the two roundings, the pages' range 2688 = 6 x 448 and the
+special cases in tests/test_oracle_formats.py.
 """
 from __future__ import annotations
 
@@ -120,3 +135,23 @@ def kv_row_values(codes, scales) -> np.ndarray:
     v = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
     s = np.repeat(e4m3_value(scales), 16, axis=-1)
     return v * s
+
+
+def kv_quantize_rows(x_bf16) -> "tuple[np.ndarray, np.ndarray]":
+    """Rotated bf16 latent rows [..., 512] (uint16 bits) -> (codes [..., 256] uint8,
+    scales [..., 32] uint8), by the reading in the module docstring."""
+    bits = np.asarray(x_bf16, dtype=np.uint16)
+    assert bits.shape[-1] == 512
+    x = (bits.astype(np.uint32) << 16).view(np.float32)             # exact bf16 values
+    g = x.reshape(bits.shape[:-1] + (32, 16))
+    amax = np.max(np.abs(g), axis=-1)                                # exact
+    s32 = (amax / np.float32(6.0)).astype(np.float32)               # binary32 division
+    scales = e4m3_from_value(s32.astype(np.float64))
+    sval = e4m3_value(scales).astype(np.float32)                     # exact in binary32
+    safe = np.where(sval > 0, sval, np.float32(1.0))[..., None]
+    q = (g / safe).astype(np.float32)                                # binary32 division
+    codes16 = e2m1_from_value(q.astype(np.float64))
+    codes16 = np.where((sval > 0)[..., None], codes16, np.uint8(0)).astype(np.uint8)
+    c = codes16.reshape(bits.shape[:-1] + (512,))
+    codes = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    return codes, scales

@@ -137,3 +137,97 @@ def test_fp4_dequant_is_exact_in_bf16():
     back = torch.from_numpy(prod).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(back, prod)
     assert np.abs(prod).max() == 2688.0
+
+
+# ------------------------------------------------------------------ main-KV quantiser
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float values that are exact in bf16 -> their bit patterns (checked exact)."""
+    b = torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16)
+    assert np.array_equal(b.to(torch.float64).numpy(), np.asarray(x, np.float64))
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_kv_quantize_roundtrip_of_representable_rows():
+    """A row whose every group holds a +-6 code is quantised back to the same bytes: its scale
+    is exactly amax / 6 and every value is exactly code x scale (negative zeros included)."""
+    rng = np.random.default_rng(5)
+    e4 = np.arange(1, 127, dtype=np.uint8)                  # positive finite scales, subnormals too
+    for _ in range(20):
+        codes16 = rng.integers(0, 16, size=512).astype(np.uint8)
+        top = rng.integers(0, 16, size=32) + 16 * np.arange(32)
+        codes16[top] = np.where(rng.random(32) < 0.5, 7, 15)
+        scales = rng.choice(e4, size=32)
+        codes = (codes16[0::2] | (codes16[1::2] << 4)).astype(np.uint8)
+        x = F.kv_row_values(codes, scales)
+        c2, s2 = F.kv_quantize_rows(_bf16_bits(x))
+        assert np.array_equal(s2, scales)
+        assert np.array_equal(c2, codes)
+
+
+def _e2m1_half_step(q: np.ndarray) -> np.ndarray:
+    """Half the E2M1 spacing around |q| (q in [0, 6])."""
+    a = np.abs(q)
+    return np.where(a <= 2.0, 0.25, np.where(a <= 4.0, 0.5, 1.0))
+
+
+def test_kv_quantize_error_bound_and_nearest_choice():
+    """On latent-like rows (unit RMS, as after RMSNorm, with a few large channels), every code
+    is a nearest E2M1 value of x / scale (brute force over the 8 magnitudes), the scale is
+    amax / 6 within E4M3's relative rounding 2^-4, and |x - dequant| is within half a step of
+    the grid (or the saturation gap amax - 6 * scale)."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((64, 512)).astype(np.float32)
+    x[:, rng.integers(0, 512, 8)] *= 8.0                    # magnitudes up to ~10 and beyond
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xv = F.bf16_value(bits)
+    codes, scales = F.kv_quantize_rows(bits)
+    s = F.e4m3_value(scales)                                   # [64, 32]
+    g = xv.reshape(64, 32, 16)
+    amax = np.abs(g).max(-1)
+    assert np.all(np.abs(s - amax / 6) <= amax / 6 * 2.0 ** -4 * (1 + 1e-12))
+    deq = F.kv_row_values(codes, scales).reshape(64, 32, 16)
+    q = g / s[..., None]
+    sat = np.abs(q) > 6.0
+    bound = np.where(sat, np.abs(g) - 6 * s[..., None], s[..., None] * _e2m1_half_step(q))
+    assert np.all(np.abs(deq - g) <= bound * (1 + 1e-6) + 1e-30)
+    # nearest magnitude by brute force (distance to each of the 8 magnitudes)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    got = np.abs(deq / s[..., None])
+    dist = np.abs(np.abs(q)[..., None] - mags)
+    assert np.all(np.abs(np.abs(np.minimum(np.abs(q), 6.0)) - got) <= dist.min(-1) + 1e-9)
+    assert np.all(np.signbit(deq) == np.signbit(g))
+
+
+def test_kv_quantize_ties_go_to_even_codes():
+    # scale 1 (amax 6): values at the midpoints of the E2M1 grid
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    expect = np.array([0, 2, 2, 4, 4, 6, 6])                # even codes
+    row = np.zeros(512, np.float32)
+    row[0] = 6.0
+    row[1:8] = mids
+    row[8:15] = -mids
+    codes, scales = F.kv_quantize_rows(_bf16_bits(row))
+    c16 = np.stack([codes & 0xF, codes >> 4], -1).reshape(512)
+    assert scales[0] == 0x38                                # 1.0
+    assert np.array_equal(c16[1:8], expect)
+    assert np.array_equal(c16[8:15], expect | 8)
+
+
+def test_kv_quantize_range_saturation_and_zero_groups():
+    figs = page_figures()
+    row = np.zeros(512, np.float32)
+    row[0] = figs["fp4_format_range"]          # 2688 = 6 x 448: the top of the format
+    row[16] = 4096.0                    # beyond it: scale and code saturate
+    row[17] = -4096.0
+    row[32] = 2.0 ** -12                # amax / 6 rounds to a zero scale byte
+    row[48] = -0.0                      # an all-zero group (one negative zero)
+    row[64] = 6 * 2.0 ** -9             # the smallest subnormal scale, exactly
+    codes, scales = F.kv_quantize_rows(_bf16_bits(row))
+    c16 = np.stack([codes & 0xF, codes >> 4], -1).reshape(512)
+    deq = F.kv_row_values(codes, scales)
+    assert scales[0] == 0x7E and c16[0] == 7 and deq[0] == figs["fp4_format_range"]
+    assert scales[1] == 0x7E and c16[16] == 7 and c16[17] == 15 and deq[16] == figs["fp4_format_range"]
+    assert scales[2] == 0 and not c16[32:48].any()
+    assert scales[3] == 0 and not c16[48:64].any()
+    assert scales[4] == 0x01 and c16[64] == 7 and deq[64] == row[64]
