@@ -21,6 +21,9 @@ roofline figure).
 Prints one JSON line (metric, value in queries/s, roofline of the scan kernel, CPU oracle
 baseline) on stdout; a per-stage breakdown goes to stderr.
 
+``--kernel quantize_kv`` instead times the FP4 main-KV quantiser on its own (2^20 latent rows
+per launch by default, ``--rows``) and prints its own JSON line (rows/s, HBM roofline).
+
 ``--summarize-pmc FETCH_DIR WRITE_DIR`` turns two rocprofv3 counter runs of this script
 (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, each with ``--calibrate-copy``) into the
 traffic summary that later runs report, and exits.
@@ -175,6 +178,89 @@ def cpu_baseline(w, inp, seconds: float):
                       f"layers) for one query of {w.name}, {el:.1f} s"}
 
 
+QUANT_ROW_BYTES = 512 * 2 + 256 + 32      # bf16 latent row in, E2M1 codes and E4M3 scales out
+
+
+def bench_quantize_kv(args) -> int:
+    """The FP4 main-KV quantiser alone: `rows` latent rows per launch (seeded normal rows with a
+    few large channels, unit RMS as after RMSNorm), launches timed with events on their stream.
+    Algorithmic bytes per launch: rows x (1024 read + 288 written)."""
+    import numpy as np
+    import torch
+
+    import hierarchical_kv_indexer_amd as H
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H.lib()
+    rows, R = args.rows, args.replicas
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    xs = []
+    for _ in range(R):       # distinct inputs and outputs per replica (past the Infinity Cache)
+        x = torch.randn((rows, 512), generator=g, device=dev, dtype=torch.float32)
+        x[:, 7] *= 8.0
+        xs.append(x.to(torch.bfloat16))
+        del x
+    codes = [torch.empty((rows, 256), dtype=torch.uint8, device=dev) for _ in range(R)]
+    scales = [torch.empty((rows, 32), dtype=torch.uint8, device=dev) for _ in range(R)]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        if args.calibrate_copy:
+            src_buf = torch.full((COPY_BYTES,), 1, dtype=torch.uint8, device=dev)
+            dst_buf = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                dst_buf.copy_(src_buf)
+            torch.cuda.synchronize()
+            del src_buf, dst_buf
+        for i in range(args.warmup):
+            r = i % R
+            H.csa2_quantize_kv_fp4(xs[r], rows, codes[r], scales[r])
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            r = i % R
+            ev[i][0].record(stream)
+            H.csa2_quantize_kv_fp4(xs[r], rows, codes[r], scales[r])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    wall = t1 - t0
+    nbytes = rows * QUANT_ROW_BYTES
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    log(f"[bench] quantize_kv: {args.steps} launches of {rows} rows, {launch_ms * 1e3:.2f} us per launch, "
+        f"{achieved:.0f} GB/s algorithmic")
+    res = {
+        "metric": "FP4 main-KV quantise rows/s (rotated bf16 latent -> E2M1 codes + E4M3 per-16 scales)",
+        "value": round(args.steps * rows / wall, 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"quantize_kv_{rows}", "rows": rows, "row_bytes": QUANT_ROW_BYTES,
+                   "replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "k_quantize_kv", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(launch_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import formats as F
+        n_cpu = 16384
+        bits = xs[0][:n_cpu].view(torch.int16).cpu().numpy().view(np.uint16)
+        t = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t < min(args.cpu_seconds, 10.0) or n == 0:
+            F.kv_quantize_rows(bits)
+            n += 1
+        el = time.perf_counter() - t
+        res["cpu_baseline"] = {"value": round(n * n_cpu / el, 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} runs of the oracle quantiser over {n_cpu} rows, {el:.1f} s"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +275,9 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--kernel", choices=("chain", "quantize_kv"), default="chain",
+                    help="quantize_kv: time the FP4 main-KV quantiser alone")
+    ap.add_argument("--rows", type=int, default=1 << 20, help="latent rows per quantiser launch")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -197,6 +286,9 @@ def main() -> int:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the sharding plan is written up with the design notes).", file=sys.stderr)
         return 2
+
+    if args.kernel == "quantize_kv":
+        return bench_quantize_kv(args)
 
     import numpy as np
     import torch

@@ -23,6 +23,7 @@ _P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_
 EXPORTS = (
     ("csa2_last_error", ctypes.c_char_p, ()),
     ("csa2_quantize_query", _I, (_P, _P, _I64, _P)),
+    ("csa2_quantize_kv_fp4", _I, (_P, _I64, _P, _P, _P)),
     ("csa2_index_scores", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
     ("csa2_index_full_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
     ("csa2_index_scan", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
@@ -97,6 +98,11 @@ def csa2_last_error() -> str:
 
 def csa2_quantize_query(in_bf16, out_e4m3, n: int, stream=None) -> None:
     _check(lib().csa2_quantize_query(_ptr(in_bf16), _ptr(out_e4m3), n, _stream(stream, in_bf16)))
+
+
+def csa2_quantize_kv_fp4(latent_bf16, rows: int, kv_codes, kv_scales, stream=None) -> None:
+    _check(lib().csa2_quantize_kv_fp4(_ptr(latent_bf16), rows, _ptr(kv_codes), _ptr(kv_scales),
+                                      _stream(stream, latent_bf16)))
 
 
 def csa2_index_scores(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,

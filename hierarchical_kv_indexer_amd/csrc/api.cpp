@@ -120,6 +120,18 @@ csa2_status csa2_quantize_query(const uint16_t* in_bf16, uint8_t* out_e4m3, int6
   return st == CSA2_OK ? ok() : st;
 }
 
+csa2_status csa2_quantize_kv_fp4(const uint16_t* latent_bf16, int64_t rows, uint8_t* kv_codes, uint8_t* kv_scales,
+                                 void* stream) {
+  REQUIRE(rows >= 0 && rows <= ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG, "rows must be in [0, 2^31]");
+  if (rows == 0) return ok();
+  REQUIRE_PTR(latent_bf16);
+  REQUIRE_PTR(kv_codes);
+  REQUIRE_PTR(kv_scales);
+  csa2_status st = hip_check(csa2::launch_quantize_kv(latent_bf16, rows, kv_codes, kv_scales, (hipStream_t)stream),
+                             "quantize_kv launch");
+  return st == CSA2_OK ? ok() : st;
+}
+
 static csa2_status check_index_common(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
                                       const float* head_w, const int32_t* n_visible, int B, int T,
                                       int n_max) {

@@ -50,6 +50,9 @@ struct TopkJob {
 hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
                        const TopkJob& a, const TopkJob& b, hipStream_t s);
 
+// kvquant.hip
+hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // attn.hip
 struct AttnPlan {
   int heads_per_wg;    // 64 (k_sparse_attn_wide) when H % 64 == 0, else 16

@@ -70,6 +70,21 @@ const char* csa2_last_error(void);
  * internally; this entry exists to verify it and for callers that keep E4M3 queries. */
 csa2_status csa2_quantize_query(const uint16_t* in_bf16, uint8_t* out_e4m3, int64_t n, void* stream);
 
+/* Main-KV quantisation, the producer of the cache csa2_sparse_attn reads (blog.4sapi.com sec.5
+ * "FP4 KV"; animattoys.com FP4 section: E2M1 codes with one E4M3 scale per 16 channels, applied
+ * to the latent after rotation, no second-level scale).  The scale rule is this library's
+ * reading (the pages give none): per group of 16 channels, scale = E4M3(amax / 6) and
+ * code = E2M1(x / scale), both quotients rounded to binary32 first, nearest-even and saturating
+ * conversions, the sign kept (-0 gives the negative-zero code); a group whose scale byte is 0
+ * stores code 0 throughout.
+ *   latent_bf16 [rows][512] bf16 (rotated latent rows)
+ *   kv_codes    [rows][256] uint8 out, channel 2i in the low nibble of byte i
+ *   kv_scales   [rows][32]  uint8 out (E4M3), scale g covers channels 16g..16g+15
+ * To append to a cache, pass kv_codes / kv_scales offset to the first row to write.
+ * NaN inputs give unspecified bytes.  Supported: 0 <= rows <= 2^31. */
+csa2_status csa2_quantize_kv_fp4(const uint16_t* latent_bf16, int64_t rows, uint8_t* kv_codes, uint8_t* kv_scales,
+                                 void* stream);
+
 /* Query preparation and the Full scan on their own: every visible position's score, no selection.
  *   idx_k      [B][k_rows_per_seq][128] E4M3 indexer keys
  *   idx_q      [B][T][32][128] bf16 indexer queries

@@ -21,7 +21,7 @@ def H():
 def declared():
     src = open(os.path.join(ROOT, "include", "csa2.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(H):
@@ -121,3 +121,10 @@ def test_chain_entries_reject(H):
                                                      FAKE, FAKE, None, FAKE, None, FAKE, ws))
     expect(H, 3, lambda: H.csa2_index_select_reindex(FAKE, 4096, FAKE, 1, 1, 4096, 8, 64, 64, None, None, 0, FAKE,
                                                      FAKE, FAKE, None, None, None, FAKE, 64))
+
+
+def test_quantize_kv_rejects(H):
+    H.csa2_quantize_kv_fp4(None, 0, None, None)                          # no rows: nothing to check
+    expect(H, 1, lambda: H.csa2_quantize_kv_fp4(FAKE, -1, FAKE, FAKE))
+    expect(H, 1, lambda: H.csa2_quantize_kv_fp4(FAKE, 4, None, FAKE))
+    expect(H, 1, lambda: H.csa2_quantize_kv_fp4(FAKE, 4, FAKE, FAKE + 8))  # misaligned scales
