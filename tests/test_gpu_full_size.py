@@ -1,5 +1,6 @@
-"""GPU parity at the full workload sizes, in the launch configuration the benchmark times: the
-whole chain runs for every query of the workload; the oracle checks sampled queries.
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times (the
+chain entries where there is a pool): the whole chain runs for every query of the workload; the
+oracle checks sampled queries.
 
   decode_1m        batch 1, 1M-entry context, Full + 4 Reindex + 15 Reuse (20 attention layers)
   decode_b8_128k   batch 8, 128K entries each, Full + 4 Reindex + 5 Reuse, 64 heads
@@ -35,6 +36,8 @@ def test_decode_1m_whole_chain():
     run_chain_and_check(w, inp, [(0, 0)])
     g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
     assert np.isin(inp["planted_pos"], g["topk"][0, 0]).all(), "planted cluster not recalled"
+    c = G.gpu_index_chain(inp, 1, 1, w.N, w.pool_blocks, w.top_k, w.n_reindex, split=True)
+    assert np.array_equal(c["topk"], g["topk"]) and np.array_equal(c["pool_pos"], g["pool_pos"])
 
 
 def test_decode_b8_128k_sampled():

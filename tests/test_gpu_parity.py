@@ -280,15 +280,22 @@ def test_attention_parity_on_oracle_sets(H):
 # ------------------------------------------------------------------ whole chain
 
 def run_chain_and_check(w, inp, queries):
+    """The path as the benchmark runs it: with a Full layer and a pool, csa2_index_chain_scan then
+    csa2_index_select_reindex; otherwise csa2_index_full and/or csa2_reindex.  Then attention."""
     B, T = w.B, w.T
-    gpu_full = G.gpu_index_full(inp, B, T, w.N, w.pool_blocks, w.top_k) if w.has_full else None
-    if not w.has_full:
-        pool_pos, pool_len = inp["pool_pos"], inp["pool_len"]
-    elif w.pool_blocks:
+    gpu_ri = None
+    if w.has_full and w.pool_blocks:
+        gpu_full = G.gpu_index_chain(inp, B, T, w.N, w.pool_blocks, w.top_k, w.n_reindex, split=True)
         pool_pos, pool_len = gpu_full["pool_pos"], gpu_full["pool_len"]
+        if w.n_reindex:
+            gpu_ri = {"topk": gpu_full["ri_topk"]}
     else:
-        pool_pos = pool_len = None
-    gpu_ri = G.gpu_reindex(inp, B, T, pool_pos, pool_len, w.top_k) if w.n_reindex else None
+        gpu_full = G.gpu_index_full(inp, B, T, w.N, w.pool_blocks, w.top_k) if w.has_full else None
+        if not w.has_full:
+            pool_pos, pool_len = inp["pool_pos"], inp["pool_len"]
+        else:
+            pool_pos = pool_len = None
+        gpu_ri = G.gpu_reindex(inp, B, T, pool_pos, pool_len, w.top_k) if w.n_reindex else None
     sets = []
     if w.has_full:
         sets.append(gpu_full["topk"])
