@@ -56,20 +56,44 @@ def quantize_query(q_bf16: np.ndarray) -> np.ndarray:
     return e4m3_from_value(bf16_value(q_bf16))
 
 
-def indexer_scores(k8: np.ndarray, q8: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """s[p] = sum_h w[h] * max(0, q8[h] . k8[p])  in float64, for every row p of k8.
+def k_rows(k, sel):
+    """Rows `sel` (a slice or index array) of an indexer K in either storage form: E4M3 bytes
+    [n][128], or the FP4 variant (codes [n][64], scales [n][8])."""
+    if isinstance(k, tuple):
+        return (k[0][sel], k[1][sel])
+    return k[sel]
 
-    k8 [n][128] E4M3 bytes (indexer K), q8 [32][128] E4M3 bytes, w [32] head weights.
-    [p1 4.2], [p2 2]: Full and Reindex layers score indexer K with their own indexer Q.
-    Rows are processed in independent chunks only to bound memory.
+
+def k_count(k) -> int:
+    return (k[0] if isinstance(k, tuple) else k).shape[0]
+
+
+def k_values(k) -> np.ndarray:
+    """Indexer K rows -> float64 [n][128].  E4M3 bytes decode directly.  The FP4 variant
+    ([p2 4]: the V4 indexer used FP4 keys; stored like the main KV, E2M1 codes with one E4M3
+    scale per 16 channels, channel 2i in the low nibble of byte i) decodes to code x scale,
+    exact in float64."""
+    if isinstance(k, tuple):
+        return kv_row_values(k[0], k[1])
+    return e4m3_value(k)
+
+
+def indexer_scores(k8, q8: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """s[p] = sum_h w[h] * max(0, q8[h] . k[p])  in float64, for every row p of k.
+
+    k: indexer K rows, E4M3 bytes [n][128] or the FP4 pair (see k_values); q8 [32][128] E4M3
+    bytes, w [32] head weights.  [p1 4.2], [p2 2]: Full and Reindex layers score indexer K
+    with their own indexer Q.  Rows are processed in independent chunks only to bound memory.
+    Every product q8 * k is exact in float64 (at most 10 significant bits) and so is the
+    128-term sum.
     """
-    k8 = np.asarray(k8, dtype=np.uint8)
     qv = e4m3_value(q8)                                   # [32][128] float64
     wv = np.asarray(w, dtype=np.float32).astype(np.float64)
-    out = np.empty(k8.shape[0], np.float64)
+    n = k_count(k8)
+    out = np.empty(n, np.float64)
     step = 1 << 16
-    for r0 in range(0, k8.shape[0], step):
-        kv = e4m3_value(k8[r0:r0 + step])                 # [n][128] float64
+    for r0 in range(0, n, step):
+        kv = k_values(k_rows(k8, slice(r0, r0 + step)))   # [n][128] float64
         d = kv @ qv.T                                     # [n][32], exact
         out[r0:r0 + step] = np.maximum(d, 0.0) @ wv
     return out
@@ -122,7 +146,7 @@ def full_layer(k8_seq: np.ndarray, q_bf16: np.ndarray, w: np.ndarray, n_vis: int
     (pool_blocks > 0) and take the Top-k over the pool ([p1 4.2], [p2 4]).  With
     pool_blocks == 0 there is no pool and the Top-k runs over every visible position."""
     q8 = quantize_query(q_bf16)
-    s = indexer_scores(k8_seq[:n_vis], q8, w)
+    s = indexer_scores(k_rows(k8_seq, slice(0, n_vis)), q8, w)
     s32 = ranking_scores(s)
     if pool_blocks > 0:
         pool = candidate_pool(block_scores(s32, n_vis, block), n_vis, block, pool_blocks)
@@ -142,7 +166,7 @@ def reindex_layer(k8_seq: np.ndarray, q_bf16: np.ndarray, w: np.ndarray,
     indexer query and weights, then take its own Top-k ([p1 4.2], [p2 4], [p5 2])."""
     pool = np.asarray(pool, dtype=np.int64)
     q8 = quantize_query(q_bf16)
-    s = indexer_scores(k8_seq[pool], q8, w)
+    s = indexer_scores(k_rows(k8_seq, pool), q8, w)
     s32 = ranking_scores(s)
     idx = top_k(pool, s32, k)
     pos_to_score = dict(zip(pool.tolist(), s.tolist()))
@@ -195,7 +219,7 @@ def query_chain(inp: Dict[str, np.ndarray], w, b: int, t: int,
     ``idx_sets_override`` [S][k] replaces the index sets used by attention (stage-wise
     checks feed the GPU's own intermediate results here)."""
     n_vis = int(inp["n_visible"][b, t])
-    k8 = inp["idx_k"][b]
+    k8 = inp["idx_k"][b] if "idx_k" in inp else (inp["idx_k_codes"][b], inp["idx_k_scales"][b])
     out: Dict[str, object] = {}
     sets = []
     if w.has_full:

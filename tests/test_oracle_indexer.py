@@ -237,3 +237,68 @@ def test_workload_shapes_match_page_figures():
         assert w.pool_cap == figs["pool_positions"] and w.top_k == figs["top_k"]
     assert workloads.IDX_HEADS == figs["indexer_heads"] and workloads.IDX_DIM == figs["indexer_head_dim"]
     assert workloads.KV_DIM // workloads.KV_SCALE_BYTES == figs["scale_group"]
+
+
+# ------------------------------------------------------------------ FP4 indexer K (variant)
+
+def _e4m3_bytes_of(values: np.ndarray) -> np.ndarray:
+    """Exactly representable values -> E4M3 bytes, through torch's cast (checked exact)."""
+    t = torch.from_numpy(np.asarray(values, np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(t.to(torch.float64).numpy(), np.asarray(values, np.float64))
+    return t.view(torch.uint8).numpy()
+
+
+def test_fp4_keys_at_unit_scale_score_like_the_same_e4m3_keys():
+    """With every scale 1, FP4 key values are E2M1 values, all exact in E4M3: the FP4 path must
+    give exactly the E4M3 path's scores on the same values (that path is pinned above)."""
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 256, size=(300, 64), dtype=np.uint8)
+    scales = np.full((300, 8), 0x38, np.uint8)                       # 1.0
+    vals = F.kv_row_values(codes, scales)                            # [300][128]
+    k8 = _e4m3_bytes_of(vals)
+    q = workloads.to_bf16_bits(rng.standard_normal((32, 128)).astype(np.float32))
+    w = rng.random(32, dtype=np.float32)
+    q8 = O.quantize_query(q)
+    assert np.array_equal(O.indexer_scores((codes, scales), q8, w), O.indexer_scores(k8, q8, w))
+
+
+def test_fp4_key_channel_order_and_scale_groups():
+    """A key with one non-zero channel c (code 1.0) and scale group g = c // 16 set to 2^(g-3):
+    the one-head score with q = e_c is w * 2^(g-3), so channel c decodes at c (even channels in
+    the low nibble) with its own group's scale."""
+    q = np.zeros((32, 128), np.float32)
+    w = np.zeros(32, np.float32)
+    w[0] = 1.0
+    scales = np.array([[0x38 + 8 * (g - 3) for g in range(8)]], np.uint8)   # 2^(g-3)
+    for c in (0, 1, 14, 15, 16, 17, 63, 64, 126, 127):
+        codes = np.zeros((1, 64), np.uint8)
+        codes[0, c // 2] = 0x2 << (4 * (c & 1))                       # E2M1 1.0
+        qq = q.copy()
+        qq[0, c] = 1.0
+        s = O.indexer_scores((codes, scales), O.quantize_query(workloads.to_bf16_bits(qq)), w)
+        assert s[0] == 2.0 ** (c // 16 - 3), c
+
+
+def test_fp4_key_scores_are_homogeneous_in_the_scales():
+    """Doubling every scale (E4M3 exponent + 1) doubles every score exactly."""
+    rng = np.random.default_rng(42)
+    codes = rng.integers(0, 256, size=(200, 64), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x70, size=(200, 8), dtype=np.uint8)
+    q8 = O.quantize_query(workloads.to_bf16_bits(rng.standard_normal((32, 128)).astype(np.float32)))
+    w = rng.random(32, dtype=np.float32)
+    s1 = O.indexer_scores((codes, scales), q8, w)
+    s2 = O.indexer_scores((codes, scales + 8), q8, w)
+    assert np.array_equal(s2, 2 * s1)
+
+
+def test_fp4_key_workload_chain_selection_properties():
+    """The tiny workload with FP4 keys: the pool holds the dense Top-K (lemma S6 on the FP4
+    scores) and the planted cluster of a small planted variant is recalled."""
+    w = workloads.small_variant(workloads.WORKLOADS["decode_1m_fp4k"], N=65536, seed=4301)
+    inp = workloads.make_inputs(w, with_attention=False)
+    assert inp["idx_k_codes"].shape == (1, 65536, 64) and inp["idx_k_scales"].shape == (1, 65536, 8)
+    r = O.query_chain(inp, w, 0, 0, with_attention=False)
+    f = r["full"]
+    dense = O.top_k(np.arange(w.N, dtype=np.int32), f["scores32"], w.top_k)
+    assert np.array_equal(f["topk"], dense)
+    assert np.isin(inp["planted_pos"], f["topk"]).all()

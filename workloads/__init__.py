@@ -17,7 +17,12 @@ per 16 channels) merged with an FP8 sliding window.
 Recipe (one ``numpy.random.SeedSequence(seed)`` per workload, one child
 generator per tensor, children spawned in the order of ``STREAMS``):
 
-  indexer K            N(0,1) float32 -> E4M3 (torch cast, values clamped to +-448 first)
+  indexer K            N(0,1) float32 -> E4M3 (torch cast, values clamped to +-448 first);
+                       FP4 variant (``idx_k_fp4``): the same draws -> E2M1 codes with one
+                       power-of-two E4M3 scale per 16 channels (the smallest power of two
+                       >= amax/6, within [2^-9, 2^8]), codes the nearest E2M1 magnitude of
+                       x / scale by table lookup (this generator's own encoder; any FP4 bytes
+                       are valid input), 64 code bytes + 8 scale bytes per position
   indexer Q (Full/RI)  N(0,1) float32 -> bf16 (torch cast, round to nearest even)
   head weights w       U(0,1) float32
   main-KV E2M1 codes   categorical over the 16 codes (``E2M1_MAG_WEIGHTS`` / 256 per
@@ -75,6 +80,7 @@ class Workload:
     user_pool: int = 0        # >0: caller-provided pools of this many positions
     prefill_tokens: int = 0   # >0: causal prefill over a context of this many tokens
     m: int = 2                # tokens per compressed entry (prefill visibility)
+    idx_k_fp4: bool = False   # indexer K stored as FP4 (E2M1 codes + E4M3 per-16 scales)
 
     @property
     def L(self) -> int:
@@ -129,6 +135,10 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_1m": Workload("decode_1m", 1003, B=1, T=1, N=1 << 20, H=16,
                           layer_set=_decode_sets([(0, 4), (1, 4), (2, 4), (3, 4), (4, 4)]),
                           n_reindex=4, planted=True),
+    # the same decode with the FP4 indexer-K variant (72 B per position instead of 128 B)
+    "decode_1m_fp4k": Workload("decode_1m_fp4k", 1006, B=1, T=1, N=1 << 20, H=16,
+                               layer_set=_decode_sets([(0, 4), (1, 4), (2, 4), (3, 4), (4, 4)]),
+                               n_reindex=4, planted=True, idx_k_fp4=True),
     # 64 queries of one 256K context with caller pools: 1 Reindex layer + 1 attention layer
     "reindex_pool_256k": Workload("reindex_pool_256k", 1004, B=1, T=64, N=262144, H=64,
                                   layer_set=(0,), n_reindex=1, has_full=False,
@@ -198,6 +208,26 @@ def draw_kv_codes(rng: np.random.Generator, rows: int) -> np.ndarray:
     return out
 
 
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+
+
+def to_fp4_pow2(x: np.ndarray):
+    """float32 [n][d] -> (codes [n][d/2] u8, scales [n][d/16] u8): per 16 channels the smallest
+    power-of-two scale >= amax/6 (clamped to [2^-9, 2^8], exact in E4M3), each channel the
+    nearest E2M1 magnitude of x / scale (a table lookup on the midpoints), sign from x."""
+    n, dch = x.shape
+    g = x.reshape(n, dch // 16, 16).astype(np.float32)
+    amax = np.abs(g).max(-1)
+    e = np.ceil(np.log2(np.maximum(amax / 6.0, 2.0 ** -9))).clip(-9, 8)
+    scale = np.exp2(e).astype(np.float32)
+    q = np.abs(g) / scale[..., None]                        # exact: division by a power of two
+    mid = (E2M1_MAGS[1:] + E2M1_MAGS[:-1]) / 2
+    mag = np.searchsorted(mid, q, side="left").astype(np.uint8)
+    c = (mag | (np.signbit(g).astype(np.uint8) << 3)).reshape(n, dch)
+    codes = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    return codes, to_e4m3_bytes(scale)
+
+
 def draw_normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(size=shape, dtype=np.float32)
 
@@ -205,7 +235,8 @@ def draw_normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
 def make_inputs(w: Workload, with_attention: bool = True) -> Dict[str, np.ndarray]:
     """All inputs of one workload as numpy arrays in the boundary's layouts.
 
-    Keys: idx_k [B][N][128] u8, idx_q [B][T][32][128] u16 (bf16 bits), head_w [B][T][32] f32,
+    Keys: idx_k [B][N][128] u8 (or, FP4 indexer K, idx_k_codes [B][N][64] u8 and
+    idx_k_scales [B][N][8] u8), idx_q [B][T][32][128] u16 (bf16 bits), head_w [B][T][32] f32,
     n_visible [B][T] i32, ri_q [Lri][B][T][32][128] u16, ri_w [Lri][B][T][32] f32,
     kv_codes [B][N][256] u8, kv_scales [B][N][32] u8, q [L][B][T][H][512] u16,
     swa [L][B][swa_rows][512] u8, swa_end [B][T] i32, and for caller pools
@@ -221,7 +252,11 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Dict[str, np.ndarra
     d["ri_q"] = to_bf16_bits(draw_normal_f32(gens["ri_q"], (w.n_reindex, B, T, IDX_HEADS, IDX_DIM)))
     d["ri_w"] = gens["ri_w"].random(size=(w.n_reindex, B, T, IDX_HEADS), dtype=np.float32)
 
-    idx_k = np.empty((B, N, IDX_DIM), np.uint8)
+    if w.idx_k_fp4:
+        idx_k = np.empty((B, N, IDX_DIM // 2), np.uint8)
+        idx_k_scales = np.empty((B, N, IDX_DIM // 16), np.uint8)
+    else:
+        idx_k = np.empty((B, N, IDX_DIM), np.uint8)
     planted_pos = None
     if w.planted:
         g = gens["planted"]
@@ -239,8 +274,14 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Dict[str, np.ndarra
                 lo, hi = max(r0, planted_pos[0]), min(r1, planted_pos[-1] + 1)
                 if lo < hi:
                     x[lo - r0:hi - r0] += delta
-            idx_k[b, r0:r1] = to_e4m3_bytes(x)
-    d["idx_k"] = idx_k
+            if w.idx_k_fp4:
+                idx_k[b, r0:r1], idx_k_scales[b, r0:r1] = to_fp4_pow2(x)
+            else:
+                idx_k[b, r0:r1] = to_e4m3_bytes(x)
+    if w.idx_k_fp4:
+        d["idx_k_codes"], d["idx_k_scales"] = idx_k, idx_k_scales
+    else:
+        d["idx_k"] = idx_k
     if planted_pos is not None:
         d["planted_pos"] = planted_pos
     d["n_visible"] = w.n_visible()
