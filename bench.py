@@ -65,21 +65,26 @@ def scan_source_hash() -> str:
     return h.hexdigest()
 
 
+def key_row_bytes(w) -> int:
+    """Bytes of one indexer-K position: 128 E4M3 bytes, or 64 E2M1 code bytes + 8 E4M3 scales."""
+    return 72 if w.idx_k_fp4 else 128
+
+
 def scan_algorithmic_bytes(w) -> int:
-    """Bytes one scan launch must move: every visible indexer-K row (128 B) of every query
-    (a prefill's queries share one context: its rows count once), plus each query's indexer
-    query and head weights."""
+    """Bytes one scan launch must move: every visible indexer-K row (128 B, or 72 B for FP4 keys)
+    of every query (a prefill's queries share one context: its rows count once), plus each query's
+    indexer query and head weights."""
     q = w.B * w.T
     if w.prefill_tokens:
         rows = w.B * int(w.n_visible().max())
     else:
         rows = int(w.n_visible().astype("int64").sum())
-    return rows * 128 + q * (IDX_Q_BYTES + IDX_W_BYTES)
+    return rows * key_row_bytes(w) + q * (IDX_Q_BYTES + IDX_W_BYTES)
 
 
 def reindex_layer_bytes(w) -> int:
     """One Reindex layer, one query: the pool's K rows, the pool, Q, w and the Top-K written."""
-    return w.pool_cap * (128 + 4) + IDX_Q_BYTES + IDX_W_BYTES + w.top_k * 4
+    return w.pool_cap * (key_row_bytes(w) + 4) + IDX_Q_BYTES + IDX_W_BYTES + w.top_k * 4
 
 
 def attention_layer_bytes(w) -> int:
@@ -312,7 +317,12 @@ def main() -> int:
 
     B, T, N, K, L, Hh, R = w.B, w.T, w.N, w.top_k, w.L, w.H, args.replicas
     Q = B * T
-    k_rep = [up(inp["idx_k"]) for _ in range(R)]
+    if w.idx_k_fp4:
+        k_rep = [up(inp["idx_k_codes"]) for _ in range(R)]
+        ks_rep = [up(inp["idx_k_scales"]) for _ in range(R)]
+    else:
+        k_rep = [up(inp["idx_k"]) for _ in range(R)]
+        ks_rep = [None] * R
     codes_rep = [up(inp["kv_codes"]) for _ in range(R)]
     scales_rep = [up(inp["kv_scales"]) for _ in range(R)]
     idx_q, head_w, n_vis = up(inp["idx_q"]), up(inp["head_w"]), up(inp["n_visible"])
@@ -341,7 +351,7 @@ def main() -> int:
     ri_sets = sets[1:] if w.has_full else sets          # Reindex outputs follow the Full layer's set
 
     def scan(r):
-        H.csa2_index_scan(k_rep[r], N, idx_q, head_w, n_vis, B, T, N, w.block, w.pool_blocks, K,
+        H.csa2_index_scan(k_rep[r], ks_rep[r], N, idx_q, head_w, n_vis, B, T, N, w.block, w.pool_blocks, K,
                           ws_full, ws_full_b)
 
     def select(r):
@@ -350,13 +360,13 @@ def main() -> int:
 
     def select_reindex(r):
         n = w.n_reindex
-        H.csa2_index_select_reindex(k_rep[r], N, n_vis, B, T, N, w.block, w.pool_blocks, K,
+        H.csa2_index_select_reindex(k_rep[r], ks_rep[r], N, n_vis, B, T, N, w.block, w.pool_blocks, K,
                                     ri_q if n else None, ri_w if n else None, n, pool_pos, pool_len,
                                     sets[0], None, ri_sets if n else None, None, ws_full, ws_full_b)
 
     def reindex(r):
         if w.n_reindex:
-            H.csa2_reindex(k_rep[r], N, ri_q, ri_w, pool_pos, pool_len, w.pool_cap, w.n_reindex, B, T, K,
+            H.csa2_reindex(k_rep[r], ks_rep[r], N, ri_q, ri_w, pool_pos, pool_len, w.pool_cap, w.n_reindex, B, T, K,
                            ri_sets, None, ws_ri, ws_ri_b)
 
     def attend(r):
@@ -476,6 +486,7 @@ def main() -> int:
                        f"caller pools of {w.user_pool}" if w.user_pool else "none"),
                    "top_k": K, "full_layer": w.has_full, "reindex_layers": w.n_reindex,
                    "attention_layers": L, "attention_heads": Hh, "indexer_heads": 32, "indexer_dim": 128,
+                   "indexer_keys": "fp4 (E2M1 + E4M3/16)" if w.idx_k_fp4 else "e4m3",
                    "swa_window": w.swa_window, "context_replicas": R,
                    "launch": "first stage direct + hipgraph" if args.graph else "direct launches",
                    "step_algorithmic_bytes": step_bytes,

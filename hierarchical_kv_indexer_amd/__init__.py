@@ -24,20 +24,20 @@ EXPORTS = (
     ("csa2_last_error", ctypes.c_char_p, ()),
     ("csa2_quantize_query", _I, (_P, _P, _I64, _P)),
     ("csa2_quantize_kv_fp4", _I, (_P, _I64, _P, _P, _P)),
-    ("csa2_index_scores", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
+    ("csa2_index_scores", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
     ("csa2_index_full_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
-    ("csa2_index_scan", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
+    ("csa2_index_scan", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
     ("csa2_index_pool", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
     ("csa2_index_topk", _I, (_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_select", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
-    ("csa2_index_full", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
+    ("csa2_index_full", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_chain_workspace", _SZ, (_I, _I, _I, _I, _I, _I, _I)),
-    ("csa2_index_chain", _I, (_P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+    ("csa2_index_chain", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                               _P, _SZ, _P)),
-    ("csa2_index_select_reindex", _I, (_P, _I64, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
+    ("csa2_index_select_reindex", _I, (_P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                                        _P, _SZ, _P)),
     ("csa2_reindex_workspace", _SZ, (_I, _I, _I, _I, _I)),
-    ("csa2_reindex", _I, (_P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
+    ("csa2_reindex", _I, (_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
     ("csa2_sparse_attn_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
     ("csa2_sparse_attn", _I, (_P, _P, _I64, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F,
                               _P, _P, _P, _SZ, _P)),
@@ -105,9 +105,9 @@ def csa2_quantize_kv_fp4(latent_bf16, rows: int, kv_codes, kv_scales, stream=Non
                                       _stream(stream, latent_bf16)))
 
 
-def csa2_index_scores(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
+def csa2_index_scores(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
                       n_max: int, scores, stream=None) -> None:
-    _check(lib().csa2_index_scores(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
+    _check(lib().csa2_index_scores(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
                                    _ptr(n_visible), B, T, n_max, _ptr(scores), _stream(stream, idx_k)))
 
 
@@ -116,19 +116,19 @@ def csa2_index_full_workspace(B: int, T: int, n_max: int, block_size: int, pool_
     return lib().csa2_index_full_workspace(B, T, n_max, block_size, pool_blocks, top_k)
 
 
-def csa2_index_full(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
+def csa2_index_full(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
                     n_max: int, block_size: int, pool_blocks: int, top_k: int, pool_pos, pool_len,
                     topk_idx, topk_score, workspace, ws_bytes: int, stream=None) -> None:
-    _check(lib().csa2_index_full(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
+    _check(lib().csa2_index_full(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
                                  _ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
                                  _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
                                  _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
 
 
-def csa2_index_scan(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
+def csa2_index_scan(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
                     n_max: int, block_size: int, pool_blocks: int, top_k: int, workspace,
                     ws_bytes: int, stream=None) -> None:
-    _check(lib().csa2_index_scan(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
+    _check(lib().csa2_index_scan(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
                                  _ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
                                  _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
 
@@ -161,22 +161,22 @@ def csa2_index_chain_workspace(B: int, T: int, n_max: int, block_size: int, pool
     return lib().csa2_index_chain_workspace(B, T, n_max, block_size, pool_blocks, top_k, L)
 
 
-def csa2_index_chain(idx_k, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int, n_max: int,
+def csa2_index_chain(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int, n_max: int,
                      block_size: int, pool_blocks: int, top_k: int, ri_q, ri_w, L: int, pool_pos, pool_len,
                      topk_idx, topk_score, ri_topk_idx, ri_topk_score, workspace, ws_bytes: int,
                      stream=None) -> None:
-    _check(lib().csa2_index_chain(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w), _ptr(n_visible),
+    _check(lib().csa2_index_chain(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q), _ptr(head_w), _ptr(n_visible),
                                   B, T, n_max, block_size, pool_blocks, top_k, _ptr(ri_q), _ptr(ri_w), L,
                                   _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
                                   _ptr(ri_topk_idx), _ptr(ri_topk_score), _ptr(workspace), ws_bytes,
                                   _stream(stream, idx_k)))
 
 
-def csa2_index_select_reindex(idx_k, k_rows_per_seq: int, n_visible, B: int, T: int, n_max: int,
+def csa2_index_select_reindex(idx_k, idx_k_scales, k_rows_per_seq: int, n_visible, B: int, T: int, n_max: int,
                               block_size: int, pool_blocks: int, top_k: int, ri_q, ri_w, L: int,
                               pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx, ri_topk_score,
                               workspace, ws_bytes: int, stream=None) -> None:
-    _check(lib().csa2_index_select_reindex(_ptr(idx_k), k_rows_per_seq, _ptr(n_visible), B, T, n_max,
+    _check(lib().csa2_index_select_reindex(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(n_visible), B, T, n_max,
                                            block_size, pool_blocks, top_k, _ptr(ri_q), _ptr(ri_w), L,
                                            _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
                                            _ptr(ri_topk_idx), _ptr(ri_topk_score), _ptr(workspace), ws_bytes,
@@ -187,10 +187,10 @@ def csa2_reindex_workspace(L: int, B: int, T: int, pool_cap: int, top_k: int) ->
     return lib().csa2_reindex_workspace(L, B, T, pool_cap, top_k)
 
 
-def csa2_reindex(idx_k, k_rows_per_seq: int, idx_q, head_w, pool_pos, pool_len, pool_cap: int,
+def csa2_reindex(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, pool_pos, pool_len, pool_cap: int,
                  L: int, B: int, T: int, top_k: int, topk_idx, topk_score, workspace,
                  ws_bytes: int, stream=None) -> None:
-    _check(lib().csa2_reindex(_ptr(idx_k), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
+    _check(lib().csa2_reindex(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
                               _ptr(pool_pos), _ptr(pool_len), pool_cap, L, B, T, top_k,
                               _ptr(topk_idx), _ptr(topk_score), _ptr(workspace), ws_bytes,
                               _stream(stream, idx_k)))

@@ -132,7 +132,8 @@ csa2_status csa2_quantize_kv_fp4(const uint16_t* latent_bf16, int64_t rows, uint
   return st == CSA2_OK ? ok() : st;
 }
 
-static csa2_status check_index_common(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
+static csa2_status check_index_common(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows,
+                                      const uint16_t* idx_q,
                                       const float* head_w, const int32_t* n_visible, int B, int T,
                                       int n_max) {
   REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1 (got %d, %d)", B, T);
@@ -142,21 +143,22 @@ static csa2_status check_index_common(const uint8_t* idx_k, int64_t k_rows, cons
   REQUIRE(k_rows >= n_max && k_rows < ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
           "need n_max <= k_rows_per_seq < 2^31 (n_max %d, k_rows %lld)", n_max, (long long)k_rows);
   REQUIRE_PTR(idx_k);
+  REQUIRE(idx_ks == nullptr || aligned16(idx_ks), CSA2_ERR_INVALID_ARG, "idx_k_scales must be 16-byte aligned");
   REQUIRE_PTR(idx_q);
   REQUIRE_PTR(head_w);
   REQUIRE_PTR(n_visible);
   return CSA2_OK;
 }
 
-csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                               const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                               float* scores, void* stream) {
-  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  csa2_status st = check_index_common(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
   if (st != CSA2_OK) return st;
   REQUIRE_PTR(scores);
   if (n_max == 0) return ok();
   const FullPlan p = plan_full(B, T, n_max, 1, 1);
-  st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+  st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                        scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg,
                                        (hipStream_t)stream),
                  "index scan launch");
@@ -191,11 +193,11 @@ static csa2_status check_workspace(const FullPlan& p, int n_max, void* workspace
   return CSA2_OK;
 }
 
-csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k, void* workspace, size_t ws_bytes,
                             void* stream) {
-  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  csa2_status st = check_index_common(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
   if (st != CSA2_OK) return st;
   if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
   const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
@@ -203,7 +205,7 @@ csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const 
   FullWs w;
   carve_full(workspace, p, n_max, &w);
   if (n_max > 0) {
-    st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+    st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg,
                                          (hipStream_t)stream),
                    "index scan launch");
@@ -308,20 +310,20 @@ csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max,
   return st == CSA2_OK ? ok() : st;
 }
 
-csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_full(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k, int32_t* pool_pos,
                             int32_t* pool_len, int32_t* topk_idx, float* topk_score, void* workspace,
                             size_t ws_bytes, void* stream) {
   // check everything (both stages) before enqueueing anything
-  csa2_status st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+  csa2_status st = check_index_common(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
   if (st != CSA2_OK) return st;
   if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
   const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
   if ((st = check_pool_args(p, pool_pos, pool_len)) != CSA2_OK) return st;
   if ((st = check_topk_args(topk_idx, topk_score)) != CSA2_OK) return st;
   if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
-  st = csa2_index_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
+  st = csa2_index_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
                        top_k, workspace, ws_bytes, stream);
   if (st != CSA2_OK) return st;
   return csa2_index_select(n_visible, B, T, n_max, block_size, pool_blocks, top_k, pool_pos, pool_len, topk_idx,
@@ -334,7 +336,7 @@ size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k) {
   return align_up((size_t)L * B * T * pool_cap * sizeof(float));
 }
 
-csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                          const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
                          int pool_cap, int L, int B, int T, int top_k, int32_t* topk_idx,
                          float* topk_score, void* workspace, size_t ws_bytes, void* stream) {
@@ -346,6 +348,8 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
   REQUIRE(top_k >= 1 && top_k <= csa2::kMaxTopK, CSA2_ERR_UNSUPPORTED, "top_k must be in [1, %d]", csa2::kMaxTopK);
   REQUIRE(top_k <= pool_cap, CSA2_ERR_INVALID_ARG, "top_k (%d) exceeds pool_cap (%d)", top_k, pool_cap);
   REQUIRE_PTR(idx_k);
+  REQUIRE(idx_k_scales == nullptr || aligned16(idx_k_scales), CSA2_ERR_INVALID_ARG,
+          "idx_k_scales must be 16-byte aligned");
   REQUIRE_PTR(idx_q);
   REQUIRE_PTR(head_w);
   REQUIRE_PTR(pool_pos);
@@ -358,7 +362,7 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
   const int Q = B * T;
   hipStream_t s = (hipStream_t)stream;
   float* ri = (float*)workspace;
-  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, k_rows_per_seq, idx_q, head_w, pool_pos, pool_len,
+  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, pool_pos, pool_len,
                                                    pool_cap, L, Q, T, ri, s),
                              "reindex score launch");
   if (st != CSA2_OK) return st;
@@ -387,7 +391,8 @@ size_t csa2_index_chain_workspace(int B, int T, int n_max, int block_size, int p
   return carve_chain(nullptr, plan_full(B, T, n_max, pool_blocks, top_k), n_max, L, nullptr, nullptr);
 }
 
-static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t* idx_k_scales,
+                               int64_t k_rows_per_seq, const uint16_t* idx_q,
                                const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                                int block_size, int pool_blocks, int top_k, const uint16_t* ri_q,
                                const float* ri_w, int L, int32_t* pool_pos, int32_t* pool_len,
@@ -395,12 +400,14 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, int64_t k_row
                                float* ri_topk_score, void* workspace, size_t ws_bytes, void* stream) {
   csa2_status st;
   if (do_scan) {
-    st = check_index_common(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
+    st = check_index_common(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
     if (st != CSA2_OK) return st;
   } else {
     REQUIRE(k_rows_per_seq >= n_max && k_rows_per_seq < ((int64_t)1 << 31), CSA2_ERR_INVALID_ARG,
             "need n_max <= k_rows_per_seq < 2^31");
     REQUIRE_PTR(idx_k);
+    REQUIRE(idx_k_scales == nullptr || aligned16(idx_k_scales), CSA2_ERR_INVALID_ARG,
+            "idx_k_scales must be 16-byte aligned");
     REQUIRE_PTR(n_visible);
   }
   if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
@@ -422,7 +429,7 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, int64_t k_row
   carve_chain(workspace, p, n_max, L, &w, &ri);
   hipStream_t s = (hipStream_t)stream;
   if (do_scan && n_max > 0) {
-    st = hip_check(csa2::launch_idx_scan(idx_k, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
+    st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, s),
                    "index scan launch");
     if (st != CSA2_OK) return st;
@@ -431,7 +438,7 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, int64_t k_row
   if (st != CSA2_OK) return st;
   csa2::TopkJob rj{};
   if (L > 0) {
-    st = hip_check(csa2::launch_ri_score(idx_k, k_rows_per_seq, ri_q, ri_w, pool_pos, pool_len, p.cap, L, p.Q, T,
+    st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, ri_q, ri_w, pool_pos, pool_len, p.cap, L, p.Q, T,
                                          ri, s),
                    "reindex score launch");
     if (st != CSA2_OK) return st;
@@ -450,24 +457,24 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, int64_t k_row
   return st == CSA2_OK ? ok() : st;
 }
 
-csa2_status csa2_index_chain(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_chain(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                              const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                              int block_size, int pool_blocks, int top_k, const uint16_t* ri_q, const float* ri_w,
                              int L, int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
                              int32_t* ri_topk_idx, float* ri_topk_score, void* workspace, size_t ws_bytes,
                              void* stream) {
-  return index_chain(true, idx_k, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
+  return index_chain(true, idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
                      top_k, ri_q, ri_w, L, pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx, ri_topk_score,
                      workspace, ws_bytes, stream);
 }
 
-csa2_status csa2_index_select_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const int32_t* n_visible,
+csa2_status csa2_index_select_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const int32_t* n_visible,
                                       int B, int T, int n_max, int block_size, int pool_blocks, int top_k,
                                       const uint16_t* ri_q, const float* ri_w, int L, int32_t* pool_pos,
                                       int32_t* pool_len, int32_t* topk_idx, float* topk_score,
                                       int32_t* ri_topk_idx, float* ri_topk_score, void* workspace,
                                       size_t ws_bytes, void* stream) {
-  return index_chain(false, idx_k, k_rows_per_seq, nullptr, nullptr, n_visible, B, T, n_max, block_size,
+  return index_chain(false, idx_k, idx_k_scales, k_rows_per_seq, nullptr, nullptr, n_visible, B, T, n_max, block_size,
                      pool_blocks, top_k, ri_q, ri_w, L, pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx,
                      ri_topk_score, workspace, ws_bytes, stream);
 }

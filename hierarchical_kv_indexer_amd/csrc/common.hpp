@@ -55,7 +55,7 @@ template <int SEL>
 __device__ __forceinline__ uint32_t e2m1x2_scaled_to_bf16x2(uint32_t w, float scale) {
   f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
   const uint32_t a = __float_as_uint(v.x * scale), b = __float_as_uint(v.y * scale);
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);          // upper halves of a (low) and b (high)
 }
 
 // E4M3 byte -> float, exact (software decode; used for scales and the query path).

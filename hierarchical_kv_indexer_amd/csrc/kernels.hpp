@@ -18,11 +18,13 @@ hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hi
 int scan_chunk_positions(int n_max, int queries);
 constexpr int kScanUnitsPerWg = kFullThreads / 64;   // 16 units of chunk/16 positions per chunk
 constexpr int kMaxFullPositions = 1 << 21;           // 256 chunks of 8192 per query: 4096 units
-hipError_t launch_idx_scan(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
+// Indexer keys: idx_ks == null: E4M3 idx_k [rows][128]; otherwise FP4 codes idx_k [rows][64] and
+// E4M3 scales idx_ks [rows][8] (one per 16 channels).
+hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
                            uint64_t* cuts, int chunk, int n_wg, hipStream_t s);
-hipError_t launch_ri_score(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
+hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
                            int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s);
 

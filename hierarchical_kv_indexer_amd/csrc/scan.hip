@@ -15,6 +15,13 @@
 // 16-byte load instruction of the wave covers 16 whole 64-byte half rows.  The channel
 // order inside an MFMA does not matter as long as the query operands use the same order,
 // which they do (both are read with the same byte offsets).
+//
+// FP4 indexer K (the variant the V4 indexer used; blog.4sapi.com sec.4): a position's key is 64
+// bytes of E2M1 codes (channel 2i in the low nibble of byte i) and 8 E4M3 scales, one per 16
+// channels, stored as two arrays.  code x scale is exact in fp16, and so is the E4M3 query, so
+// that contraction runs on the fp16 MFMA, again with exact products.  Lane (j, g) then takes channels [32g, 32g+32) of row j: its 16
+// code bytes and the row's 8 scale bytes (two of which it uses), and MFMA chunk c covers its
+// channels 32g + 8c .. +7 on both operands.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,7 +44,8 @@ hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hi
 
 // The 32x128 query of one indexer head set, rounded to E4M3 and held as bf16 in LDS.
 // NT threads, 4096/NT consecutive values each, loaded with 16-byte (or 8-byte) loads.
-template <int NT>
+// kF16: the values are held as fp16 instead of bf16 (exact either way: E4M3 fits both).
+template <int NT, bool kF16 = false>
 __device__ __forceinline__ void stage_query(const uint16_t* __restrict__ q, uint16_t* qlds) {
   constexpr int kPer = kIdxHeads * kIdxDim / NT;      // values per thread (16 or 4)
   static_assert(kPer == 16 || kPer == 4, "query staging assumes 256 or 1024 threads");
@@ -56,7 +64,11 @@ __device__ __forceinline__ void stage_query(const uint16_t* __restrict__ q, uint
   for (int i = 0; i < kPer / 2; ++i) {
     const float lo = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(w[i] & 0xffffu)));
     const float hi = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(w[i] >> 16)));
-    o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    if constexpr (kF16)
+      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    else
+      o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
   }
   if constexpr (kPer == 16) {
     *(u32x4*)(qlds + base) = u32x4{o[0], o[1], o[2], o[3]};
@@ -123,9 +135,92 @@ __device__ __forceinline__ void load_row(const uint8_t* __restrict__ row, int g,
   hi = *(const u32x4*)(row + 64 + 16 * g);
 }
 
+// The raw bytes of one tile row as one lane holds them: E4M3 keys, the lane's two 16-byte pieces;
+// FP4 keys, its 16 code bytes and the two scale bytes of its channels (groups 2g and 2g+1).
+template <bool kFp4> struct TileRaw;
+template <> struct TileRaw<false> { u32x4 lo, hi; };
+template <> struct TileRaw<true> { u32x4 codes; uint32_t sc; };
+
+__device__ __forceinline__ void load_row_fp4(const uint8_t* __restrict__ codes_row,
+                                             const uint8_t* __restrict__ scales_row, int g, TileRaw<true>& r) {
+  r.codes = *(const u32x4*)(codes_row + 16 * g);
+  r.sc = *(const uint16_t*)(scales_row + 2 * g);
+}
+
+// Query operands in the FP4 channel order (chunk c of lane group g: channels 32g + 8c .. +7).
+__device__ __forceinline__ void load_ctx_fp4(TileCtx& cx, const uint16_t* qlds, const float* __restrict__ w) {
+  const int lane = threadIdx.x & 63, j = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      cx.qa[hh][c] = *(const u32x4*)(qlds + (16 * hh + j) * kIdxDim + 32 * g + 8 * c);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    cx.w[v] = w[4 * g + v];
+    cx.w[4 + v] = w[16 + 4 * g + v];
+  }
+}
+
+// Score of this lane's row from FP4 keys (same head sum as tile_score).  The keys are decoded
+// to fp16 (E2M1 by the hardware conversion, times the E4M3 scale in packed fp16: every product
+// has at most 6 significant bits within [2^-10, 2688], so it is exact) and the query operands
+// are fp16 too, so the contraction runs on the fp16 MFMA with exact products.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_scaled_to_f16x2(uint32_t w, h2 s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL) * s);
+}
+__device__ __forceinline__ float tile_score_fp4(const TileCtx& cx, const TileRaw<true>& r) {
+  const h2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, false);   // groups 2g, 2g+1 (exact)
+  u32x4 b[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const h2 s = c < 2 ? h2{sc.x, sc.x} : h2{sc.y, sc.y};
+    b[c] = u32x4{e2m1x2_scaled_to_f16x2<0>(r.codes[c], s), e2m1x2_scaled_to_f16x2<1>(r.codes[c], s),
+                 e2m1x2_scaled_to_f16x2<2>(r.codes[c], s), e2m1x2_scaled_to_f16x2<3>(r.codes[c], s)};
+  }
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    a0 = mfma16x16x32_f16(cx.qa[0][c], b[c], a0);
+    a1 = mfma16x16x32_f16(cx.qa[1][c], b[c], a1);
+  }
+  float p = 0.f;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) p = fmaf(cx.w[v], relu_bits(a0[v]), p);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) p = fmaf(cx.w[4 + v], relu_bits(a1[v]), p);
+  return sum_xor32(sum_xor16(p));
+}
+
+// One tile row of either key format.
+template <bool kFp4>
+__device__ __forceinline__ void load_key(const uint8_t* __restrict__ kseq, const uint8_t* __restrict__ sseq,
+                                         int64_t p, int g, TileRaw<kFp4>& r) {
+  if constexpr (kFp4) load_row_fp4(kseq + p * (kIdxDim / 2), sseq + p * (kIdxDim / 16), g, r);
+  else load_row(kseq + p * kIdxDim, g, r.lo, r.hi);
+}
+template <bool kFp4>
+__device__ __forceinline__ float key_score(const TileCtx& cx, const TileRaw<kFp4>& r) {
+  if constexpr (kFp4) return tile_score_fp4(cx, r);
+  else return tile_score(cx, r.lo, r.hi);
+}
+template <bool kFp4>
+__device__ __forceinline__ void key_ctx(TileCtx& cx, const uint16_t* qlds, const float* __restrict__ w) {
+  if constexpr (kFp4) load_ctx_fp4(cx, qlds, w);
+  else load_ctx(cx, qlds, w);
+}
+
 // ---------------------------------------------------------------------------- Full scan
 
-constexpr int kScanU = 3;                       // tiles per pipeline stage of a wave
+// Tiles per pipeline stage of a wave (6 FP4 tiles measured no faster than 3: the loop is bound by
+// its instruction issue, not by the bytes in flight).
+template <bool kFp4> constexpr int kScanU = 3;
 constexpr int kFullWaves = kFullThreads / 64;   // 16
 static_assert(kFullWaves == kScanUnitsPerWg, "one unit per wave in the epilogue");
 
@@ -156,8 +251,10 @@ __device__ __forceinline__ uint64_t wave_pop_best(uint32_t& key, uint32_t& blk) 
 // (score key << 32 | ~block): lists[q][unit][0..3] = the four best (0 = none) and
 // cuts[q][unit] = the fifth best (0 = none), so every block of the unit that is not listed
 // ranks at or below cuts[q][unit].  Requires chunk % 1024 == 0 and chunk <= 8192.
+template <bool kFp4>
 __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
-    const uint8_t* __restrict__ idx_k, int64_t k_rows, const uint16_t* __restrict__ idx_q,
+    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
+    const uint16_t* __restrict__ idx_q,
     const float* __restrict__ head_w, const int32_t* __restrict__ n_visible, int T, int n_max,
     int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
     uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
@@ -175,7 +272,8 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   const int p_end = min(p_begin + chunk, nv);
   const int npos = max(0, p_end - p_begin);
   const int ntiles = (npos + 15) >> 4;
-  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * kIdxDim;
+  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
+  const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
   const int plast = npos > 0 ? p_end - 1 : 0;
   // Workgroups start at different tiles of their chunk and wrap around, so workgroups that
   // stream in lockstep touch different address offsets at a time.
@@ -184,34 +282,35 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
 
   // Rows of tiles past the chunk are clamped to its last row, so every stage loads and
   // computes unconditionally; results of such tiles are never stored.
-  u32x4 loA[kScanU], hiA[kScanU], loB[kScanU], hiB[kScanU];
-  auto load_stage = [&](u32x4(&lo)[kScanU], u32x4(&hi)[kScanU], int t0) {
+  constexpr int kU = kScanU<kFp4>;
+  TileRaw<kFp4> rA[kU], rB[kU];
+  auto load_stage = [&](TileRaw<kFp4>(&r)[kU], int t0) {
 #pragma unroll
-    for (int u = 0; u < kScanU; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int t = t0 + u;
       const int p = min(p_begin + 16 * (t < ntiles ? phys(t) : t) + j, plast);
-      load_row(kseq + (size_t)p * kIdxDim, g, lo[u], hi[u]);
+      load_key<kFp4>(kseq, sseq, p, g, r[u]);
     }
   };
-  int tA = wave * kScanU;                          // first stage of each wave: static
-  if (tA < ntiles) load_stage(loA, hiA, tA);       // in flight during the query prep
+  int tA = wave * kU;                              // first stage of each wave: static
+  if (tA < ntiles) load_stage(rA, tA);             // in flight during the query prep
 
   if (ntiles > 0) {
-    stage_query<kFullThreads>(idx_q + (size_t)q * kIdxHeads * kIdxDim, qlds);
-    if (threadIdx.x == 0) *ctr = kFullWaves * kScanU;
+    stage_query<kFullThreads, kFp4>(idx_q + (size_t)q * kIdxHeads * kIdxDim, qlds);
+    if (threadIdx.x == 0) *ctr = kFullWaves * kU;
     __syncthreads();
     TileCtx cx;
-    load_ctx(cx, qlds, head_w + (size_t)q * kIdxHeads);
+    key_ctx<kFp4>(cx, qlds, head_w + (size_t)q * kIdxHeads);
     auto grab = [&]() {                            // next stage of this wave (monotonic)
       int v = 0;
-      if (lane == 0) v = atomicAdd(ctr, kScanU);
+      if (lane == 0) v = atomicAdd(ctr, kU);
       return __builtin_amdgcn_readfirstlane(v);
     };
-    auto compute_stage = [&](const u32x4(&lo)[kScanU], const u32x4(&hi)[kScanU], int t0) {
+    auto compute_stage = [&](const TileRaw<kFp4>(&r)[kU], int t0) {
 #pragma unroll
-      for (int u = 0; u < kScanU; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int t = t0 + u;
-        const float sc = tile_score(cx, lo[u], hi[u]);
+        const float sc = key_score<kFp4>(cx, r[u]);
         if (t < ntiles) {
           const int tp = phys(t);
           const bool valid = 16 * tp + j < npos;
@@ -223,12 +322,12 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     };
     int tB = grab();
     while (tA < ntiles) {
-      load_stage(loB, hiB, tB);
-      compute_stage(loA, hiA, tA);
+      load_stage(rB, tB);
+      compute_stage(rA, tA);
       tA = grab();
       if (tB >= ntiles) break;                     // later grabs only go further
-      load_stage(loA, hiA, tA);
-      compute_stage(loB, hiB, tB);
+      load_stage(rA, tA);
+      compute_stage(rB, tB);
       tB = grab();
     }
   }
@@ -273,12 +372,18 @@ int scan_chunk_positions(int n_max, int queries) {
   return (int)c;
 }
 
-hipError_t launch_idx_scan(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
+hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
                            uint64_t* cuts, int chunk, int n_wg, hipStream_t s) {
-  hipLaunchKernelGGL(k_idx_scan, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k, k_rows,
-                     idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
+  if (idx_ks)
+    hipLaunchKernelGGL(k_idx_scan<true>, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
+                       idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
+                       cuts);
+  else
+    hipLaunchKernelGGL(k_idx_scan<false>, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
+                       idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
+                       cuts);
   return hipGetLastError();
 }
 
@@ -289,8 +394,10 @@ constexpr int kRiTilesPerWave = 2;
 // grid (n_chunks, L*Q).  Item it = l*Q + q scores pool slots [x*chunk, (x+1)*chunk) of query
 // q (chunk = 64 * kRiTilesPerWave) with layer l's query and weights.  Slots beyond pool_len or
 // holding positions outside [0, k_rows) are not written.
+template <bool kFp4>
 __global__ __launch_bounds__(kScanThreads) void k_ri_score(
-    const uint8_t* __restrict__ idx_k, int64_t k_rows, const uint16_t* __restrict__ idx_q,
+    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
+    const uint16_t* __restrict__ idx_q,
     const float* __restrict__ head_w, const int32_t* __restrict__ pool_pos,
     const int32_t* __restrict__ pool_len, int cap, int Q, int T, float* __restrict__ ri_scores) {
   __shared__ __attribute__((aligned(16))) uint16_t qlds[kIdxHeads * kIdxDim];
@@ -312,21 +419,22 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
     const int slot = sw + 16 * u + j;
     pos[u] = slot < s_end ? pp[slot] : -1;
   }
-  stage_query<kScanThreads>(idx_q + (size_t)it * kIdxHeads * kIdxDim, qlds);
-  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * kIdxDim;
-  u32x4 lo[kRiTilesPerWave], hi[kRiTilesPerWave];
+  stage_query<kScanThreads, kFp4>(idx_q + (size_t)it * kIdxHeads * kIdxDim, qlds);
+  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
+  const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
+  TileRaw<kFp4> raw[kRiTilesPerWave];
   bool ok[kRiTilesPerWave];
 #pragma unroll
   for (int u = 0; u < kRiTilesPerWave; ++u) {
     ok[u] = pos[u] >= 0 && (int64_t)pos[u] < k_rows;
-    load_row(kseq + (size_t)(ok[u] ? pos[u] : 0) * kIdxDim, g, lo[u], hi[u]);
+    load_key<kFp4>(kseq, sseq, ok[u] ? pos[u] : 0, g, raw[u]);
   }
   __syncthreads();
   TileCtx cx;
-  load_ctx(cx, qlds, head_w + (size_t)it * kIdxHeads);
+  key_ctx<kFp4>(cx, qlds, head_w + (size_t)it * kIdxHeads);
 #pragma unroll
   for (int u = 0; u < kRiTilesPerWave; ++u) {
-    const float sc = tile_score(cx, lo[u], hi[u]);
+    const float sc = key_score<kFp4>(cx, raw[u]);
     if (g == 0) sbuf[wave][16 * u + j] = sc;
   }
   float* out = ri_scores + (size_t)it * cap;
@@ -337,13 +445,17 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
   }
 }
 
-hipError_t launch_ri_score(const uint8_t* idx_k, int64_t k_rows, const uint16_t* idx_q,
+hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
                            int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s) {
   const int chunk = 64 * kRiTilesPerWave;
   const int n_chunks = (pool_cap + chunk - 1) / chunk;
-  hipLaunchKernelGGL(k_ri_score, dim3(n_chunks, L * Q), dim3(kScanThreads), 0, s, idx_k, k_rows,
-                     idx_q, head_w, pool_pos, pool_len, pool_cap, Q, T, ri_scores);
+  if (idx_ks)
+    hipLaunchKernelGGL(k_ri_score<true>, dim3(n_chunks, L * Q), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
+                       idx_q, head_w, pool_pos, pool_len, pool_cap, Q, T, ri_scores);
+  else
+    hipLaunchKernelGGL(k_ri_score<false>, dim3(n_chunks, L * Q), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
+                       idx_q, head_w, pool_pos, pool_len, pool_cap, Q, T, ri_scores);
   return hipGetLastError();
 }
 

@@ -25,6 +25,13 @@
  *   - attention: one softmax over the selected main-KV rows and the window's SWA rows,
  *     keys = values (a shared 512-wide latent), no sink, no bias.
  *
+ * Indexer keys, in every call that reads them (idx_k, idx_k_scales):
+ *   - idx_k_scales == NULL: idx_k is [B][k_rows_per_seq][128] E4M3 bytes;
+ *   - otherwise the FP4 variant (blog.4sapi.com sec.4: the V4 indexer used FP4 keys): idx_k is
+ *     [B][k_rows_per_seq][64] E2M1 code bytes (channel 2i in the low nibble of byte i) and
+ *     idx_k_scales [B][k_rows_per_seq][8] E4M3 scales, scale g covering channels 16g..16g+15;
+ *     a key is code x scale (exact), 72 bytes per position instead of 128.
+ *
  * Conventions for every call:
  *   - tensor arguments are DEVICE pointers owned by the caller (except where marked host),
  *     row-major and contiguous; they must be 16-byte aligned;
@@ -86,13 +93,13 @@ csa2_status csa2_quantize_kv_fp4(const uint16_t* latent_bf16, int64_t rows, uint
                                  void* stream);
 
 /* Query preparation and the Full scan on their own: every visible position's score, no selection.
- *   idx_k      [B][k_rows_per_seq][128] E4M3 indexer keys
+ *   idx_k, idx_k_scales  indexer keys, E4M3 or FP4 (see above)
  *   idx_q      [B][T][32][128] bf16 indexer queries
  *   head_w     [B][T][32] float head weights
  *   n_visible  [B][T] int32 visible positions of each query (clamped to [0, n_max])
  *   scores     [B][T][n_max] float out; entries at or beyond n_visible are left untouched
  * Requires n_max <= k_rows_per_seq. */
-csa2_status csa2_index_scores(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                               const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                               float* scores, void* stream);
 
@@ -124,7 +131,7 @@ size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int po
  *   csa2_index_topk:   the Top-K over the pool (reads the workspace and the pool)
  *   csa2_index_select: the pool and its Top-K in one pass (same results as csa2_index_pool
  *                      followed by csa2_index_topk) */
-csa2_status csa2_index_scan(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k,
                             void* workspace, size_t ws_bytes, void* stream);
@@ -141,7 +148,7 @@ csa2_status csa2_index_select(const int32_t* n_visible, int B, int T, int n_max,
                               int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
                               void* workspace, size_t ws_bytes, void* stream);
 
-csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_full(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k,
                             int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
@@ -157,7 +164,7 @@ csa2_status csa2_index_full(const uint8_t* idx_k, int64_t k_rows_per_seq, const 
  *   topk_idx   [L][B][T][top_k] int32 out; topk_score [L][B][T][top_k] float out or NULL
  * Supported: 1 <= top_k <= 2048, top_k <= pool_cap <= 16384. */
 size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k);
-csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                          const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
                          int pool_cap, int L, int B, int T, int top_k,
                          int32_t* topk_idx, float* topk_score,
@@ -179,13 +186,13 @@ csa2_status csa2_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const uin
  * on the same workspace (it reads the scan's results from there).
  * Supported: as csa2_index_full with pool_blocks >= 1, L >= 0 and (L+1)*B*T <= 65535. */
 size_t csa2_index_chain_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k, int L);
-csa2_status csa2_index_chain(const uint8_t* idx_k, int64_t k_rows_per_seq, const uint16_t* idx_q,
+csa2_status csa2_index_chain(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
                              const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                              int block_size, int pool_blocks, int top_k, const uint16_t* ri_q, const float* ri_w,
                              int L, int32_t* pool_pos, int32_t* pool_len, int32_t* topk_idx, float* topk_score,
                              int32_t* ri_topk_idx, float* ri_topk_score, void* workspace, size_t ws_bytes,
                              void* stream);
-csa2_status csa2_index_select_reindex(const uint8_t* idx_k, int64_t k_rows_per_seq, const int32_t* n_visible,
+csa2_status csa2_index_select_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const int32_t* n_visible,
                                       int B, int T, int n_max, int block_size, int pool_blocks, int top_k,
                                       const uint16_t* ri_q, const float* ri_w, int L, int32_t* pool_pos,
                                       int32_t* pool_len, int32_t* topk_idx, float* topk_score,

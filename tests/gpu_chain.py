@@ -49,10 +49,17 @@ def empty(shape, dtype) -> torch.Tensor:
 
 # ------------------------------------------------------------------ library calls
 
+def keys(inp):
+    """Indexer keys on the device as the C ABI takes them: (idx_k, idx_k_scales or None, rows)."""
+    if "idx_k" in inp:
+        return dev(inp["idx_k"]), None, inp["idx_k"].shape[1]
+    return dev(inp["idx_k_codes"]), dev(inp["idx_k_scales"]), inp["idx_k_codes"].shape[1]
+
+
 def gpu_index_scores(inp, B, T, n_max):
     out = torch.full((B, T, max(n_max, 1)), float("nan"), dtype=torch.float32, device=DEV)
-    k = dev(inp["idx_k"])
-    H.csa2_index_scores(k, inp["idx_k"].shape[1], dev(inp["idx_q"]), dev(inp["head_w"]),
+    k, ks, rows = keys(inp)
+    H.csa2_index_scores(k, ks, rows, dev(inp["idx_q"]), dev(inp["head_w"]),
                         dev(inp["n_visible"]), B, T, n_max, out)
     return host(out)
 
@@ -65,7 +72,8 @@ def gpu_index_full(inp, B, T, n_max, pool_blocks, top_k, block=8):
     sc = empty((B, T, top_k), torch.float32)
     ws_bytes = H.csa2_index_full_workspace(B, T, n_max, block, pool_blocks, top_k)
     ws = empty((ws_bytes,), torch.uint8)
-    H.csa2_index_full(dev(inp["idx_k"]), inp["idx_k"].shape[1], dev(inp["idx_q"]), dev(inp["head_w"]),
+    k, ks, rows = keys(inp)
+    H.csa2_index_full(k, ks, rows, dev(inp["idx_q"]), dev(inp["head_w"]),
                       dev(inp["n_visible"]), B, T, n_max, block, pool_blocks, top_k, pool_pos,
                       pool_len, idx, sc, ws, ws_bytes)
     out = {"topk": host(idx), "topk_score": host(sc)}
@@ -81,7 +89,8 @@ def gpu_reindex(inp, B, T, pool_pos, pool_len, top_k, L=None):
     sc = empty((L, B, T, top_k), torch.float32)
     ws_bytes = H.csa2_reindex_workspace(L, B, T, cap, top_k)
     ws = empty((ws_bytes,), torch.uint8)
-    H.csa2_reindex(dev(inp["idx_k"]), inp["idx_k"].shape[1], dev(inp["ri_q"][:L]), dev(inp["ri_w"][:L]),
+    k, ks, rows = keys(inp)
+    H.csa2_reindex(k, ks, rows, dev(inp["ri_q"][:L]), dev(inp["ri_w"][:L]),
                    dev(pool_pos), dev(pool_len), cap, L, B, T, top_k, idx, sc, ws, ws_bytes)
     return {"topk": host(idx), "topk_score": host(sc)}
 
@@ -95,16 +104,16 @@ def gpu_index_chain(inp, B, T, n_max, pool_blocks, top_k, L, split=False, block=
     ri_sc = empty((max(L, 1), B, T, top_k), torch.float32)
     ws_bytes = H.csa2_index_chain_workspace(B, T, n_max, block, pool_blocks, top_k, L)
     ws = empty((ws_bytes,), torch.uint8)
-    k, q, hw, nv = dev(inp["idx_k"]), dev(inp["idx_q"]), dev(inp["head_w"]), dev(inp["n_visible"])
+    k, ks, rows = keys(inp)
+    q, hw, nv = dev(inp["idx_q"]), dev(inp["head_w"]), dev(inp["n_visible"])
     rq = dev(inp["ri_q"][:L]) if L else None
     rw = dev(inp["ri_w"][:L]) if L else None
-    rows = inp["idx_k"].shape[1]
     if split:
-        H.csa2_index_scan(k, rows, q, hw, nv, B, T, n_max, block, pool_blocks, top_k, ws, ws_bytes)
-        H.csa2_index_select_reindex(k, rows, nv, B, T, n_max, block, pool_blocks, top_k, rq, rw, L, pool_pos,
+        H.csa2_index_scan(k, ks, rows, q, hw, nv, B, T, n_max, block, pool_blocks, top_k, ws, ws_bytes)
+        H.csa2_index_select_reindex(k, ks, rows, nv, B, T, n_max, block, pool_blocks, top_k, rq, rw, L, pool_pos,
                                     pool_len, idx, sc, ri_idx if L else None, ri_sc if L else None, ws, ws_bytes)
     else:
-        H.csa2_index_chain(k, rows, q, hw, nv, B, T, n_max, block, pool_blocks, top_k, rq, rw, L, pool_pos,
+        H.csa2_index_chain(k, ks, rows, q, hw, nv, B, T, n_max, block, pool_blocks, top_k, rq, rw, L, pool_pos,
                            pool_len, idx, sc, ri_idx if L else None, ri_sc if L else None, ws, ws_bytes)
     out = {"topk": host(idx), "topk_score": host(sc), "pool_pos": host(pool_pos), "pool_len": host(pool_len)}
     if L:
@@ -129,10 +138,17 @@ def gpu_attention(inp, w, idx_sets: np.ndarray, layers: Optional[Sequence[int]] 
 
 # ------------------------------------------------------------------ comparisons
 
-def score_abs_bound(k8_rows: np.ndarray, q_bf16: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """A = sum_h |w_h| sum_c |q8_hc| |k_pc| for each row."""
+def host_keys(inp, b):
+    """Indexer keys of sequence b as the oracle takes them (E4M3 bytes or the FP4 pair)."""
+    if "idx_k" in inp:
+        return inp["idx_k"][b]
+    return (inp["idx_k_codes"][b], inp["idx_k_scales"][b])
+
+
+def score_abs_bound(k8_rows, q_bf16: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """A = sum_h |w_h| sum_c |q8_hc| |k_pc| for each row (keys in either storage form)."""
     qa = np.abs(F.e4m3_value(O.quantize_query(q_bf16)))
-    ka = np.abs(F.e4m3_value(k8_rows))
+    ka = np.abs(O.k_values(k8_rows))
     return ka @ qa.T @ np.abs(w.astype(np.float64))
 
 

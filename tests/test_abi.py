@@ -52,16 +52,17 @@ def expect(H, status, fn, *args):
 
 
 def test_index_full_rejects(H):
-    ok = [FAKE, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30]
+    ok = [FAKE, None, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30]
     def call(**ch):
         a = list(ok)
-        names = ["idx_k", "k_rows", "idx_q", "head_w", "nvis", "B", "T", "n_max", "block", "P", "K",
+        names = ["idx_k", "idx_ks", "k_rows", "idx_q", "head_w", "nvis", "B", "T", "n_max", "block", "P", "K",
                  "pool_pos", "pool_len", "topk_idx", "topk_score", "ws", "ws_bytes"]
         for k, v in ch.items():
             a[names.index(k)] = v
         return lambda: H.csa2_index_full(*a)
     expect(H, 1, call(idx_k=None))
     expect(H, 1, call(idx_q=FAKE + 4))                 # misaligned
+    expect(H, 1, call(idx_ks=FAKE + 8))                # misaligned FP4 key scales
     expect(H, 2, call(block=16))
     expect(H, 1, call(K=600))                          # top_k > pool capacity
     expect(H, 2, call(K=4096))
@@ -73,9 +74,9 @@ def test_index_full_rejects(H):
 
 
 def test_reindex_and_attention_reject(H):
-    expect(H, 1, lambda: H.csa2_reindex(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 512, 1, 1, 1, 1024, FAKE, None, FAKE, 1 << 30))
-    expect(H, 2, lambda: H.csa2_reindex(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 20000, 1, 1, 1, 512, FAKE, None, FAKE, 1 << 30))
-    expect(H, 3, lambda: H.csa2_reindex(FAKE, 100, FAKE, FAKE, FAKE, FAKE, 1024, 1, 1, 1, 512, FAKE, None, FAKE, 8))
+    expect(H, 1, lambda: H.csa2_reindex(FAKE, None, 100, FAKE, FAKE, FAKE, FAKE, 512, 1, 1, 1, 1024, FAKE, None, FAKE, 1 << 30))
+    expect(H, 2, lambda: H.csa2_reindex(FAKE, None, 100, FAKE, FAKE, FAKE, FAKE, 20000, 1, 1, 1, 512, FAKE, None, FAKE, 1 << 30))
+    expect(H, 3, lambda: H.csa2_reindex(FAKE, None, 100, FAKE, FAKE, FAKE, FAKE, 1024, 1, 1, 1, 512, FAKE, None, FAKE, 8))
     base = [FAKE, FAKE, 100, FAKE, FAKE, [0, 0], 1, FAKE, 128, FAKE, 128, 2, 1, 1, 16, 512, 0.04, FAKE, None, None, 0]
     a = list(base); a[14] = 24                                       # H not a multiple of 16
     expect(H, 2, lambda: H.csa2_sparse_attn(*a))
@@ -106,7 +107,7 @@ def test_chain_entries_reject(H):
 
     def chain(pool_blocks=64, L=2, ri_q=FAKE, ws_bytes=ws, **kw):
         a = dict(ok, **kw)
-        H.csa2_index_chain(FAKE, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, pool_blocks, 64, ri_q, FAKE, L,
+        H.csa2_index_chain(FAKE, None, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, pool_blocks, 64, ri_q, FAKE, L,
                            a["pool_pos"], a["pool_len"], a["topk_idx"], a["topk_score"], a["ri_topk_idx"],
                            a["ri_topk_score"], FAKE, ws_bytes)
 
@@ -117,9 +118,9 @@ def test_chain_entries_reject(H):
     expect(H, 2, lambda: chain(L=70000))
     expect(H, 3, lambda: chain(ws_bytes=ws - 256))
     # without the scan: the Full query is not needed, the keys and the pool still are
-    expect(H, 1, lambda: H.csa2_index_select_reindex(None, 4096, FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, 2, FAKE,
+    expect(H, 1, lambda: H.csa2_index_select_reindex(None, None, 4096, FAKE, 1, 1, 4096, 8, 64, 64, FAKE, FAKE, 2, FAKE,
                                                      FAKE, FAKE, None, FAKE, None, FAKE, ws))
-    expect(H, 3, lambda: H.csa2_index_select_reindex(FAKE, 4096, FAKE, 1, 1, 4096, 8, 64, 64, None, None, 0, FAKE,
+    expect(H, 3, lambda: H.csa2_index_select_reindex(FAKE, None, 4096, FAKE, 1, 1, 4096, 8, 64, 64, None, None, 0, FAKE,
                                                      FAKE, FAKE, None, None, None, FAKE, 64))
 
 

@@ -3,6 +3,7 @@ chain entries where there is a pool): the whole chain runs for every query of th
 oracle checks sampled queries.
 
   decode_1m        batch 1, 1M-entry context, Full + 4 Reindex + 15 Reuse (20 attention layers)
+  decode_1m_fp4k   the same with FP4 indexer keys
   decode_b8_128k   batch 8, 128K entries each, Full + 4 Reindex + 5 Reuse, 64 heads
   reindex_pool_256k  64 queries with their own 16384-position pools over a 256K context
   prefill_4k_64k   4096 causal queries over 32768 entries, Full + 5 Reuse, 64 heads
@@ -38,6 +39,16 @@ def test_decode_1m_whole_chain():
     assert np.isin(inp["planted_pos"], g["topk"][0, 0]).all(), "planted cluster not recalled"
     c = G.gpu_index_chain(inp, 1, 1, w.N, w.pool_blocks, w.top_k, w.n_reindex, split=True)
     assert np.array_equal(c["topk"], g["topk"]) and np.array_equal(c["pool_pos"], g["pool_pos"])
+
+
+def test_decode_1m_fp4_keys_whole_chain():
+    """The 1M decode with the FP4 indexer-K variant (72 B per position)."""
+    w = workloads.WORKLOADS["decode_1m_fp4k"]
+    inp = workloads.make_inputs(w)
+    _announce(w.name, [(0, 0)])
+    run_chain_and_check(w, inp, [(0, 0)])
+    g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
+    assert np.isin(inp["planted_pos"], g["topk"][0, 0]).all(), "planted cluster not recalled"
 
 
 def test_decode_b8_128k_sampled():

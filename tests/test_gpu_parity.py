@@ -58,6 +58,36 @@ def test_scan_every_e4m3_code_exact():
     assert np.array_equal(s[0, 1], np.maximum(-v, 0).astype(np.float32))
 
 
+def test_scan_every_fp4_key_code_and_scale_exact():
+    """FP4 keys: row r holds code r % 16 in channel c(r) with scale byte r // 16 in that channel's
+    group (every code x every finite positive scale, channels spread over all lanes and groups);
+    queries +1 / -1 on that channel give ReLU(+-code x scale) exactly."""
+    sc_bytes = np.arange(1, 127, dtype=np.uint8)                 # every finite positive E4M3 scale
+    n = 16 * len(sc_bytes)
+    codes = np.zeros((1, n, 64), np.uint8)
+    scales = np.zeros((1, n, 8), np.uint8)
+    r = np.arange(n)
+    code, sb = (r % 16).astype(np.uint8), sc_bytes[r // 16]
+    ch = (r * 37) % 128
+    codes[0, r, ch // 2] = code << (4 * (ch & 1))
+    scales[0, r, ch // 16] = sb
+    rows_by_ch = {}
+    for i, c in enumerate(ch):
+        rows_by_ch.setdefault(int(c), []).append(i)
+    for c, rows in sorted(rows_by_ch.items())[:128]:
+        qf = np.zeros((1, 2, 32, 128), np.float32)
+        qf[0, 0, 0, c], qf[0, 1, 0, c] = 1.0, -1.0
+        w = np.zeros((1, 2, 32), np.float32)
+        w[:, :, 0] = 1.0
+        sel = np.array(rows)
+        inp = {"idx_k_codes": codes[:, sel], "idx_k_scales": scales[:, sel], "idx_q": workloads.to_bf16_bits(qf),
+               "head_w": w, "n_visible": np.full((1, 2), len(sel), np.int32)}
+        s = G.gpu_index_scores(inp, 1, 2, len(sel))
+        v = F.e2m1_value(code[sel]) * F.e4m3_value(sb[sel])
+        assert np.array_equal(s[0, 0], np.maximum(v, 0).astype(np.float32)), c
+        assert np.array_equal(s[0, 1], np.maximum(-v, 0).astype(np.float32)), c
+
+
 def test_fp4_dequant_every_code_and_scale_exact():
     # one main row per query, no window: the output is the dequantised row itself
     rows = 8
@@ -82,9 +112,11 @@ def test_fp4_dequant_every_code_and_scale_exact():
 
 # ------------------------------------------------------------------ indexer stages
 
+@pytest.mark.parametrize("fp4", [False, True])
 @pytest.mark.parametrize("B,T,N,nv", [(1, 1, 4096, None), (2, 3, 4093, [4093, 4000, 17, 0, 8, 1])])
-def test_index_scores_parity(B, T, N, nv):
-    w = small(B=B, T=T, N=N, seed=2000 + N)
+def test_index_scores_parity(B, T, N, nv, fp4):
+    """Scores of every visible position, E4M3 keys and FP4 keys."""
+    w = small(B=B, T=T, N=N, seed=2000 + N, idx_k_fp4=fp4)
     inp = workloads.make_inputs(w, with_attention=False)
     if nv is not None:
         inp["n_visible"] = np.array(nv, np.int32).reshape(B, T)
@@ -93,15 +125,17 @@ def test_index_scores_parity(B, T, N, nv):
         for t in range(T):
             n = int(inp["n_visible"][b, t])
             q8 = O.quantize_query(inp["idx_q"][b, t])
-            ref = O.indexer_scores(inp["idx_k"][b, :n], q8, inp["head_w"][b, t])
-            bound = G.score_abs_bound(inp["idx_k"][b, :n], inp["idx_q"][b, t], inp["head_w"][b, t])
+            keys = O.k_rows(G.host_keys(inp, b), slice(0, n))
+            ref = O.indexer_scores(keys, q8, inp["head_w"][b, t])
+            bound = G.score_abs_bound(keys, inp["idx_q"][b, t], inp["head_w"][b, t])
             G.assert_scores_close(s[b, t, :n], ref, bound, f"b{b} t{t}")
             assert np.all(np.isnan(s[b, t, n:])), "scores beyond n_visible must be untouched"
 
 
 def check_full(w, inp, gpu, b, t):
     n = int(inp["n_visible"][b, t])
-    ref = O.full_layer(inp["idx_k"][b], inp["idx_q"][b, t], inp["head_w"][b, t], n, w.block,
+    keys = G.host_keys(inp, b)
+    ref = O.full_layer(keys, inp["idx_q"][b, t], inp["head_w"][b, t], n, w.block,
                        w.pool_blocks, w.top_k)
     s = ref["scores"]
     nd = 0
@@ -111,7 +145,7 @@ def check_full(w, inp, gpu, b, t):
     nd += G.assert_topk_equiv(gpu["topk"][b, t], ref["topk"], lambda p: s[p], f"topk b{b} t{t}")
     g = gpu["topk"][b, t]
     sel = g[g >= 0]
-    bound = G.score_abs_bound(inp["idx_k"][b][sel], inp["idx_q"][b, t], inp["head_w"][b, t])
+    bound = G.score_abs_bound(O.k_rows(keys, sel), inp["idx_q"][b, t], inp["head_w"][b, t])
     G.assert_scores_close(gpu["topk_score"][b, t][:len(sel)], s[sel], bound, "topk_score")
     assert np.all(gpu["topk_score"][b, t][len(sel):] == 0)
     return ref, nd
@@ -150,7 +184,7 @@ def test_stage_entries_match_index_full(P):
     wsb = H.csa2_index_full_workspace(1, T, N, 8, P, K)
     ws = G.empty((wsb,), torch.uint8)
     k, q, hw, nv = G.dev(inp["idx_k"]), G.dev(inp["idx_q"]), G.dev(inp["head_w"]), G.dev(inp["n_visible"])
-    H.csa2_index_scan(k, N, q, hw, nv, 1, T, N, 8, P, K, ws, wsb)
+    H.csa2_index_scan(k, None, N, q, hw, nv, 1, T, N, 8, P, K, ws, wsb)
     H.csa2_index_pool(nv, 1, T, N, 8, P, K, pool_pos, pool_len, ws, wsb)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -164,12 +198,12 @@ def test_stage_entries_match_index_full(P):
         assert np.array_equal(G.host(pool_len), ref["pool_len"])
 
 
-@pytest.mark.parametrize("L,split", [(2, False), (2, True), (0, False)])
-def test_index_chain_matches_full_then_reindex(L, split):
+@pytest.mark.parametrize("L,split,fp4", [(2, False, False), (2, True, False), (0, False, False), (2, True, True)])
+def test_index_chain_matches_full_then_reindex(L, split, fp4):
     """The one-call indexer (Full Top-K launched with the Reindex Top-K) gives the same bits as
     csa2_index_full followed by csa2_reindex on its pool; ragged n_visible per query."""
     B, T, N, P, K = 2, 2, 20000, 256, 300
-    w = small(B=B, T=T, N=N, pool_blocks=P, top_k=K, n_reindex=max(L, 1), seed=3200 + L)
+    w = small(B=B, T=T, N=N, pool_blocks=P, top_k=K, n_reindex=max(L, 1), seed=3200 + L, idx_k_fp4=fp4)
     inp = workloads.make_inputs(w, with_attention=False)
     inp["n_visible"] = np.array([[20000, 13001], [2047, 19999]], np.int32)
     ref = G.gpu_index_full(inp, B, T, N, P, K)
@@ -324,6 +358,15 @@ def test_chain_tiny_decode():
 
 def test_chain_planted_64k():
     w = small("decode_1m", N=65536, seed=81)
+    inp = workloads.make_inputs(w)
+    run_chain_and_check(w, inp, [(0, 0)])
+    g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
+    assert np.isin(inp["planted_pos"], g["topk"][0, 0]).all()
+
+
+def test_chain_planted_64k_fp4_keys():
+    """The whole chain with FP4 indexer keys: Full layer, pool, Reindex, attention."""
+    w = small("decode_1m_fp4k", N=65536, seed=83)
     inp = workloads.make_inputs(w)
     run_chain_and_check(w, inp, [(0, 0)])
     g = G.gpu_index_full(inp, 1, 1, w.N, w.pool_blocks, w.top_k)
