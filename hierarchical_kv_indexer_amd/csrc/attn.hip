@@ -135,9 +135,12 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
   for (int c = 0; c < 16; ++c) qa[c] = *(const u32x4*)(qh + (size_t)j * kKvDim + 32 * c + 8 * g);
 
-  f32x4 o[8];
+  f32x4 o[8];                                       // MFMA-initialised, as in k_sparse_attn_wide
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) o[t] = mfma16x16x32(z, z, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
   float m_run[4], l_run[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
@@ -321,9 +324,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
 #pragma unroll
   for (int c = 0; c < 16; ++c) qa[c] = *(const u32x4*)(qh + (size_t)j * kKvDim + 32 * c + 8 * g);
 
+  // Accumulators start as MFMA results (of zero operands), so the compiler keeps them in the
+  // accumulation registers across the loop instead of copying them in and out every chunk.
   f32x4 o[32];                                     // tile 8*blk + t: dims 128*blk + 8j + t
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int t = 0; t < 32; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 32; ++t) o[t] = mfma16x16x32(z, z, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
   float m_run[4], l_run[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }

@@ -311,6 +311,29 @@ def test_attention_parity_on_oracle_sets(H):
     assert worst < 1e-2
 
 
+@pytest.mark.parametrize("NH", [16, 64])
+def test_attention_rescales_when_logits_grow_by_chunk(NH):
+    """Every 64-row chunk's logits exceed the previous chunk's by more than 2^8 (log2 units), so
+    the running max moves (and the output is rescaled) at every chunk of a workgroup; 512
+    (layer, query, head group) items keep the rows in one split per item."""
+    L, T, K, N = 8, 64, 512, 640
+    w = small(B=1, T=T, N=N, H=NH, layer_set=tuple(range(L)), n_reindex=0, pool_blocks=0, top_k=K, seed=99)
+    inp = workloads.make_inputs(w)
+    # main row p: every channel E2M1 1.0 x scale 0.5 + 0.25 * (p // 64) (exact in E4M3)
+    sc = 0.5 + 0.25 * (np.arange(N) // 64)
+    inp["kv_codes"][:] = 0x22
+    inp["kv_scales"][:] = workloads.to_e4m3_bytes(np.repeat(sc[None, :, None], 32, axis=2).astype(np.float32))
+    inp["q"][:] = workloads.to_bf16_bits(np.ones(inp["q"].shape, np.float32))
+    sets = np.tile(np.arange(K, dtype=np.int32), (L, 1, T, 1))
+    out, lse = G.gpu_attention(inp, w, sets)
+    for (l, t) in [(0, 0), (3, T // 2), (L - 1, T - 1)]:
+        rows = O.attention_rows(inp["kv_codes"][0], inp["kv_scales"][0], sets[l, 0, t], inp["swa"][l, 0],
+                                int(inp["swa_end"][0, t]), w.swa_window)
+        o, ls = O.attention(inp["q"][l, 0, t], rows, 1 / math.sqrt(512))
+        G.assert_attention_close(out[l, 0, t], o, f"l{l} t{t}")
+        assert np.allclose(lse[l, 0, t], ls, rtol=1e-3, atol=1e-3)
+
+
 # ------------------------------------------------------------------ whole chain
 
 def run_chain_and_check(w, inp, queries):
