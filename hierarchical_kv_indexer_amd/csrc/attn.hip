@@ -277,12 +277,47 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   }
 }
 
-// The same computation for 64 heads per workgroup (H % 64 == 0): wave w owns heads
-// 64*blockIdx.y + 16w .. +15 over every row of the chunk, so each gathered row is dequantised
-// once for all 64 heads.  A wave's softmax state, P tile and output (16 heads x 512 dims) are
-// its own: S = Q X^T takes 4 row tiles x 16 MFMAs and O += P X 32 dim tiles x 2 MFMAs per chunk,
-// with no cross-wave reduction.  grid (n_splits, H/64, L*Q); outputs as k_sparse_attn.
-__global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
+// 64 heads per workgroup (H % 64 == 0), 8 waves.  Wave w owns head group hg = w % 4 (heads
+// 64*blockIdx.y + 16*hg .. +15) and half hf = w / 4: for S = Q X^T it scores rows 32*hf .. +31 of
+// each 64-row chunk, for O += P X it accumulates dims 256*hf .. +255 over all 64 rows.  The two
+// waves of a head group exchange their row maxima and P tiles through LDS, so each gathered row is
+// dequantised once for all 64 heads and a wave holds 16 heads x 256 dims of accumulators (two
+// waves per SIMD fit).  grid (n_splits, H/64, L*Q); outputs as k_sparse_attn.
+constexpr int kWideThreads = 512;
+
+struct RawRow8 {         // this thread's eighth (64 channels) of one chunk row
+  u32x4 d[4];            // main: d[0..1] = 32 code bytes; SWA: d[0..3] = 64 E4M3 bytes
+  uint32_t sc;           // main: 4 scale bytes
+  int kind;              // 0 empty, 1 main, 2 SWA
+};
+
+// Dequantise this thread's eighth row into LDS (64 bf16 = 8 x 16 bytes).
+__device__ __forceinline__ void store_row8(const RawRow8& r, uint16_t* xrow, int eighth) {
+  u32x4* dst = (u32x4*)(xrow + 64 * eighth);
+  if (r.kind == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                      // scale group i: 8 code bytes, 16 channels
+      const float s = e4m3_to_f32((r.sc >> (8 * i)) & 0xffu);
+      const uint32_t w0 = r.d[i >> 1][(i & 1) * 2], w1 = r.d[i >> 1][(i & 1) * 2 + 1];
+      dst[2 * i] = u32x4{e2m1x2_scaled_to_bf16x2<0>(w0, s), e2m1x2_scaled_to_bf16x2<1>(w0, s),
+                         e2m1x2_scaled_to_bf16x2<2>(w0, s), e2m1x2_scaled_to_bf16x2<3>(w0, s)};
+      dst[2 * i + 1] = u32x4{e2m1x2_scaled_to_bf16x2<0>(w1, s), e2m1x2_scaled_to_bf16x2<1>(w1, s),
+                             e2m1x2_scaled_to_bf16x2<2>(w1, s), e2m1x2_scaled_to_bf16x2<3>(w1, s)};
+    }
+  } else if (r.kind == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dst[2 * i] = e4m3x8_to_bf16x8(r.d[i].x, r.d[i].y);
+      dst[2 * i + 1] = e4m3x8_to_bf16x8(r.d[i].z, r.d[i].w);
+    }
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = z;
+  }
+}
+
+__global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t kv_rows,
     const uint16_t* __restrict__ qg, const int32_t* __restrict__ idx_sets, LayerSets sets,
     const uint8_t* __restrict__ swa, int swa_rows, const int32_t* __restrict__ swa_end, int window,
@@ -291,11 +326,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t X[kRows * kXStride];
   __shared__ __attribute__((aligned(16))) uint16_t P[4 * 16 * kPStride];
+  __shared__ float red_m[2][64], red_l[2][64];           // [half][16 * head group + head]
   __shared__ int32_t rowok[kRows];
 
   const int split = blockIdx.x, hq = blockIdx.y, lq = blockIdx.z;
   const int l = lq / Q, q = lq % Q, b = q / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hg = wave & 3, hf = wave >> 2;
   const int j = lane & 15, g = lane >> 4;
   const int32_t* idx = idx_sets + ((size_t)sets.set[l] * Q + q) * k;
   int we = swa_end[q];
@@ -308,7 +345,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
   const uint8_t* scales_seq = kv_scales + (size_t)b * kv_rows * kKvScaleBytes;
   const uint8_t* swa_seq = swa + ((size_t)l * B + b) * (size_t)swa_rows * kKvDim;
 
-  const int my_row = tid >> 2, quarter = tid & 3;
+  const int my_row = tid >> 3, eighth = tid & 7;
   auto row_index = [&](int c) {
     const int slot = s0 + c * kRows + my_row;
     if (slot >= s1 || slot >= k) return -1;
@@ -318,112 +355,123 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
   int pos_cur = nchunks > 0 ? row_index(0) : -1;
   int pos_next = nchunks > 1 ? row_index(1) : -1;
 
-  const int hbase = 64 * hq + 16 * wave;           // this wave's first head
+  const int hbase = 64 * hq + 16 * hg;              // this wave's first head
   const uint16_t* qh = qg + (((size_t)l * Q + q) * H + hbase) * kKvDim;
   u32x4 qa[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) qa[c] = *(const u32x4*)(qh + (size_t)j * kKvDim + 32 * c + 8 * g);
 
   // Accumulators start as MFMA results (of zero operands), so the compiler keeps them in the
-  // accumulation registers across the loop instead of copying them in and out every chunk.
-  f32x4 o[32];                                     // tile 8*blk + t: dims 128*blk + 8j + t
+  // accumulation registers across the loop.
+  f32x4 o[16];                                       // tile 8*blk + t: dims 256*hf + 128*blk + 8j + t
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int t = 0; t < 32; ++t) o[t] = mfma16x16x32(z, z, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int t = 0; t < 16; ++t) o[t] = mfma16x16x32(z, z, f32x4{0.f, 0.f, 0.f, 0.f});
   }
   float m_run[4], l_run[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
-  uint16_t* Pw = P + wave * 16 * kPStride;
+  uint16_t* Pg = P + hg * 16 * kPStride;
 
-  auto load_chunk = [&](RawRow& r, int c, int pos) {
+  auto load_chunk = [&](RawRow8& r, int c, int pos) {
     const int slot = s0 + c * kRows + my_row;
     r.kind = 0;
     if (slot < s1) {
       if (slot < k) {
         if (pos >= 0) {
-          const u32x4* cp = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 64 * quarter);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r.d[i] = cp[i];
-          r.sc = *(const u32x2*)(scales_seq + (size_t)pos * kKvScaleBytes + 8 * quarter);
+          const u32x4* cp = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 32 * eighth);
+          r.d[0] = cp[0];
+          r.d[1] = cp[1];
+          r.sc = *(const uint32_t*)(scales_seq + (size_t)pos * kKvScaleBytes + 4 * eighth);
           r.kind = 1;
         }
       } else {
-        const u32x4* cp = (const u32x4*)(swa_seq + (size_t)(ws + slot - k) * kKvDim + 128 * quarter);
+        const u32x4* cp = (const u32x4*)(swa_seq + (size_t)(ws + slot - k) * kKvDim + 64 * eighth);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r.d[i] = cp[i];
+        for (int i = 0; i < 4; ++i) r.d[i] = cp[i];
         r.kind = 2;
       }
     }
   };
-  RawRow raw;
+  RawRow8 raw;
   if (nchunks > 0) load_chunk(raw, 0, pos_cur);
 
   for (int c = 0; c < nchunks; ++c) {
-    store_row(raw, X + my_row * kXStride, quarter);
-    if (quarter == 0) rowok[my_row] = raw.kind != 0;
-    __syncthreads();
+    store_row8(raw, X + my_row * kXStride, eighth);
+    if (eighth == 0) rowok[my_row] = raw.kind != 0;
+    __syncthreads();                                 // X complete
     if (c + 1 < nchunks) {
       load_chunk(raw, c + 1, pos_next);
       pos_next = c + 2 < nchunks ? row_index(c + 2) : -1;
     }
 
-    // S[head 4g+v][row 16r + j]
-    f32x4 s[4];
+    // S[head 4g+v][row 32*hf + 16r + j]
+    f32x4 s[2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        s[r] = mfma16x16x32(qa[cc], *(const u32x4*)(X + (16 * r + j) * kXStride + 32 * cc + 8 * g), s[r]);
-    bool ok[4];
+      for (int r = 0; r < 2; ++r)
+        s[r] = mfma16x16x32(qa[cc], *(const u32x4*)(X + (32 * hf + 16 * r + j) * kXStride + 32 * cc + 8 * g), s[r]);
+    float sv[2][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ok[r] = rowok[16 * r + j] != 0;
-    // The reference point m_run of a head moves only when the chunk's max exceeds it by more
-    // than kLazyLog2, so P <= 2^kLazyLog2 and O is rescaled only on such a move (numerator
-    // and denominator share the reference point: the softmax is unchanged).
+    for (int r = 0; r < 2; ++r) {
+      const bool ok = rowok[32 * hf + 16 * r + j] != 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv[r][v] = ok ? s[r][v] * scale_log2 : -INFINITY;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float m = row16_max(fmaxf(sv[0][v], sv[1][v]));
+      if (j == 0) red_m[hf][16 * hg + 4 * g + v] = m;
+    }
+    __syncthreads();                                 // both halves' maxima
+    // The reference point of a head moves only when the chunk's max exceeds it by more than
+    // kLazyLog2, so P <= 2^kLazyLog2 and O is rescaled only on such a move.  Both waves of a head
+    // group take identical decisions (same maxima, same order).
     float alpha[4];
     bool moved = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      float sv[4], m = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[r] = ok[r] ? s[r][v] * scale_log2 : -INFINITY;
-        m = fmaxf(m, sv[r]);
-      }
-      m = row16_max(m);
-      const bool mv = m > m_run[v] + kLazyLog2;              // true from -inf to finite
+      const int hh = 16 * hg + 4 * g + v;
+      const float m = fmaxf(red_m[0][hh], red_m[1][hh]);
+      const bool mv = m > m_run[v] + kLazyLog2;      // true from -inf to finite
       const float mnew = mv ? m : m_run[v];
       alpha[v] = (mv && m_run[v] != -INFINITY) ? exp2f(m_run[v] - mnew) : 1.f;
       moved |= mv && m_run[v] != -INFINITY;
       float ps = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = mnew == -INFINITY ? 0.f : exp2f(sv[r] - mnew);
+      for (int r = 0; r < 2; ++r) {
+        const float p = mnew == -INFINITY ? 0.f : exp2f(sv[r][v] - mnew);
         const uint32_t pb = f32_to_bf16_rne(p);
-        Pw[(4 * g + v) * kPStride + 16 * r + j] = (uint16_t)pb;
+        Pg[(4 * g + v) * kPStride + 32 * hf + 16 * r + j] = (uint16_t)pb;
         ps += bf16_bits_to_f32(pb);
       }
-      l_run[v] = l_run[v] * alpha[v] + row16_sum(ps);
+      ps = row16_sum(ps);
+      if (j == 0) red_l[hf][hh] = ps;
       m_run[v] = mnew;
     }
-    if (__ballot(moved) != 0) {                              // wave-uniform, rare
+    __syncthreads();                                 // P tiles and both halves' sums
 #pragma unroll
-      for (int t = 0; t < 32; ++t)
+    for (int v = 0; v < 4; ++v) {
+      const int hh = 16 * hg + 4 * g + v;
+      l_run[v] = l_run[v] * alpha[v] + (red_l[0][hh] + red_l[1][hh]);
+    }
+    if (__ballot(moved) != 0) {                      // wave-uniform, rare
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[t][v] *= alpha[v];
     }
-    // O[head 4g+v][dim 128*blk + 8j + t] += sum_r P[head][r] X[r][dim]; the P tile is this
-    // wave's own, so it is read back without a barrier (a wave's LDS accesses are ordered).
+    // O[head 4g+v][dim 256*hf + 128*blk + 8j + t] += sum_r P[head][r] X[r][dim]
 #pragma unroll
     for (int kk = 0; kk < kRows / 32; ++kk) {
-      const u32x4 pa = *(const u32x4*)(Pw + j * kPStride + 32 * kk + 8 * g);
+      const u32x4 pa = *(const u32x4*)(Pg + j * kPStride + 32 * kk + 8 * g);
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const uint16_t* xc = X + (32 * kk + 8 * g) * kXStride + 128 * blk + 8 * j;
+      for (int blk = 0; blk < 2; ++blk) {
+        const uint16_t* xc = X + (32 * kk + 8 * g) * kXStride + 256 * hf + 128 * blk + 8 * j;
         u32x4 xv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) xv[e] = *(const u32x4*)(xc + e * kXStride);
@@ -440,7 +488,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
         }
       }
     }
-    if (c + 1 < nchunks) __syncthreads();   // X and rowok are rewritten by the next chunk
+    if (c + 1 < nchunks) __syncthreads();            // X, P, red_m, red_l and rowok are rewritten
   }
 
   const size_t hrow = (size_t)lq * H;
@@ -450,25 +498,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn_wide(
     if (n_splits == 1) {
       const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
+      for (int blk = 0; blk < 2; ++blk) {
         u32x4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           pk[i] = f32_to_bf16_rne(o[8 * blk + 2 * i][v] * inv) |
                   (f32_to_bf16_rne(o[8 * blk + 2 * i + 1][v] * inv) << 16);
-        *(u32x4*)(out + (hrow + h) * kKvDim + 128 * blk + 8 * j) = pk;
+        *(u32x4*)(out + (hrow + h) * kKvDim + 256 * hf + 128 * blk + 8 * j) = pk;
       }
-      if (lse && j == 0)
+      if (lse && hf == 0 && j == 0)
         lse[hrow + h] = l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * 0.69314718055994531f : -INFINITY;
     } else {
       const size_t pr = (hrow + h) * n_splits + split;
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        f32x4* po = (f32x4*)(part_o + pr * kKvDim + 128 * blk + 8 * j);
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x4* po = (f32x4*)(part_o + pr * kKvDim + 256 * hf + 128 * blk + 8 * j);
         po[0] = f32x4{o[8 * blk][v], o[8 * blk + 1][v], o[8 * blk + 2][v], o[8 * blk + 3][v]};
         po[1] = f32x4{o[8 * blk + 4][v], o[8 * blk + 5][v], o[8 * blk + 6][v], o[8 * blk + 7][v]};
       }
-      if (j == 0) {
+      if (hf == 0 && j == 0) {
         part_ml[pr * 2] = m_run[v];
         part_ml[pr * 2 + 1] = l_run[v];
       }
@@ -549,7 +597,7 @@ hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales,
   float* part_o = (float*)workspace;
   float* part_ml = part_o ? part_o + (size_t)L * Q * H * p.n_splits * kKvDim : nullptr;
   if (p.heads_per_wg == 64)
-    hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.n_splits, H / 64, L * Q), dim3(kAttnThreads), 0, s,
+    hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.n_splits, H / 64, L * Q), dim3(kWideThreads), 0, s,
                        kv_codes, kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q,
                        B, T, H, k, scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
   else
