@@ -277,7 +277,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   }
 }
 
-// 64 heads per workgroup (H % 64 == 0), 8 waves.  Wave w owns head group hg = w % 4 (heads
+// 64 heads per workgroup (H % 64 == 0), 8 waves, X double-buffered.  Wave w owns head group hg = w % 4 (heads
 // 64*blockIdx.y + 16*hg .. +15) and half hf = w / 4: for S = Q X^T it scores rows 32*hf .. +31 of
 // each 64-row chunk, for O += P X it accumulates dims 256*hf .. +255 over all 64 rows.  The two
 // waves of a head group exchange their row maxima and P tiles through LDS, so each gathered row is
@@ -324,10 +324,10 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     int Q, int B, int T, int H, int k, float scale_log2, int split_rows, int n_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t X[kRows * kXStride];
+  __shared__ __attribute__((aligned(16))) uint16_t X[2][kRows * kXStride];   // chunk c in X[c & 1]
   __shared__ __attribute__((aligned(16))) uint16_t P[4 * 16 * kPStride];
   __shared__ float red_m[2][64], red_l[2][64];           // [half][16 * head group + head]
-  __shared__ int32_t rowok[kRows];
+  __shared__ int32_t rowok[2][kRows];
 
   const int split = blockIdx.x, hq = blockIdx.y, lq = blockIdx.z;
   const int l = lq / Q, q = lq % Q, b = q / T;
@@ -352,8 +352,8 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     const int pos = idx[slot];
     return (pos >= 0 && (int64_t)pos < kv_rows) ? pos : -1;
   };
-  int pos_cur = nchunks > 0 ? row_index(0) : -1;
-  int pos_next = nchunks > 1 ? row_index(1) : -1;
+  int pos_a = nchunks > 0 ? row_index(0) : -1;
+  int pos_b = nchunks > 1 ? row_index(1) : -1;
 
   const int hbase = 64 * hq + 16 * hg;              // this wave's first head
   const uint16_t* qh = qg + (((size_t)l * Q + q) * H + hbase) * kKvDim;
@@ -394,18 +394,20 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       }
     }
   };
+  // Pipeline: chunk c is scored from X[c & 1] while chunk c+1 is dequantised into the other buffer
+  // (between the softmax and O += P X of chunk c) and the raw rows of chunk c+2 are in flight.
   RawRow8 raw;
-  if (nchunks > 0) load_chunk(raw, 0, pos_cur);
+  if (nchunks > 0) {
+    load_chunk(raw, 0, pos_a);
+    store_row8(raw, X[0] + my_row * kXStride, eighth);
+    if (eighth == 0) rowok[0][my_row] = raw.kind != 0;
+  }
+  if (nchunks > 1) load_chunk(raw, 1, pos_b);
+  int pos_c = nchunks > 2 ? row_index(2) : -1;
+  __syncthreads();
 
   for (int c = 0; c < nchunks; ++c) {
-    store_row8(raw, X + my_row * kXStride, eighth);
-    if (eighth == 0) rowok[my_row] = raw.kind != 0;
-    __syncthreads();                                 // X complete
-    if (c + 1 < nchunks) {
-      load_chunk(raw, c + 1, pos_next);
-      pos_next = c + 2 < nchunks ? row_index(c + 2) : -1;
-    }
-
+    const uint16_t* Xc = X[c & 1];
     // S[head 4g+v][row 32*hf + 16r + j]
     f32x4 s[2];
 #pragma unroll
@@ -414,11 +416,11 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     for (int cc = 0; cc < 16; ++cc)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        s[r] = mfma16x16x32(qa[cc], *(const u32x4*)(X + (32 * hf + 16 * r + j) * kXStride + 32 * cc + 8 * g), s[r]);
+        s[r] = mfma16x16x32(qa[cc], *(const u32x4*)(Xc + (32 * hf + 16 * r + j) * kXStride + 32 * cc + 8 * g), s[r]);
     float sv[2][4];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const bool ok = rowok[32 * hf + 16 * r + j] != 0;
+      const bool ok = rowok[c & 1][32 * hf + 16 * r + j] != 0;
 #pragma unroll
       for (int v = 0; v < 4; ++v) sv[r][v] = ok ? s[r][v] * scale_log2 : -INFINITY;
     }
@@ -465,13 +467,23 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
 #pragma unroll
         for (int v = 0; v < 4; ++v) o[t][v] *= alpha[v];
     }
+    // the next chunk into the other buffer (last read before the previous barrier), then the
+    // raw rows of the chunk after it
+    if (c + 1 < nchunks) {
+      store_row8(raw, X[(c + 1) & 1] + my_row * kXStride, eighth);
+      if (eighth == 0) rowok[(c + 1) & 1][my_row] = raw.kind != 0;
+      if (c + 2 < nchunks) {
+        load_chunk(raw, c + 2, pos_c);
+        pos_c = c + 3 < nchunks ? row_index(c + 3) : -1;
+      }
+    }
     // O[head 4g+v][dim 256*hf + 128*blk + 8j + t] += sum_r P[head][r] X[r][dim]
 #pragma unroll
     for (int kk = 0; kk < kRows / 32; ++kk) {
       const u32x4 pa = *(const u32x4*)(Pg + j * kPStride + 32 * kk + 8 * g);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const uint16_t* xc = X + (32 * kk + 8 * g) * kXStride + 256 * hf + 128 * blk + 8 * j;
+        const uint16_t* xc = Xc + (32 * kk + 8 * g) * kXStride + 256 * hf + 128 * blk + 8 * j;
         u32x4 xv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) xv[e] = *(const u32x4*)(xc + e * kXStride);
@@ -488,7 +500,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
         }
       }
     }
-    if (c + 1 < nchunks) __syncthreads();            // X, P, red_m, red_l and rowok are rewritten
+    if (c + 1 < nchunks) __syncthreads();            // next chunk's X and rowok written; P, red_* free
   }
 
   const size_t hrow = (size_t)lq * H;
