@@ -62,7 +62,7 @@ struct Carver {
 
 struct FullPlan {
   int Q, nb_max, nb_stride, chunk, n_wg, n_units, blocks_per_unit, P, cap;
-  bool internal_pool;
+  bool internal_pool, multi_query;
 };
 
 constexpr int kMaxPositions = 1 << 23;   // scores only: 1024 chunks of 8192 positions per query
@@ -72,7 +72,8 @@ FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
   p.Q = B * T;
   p.nb_max = (n_max + csa2::kBlock - 1) / csa2::kBlock;
   p.nb_stride = (p.nb_max + 63) / 64 * 64;                 // 256-byte rows of block keys
-  p.chunk = csa2::scan_chunk_positions(n_max, p.Q);
+  p.multi_query = csa2::scan_multi_query(T, n_max);
+  p.chunk = p.multi_query ? csa2::scan_mq_chunk(n_max, B, T) : csa2::scan_chunk_positions(n_max, p.Q);
   p.n_wg = n_max > 0 ? (n_max + p.chunk - 1) / p.chunk : 1;
   p.n_units = p.n_wg * csa2::kScanUnitsPerWg;
   p.blocks_per_unit = p.chunk / (csa2::kBlock * csa2::kScanUnitsPerWg);
@@ -159,7 +160,7 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   if (n_max == 0) return ok();
   const FullPlan p = plan_full(B, T, n_max, 1, 1);
   st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                       scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg,
+                                       scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg, p.multi_query,
                                        (hipStream_t)stream),
                  "index scan launch");
   return st == CSA2_OK ? ok() : st;
@@ -206,7 +207,7 @@ csa2_status csa2_index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, i
   carve_full(workspace, p, n_max, &w);
   if (n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg,
+                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query,
                                          (hipStream_t)stream),
                    "index scan launch");
     if (st != CSA2_OK) return st;
@@ -430,7 +431,7 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   hipStream_t s = (hipStream_t)stream;
   if (do_scan && n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, s),
+                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query, s),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }

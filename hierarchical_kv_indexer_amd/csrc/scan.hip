@@ -42,6 +42,33 @@ hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hi
   return hipGetLastError();
 }
 
+// The E4M3 value nearest to x (ties to the even code), saturating at +-448, without branches:
+// the E4M3 grid spacing at |x| is 2^(e-3) for |x| in [2^e, 2^(e+1)), e >= -6, and 2^-9 below
+// 2^-6, so rounding |x| / spacing to an integer (ties to even) and scaling back is the encoding
+// followed by the decoding.  Both scalings are exact.  NaN stays NaN.
+__device__ __forceinline__ float round_e4m3(float x) {
+  const float a = fabsf(x);
+  const int e = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+  const float step = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
+  const float inv = __uint_as_float((uint32_t)(127 - (e - 3)) << 23);   // 1 / step, exact
+  float r = __builtin_rintf(a * inv) * step;
+  r = r > 448.f ? 448.f : r;
+  return __builtin_copysignf(r, x);
+}
+
+// Two bf16 query values (low half first) rounded to E4M3 and returned as a bf16 pair, or an fp16
+// pair with kF16 (E4M3 values are exact in both).
+template <bool kF16>
+__device__ __forceinline__ uint32_t q8_pair(uint32_t w) {
+  const float lo = round_e4m3(bf16_bits_to_f32(w & 0xffffu));
+  const float hi = round_e4m3(bf16_bits_to_f32(w >> 16));
+  if constexpr (kF16)
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+  else
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
 // The 32x128 query of one indexer head set, rounded to E4M3 and held as bf16 in LDS.
 // NT threads, 4096/NT consecutive values each, loaded with 16-byte (or 8-byte) loads.
 // kF16: the values are held as fp16 instead of bf16 (exact either way: E4M3 fits both).
@@ -61,15 +88,7 @@ __device__ __forceinline__ void stage_query(const uint16_t* __restrict__ q, uint
   }
   uint32_t o[kPer / 2];
 #pragma unroll
-  for (int i = 0; i < kPer / 2; ++i) {
-    const float lo = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(w[i] & 0xffffu)));
-    const float hi = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(w[i] >> 16)));
-    if constexpr (kF16)
-      o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
-    else
-      o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-  }
+  for (int i = 0; i < kPer / 2; ++i) o[i] = q8_pair<kF16>(w[i]);
   if constexpr (kPer == 16) {
     *(u32x4*)(qlds + base) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(qlds + base + 8) = u32x4{o[4], o[5], o[6], o[7]};
@@ -110,17 +129,27 @@ __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(
 // Score of this lane's row (column j of the tile); every lane of a column gets the same value.
 // The 8 heads of a lane are summed in a fixed order, then the four k-groups are combined as
 // (g0 + g1) + (g2 + g3), identically on every lane.
-__device__ __forceinline__ float tile_score(const TileCtx& cx, u32x4 lo, u32x4 hi) {
-  u32x4 b[4];
-  b[0] = e4m3x8_to_bf16x8(lo.x, lo.y);
-  b[1] = e4m3x8_to_bf16x8(lo.z, lo.w);
-  b[2] = e4m3x8_to_bf16x8(hi.x, hi.y);
-  b[3] = e4m3x8_to_bf16x8(hi.z, hi.w);
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+
+// Score of this lane's row from the key operands b[c] (bf16, or fp16 with kF16), laid out as the
+// query operands.  The 8 heads of a lane are summed in a fixed order, then the four k-groups are
+// combined as (g0 + g1) + (g2 + g3), identically on every lane.
+template <bool kF16>
+__device__ __forceinline__ float operand_score(const TileCtx& cx, const u32x4 (&b)[4]) {
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    a0 = mfma16x16x32(cx.qa[0][c], b[c], a0);
-    a1 = mfma16x16x32(cx.qa[1][c], b[c], a1);
+    if constexpr (kF16) {
+      a0 = mfma16x16x32_f16(cx.qa[0][c], b[c], a0);
+      a1 = mfma16x16x32_f16(cx.qa[1][c], b[c], a1);
+    } else {
+      a0 = mfma16x16x32(cx.qa[0][c], b[c], a0);
+      a1 = mfma16x16x32(cx.qa[1][c], b[c], a1);
+    }
   }
   float p = 0.f;
 #pragma unroll
@@ -128,6 +157,21 @@ __device__ __forceinline__ float tile_score(const TileCtx& cx, u32x4 lo, u32x4 h
 #pragma unroll
   for (int v = 0; v < 4; ++v) p = fmaf(cx.w[4 + v], relu_bits(a1[v]), p);
   return sum_xor32(sum_xor16(p));
+}
+
+// E4M3 key bytes of a lane (two 16-byte pieces of its row) as bf16 operands (exact).
+__device__ __forceinline__ void e4m3_operands(u32x4 lo, u32x4 hi, u32x4 (&b)[4]) {
+  b[0] = e4m3x8_to_bf16x8(lo.x, lo.y);
+  b[1] = e4m3x8_to_bf16x8(lo.z, lo.w);
+  b[2] = e4m3x8_to_bf16x8(hi.x, hi.y);
+  b[3] = e4m3x8_to_bf16x8(hi.z, hi.w);
+}
+
+// Score of this lane's row (column j of the tile); every lane of a column gets the same value.
+__device__ __forceinline__ float tile_score(const TileCtx& cx, u32x4 lo, u32x4 hi) {
+  u32x4 b[4];
+  e4m3_operands(lo, hi, b);
+  return operand_score<false>(cx, b);
 }
 
 __device__ __forceinline__ void load_row(const uint8_t* __restrict__ row, int g, u32x4& lo, u32x4& hi) {
@@ -162,40 +206,28 @@ __device__ __forceinline__ void load_ctx_fp4(TileCtx& cx, const uint16_t* qlds, 
   }
 }
 
-// Score of this lane's row from FP4 keys (same head sum as tile_score).  The keys are decoded
-// to fp16 (E2M1 by the hardware conversion, times the E4M3 scale in packed fp16: every product
-// has at most 6 significant bits within [2^-10, 2688], so it is exact) and the query operands
-// are fp16 too, so the contraction runs on the fp16 MFMA with exact products.
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
-}
+// FP4 keys (same head sum as tile_score): the keys are decoded to fp16 (E2M1 by the hardware
+// conversion, times the E4M3 scale in packed fp16: every product has at most 6 significant bits
+// within [2^-10, 2688], so it is exact) and the query operands are fp16 too, so the contraction
+// runs on the fp16 MFMA with exact products.
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1x2_scaled_to_f16x2(uint32_t w, h2 s) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL) * s);
 }
-__device__ __forceinline__ float tile_score_fp4(const TileCtx& cx, const TileRaw<true>& r) {
-  const h2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, false);   // groups 2g, 2g+1 (exact)
-  u32x4 b[4];
+// 16 code bytes (channels 32g .. 32g+31) and the two scale bytes of their groups -> fp16 operands.
+__device__ __forceinline__ void fp4_operands(u32x4 codes, uint32_t sc2, u32x4 (&b)[4]) {
+  const h2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc2, 1.0f, false);   // groups 2g, 2g+1 (exact)
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const h2 s = c < 2 ? h2{sc.x, sc.x} : h2{sc.y, sc.y};
-    b[c] = u32x4{e2m1x2_scaled_to_f16x2<0>(r.codes[c], s), e2m1x2_scaled_to_f16x2<1>(r.codes[c], s),
-                 e2m1x2_scaled_to_f16x2<2>(r.codes[c], s), e2m1x2_scaled_to_f16x2<3>(r.codes[c], s)};
+    b[c] = u32x4{e2m1x2_scaled_to_f16x2<0>(codes[c], s), e2m1x2_scaled_to_f16x2<1>(codes[c], s),
+                 e2m1x2_scaled_to_f16x2<2>(codes[c], s), e2m1x2_scaled_to_f16x2<3>(codes[c], s)};
   }
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    a0 = mfma16x16x32_f16(cx.qa[0][c], b[c], a0);
-    a1 = mfma16x16x32_f16(cx.qa[1][c], b[c], a1);
-  }
-  float p = 0.f;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) p = fmaf(cx.w[v], relu_bits(a0[v]), p);
-#pragma unroll
-  for (int v = 0; v < 4; ++v) p = fmaf(cx.w[4 + v], relu_bits(a1[v]), p);
-  return sum_xor32(sum_xor16(p));
+}
+__device__ __forceinline__ float tile_score_fp4(const TileCtx& cx, const TileRaw<true>& r) {
+  u32x4 b[4];
+  fp4_operands(r.codes, r.sc, b);
+  return operand_score<true>(cx, b);
 }
 
 // One tile row of either key format.
@@ -359,6 +391,229 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   }
 }
 
+// ---------------------------------------------------------------------------- multi-query Full scan
+
+// When many queries of one sequence scan the same keys (a prefill chunk), a workgroup scores a
+// chunk of positions for 16 consecutive queries of the sequence, one per wave.  Each step stages
+// 128 key rows in LDS already converted to MFMA operands (bf16 for E4M3 keys, fp16 for FP4 keys,
+// both exact, channels in their natural order), so the key stream is read and converted once per
+// 16 queries.  A wave scores 32 positions at a time with 32x32x16 MFMAs (32 heads x 32 positions):
+// each lane then holds 16 heads of one position, so the head sum is 16 fused multiply-adds and
+// one exchange with lane l ^ 32, and the block maxima of the 32 positions come from one 8-lane
+// reduction.  Products are exact and accumulated in fp32, as in k_idx_scan, though in a different
+// order.  Outputs are those of k_idx_scan for every query of the group (unit u of a chunk covers
+// its positions [u*chunk/16, (u+1)*chunk/16)).
+constexpr int kMqQueries = kFullWaves;        // 16 queries per workgroup, one per wave
+constexpr int kMqRows = 128;                  // key rows per staged step
+constexpr int kMqStride = 2 * kIdxDim + 16;   // LDS bytes per staged row: 128 16-bit operands + pad
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <bool kF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (kF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// A wave's query for 32x32x16 MFMAs: lane l holds head l % 32, channels 16c + 8(l/32) .. +7 in
+// qa[c] (rounded to E4M3, as bf16 or fp16), and the weights of the heads its outputs hold:
+// output v of lane l is head 8(v/4) + 4(l/32) + v%4.
+struct Ctx32 {
+  u32x4 qa[8];
+  float w[16];
+};
+
+template <bool kF16>
+__device__ __forceinline__ void load_ctx32(Ctx32& cx, const uint16_t* __restrict__ q, const float* __restrict__ w) {
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const u32x4 v = *(const u32x4*)(q + r * kIdxDim + 16 * c + 8 * h);
+    cx.qa[c] = u32x4{q8_pair<kF16>(v.x), q8_pair<kF16>(v.y), q8_pair<kF16>(v.z), q8_pair<kF16>(v.w)};
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cx.w[v] = w[8 * (v >> 2) + 4 * h + (v & 3)];
+}
+
+// Score of position l % 32 of a 32-row group of the staged step (row pointer `row`: this lane's
+// row); lanes l and l ^ 32 return the same value.
+template <bool kF16>
+__device__ __forceinline__ float score32(const Ctx32& cx, const unsigned char* row) {
+  const int h = (threadIdx.x >> 5) & 1;
+  u32x4 bk[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) bk[c] = *(const u32x4*)(row + 32 * c + 16 * h);
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc = mfma32x32x16<kF16>(cx.qa[c], bk[c], acc);
+  float p = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p = fmaf(cx.w[v], relu_bits(acc[v]), p);
+  return sum_xor32(p);
+}
+
+// grid (n_wg, B * ceil(T/16)).  Step s of the chunk stages key rows p_begin + 128s .. +127 (rows
+// past the group's last visible position are clamped to it and never scored), double-buffered:
+// step s+1 is converted into the other buffer while step s is scored, and the loads of step s+2
+// are then in flight.  Staging: E4M3, thread t converts bytes 16*(t%8) .. +15 of row t/8 (channels
+// 16*(t%8) .. +15); FP4 (threads below 512), the 16 code bytes of row t/4 holding channels
+// 32*(t%4) .. +31 and the two scales of their groups.
+template <bool kFp4>
+__global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
+    const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
+    const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w, const int32_t* __restrict__ n_visible,
+    int T, int n_max, int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
+    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
+  __shared__ __attribute__((aligned(16))) unsigned char stage[2][kMqRows * kMqStride];
+  __shared__ __attribute__((aligned(16))) float sstage[2][kMqQueries][kMqRows];   // scores of a step
+  __shared__ uint32_t wkeys[kMqQueries][kMqMaxChunk / kBlock];
+  const int groups = (T + kMqQueries - 1) / kMqQueries;
+  const int b = blockIdx.y / groups, t0 = (blockIdx.y % groups) * kMqQueries;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nq = min(kMqQueries, T - t0);
+  const int p_begin = blockIdx.x * chunk;
+  auto visible = [&](int i) {                 // clamped n_visible of query t0 + i of the group
+    const int v = n_visible[b * T + t0 + i];
+    return v < 0 ? 0 : (v > n_max ? n_max : v);
+  };
+  int nv_max = 0;                             // the group's visible range
+  for (int i = 0; i < nq; ++i) nv_max = max(nv_max, visible(i));
+  const bool has_q = wave < nq;
+  const int q = b * T + t0 + (has_q ? wave : 0);
+  const int p_end_q = has_q ? min(p_begin + chunk, visible(wave)) : p_begin;   // this wave's query
+  const int p_end = min(p_begin + chunk, nv_max);
+  const int npos = max(0, p_end - p_begin);
+  const int nsteps = (npos + kMqRows - 1) / kMqRows;
+  const int nblk_g = (npos + kBlock - 1) / kBlock;                          // the group's blocks
+  const int plast = p_end > p_begin ? p_end - 1 : 0;
+  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
+  const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
+
+  const int srow = kFp4 ? tid >> 2 : tid >> 3, piece = kFp4 ? tid & 3 : tid & 7;
+  const bool stager = !kFp4 || tid < 4 * kMqRows;
+  u32x4 pre = {0u, 0u, 0u, 0u};
+  uint32_t pre_sc = 0u;
+  auto load_step = [&](int st) {
+    const int64_t p = min(p_begin + kMqRows * st + srow, plast);
+    if constexpr (kFp4) {
+      if (stager) {
+        pre = *(const u32x4*)(kseq + p * (kIdxDim / 2) + 16 * piece);
+        pre_sc = *(const uint16_t*)(sseq + p * (kIdxDim / 16) + 2 * piece);
+      }
+    } else {
+      pre = *(const u32x4*)(kseq + p * kIdxDim + 16 * piece);
+    }
+  };
+  auto store_step = [&](int buf) {
+    unsigned char* d = stage[buf] + srow * kMqStride;
+    if constexpr (kFp4) {
+      if (stager) {
+        u32x4 o[4];
+        fp4_operands(pre, pre_sc, o);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) *(u32x4*)(d + 64 * piece + 16 * c) = o[c];
+      }
+    } else {
+      *(u32x4*)(d + 32 * piece) = e4m3x8_to_bf16x8(pre.x, pre.y);
+      *(u32x4*)(d + 32 * piece + 16) = e4m3x8_to_bf16x8(pre.z, pre.w);
+    }
+  };
+
+  // Scores of step s go to sstage[s & 1] and are written to global memory, coalesced, during step
+  // s+1 (by every thread: query tid / 64, two positions each), so the stores have a whole step to
+  // complete before the next wait on the staged key loads.
+  const int oq = tid >> 6, opos = 2 * (tid & 63);
+  const int oq_end = oq < nq ? min(p_begin + chunk, visible(oq)) : p_begin;
+  float* oscores = scores + (size_t)(b * T + t0 + (oq < nq ? oq : 0)) * n_max;
+  auto flush_scores = [&](int st) {
+    const int p = p_begin + kMqRows * st + opos;
+    const f32x2 v = *(const f32x2*)&sstage[st & 1][oq][opos];
+    if (p + 1 < oq_end) {
+      __builtin_nontemporal_store(v, (f32x2*)(oscores + p));
+    } else if (p < oq_end) {
+      __builtin_nontemporal_store(v.x, oscores + p);
+    }
+  };
+  uint32_t* wk = wkeys[wave];
+  if (nsteps > 0) {
+    load_step(0);
+    Ctx32 cx;
+    if (has_q) load_ctx32<kFp4>(cx, idx_q + (size_t)q * kIdxHeads * kIdxDim, head_w + (size_t)q * kIdxHeads);
+    store_step(0);
+    if (nsteps > 1) load_step(1);
+    __syncthreads();
+    const int r32 = lane & 31;
+    for (int st = 0; st < nsteps; ++st) {
+      if (st > 0) flush_scores(st - 1);
+      const unsigned char* d = stage[st & 1] + r32 * kMqStride;
+      float* so = sstage[st & 1][wave];
+      if (has_q && p_begin + kMqRows * st < p_end_q) {
+#pragma unroll 2
+        for (int m = 0; m < kMqRows / 32; ++m) {
+          const float sc = score32<kFp4>(cx, d + 32 * m * kMqStride);
+          const int pl = kMqRows * st + 32 * m + r32;               // position within the chunk
+          const bool valid = p_begin + pl < p_end_q;
+          const uint32_t key = max8_u32(valid ? score_key(sc) : 0u);
+          if (lane < 32) so[32 * m + r32] = sc;
+          if ((lane & 0x27) == 0 && pl < 8 * nblk_g) wk[pl >> 3] = key;   // lanes 0, 8, 16, 24
+        }
+      }
+      if (st + 1 < nsteps) {
+        store_step((st + 1) & 1);          // that buffer was last read before the previous barrier
+        if (st + 2 < nsteps) load_step(st + 2);
+      }
+      __syncthreads();
+    }
+    flush_scores(nsteps - 1);
+  }
+  if (!has_q) return;
+  // block keys and unit lists of this wave's query (its own LDS keys: no barrier needed)
+  const int nblk = (max(0, p_end_q - p_begin) + kBlock - 1) / kBlock;
+  if (blkkey) {
+    uint32_t* brow = blkkey + (size_t)q * nb_max + p_begin / kBlock;
+    for (int i = lane; i < nblk; i += 64) brow[i] = wk[i];
+  }
+  if (!lists) return;
+  // lane u < 16 keeps the five best ranking keys of unit u, inserted one block at a time (the
+  // keys are distinct, so the visiting order does not matter; it is rotated per lane to spread
+  // the LDS reads over the banks)
+  const int bpu = chunk / (kBlock * kScanUnitsPerWg);
+  if (lane < kScanUnitsPerWg) {
+    const int ub = lane * bpu;
+    uint64_t best[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
+    const int rot = lane % bpu;
+    for (int i = 0; i < bpu; ++i) {
+      const int o = i + rot < bpu ? i + rot : i + rot - bpu;
+      uint64_t x = ub + o < nblk ? rank_key(wk[ub + o], (uint32_t)(p_begin / kBlock + ub + o)) : 0ull;
+#pragma unroll
+      for (int r = 0; r < 5; ++r) {
+        const uint64_t hi = x > best[r] ? x : best[r];
+        x = x > best[r] ? best[r] : x;
+        best[r] = hi;
+      }
+    }
+    const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kScanUnitsPerWg + lane;
+    u32x4* lp = (u32x4*)(lists + unit * 4);
+    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
+    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
+    cuts[unit] = best[4];
+  }
+}
+
+bool scan_multi_query(int T, int n_max) { return T >= kScanMqMinT && n_max <= kMqMaxPositions; }
+
+int scan_mq_chunk(int n_max, int B, int T) {
+  // 4096 positions, or fewer (down to 1024) while the grid is under ~1024 workgroups
+  const long long groups = (long long)B * ((T + kMqQueries - 1) / kMqQueries);
+  int c = kMqMaxChunk;
+  while (c > 1024 && (long long)((n_max + c - 1) / c) * groups < 1024) c /= 2;
+  return c;
+}
+
 int scan_chunk_positions(int n_max, int queries) {
   // about one workgroup per CU (256) over all queries, at most 256 workgroups per query (the
   // pool takes at most 4096 units); multiples of 1024 positions, at most 8192 (LDS staging)
@@ -375,7 +630,18 @@ int scan_chunk_positions(int n_max, int queries) {
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                           uint64_t* cuts, int chunk, int n_wg, hipStream_t s) {
+                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, hipStream_t s) {
+  if (multi_query) {
+    const int groups = (Q / T) * ((T + kMqQueries - 1) / kMqQueries);
+    if (chunk % 1024 != 0 || chunk > kMqMaxChunk || Q % T != 0) return hipErrorInvalidValue;
+    if (idx_ks)
+      hipLaunchKernelGGL(k_idx_scan_mq<true>, dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
+                         idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
+    else
+      hipLaunchKernelGGL(k_idx_scan_mq<false>, dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
+                         idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
+    return hipGetLastError();
+  }
   if (idx_ks)
     hipLaunchKernelGGL(k_idx_scan<true>, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
                        idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,

@@ -88,6 +88,40 @@ def test_scan_every_fp4_key_code_and_scale_exact():
         assert np.array_equal(s[0, 1], np.maximum(-v, 0).astype(np.float32)), c
 
 
+@pytest.mark.parametrize("fp4", [False, True])
+@pytest.mark.parametrize("multi_query", [False, True])
+def test_scan_query_rounding_every_bf16(multi_query, fp4):
+    """The scan's E4M3 rounding of the query, for every bf16 pattern, in both scan kernels (one
+    query per workgroup, and 16 queries of a sequence per workgroup).  Key rows 2c / 2c+1 hold
+    +1 / -1 in channel c and query t weights only head t % 32, so its scores are
+    ReLU(+-q8[t % 32][c]) exactly: 512 queries reveal all 65536 rounded values."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits[np.isnan(F.bf16_value(bits))] = 0
+    vals = bits.reshape(16, 32, 128)
+    q = np.repeat(vals, 32, axis=0)                                  # query t: group t // 32
+    w = np.zeros((512, 32), np.float32)
+    w[np.arange(512), np.arange(512) % 32] = 1.0
+    ch = np.arange(128)
+    if fp4:
+        codes = np.zeros((256, 64), np.uint8)
+        codes[2 * ch, ch // 2] = np.uint8(0x2) << (4 * (ch & 1))     # E2M1 +1.0
+        codes[2 * ch + 1, ch // 2] = np.uint8(0xA) << (4 * (ch & 1)) # E2M1 -1.0
+        keys = {"idx_k_codes": codes, "idx_k_scales": np.full((256, 8), 0x38, np.uint8)}
+    else:
+        k8 = np.zeros((256, 128), np.uint8)
+        k8[2 * ch, ch], k8[2 * ch + 1, ch] = 0x38, 0xB8               # E4M3 +1.0 / -1.0
+        keys = {"idx_k": k8}
+    B, T = (1, 512) if multi_query else (512, 1)
+    inp = {kk: np.broadcast_to(v, (B,) + v.shape).copy() for kk, v in keys.items()}
+    inp.update(idx_q=q.reshape(B, T, 32, 128), head_w=w.reshape(B, T, 32),
+               n_visible=np.full((B, T), 256, np.int32))
+    s = G.gpu_index_scores(inp, B, T, 256).reshape(512, 256)
+    q8 = F.e4m3_value(O.quantize_query(bits)).reshape(16, 32, 128)
+    ref = q8[np.arange(512) // 32, np.arange(512) % 32]             # [512][128]
+    assert np.array_equal(s[:, 0::2], np.maximum(ref, 0).astype(np.float32))
+    assert np.array_equal(s[:, 1::2], np.maximum(-ref, 0).astype(np.float32))
+
+
 def test_fp4_dequant_every_code_and_scale_exact():
     # one main row per query, no window: the output is the dequantised row itself
     rows = 8
@@ -112,13 +146,28 @@ def test_fp4_dequant_every_code_and_scale_exact():
 
 # ------------------------------------------------------------------ indexer stages
 
+def ragged_visibility(B, T, N, seed):
+    """Per-query visible counts for multi-query scans: a causal ramp ending at N with a few
+    empty, tiny and chunk-straddling counts mixed in."""
+    rng = np.random.default_rng(seed)
+    nv = np.minimum(N, N - T + 1 + np.arange(T))[None, :].repeat(B, 0)
+    special = [0, 1, 7, 8, 17, 1023, 1024, 1025, 4095, 4097]
+    pick = rng.choice(B * T, size=min(len(special), B * T), replace=False)
+    nv.reshape(-1)[pick] = np.minimum(special[:len(pick)], N)
+    return nv.astype(np.int32)
+
+
 @pytest.mark.parametrize("fp4", [False, True])
-@pytest.mark.parametrize("B,T,N,nv", [(1, 1, 4096, None), (2, 3, 4093, [4093, 4000, 17, 0, 8, 1])])
+@pytest.mark.parametrize("B,T,N,nv", [(1, 1, 4096, None), (2, 3, 4093, [4093, 4000, 17, 0, 8, 1]),
+                                      (2, 37, 9000, "ragged")])
 def test_index_scores_parity(B, T, N, nv, fp4):
-    """Scores of every visible position, E4M3 keys and FP4 keys."""
+    """Scores of every visible position, E4M3 keys and FP4 keys; T = 37 runs the multi-query scan
+    (groups of 16, 16 and 5 queries) over ragged causal visibility."""
     w = small(B=B, T=T, N=N, seed=2000 + N, idx_k_fp4=fp4)
     inp = workloads.make_inputs(w, with_attention=False)
-    if nv is not None:
+    if isinstance(nv, str):
+        inp["n_visible"] = ragged_visibility(B, T, N, 7)
+    elif nv is not None:
         inp["n_visible"] = np.array(nv, np.int32).reshape(B, T)
     s = G.gpu_index_scores(inp, B, T, N)
     for b in range(B):
@@ -155,12 +204,15 @@ def check_full(w, inp, gpu, b, t):
     (4096, 64, 64, None),            # tiny decode workload
     (20003, 128, 256, None),         # ragged, several scan WGs
     (5000, 64, 512, [5000, 300, 511, 0]),   # n_vis < K, n_vis = 0, pool larger than nb
+    (9000, 128, 256, 20),            # multi-query scan: 20 queries, ragged causal visibility
 ])
 def test_index_full_parity(N, P, K, nv):
-    T = 1 if nv is None else len(nv)
+    T = 1 if nv is None else (nv if isinstance(nv, int) else len(nv))
     w = small(T=T, N=N, pool_blocks=P, top_k=K, seed=3000 + N)
     inp = workloads.make_inputs(w, with_attention=False)
-    if nv is not None:
+    if isinstance(nv, int):
+        inp["n_visible"] = ragged_visibility(1, T, N, 11)
+    elif nv is not None:
         inp["n_visible"] = np.array(nv, np.int32).reshape(1, T)
     gpu = G.gpu_index_full(inp, 1, T, N, P, K)
     for t in range(T):
