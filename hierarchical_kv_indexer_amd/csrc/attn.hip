@@ -118,7 +118,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   const uint8_t* scales_seq = kv_scales + (size_t)b * kv_rows * kKvScaleBytes;
   const uint8_t* swa_seq = swa + ((size_t)l * B + b) * (size_t)swa_rows * kKvDim;
 
-  const int my_row = tid >> 2, quarter = tid & 3;
+  // lane l of wave w takes row 16w + l % 16, quarter l / 16: the 16 lanes of each LDS write pass
+  // then hold 16 different rows (one 16-byte slot each), which keeps the dequantised stores free
+  // of bank conflicts (with four quarters of one row per pass they conflict four ways)
+  const int my_row = 16 * (tid >> 6) + (tid & 15), quarter = (tid >> 4) & 3;
   // main-row index of this thread's row in chunk c (-1: none), prefetched one chunk ahead
   auto row_index = [&](int c) {
     const int slot = s0 + c * kRows + my_row;
@@ -345,7 +348,9 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
   const uint8_t* scales_seq = kv_scales + (size_t)b * kv_rows * kKvScaleBytes;
   const uint8_t* swa_seq = swa + ((size_t)l * B + b) * (size_t)swa_rows * kKvDim;
 
-  const int my_row = tid >> 3, eighth = tid & 7;
+  // lane l of wave w takes row 8w + l % 8, eighth l / 8 (rows differ within each LDS write pass;
+  // see k_sparse_attn)
+  const int my_row = 8 * (tid >> 6) + (tid & 7), eighth = (tid >> 3) & 7;
   auto row_index = [&](int c) {
     const int slot = s0 + c * kRows + my_row;
     if (slot >= s1 || slot >= k) return -1;
