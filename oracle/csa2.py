@@ -16,6 +16,11 @@ Sources (DeepSeek-V4.1-Flash pages):
   [p5 2]    alphalab.site, section "2. CSA2": only the decoder's first Full layer builds the pool.
   [p2 5]    blog.4sapi.com, section 5 "FP4 KV": main KV in E2M1 with one E4M3 scale per 16
             channels, SWA KV in FP8.
+  [p2 3]    blog.4sapi.com, section 3 (how CSA2 is laid out): the encoder's layers 3-20 form three
+            groups of six, one Full and five Reuse layers, over a sequence compressed m = 2
+            tokens per entry.
+  [p3 modes] animattoys.com, the mode configuration: encoder groups of one Full then five Reuse
+            layers; decoder groups with Reindex layers.
 
 Readings where the pages are silent (each one is listed in the design notes):
   * indexer score  s[p] = sum_h w_h * ReLU(q_h . k_p), with one 128-dim key per position
@@ -42,7 +47,7 @@ from typing import Dict, List, Optional
 
 import numpy as np
 
-from .formats import bf16_value, e4m3_from_value, e4m3_value, kv_row_values
+from .formats import bf16_value, e4m3_from_value, e4m3_value, kv_quantize_rows, kv_row_values
 
 IDX_HEADS = 32
 IDX_DIM = 128
@@ -250,3 +255,57 @@ def query_chain(inp: Dict[str, np.ndarray], w, b: int, t: int,
     out["attn_out"] = o_all
     out["attn_lse"] = lse_all
     return out
+
+
+# ---------------------------------------------------------------- encoder prefill, chunk by chunk
+
+def visible_entries(p: int, m: int) -> int:
+    """Compressed entries visible to the token at absolute position p ([p2 3], m tokens per
+    entry): entry j covers tokens [j*m, (j+1)*m) and is visible once all of them are at or
+    before p, i.e. (j+1)*m <= p+1 (a reading: the pages do not say how a partial entry is
+    treated).  The count is floor((p+1)/m)."""
+    return (p + 1) // m
+
+
+def encoder_chunk(idx_k: np.ndarray, kv_codes: np.ndarray, kv_scales: np.ndarray,
+                  new_idx_k: Optional[np.ndarray], new_latent: Optional[np.ndarray],
+                  idx_q: np.ndarray, head_w: np.ndarray, q: np.ndarray, swa: np.ndarray,
+                  p0: int, m: int, top_k: int, window: int) -> Dict[str, np.ndarray]:
+    """One chunk of an encoder prefill through its CSA2 groups ([p2 3], [p3 modes]; [p5 2]: the
+    hierarchical indexer is decoder-only, so an encoder Full layer ranks every visible entry).
+
+    The chunk holds the tokens at positions p0 .. p0+T-1 of B sequences.  Per group g: the
+    entries the chunk completes (rows floor(p0/m) .. floor((p0+T)/m) - 1) are appended to the
+    group's caches (indexer keys rounded to E4M3, main KV quantised to FP4), in place; each
+    token's Full layer ranks the entries visible to it and keeps its Top-k; every layer of the
+    group (the Full layer and its Reuse layers) attends over that index set and its own window.
+
+    idx_k [G][B][k_rows][128] E4M3, kv_codes [G][B][k_rows][256], kv_scales [G][B][k_rows][32]
+    (caches, modified); new_idx_k [G][B][n_new][128] / new_latent [G][B][n_new][512] bf16 or
+    None; idx_q [G][B][T][32][128]; head_w [G][B][T][32]; q [G][Lg][B][T][H][512];
+    swa [G][Lg][B][hist+T][512] E4M3 with row r = token p0 - hist + r, hist = min(p0, window-1).
+    Returns out [G][Lg][B][T][H][512] float64 and topk [G][B][T][top_k]."""
+    G, B, T = idx_q.shape[:3]
+    Lg, H = q.shape[1], q.shape[4]
+    n_before, n_after = p0 // m, (p0 + T) // m
+    hist = min(p0, window - 1) if window > 0 else 0
+    assert swa.shape[3] == hist + T
+    scale = 1.0 / np.sqrt(KV_DIM)
+    out = np.zeros((G, Lg, B, T, H, KV_DIM))
+    topk = np.full((G, B, T, top_k), -1, np.int32)
+    for g in range(G):
+        for b in range(B):
+            if new_idx_k is not None:
+                idx_k[g, b, n_before:n_after] = e4m3_from_value(bf16_value(new_idx_k[g, b]))
+            if new_latent is not None:
+                kv_codes[g, b, n_before:n_after], kv_scales[g, b, n_before:n_after] = \
+                    kv_quantize_rows(new_latent[g, b])
+            for t in range(T):
+                n_vis = visible_entries(p0 + t, m)
+                f = full_layer(idx_k[g, b], idx_q[g, b, t], head_w[g, b, t], n_vis, 8, 0, top_k)
+                topk[g, b, t] = f["topk"]
+                for l in range(Lg):
+                    rows = attention_rows(kv_codes[g, b], kv_scales[g, b], f["topk"], swa[g, l, b],
+                                          hist + t + 1, window)
+                    out[g, l, b, t] = attention(q[g, l, b, t], rows, scale)[0]
+    return {"out": out, "topk": topk}

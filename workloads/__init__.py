@@ -314,6 +314,115 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Dict[str, np.ndarra
     return d
 
 
+# ---------------------------------------------------------------- encoder prefill
+
+ENC_STREAMS = ("enc_k", "enc_latent", "enc_idx_q", "enc_w", "enc_q", "enc_swa",
+               "enc_cache_k", "enc_cache_codes", "enc_cache_scales")
+
+
+@dataclasses.dataclass(frozen=True)
+class EncoderPrefill:
+    """A prompt run through the encoder's CSA2 groups in chunks of T tokens (G groups of one
+    Full layer and layers-1 Reuse layers, m tokens per compressed entry).  The measured chunk
+    is the last one: tokens prompt - T .. prompt - 1."""
+    name: str
+    seed: int
+    B: int
+    G: int
+    layers: int
+    H: int
+    prompt: int
+    T: int
+    m: int = 2
+    top_k: int = 512
+    swa_window: int = 128
+
+    @property
+    def k_rows(self) -> int:
+        return self.prompt // self.m
+
+    @property
+    def p0(self) -> int:
+        return self.prompt - self.T
+
+    def hist(self, p0: int) -> int:
+        return min(p0, self.swa_window - 1) if self.swa_window > 0 else 0
+
+
+ENCODER_WORKLOADS: Dict[str, EncoderPrefill] = {
+    # the last 256-token chunk of a 1M-token prompt: 3 groups x (Full + 5 Reuse), 512K entries
+    "encoder_1m": EncoderPrefill("encoder_1m", 1007, B=1, G=3, layers=6, H=64, prompt=1 << 20, T=256),
+}
+
+
+def _enc_gens(seed: int):
+    ss = np.random.SeedSequence(seed)
+    return dict(zip(ENC_STREAMS, (np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(len(ENC_STREAMS)))))
+
+
+def make_encoder_prompt(w: EncoderPrefill) -> Dict[str, np.ndarray]:
+    """Every token of the prompt, for chunk-by-chunk runs from an empty cache:
+    new_idx_k [G][B][n][128] and new_latent [G][B][n][512] bf16 (n = prompt // m entries, N(0,1)),
+    idx_q [G][B][P][32][128] bf16, head_w [G][B][P][32] U(0,1), q [G][layers][B][P][H][512] bf16,
+    swa [G][layers][B][P][512] E4M3 (row = token)."""
+    g = _enc_gens(w.seed)
+    G, B, P, L, H = w.G, w.B, w.prompt, w.layers, w.H
+    n = P // w.m
+    d: Dict[str, np.ndarray] = {}
+    d["new_idx_k"] = to_bf16_bits(draw_normal_f32(g["enc_k"], (G, B, n, IDX_DIM)))
+    d["new_latent"] = to_bf16_bits(draw_normal_f32(g["enc_latent"], (G, B, n, KV_DIM)))
+    d["idx_q"] = to_bf16_bits(draw_normal_f32(g["enc_idx_q"], (G, B, P, IDX_HEADS, IDX_DIM)))
+    d["head_w"] = g["enc_w"].random(size=(G, B, P, IDX_HEADS), dtype=np.float32)
+    d["q"] = to_bf16_bits(draw_normal_f32(g["enc_q"], (G, L, B, P, H, KV_DIM)))
+    d["swa"] = to_e4m3_bytes(draw_normal_f32(g["enc_swa"], (G, L, B, P, KV_DIM)))
+    return d
+
+
+def encoder_chunk_args(w: EncoderPrefill, prompt: Dict[str, np.ndarray], p0: int, T: int) -> Dict[str, np.ndarray]:
+    """The arguments of the chunk p0 .. p0+T-1 sliced from make_encoder_prompt's arrays."""
+    n0, n1 = p0 // w.m, (p0 + T) // w.m
+    h = w.hist(p0)
+    return {"new_idx_k": prompt["new_idx_k"][:, :, n0:n1], "new_latent": prompt["new_latent"][:, :, n0:n1],
+            "idx_q": prompt["idx_q"][:, :, p0:p0 + T], "head_w": prompt["head_w"][:, :, p0:p0 + T],
+            "q": prompt["q"][:, :, :, p0:p0 + T], "swa": prompt["swa"][:, :, :, p0 - h:p0 + T]}
+
+
+def make_encoder_chunk(w: EncoderPrefill) -> Dict[str, np.ndarray]:
+    """The last chunk of the prompt with the caches already holding every earlier entry, drawn
+    directly in their storage formats (indexer keys N(0,1) -> E4M3; main KV E2M1 codes and
+    U(0.5,2) -> E4M3 scales as in make_inputs): idx_k [G][B][k_rows][128], kv_codes
+    [G][B][k_rows][256], kv_scales [G][B][k_rows][32] (rows at or beyond floor(p0/m) zero), and
+    the chunk's arguments as encoder_chunk_args gives them."""
+    g = _enc_gens(w.seed)
+    G, B, L, H, T, p0 = w.G, w.B, w.layers, w.H, w.T, w.p0
+    n0, n1 = p0 // w.m, (p0 + T) // w.m
+    h = w.hist(p0)
+    d: Dict[str, np.ndarray] = {}
+    d["idx_k"] = np.zeros((G, B, w.k_rows, IDX_DIM), np.uint8)
+    d["kv_codes"] = np.zeros((G, B, w.k_rows, KV_CODE_BYTES), np.uint8)
+    d["kv_scales"] = np.zeros((G, B, w.k_rows, KV_SCALE_BYTES), np.uint8)
+    chunk = 1 << 17
+    for gi in range(G):
+        for b in range(B):
+            for r0 in range(0, n0, chunk):
+                r1 = min(n0, r0 + chunk)
+                d["idx_k"][gi, b, r0:r1] = to_e4m3_bytes(draw_normal_f32(g["enc_cache_k"], (r1 - r0, IDX_DIM)))
+                d["kv_codes"][gi, b, r0:r1] = draw_kv_codes(g["enc_cache_codes"], r1 - r0)
+                d["kv_scales"][gi, b, r0:r1] = to_e4m3_bytes(
+                    g["enc_cache_scales"].uniform(0.5, 2.0, size=(r1 - r0, KV_SCALE_BYTES)).astype(np.float32))
+    d["new_idx_k"] = to_bf16_bits(draw_normal_f32(g["enc_k"], (G, B, n1 - n0, IDX_DIM)))
+    d["new_latent"] = to_bf16_bits(draw_normal_f32(g["enc_latent"], (G, B, n1 - n0, KV_DIM)))
+    d["idx_q"] = to_bf16_bits(draw_normal_f32(g["enc_idx_q"], (G, B, T, IDX_HEADS, IDX_DIM)))
+    d["head_w"] = g["enc_w"].random(size=(G, B, T, IDX_HEADS), dtype=np.float32)
+    q = np.empty((G, L, B, T, H, KV_DIM), np.uint16)
+    for gi in range(G):
+        for l in range(L):
+            q[gi, l] = to_bf16_bits(draw_normal_f32(g["enc_q"], (B, T, H, KV_DIM)))
+    d["q"] = q
+    d["swa"] = to_e4m3_bytes(draw_normal_f32(g["enc_swa"], (G, L, B, h + T, KV_DIM)))
+    return d
+
+
 def small_variant(w: Workload, **changes) -> Workload:
     """A copy of a workload with some fields changed (for parity cases at reduced size)."""
     return dataclasses.replace(w, **changes)
