@@ -41,6 +41,9 @@ EXPORTS = (
     ("csa2_sparse_attn_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
     ("csa2_sparse_attn", _I, (_P, _P, _I64, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F,
                               _P, _P, _P, _SZ, _P)),
+    ("csa2_encoder_chunk_workspace", _SZ, (_I, _I, _I64, _I, _I, _I, _I)),
+    ("csa2_encoder_chunk", _I, (_I, _I, _P, _P, _P, _P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I64, _I, _I,
+                                _I, _I, _F, _P, _P, _P, _SZ, _P)),
 )
 
 _lib = None
@@ -211,3 +214,19 @@ def csa2_sparse_attn(kv_codes, kv_scales, kv_rows_per_seq: int, q, idx_sets,
                                   _ptr(swa_kv), swa_rows, _ptr(swa_end), swa_window, L, B, T, H,
                                   top_k, softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
                                   ws_bytes, _stream(stream, kv_codes)))
+
+
+def csa2_encoder_chunk_workspace(B: int, T: int, k_rows: int, layers: int, H: int, top_k: int,
+                                 swa_window: int) -> int:
+    return lib().csa2_encoder_chunk_workspace(B, T, k_rows, layers, H, top_k, swa_window)
+
+
+def csa2_encoder_chunk(G: int, layers: int, new_idx_k, new_latent, idx_k, kv_codes, kv_scales,
+                       k_rows: int, idx_q, head_w, q, swa_kv, swa_rows: int, B: int, T: int, p0: int,
+                       m: int, H: int, top_k: int, swa_window: int, softmax_scale: float, out,
+                       topk_idx, workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().csa2_encoder_chunk(G, layers, _ptr(new_idx_k), _ptr(new_latent), _ptr(idx_k),
+                                    _ptr(kv_codes), _ptr(kv_scales), k_rows, _ptr(idx_q), _ptr(head_w),
+                                    _ptr(q), _ptr(swa_kv), swa_rows, B, T, p0, m, H, top_k, swa_window,
+                                    softmax_scale, _ptr(out), _ptr(topk_idx), _ptr(workspace), ws_bytes,
+                                    _stream(stream, idx_k)))

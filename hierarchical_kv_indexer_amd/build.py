@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ("scan.hip", "select.hip", "attn.hip", "kvquant.hip", "api.cpp")
+SOURCES = ("scan.hip", "select.hip", "attn.hip", "kvquant.hip", "encoder.hip", "api.cpp")
 ARCH = "gfx950"
 
 CFLAGS = [

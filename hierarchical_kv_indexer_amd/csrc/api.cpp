@@ -2,6 +2,7 @@
 // The operations and their readings are documented in include/csa2.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -525,6 +526,120 @@ csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, 
                                                       need ? workspace : nullptr, (hipStream_t)stream),
                              "sparse attention launch");
   return st == CSA2_OK ? ok() : st;
+}
+
+// ---------------------------------------------------------------------------- encoder chunk
+
+namespace {
+
+struct EncoderWs {
+  void* full;          // csa2_index_full workspace (no pool), sized for k_rows entries
+  size_t full_bytes;
+  int32_t* topk;       // [B][T][top_k] index set of the current group (when the caller keeps none)
+  int32_t* n_visible;  // [B][T]
+  int32_t* swa_end;    // [B][T]
+  void* attn;          // csa2_sparse_attn workspace
+  size_t attn_bytes;
+};
+
+size_t carve_encoder(void* ws, int B, int T, int64_t k_rows, int layers, int H, int top_k, int swa_window,
+                     EncoderWs* out) {
+  Carver c{(char*)ws};
+  EncoderWs w;
+  w.full_bytes = csa2_index_full_workspace(B, T, (int)k_rows, csa2::kBlock, 0, top_k);
+  w.full = c.take<char>(w.full_bytes);
+  w.topk = c.take<int32_t>((size_t)B * T * top_k);
+  w.n_visible = c.take<int32_t>((size_t)B * T);
+  w.swa_end = c.take<int32_t>((size_t)B * T);
+  w.attn_bytes = csa2_sparse_attn_workspace(layers, B, T, H, top_k, swa_window);
+  w.attn = c.take<char>(w.attn_bytes);
+  if (out) *out = w;
+  return c.off;
+}
+
+}  // namespace
+
+size_t csa2_encoder_chunk_workspace(int B, int T, int64_t k_rows, int layers, int H, int top_k, int swa_window) {
+  if (B < 1 || T < 1 || k_rows < 0 || k_rows > csa2::kMaxFullPositions || layers < 1 || layers > csa2::kMaxLayers ||
+      H < 16 || H % 16 != 0 || top_k < 1 || top_k > csa2::kMaxTopK || swa_window < 0)
+    return 0;
+  return carve_encoder(nullptr, B, T, k_rows, layers, H, top_k, swa_window, nullptr);
+}
+
+csa2_status csa2_encoder_chunk(int G, int layers, const uint16_t* new_idx_k, const uint16_t* new_latent,
+                               uint8_t* idx_k, uint8_t* kv_codes, uint8_t* kv_scales, int64_t k_rows,
+                               const uint16_t* idx_q, const float* head_w, const uint16_t* q,
+                               const uint8_t* swa_kv, int swa_rows, int B, int T, int64_t p0, int m, int H,
+                               int top_k, int swa_window, float softmax_scale, uint16_t* out, int32_t* topk_idx,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  REQUIRE(G >= 1, CSA2_ERR_INVALID_ARG, "G must be >= 1");
+  REQUIRE(layers >= 1 && layers <= csa2::kMaxLayers, CSA2_ERR_UNSUPPORTED, "layers must be in [1, %d]",
+          csa2::kMaxLayers);
+  REQUIRE(B >= 1 && T >= 1, CSA2_ERR_INVALID_ARG, "B and T must be >= 1");
+  REQUIRE((int64_t)B * T <= 65535 && (int64_t)layers * B * T <= 65535, CSA2_ERR_UNSUPPORTED,
+          "B*T and layers*B*T must be <= 65535");
+  REQUIRE(m >= 1, CSA2_ERR_INVALID_ARG, "m must be >= 1");
+  REQUIRE(p0 >= 0, CSA2_ERR_INVALID_ARG, "p0 must be >= 0");
+  REQUIRE(swa_window >= 0 && swa_window <= 4096, CSA2_ERR_UNSUPPORTED, "swa_window must be in [0, 4096]");
+  REQUIRE(k_rows >= 1 && k_rows <= csa2::kMaxFullPositions, CSA2_ERR_UNSUPPORTED, "k_rows must be in [1, %d]",
+          csa2::kMaxFullPositions);
+  const int64_t n_before = p0 / m, n_after = (p0 + T) / m;
+  REQUIRE(n_after <= k_rows, CSA2_ERR_INVALID_ARG, "the chunk completes entries up to %lld > k_rows %lld",
+          (long long)n_after, (long long)k_rows);
+  const int hist = (int)std::min<int64_t>(p0, swa_window > 0 ? swa_window - 1 : 0);
+  REQUIRE(swa_rows == hist + T, CSA2_ERR_INVALID_ARG, "swa_rows must be min(p0, swa_window - 1) + T = %d (got %d)",
+          hist + T, swa_rows);
+  REQUIRE_PTR(idx_k);
+  REQUIRE_PTR(kv_codes);
+  REQUIRE_PTR(kv_scales);
+  REQUIRE_PTR(swa_kv);
+  REQUIRE(new_latent == nullptr || aligned16(new_latent), CSA2_ERR_INVALID_ARG, "new_latent must be 16-byte aligned");
+  const size_t need = carve_encoder(nullptr, B, T, k_rows, layers, H, top_k, swa_window, nullptr);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", need, ws_bytes);
+  EncoderWs w;
+  carve_encoder(workspace, B, T, k_rows, layers, H, top_k, swa_window, &w);
+  hipStream_t s = (hipStream_t)stream;
+  csa2_status st = hip_check(csa2::launch_causal_visibility(B, T, p0, m, hist, w.n_visible, w.swa_end, s),
+                             "visibility launch");
+  if (st != CSA2_OK) return st;
+  const int64_t n_new = n_after - n_before;
+  int32_t layer_set[csa2::kMaxLayers] = {0};
+  for (int g = 0; g < G; ++g) {
+    const size_t gb = (size_t)g * B;
+    for (int b = 0; b < B && n_new > 0; ++b) {
+      const size_t row0 = (gb + b) * (size_t)k_rows + (size_t)n_before;   // first appended cache row
+      const size_t src = (gb + b) * (size_t)n_new;                          // its entry in the new arrays
+      if (new_idx_k) {
+        st = hip_check(csa2::launch_quantize_query(new_idx_k + src * csa2::kIdxDim, idx_k + row0 * csa2::kIdxDim,
+                                                   n_new * csa2::kIdxDim, s),
+                       "indexer-key append launch");
+        if (st != CSA2_OK) return st;
+      }
+      if (new_latent) {
+        st = hip_check(csa2::launch_quantize_kv(new_latent + src * csa2::kKvDim, n_new,
+                                                kv_codes + row0 * csa2::kKvCodeBytes,
+                                                kv_scales + row0 * csa2::kKvScaleBytes, s),
+                       "main-KV append launch");
+        if (st != CSA2_OK) return st;
+      }
+    }
+    int32_t* topk = topk_idx ? topk_idx + gb * T * top_k : w.topk;
+    st = csa2_index_full(idx_k + gb * (size_t)k_rows * csa2::kIdxDim, nullptr, k_rows,
+                         idx_q ? idx_q + gb * T * csa2::kIdxHeads * csa2::kIdxDim : nullptr,
+                         head_w ? head_w + gb * T * csa2::kIdxHeads : nullptr, w.n_visible, B, T, (int)n_after,
+                         csa2::kBlock, 0, top_k, nullptr, nullptr, topk, nullptr, w.full, w.full_bytes, stream);
+    if (st != CSA2_OK) return st;
+    const size_t lb = (size_t)g * layers * B;
+    st = csa2_sparse_attn(kv_codes + gb * (size_t)k_rows * csa2::kKvCodeBytes,
+                          kv_scales + gb * (size_t)k_rows * csa2::kKvScaleBytes, k_rows,
+                          q ? q + lb * T * H * csa2::kKvDim : nullptr, topk, layer_set, 1,
+                          swa_kv + lb * (size_t)swa_rows * csa2::kKvDim, swa_rows, w.swa_end, swa_window, layers, B,
+                          T, H, top_k, softmax_scale, out ? out + lb * T * H * csa2::kKvDim : nullptr, nullptr,
+                          w.attn_bytes ? w.attn : nullptr, w.attn_bytes, stream);
+    if (st != CSA2_OK) return st;
+  }
+  return ok();
 }
 
 }  // extern "C"

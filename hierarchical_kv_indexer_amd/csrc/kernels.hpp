@@ -59,6 +59,11 @@ struct TopkJob {
 hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
                        const TopkJob& a, const TopkJob& b, hipStream_t s);
 
+// encoder.hip
+// n_visible[b][t] = floor((p0 + t + 1) / m), swa_end[b][t] = hist + t + 1.
+hipError_t launch_causal_visibility(int B, int T, int64_t p0, int m, int hist, int32_t* n_visible,
+                                    int32_t* swa_end, hipStream_t s);
+
 // kvquant.hip
 hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, uint8_t* codes, uint8_t* scales, hipStream_t s);
 

@@ -221,6 +221,43 @@ csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, 
                              int L, int B, int T, int H, int top_k, float softmax_scale,
                              uint16_t* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* One chunk of an encoder prefill through the encoder's CSA2 groups (blog.4sapi.com sec.3, the
+ * encoder's layers 3-20: three groups of six, one Full layer and five Reuse layers, over a
+ * sequence compressed m = 2 tokens per entry; animattoys.com, the mode configuration of the
+ * encoder and decoder; alphalab.site sec."2. CSA2": the hierarchical indexer is decoder-only, so
+ * an encoder Full layer ranks every visible entry).  The chunk holds the tokens at positions
+ * p0 .. p0+T-1 of B sequences.  For each group g in turn it
+ *   1. appends the entries the chunk completes, cache rows [floor(p0/m), floor((p0+T)/m)): the
+ *      indexer keys rounded to E4M3 (as csa2_quantize_query) and the main KV quantised to FP4 (as
+ *      csa2_quantize_kv_fp4);
+ *   2. runs the Full layer: token t scores the floor((p0+t+1)/m) entries visible to it (an entry
+ *      is visible once all m of its tokens are at or before the token) and keeps its Top-top_k,
+ *      as csa2_index_full with pool_blocks == 0;
+ *   3. runs the attention of the group's `layers` layers, which all use that index set (the Full
+ *      layer and its Reuse layers), each with its own sliding window, as csa2_sparse_attn.
+ * Arguments (n_new = floor((p0+T)/m) - floor(p0/m) entries per sequence and group):
+ *   new_idx_k   [G][B][n_new][128] bf16 new indexer-key entries, or NULL (caches already hold them)
+ *   new_latent  [G][B][n_new][512] bf16 new main-KV entries (rotated), 16-byte aligned, or NULL
+ *   idx_k       [G][B][k_rows][128] E4M3 indexer-key caches, appended in place
+ *   kv_codes    [G][B][k_rows][256], kv_scales [G][B][k_rows][32] main-KV caches, appended in place
+ *   idx_q       [G][B][T][32][128] bf16 indexer queries;  head_w [G][B][T][32] float
+ *   q           [G][layers][B][T][H][512] bf16 attention queries
+ *   swa_kv      [G][layers][B][swa_rows][512] E4M3 window rows: row r holds the token at position
+ *               p0 - hist + r, hist = min(p0, swa_window - 1), swa_rows = hist + T
+ *   out         [G][layers][B][T][H][512] bf16 out
+ *   topk_idx    [G][B][T][top_k] int32 out (each group's index set, ascending, -1 padded) or NULL
+ *   workspace   device scratch of csa2_encoder_chunk_workspace(...) bytes, 16-byte aligned
+ * Work is enqueued on `stream` in group order; the caches must not be read or written by other
+ * work in the meantime.  Supported: m >= 1, floor((p0+T)/m) <= k_rows <= 2^21,
+ * layers*B*T <= 65535, H % 16 == 0, 1 <= top_k <= 2048, 0 <= swa_window <= 4096. */
+size_t csa2_encoder_chunk_workspace(int B, int T, int64_t k_rows, int layers, int H, int top_k, int swa_window);
+csa2_status csa2_encoder_chunk(int G, int layers, const uint16_t* new_idx_k, const uint16_t* new_latent,
+                               uint8_t* idx_k, uint8_t* kv_codes, uint8_t* kv_scales, int64_t k_rows,
+                               const uint16_t* idx_q, const float* head_w, const uint16_t* q,
+                               const uint8_t* swa_kv, int swa_rows, int B, int T, int64_t p0, int m, int H,
+                               int top_k, int swa_window, float softmax_scale, uint16_t* out, int32_t* topk_idx,
+                               void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,3 +212,38 @@ def assert_attention_close(o_gpu_bits, o_ref, what=""):
         worst = max(worst, rel)
         assert rel <= ATTN_REL, f"{what}: head {h} max rel err {rel:.3g}"
     return worst
+
+
+# ---------------------------------------------------------------- encoder prefill
+
+class GpuEncoder:
+    """Device caches and workspace of an encoder prefill run chunk by chunk through
+    csa2_encoder_chunk."""
+
+    def __init__(self, w, max_T: int):
+        self.w = w
+        n = max(w.prompt // w.m, 1)
+        self.idx_k = torch.zeros((w.G, w.B, n, 128), dtype=torch.uint8, device=DEV)
+        self.kv_codes = torch.zeros((w.G, w.B, n, 256), dtype=torch.uint8, device=DEV)
+        self.kv_scales = torch.zeros((w.G, w.B, n, 32), dtype=torch.uint8, device=DEV)
+        self.k_rows = n
+        self.ws_bytes = H.csa2_encoder_chunk_workspace(w.B, max_T, n, w.layers, w.H, w.top_k, w.swa_window)
+        self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=DEV)
+
+    def load_caches(self, idx_k, kv_codes, kv_scales):
+        self.idx_k.copy_(torch.from_numpy(idx_k))
+        self.kv_codes.copy_(torch.from_numpy(kv_codes))
+        self.kv_scales.copy_(torch.from_numpy(kv_scales))
+
+    def chunk(self, a: Dict[str, np.ndarray], p0: int, T: int):
+        """Runs one chunk; returns (out [G][layers][B][T][H][512] bf16 bits, topk [G][B][T][k])."""
+        w = self.w
+        out = empty((w.G, w.layers, w.B, T, w.H, 512), torch.int16)
+        topk = empty((w.G, w.B, T, w.top_k), torch.int32)
+        nn = a["new_idx_k"].shape[2]
+        H.csa2_encoder_chunk(w.G, w.layers, dev(a["new_idx_k"]) if nn else None,
+                             dev(a["new_latent"]) if nn else None, self.idx_k, self.kv_codes,
+                             self.kv_scales, self.k_rows, dev(a["idx_q"]), dev(a["head_w"]), dev(a["q"]),
+                             dev(a["swa"]), a["swa"].shape[3], w.B, T, p0, w.m, w.H, w.top_k,
+                             w.swa_window, 1.0 / math.sqrt(512), out, topk, self.ws, self.ws_bytes)
+        return host(out), host(topk)

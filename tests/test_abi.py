@@ -129,3 +129,30 @@ def test_quantize_kv_rejects(H):
     expect(H, 1, lambda: H.csa2_quantize_kv_fp4(FAKE, -1, FAKE, FAKE))
     expect(H, 1, lambda: H.csa2_quantize_kv_fp4(FAKE, 4, None, FAKE))
     expect(H, 1, lambda: H.csa2_quantize_kv_fp4(FAKE, 4, FAKE, FAKE + 8))  # misaligned scales
+
+
+def test_encoder_chunk_rejects(H):
+    assert H.csa2_encoder_chunk_workspace(1, 256, 1 << 19, 6, 64, 512, 128) > 256 * (1 << 19) * 4
+    assert H.csa2_encoder_chunk_workspace(1, 256, 1 << 22, 6, 64, 512, 128) == 0      # k_rows beyond 2^21
+    assert H.csa2_encoder_chunk_workspace(1, 256, 1 << 19, 6, 24, 512, 128) == 0      # H % 16 != 0
+    ws = H.csa2_encoder_chunk_workspace(1, 128, 4096, 6, 64, 512, 128)
+    # G, layers, new_idx_k, new_latent, idx_k, kv_codes, kv_scales, k_rows, idx_q, head_w, q, swa, swa_rows,
+    # B, T, p0, m, H, top_k, window, scale, out, topk, ws, ws_bytes
+    ok = [3, 6, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, 127 + 128, 1, 128, 1024, 2, 64, 512,
+          128, 0.044, FAKE, None, FAKE, ws]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lambda: H.csa2_encoder_chunk(*a)
+    expect(H, 1, call(0, 0))                    # G
+    expect(H, 2, call(1, 65))                   # layers
+    expect(H, 1, call(16, 0))                   # m
+    expect(H, 1, call(15, 8192))                # entries beyond k_rows
+    expect(H, 1, call(12, 128))                 # swa_rows != min(p0, window - 1) + T
+    expect(H, 1, call(4, None))                 # idx_k
+    expect(H, 1, call(3, FAKE + 2))             # new_latent alignment
+    expect(H, 3, call(24, 64))                  # workspace
+    a = list(ok)
+    a[15], a[12] = 0, 128                       # first chunk: no history rows
+    a[24] = 8
+    expect(H, 3, lambda: H.csa2_encoder_chunk(*a))
