@@ -266,6 +266,137 @@ def bench_quantize_kv(args) -> int:
     return 0
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 matrix peak
+
+
+def bench_encoder(args, w) -> int:
+    """One chunk of an encoder prefill (csa2_encoder_chunk): the last `T` tokens of a prompt of
+    `prompt` tokens through `G` groups of one Full and `layers`-1 Reuse layers.  The caches
+    already hold every earlier entry; each step appends the chunk's entries again (the same
+    bytes) and recomputes the chunk.  The roofline is that of the Full scan (the multi-query
+    k_idx_scan_mq, bf16 MFMA), timed on its own through csa2_index_scan with the arguments the
+    chunk entry passes it: FLOPs per launch = 8192 x the visible entries of every token."""
+    import numpy as np
+    import torch
+
+    import hierarchical_kv_indexer_amd as H
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H.lib()
+    t_gen = time.perf_counter()
+    inp = workloads.make_encoder_chunk(w)
+    log(f"[bench] generated {w.name} inputs in {time.perf_counter() - t_gen:.1f} s")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    G_, L, B, T, Hh, K, m, p0 = w.G, w.layers, w.B, w.T, w.H, w.top_k, w.m, w.p0
+    d = {k: up(v) for k, v in inp.items()}
+    inp = None
+    swa_rows = w.hist(p0) + T
+    out = torch.empty((G_, L, B, T, Hh, 512), dtype=torch.int16, device=dev)
+    ws_bytes = H.csa2_encoder_chunk_workspace(B, T, w.k_rows, L, Hh, K, w.swa_window)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(512)
+    stream = torch.cuda.Stream()
+
+    def step():
+        H.csa2_encoder_chunk(G_, L, d["new_idx_k"], d["new_latent"], d["idx_k"], d["kv_codes"], d["kv_scales"],
+                             w.k_rows, d["idx_q"], d["head_w"], d["q"], d["swa"], swa_rows, B, T, p0, m, Hh, K,
+                             w.swa_window, scale, out, None, ws, ws_bytes, stream)
+
+    n_after = (p0 + T) // m
+    nv = np.array([(p0 + t + 1) // m for t in range(T)], np.int32)
+    nv_dev = up(np.broadcast_to(nv, (B, T)).copy())
+    fws_bytes = H.csa2_index_full_workspace(B, T, n_after, 8, 0, K)
+    fws = torch.empty((fws_bytes,), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # the Full scan of group 0 on its own, as the chunk entry launches it
+        n_scan = max(3, min(20, args.steps))
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_scan)]
+        for i in range(n_scan):
+            ev[i][0].record(stream)
+            H.csa2_index_scan(d["idx_k"][0], None, w.k_rows, d["idx_q"][0], d["head_w"][0], nv_dev, B, T, n_after,
+                              8, 0, K, fws, fws_bytes, stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+    wall = t1 - t0
+    scan_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 8192.0 * B * float(nv.astype(np.int64).sum())
+    achieved = flops / (scan_ms * 1e-3) / 1e12
+    step_flops = G_ * flops + G_ * L * B * T * Hh * 4.0 * 512 * (K + w.swa_window)
+    log(f"[bench] {args.steps} steps in {wall:.3f} s: {wall * 1e3 / args.steps:.3f} ms/step; Full scan "
+        f"{scan_ms * 1e3:.1f} us ({achieved:.0f} TFLOP/s bf16); whole chunk {step_flops * args.steps / wall / 1e12:.0f} "
+        f"TFLOP/s")
+    res = {
+        "metric": "encoder prefill tokens/s (chunk at the end of a long prompt, Full + Reuse groups)",
+        "value": round(args.steps * B * T / wall, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "prompt_tokens": w.prompt, "chunk_tokens": T, "m": m,
+                   "visible_entries_last_token": int(nv[-1]), "groups": G_, "layers_per_group": L,
+                   "attention_heads": Hh, "indexer_heads": 32, "indexer_dim": 128, "top_k": K,
+                   "swa_window": w.swa_window, "step_flops": step_flops},
+        "roofline": {"bound": "mfma", "kernel": "k_idx_scan_mq", "achieved": round(achieved, 1),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "algorithmic_flops_per_launch": flops, "avg_launch_us": round(scan_ms * 1e3, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_encoder(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline_encoder(w, seconds: float):
+    """The oracle, as it stands, on this host: the measured chunk's tokens through the first group
+    (Full layer over every visible entry, then the group's attention layers), one token after the
+    other as one-token chunks (each appends the entries it completes); the rate is divided by the
+    number of groups.  Inputs come from the same generator (group 0's draws)."""
+    import dataclasses
+
+    import workloads
+    from oracle import csa2 as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    inp = workloads.make_encoder_chunk(dataclasses.replace(w, G=1))
+    h, n0 = w.hist(w.p0), w.p0 // w.m
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        p = w.p0 + n
+        e0, e1 = p // w.m - n0, (p + 1) // w.m - n0          # entries this token completes
+        hp = w.hist(p)
+        O.encoder_chunk(inp["idx_k"], inp["kv_codes"], inp["kv_scales"], inp["new_idx_k"][:, :, e0:e1],
+                        inp["new_latent"][:, :, e0:e1], inp["idx_q"][:, :, n:n + 1], inp["head_w"][:, :, n:n + 1],
+                        inp["q"][:, :, :, n:n + 1], inp["swa"][:, :, :, h + n - hp:h + n + 1], p, w.m, w.top_k,
+                        w.swa_window)
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and n >= 2) or n >= min(w.T, 50):
+            break
+    return {"value": n / el / w.G, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} tokens of the chunk through 1 of {w.G} groups (Full layer over "
+                      f"{(w.p0 + 1) // w.m}+ entries, {w.layers} attention layers), {el:.1f} s; rate / {w.G}"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +425,9 @@ def main() -> int:
 
     if args.kernel == "quantize_kv":
         return bench_quantize_kv(args)
+    import workloads
+    if args.workload in workloads.ENCODER_WORKLOADS:
+        return bench_encoder(args, workloads.ENCODER_WORKLOADS[args.workload])
 
     import numpy as np
     import torch

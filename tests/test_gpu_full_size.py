@@ -7,7 +7,11 @@ oracle checks sampled queries.
   decode_b8_128k   batch 8, 128K entries each, Full + 4 Reindex + 5 Reuse, 64 heads
   reindex_pool_256k  64 queries with their own 16384-position pools over a 256K context
   prefill_4k_64k   4096 causal queries over 32768 entries, Full + 5 Reuse, 64 heads
+  encoder_1m       the last 256-token chunk of a 1M-token prompt (512K entries) through 3 encoder
+                   groups of Full + 5 Reuse, 64 heads (csa2_encoder_chunk)
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -92,3 +96,36 @@ def test_decode_1m_all_keys_equal():
     ri = G.gpu_reindex(inp, 1, 1, g["pool_pos"], g["pool_len"], w.top_k)
     for r in range(w.n_reindex):
         assert np.array_equal(ri["topk"][r, 0, 0], np.arange(w.top_k, dtype=np.int32))
+
+
+def test_encoder_1m_chunk_sampled():
+    """The encoder chunk at 1M tokens as the benchmark launches it: the appended cache rows equal
+    the oracle's quantisers' bytes, and sampled tokens' index sets and attention outputs (first
+    and last layer of every group) match the oracle over the oracle's own caches."""
+    from oracle import csa2 as O
+    from oracle import formats as F
+    w = workloads.ENCODER_WORKLOADS["encoder_1m"]
+    inp = workloads.make_encoder_chunk(w)
+    p0, T, m = w.p0, w.T, w.m
+    n0, n1 = p0 // m, (p0 + T) // m
+    gpu = G.GpuEncoder(w, T)
+    gpu.load_caches(inp["idx_k"], inp["kv_codes"], inp["kv_scales"])
+    out, topk = gpu.chunk(inp, p0, T)
+    # the oracle's caches: the generated rows plus the chunk's entries appended by its quantisers
+    idx_k, codes, scales = inp["idx_k"], inp["kv_codes"], inp["kv_scales"]
+    idx_k[:, :, n0:n1] = F.e4m3_from_value(F.bf16_value(inp["new_idx_k"]))
+    codes[:, :, n0:n1], scales[:, :, n0:n1] = F.kv_quantize_rows(inp["new_latent"])
+    assert np.array_equal(G.host(gpu.idx_k[:, :, n0:n1]), idx_k[:, :, n0:n1])
+    assert np.array_equal(G.host(gpu.kv_codes[:, :, n0:n1]), codes[:, :, n0:n1])
+    assert np.array_equal(G.host(gpu.kv_scales[:, :, n0:n1]), scales[:, :, n0:n1])
+    h = w.hist(p0)
+    for g, t in [(0, 0), (1, 127), (2, T - 1)]:
+        _announce(w.name, [(g, t)])
+        n_vis = O.visible_entries(p0 + t, m)
+        f = O.full_layer(idx_k[g, 0], inp["idx_q"][g, 0, t], inp["head_w"][g, 0, t], n_vis, 8, 0, w.top_k)
+        G.assert_topk_equiv(topk[g, 0, t], f["topk"], lambda p: f["scores"][p], f"encoder g{g} t{t}")
+        for l in (0, w.layers - 1):
+            rows = O.attention_rows(codes[g, 0], scales[g, 0], topk[g, 0, t], inp["swa"][g, l, 0], h + t + 1,
+                                    w.swa_window)
+            o, _ = O.attention(inp["q"][g, l, 0, t], rows, 1.0 / math.sqrt(512))
+            G.assert_attention_close(out[g, l, 0, t], o, f"encoder g{g} l{l} t{t}")
