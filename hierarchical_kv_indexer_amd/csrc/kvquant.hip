@@ -26,6 +26,8 @@
 // A thread converts whole 16-channel groups (32 bytes of bf16 in, 8 code bytes and one scale
 // byte out); consecutive threads take consecutive groups, so a wave reads two whole rows with
 // contiguous 16-byte loads.  The grid is capped and strides over the groups.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -106,6 +108,10 @@ hipError_t launch_quantize_kv(const uint16_t* x, int64_t rows, uint8_t* codes, u
   if (rows <= 0) return hipSuccess;
   const int64_t groups = rows * 32;
   int64_t blocks = (groups + kQuantThreads * 16 - 1) / (kQuantThreads * 16);   // >= 16 groups a thread
+  // short appends (a few hundred rows) are latency-bound: spread them to one group per thread
+  // over up to 256 workgroups instead of looping in a few
+  const int64_t spread = std::min<int64_t>(256, (groups + kQuantThreads - 1) / kQuantThreads);
+  if (blocks < spread) blocks = spread;
   if (blocks > 1024) blocks = 1024;         // 4 per CU: measured best between 256 and 8192
   hipLaunchKernelGGL(k_quantize_kv, dim3((unsigned)blocks), dim3(kQuantThreads), 0, s, x, rows, codes, scales);
   return hipGetLastError();
