@@ -397,6 +397,66 @@ def cpu_baseline_encoder(w, seconds: float):
                       f"{(w.p0 + 1) // w.m}+ entries, {w.layers} attention layers), {el:.1f} s; rate / {w.G}"}
 
 
+def study_hsi_recall(args) -> int:
+    """Recall study of the hierarchical indexer: on planted-needle contexts of 64K, 256K and 1M
+    positions (workloads.make_recall_context), the Full layer's pool of P blocks ranked by each
+    block score (max / sum / top-2 mean) and a Reindex layer's Top-512 inside that pool.  Reports,
+    per (context, P, block score): the share of each needle family in the Full Top-512 and in the
+    Reindex Top-512, and the share of the Reindex layer's dense Top-512 (over every position, no
+    pool) that its pool-restricted Top-512 keeps.  Prints one JSON line per configuration."""
+    import numpy as np
+    import torch
+
+    import hierarchical_kv_indexer_amd as H
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H.lib()
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    K = 512
+    modes = {0: "max", 1: "sum", 2: "top2"}
+    rows = []
+    for N, seed in ((1 << 16, 4101), (1 << 18, 4102), (1 << 20, 4103)):
+        ctx = workloads.make_recall_context(N, seed)
+        k, q, hw, nv = up(ctx["idx_k"]), up(ctx["idx_q"]), up(ctx["head_w"]), up(ctx["n_visible"])
+        rq, rw = up(ctx["ri_q"]), up(ctx["ri_w"])
+        # the Reindex layer's dense Top-512 (no pool)
+        wsd = H.csa2_index_full_workspace(1, 1, N, 8, 0, K)
+        ws = torch.empty((wsd,), dtype=torch.uint8, device=dev)
+        dense = torch.empty((1, 1, K), dtype=torch.int32, device=dev)
+        H.csa2_index_full(k, None, N, rq[0], rw[0], nv, 1, 1, N, 8, 0, K, None, None, dense, None, ws, wsd)
+        dense_set = set(dense.cpu().numpy().reshape(-1).tolist()) - {-1}
+        for P in (256, 512, 1024, 2048):
+            wsb = H.csa2_index_chain_workspace(1, 1, N, 8, P, K, 1)
+            ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+            pool_pos = torch.empty((1, 1, P * 8), dtype=torch.int32, device=dev)
+            pool_len = torch.empty((1, 1), dtype=torch.int32, device=dev)
+            ftop = torch.empty((1, 1, K), dtype=torch.int32, device=dev)
+            rtop = torch.empty((1, 1, 1, K), dtype=torch.int32, device=dev)
+            for bs, name in modes.items():
+                H.csa2_index_scan_blocks(k, None, N, q, hw, nv, 1, 1, N, 8, P, K, bs, ws, wsb)
+                H.csa2_index_select_reindex(k, None, N, nv, 1, 1, N, 8, P, K, rq, rw, 1, pool_pos, pool_len, ftop,
+                                            None, rtop, None, ws, wsb)
+                torch.cuda.synchronize()
+                f = ftop.cpu().numpy().reshape(-1)
+                r = rtop.cpu().numpy().reshape(-1)
+                row = {"context": N, "pool_blocks": P, "block_score": name,
+                       "full_topk": {fam: round(float(np.isin(pos, f).mean()), 4) for fam, pos in ctx["families"].items()},
+                       "reindex_topk": {fam: round(float(np.isin(pos, r).mean()), 4)
+                                        for fam, pos in ctx["families"].items()},
+                       "reindex_dense_kept": round(len(dense_set & set(r.tolist())) / max(1, len(dense_set)), 4)}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +474,8 @@ def main() -> int:
     ap.add_argument("--kernel", choices=("chain", "quantize_kv"), default="chain",
                     help="quantize_kv: time the FP4 main-KV quantiser alone")
     ap.add_argument("--rows", type=int, default=1 << 20, help="latent rows per quantiser launch")
+    ap.add_argument("--study", choices=("hsi_recall",), default=None,
+                    help="hsi_recall: recall of planted needles under block-score variants and pool sizes")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -425,6 +487,8 @@ def main() -> int:
 
     if args.kernel == "quantize_kv":
         return bench_quantize_kv(args)
+    if args.study == "hsi_recall":
+        return study_hsi_recall(args)
     import workloads
     if args.workload in workloads.ENCODER_WORKLOADS:
         return bench_encoder(args, workloads.ENCODER_WORKLOADS[args.workload])

@@ -27,6 +27,7 @@ EXPORTS = (
     ("csa2_index_scores", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
     ("csa2_index_full_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
     ("csa2_index_scan", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
+    ("csa2_index_scan_blocks", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
     ("csa2_index_pool", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
     ("csa2_index_topk", _I, (_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
     ("csa2_index_select", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P)),
@@ -135,6 +136,14 @@ def csa2_index_scan(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_v
                                  _ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k,
                                  _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
 
+
+
+def csa2_index_scan_blocks(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
+                           n_max: int, block_size: int, pool_blocks: int, top_k: int, block_score: int,
+                           workspace, ws_bytes: int, stream=None) -> None:
+    _check(lib().csa2_index_scan_blocks(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q),
+                                        _ptr(head_w), _ptr(n_visible), B, T, n_max, block_size, pool_blocks,
+                                        top_k, block_score, _ptr(workspace), ws_bytes, _stream(stream, idx_k)))
 
 def csa2_index_pool(n_visible, B: int, T: int, n_max: int, block_size: int, pool_blocks: int,
                     top_k: int, pool_pos, pool_len, workspace, ws_bytes: int, stream=None) -> None:

@@ -162,7 +162,7 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   const FullPlan p = plan_full(B, T, n_max, 1, 1);
   st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                        scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg, p.multi_query,
-                                       (hipStream_t)stream),
+                                       csa2::kBlockMax, (hipStream_t)stream),
                  "index scan launch");
   return st == CSA2_OK ? ok() : st;
 }
@@ -195,25 +195,43 @@ static csa2_status check_workspace(const FullPlan& p, int n_max, void* workspace
   return CSA2_OK;
 }
 
-csa2_status csa2_index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
-                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
-                            int block_size, int pool_blocks, int top_k, void* workspace, size_t ws_bytes,
-                            void* stream) {
+static csa2_status index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq,
+                              const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int B, int T,
+                              int n_max, int block_size, int pool_blocks, int top_k, int block_score,
+                              void* workspace, size_t ws_bytes, void* stream) {
   csa2_status st = check_index_common(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
   if (st != CSA2_OK) return st;
   if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
+  REQUIRE(block_score >= csa2::kBlockMax && block_score <= csa2::kBlockTop2, CSA2_ERR_INVALID_ARG,
+          "block_score must be 0 (max), 1 (sum) or 2 (top-2 mean); got %d", block_score);
   const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
   if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
   FullWs w;
   carve_full(workspace, p, n_max, &w);
   if (n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query,
-                                         (hipStream_t)stream),
+                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg,
+                                         p.multi_query, block_score, (hipStream_t)stream),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }
   return ok();
+}
+
+csa2_status csa2_index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
+                            const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
+                            int block_size, int pool_blocks, int top_k, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  return index_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size,
+                    pool_blocks, top_k, csa2::kBlockMax, workspace, ws_bytes, stream);
+}
+
+csa2_status csa2_index_scan_blocks(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq,
+                                   const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int B,
+                                   int T, int n_max, int block_size, int pool_blocks, int top_k, int block_score,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  return index_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size,
+                    pool_blocks, top_k, block_score, workspace, ws_bytes, stream);
 }
 
 static csa2_status check_pool_args(const FullPlan& p, int32_t* pool_pos, int32_t* pool_len) {
@@ -432,7 +450,8 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   hipStream_t s = (hipStream_t)stream;
   if (do_scan && n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query, s),
+                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query,
+                                         csa2::kBlockMax, s),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }

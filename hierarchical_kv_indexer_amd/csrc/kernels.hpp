@@ -16,6 +16,8 @@ struct LayerSets { int32_t set[kMaxLayers]; };
 // scan.hip
 hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hipStream_t s);
 int scan_chunk_positions(int n_max, int queries);
+// Block score of the pool (see block_key in scan.hip).
+constexpr int kBlockMax = 0, kBlockSum = 1, kBlockTop2 = 2;
 // Sequences with at least kScanMqMinT queries and at most kMqMaxPositions positions share key
 // tiles between 16 queries per workgroup (k_idx_scan_mq), in chunks of at most kMqMaxChunk.
 constexpr int kScanMqMinT = 8;
@@ -30,7 +32,7 @@ constexpr int kMaxFullPositions = 1 << 21;           // 256 chunks of 8192 per q
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, hipStream_t s);
+                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, hipStream_t s);
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
                            int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s);

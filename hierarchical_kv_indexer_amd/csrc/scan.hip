@@ -248,6 +248,48 @@ __device__ __forceinline__ void key_ctx(TileCtx& cx, const uint16_t* qlds, const
   else load_ctx(cx, qlds, w);
 }
 
+// ---------------------------------------------------------------------------- block scores
+
+// Block score variants for the candidate pool (the order key of one block of 8 positions, held by
+// an aligned group of 8 lanes, each with one position's score and whether it is visible):
+//   kBlockMax   the largest visible score (the pool's block score);
+//   kBlockSum   the sum of the visible scores (fp32, pairwise in a fixed order);
+//   kBlockTop2  the mean of the two largest visible scores (one visible score: that score).
+// A block with no visible position gets key 0.  Every lane of the group returns the same key.
+// Called by whole waves (the top-2 variant counts with ballots).
+__device__ __forceinline__ float max8_f32(float x) {
+  x = fmaxf(x, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(x))));    // quad_perm [1,0,3,2]
+  x = fmaxf(x, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(x))));    // quad_perm [2,3,0,1]
+  x = fmaxf(x, __uint_as_float(dpp_mov<0x141>(__float_as_uint(x))));   // row_half_mirror
+  return x;
+}
+__device__ __forceinline__ float sum8_f32(float x) {
+  x += __uint_as_float(dpp_mov<0xB1>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<0x4E>(__float_as_uint(x)));
+  x += __uint_as_float(dpp_mov<0x141>(__float_as_uint(x)));
+  return x;
+}
+template <int kBS>
+__device__ __forceinline__ uint32_t block_key(float sc, bool valid) {
+  if constexpr (kBS == kBlockMax) {
+    return max8_u32(valid ? score_key(sc) : 0u);
+  } else if constexpr (kBS == kBlockSum) {
+    const uint64_t group = 0xffull << (threadIdx.x & 56);
+    const bool any = (__ballot(valid) & group) != 0;
+    const float sum = sum8_f32(valid ? sc : 0.f);
+    return any ? score_key(sum) : 0u;
+  } else {
+    const uint64_t group = 0xffull << (threadIdx.x & 56);
+    const int nvalid = __popcll(__ballot(valid) & group);
+    const float x = valid ? sc : -INFINITY;
+    const float m1 = max8_f32(x);
+    const int n_m1 = __popcll(__ballot(valid && x == m1) & group);
+    const float second = max8_f32(x == m1 ? -INFINITY : x);
+    const float m2 = n_m1 >= 2 ? m1 : second;
+    return nvalid == 0 ? 0u : score_key(nvalid >= 2 ? (m1 + m2) * 0.5f : m1);
+  }
+}
+
 // ---------------------------------------------------------------------------- Full scan
 
 // Tiles per pipeline stage of a wave (6 FP4 tiles measured no faster than 3: the loop is bound by
@@ -283,7 +325,7 @@ __device__ __forceinline__ uint64_t wave_pop_best(uint32_t& key, uint32_t& blk) 
 // (score key << 32 | ~block): lists[q][unit][0..3] = the four best (0 = none) and
 // cuts[q][unit] = the fifth best (0 = none), so every block of the unit that is not listed
 // ranks at or below cuts[q][unit].  Requires chunk % 1024 == 0 and chunk <= 8192.
-template <bool kFp4>
+template <bool kFp4, int kBS>
 __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
     const uint16_t* __restrict__ idx_q,
@@ -346,7 +388,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
         if (t < ntiles) {
           const int tp = phys(t);
           const bool valid = 16 * tp + j < npos;
-          const uint32_t key = max8_u32(valid ? score_key(sc) : 0u);
+          const uint32_t key = block_key<kBS>(sc, valid);
           if (g == 0) sbuf[16 * tp + j] = sc;
           if ((lane & 0x37) == 0) wkeys[2 * tp + (lane >> 3)] = key;   // lanes 0, 8
         }
@@ -462,7 +504,7 @@ __device__ __forceinline__ float score32(const Ctx32& cx, const unsigned char* r
 // are then in flight.  Staging: E4M3, thread t converts bytes 16*(t%8) .. +15 of row t/8 (channels
 // 16*(t%8) .. +15); FP4 (threads below 512), the 16 code bytes of row t/4 holding channels
 // 32*(t%4) .. +31 and the two scales of their groups.
-template <bool kFp4>
+template <bool kFp4, int kBS>
 __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
     const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w, const int32_t* __restrict__ n_visible,
@@ -557,7 +599,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
           const float sc = score32<kFp4>(cx, d + 32 * m * kMqStride);
           const int pl = kMqRows * st + 32 * m + r32;               // position within the chunk
           const bool valid = p_begin + pl < p_end_q;
-          const uint32_t key = max8_u32(valid ? score_key(sc) : 0u);
+          const uint32_t key = block_key<kBS>(sc, valid);
           if (lane < 32) so[32 * m + r32] = sc;
           if ((lane & 0x27) == 0 && pl < 8 * nblk_g) wk[pl >> 3] = key;   // lanes 0, 8, 16, 24
         }
@@ -627,29 +669,50 @@ int scan_chunk_positions(int n_max, int queries) {
   return (int)c;
 }
 
+template <bool kFp4, int kBS>
+static void launch_scan_variant(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
+                                const float* head_w, const int32_t* n_visible, int Q, int T, int n_max, float* scores,
+                                uint32_t* blkkey, int nb_max, uint64_t* lists, uint64_t* cuts, int chunk, int n_wg,
+                                bool multi_query, hipStream_t s) {
+  if (multi_query) {
+    const int groups = (Q / T) * ((T + kMqQueries - 1) / kMqQueries);
+    hipLaunchKernelGGL((k_idx_scan_mq<kFp4, kBS>), dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
+                       idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
+  } else {
+    hipLaunchKernelGGL((k_idx_scan<kFp4, kBS>), dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
+                       idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
+                       cuts);
+  }
+}
+
+template <bool kFp4>
+static void launch_scan_format(int block_score, const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows,
+                               const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int Q, int T,
+                               int n_max, float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
+                               uint64_t* cuts, int chunk, int n_wg, bool multi_query, hipStream_t s) {
+  if (block_score == kBlockSum)
+    launch_scan_variant<kFp4, kBlockSum>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
+                                         nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+  else if (block_score == kBlockTop2)
+    launch_scan_variant<kFp4, kBlockTop2>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores,
+                                          blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+  else
+    launch_scan_variant<kFp4, kBlockMax>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
+                                         nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+}
+
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, hipStream_t s) {
-  if (multi_query) {
-    const int groups = (Q / T) * ((T + kMqQueries - 1) / kMqQueries);
-    if (chunk % 1024 != 0 || chunk > kMqMaxChunk || Q % T != 0) return hipErrorInvalidValue;
-    if (idx_ks)
-      hipLaunchKernelGGL(k_idx_scan_mq<true>, dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
-                         idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
-    else
-      hipLaunchKernelGGL(k_idx_scan_mq<false>, dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
-                         idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
-    return hipGetLastError();
-  }
+                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, hipStream_t s) {
+  if (block_score < kBlockMax || block_score > kBlockTop2) return hipErrorInvalidValue;
+  if (multi_query && (chunk % 1024 != 0 || chunk > kMqMaxChunk || Q % T != 0)) return hipErrorInvalidValue;
   if (idx_ks)
-    hipLaunchKernelGGL(k_idx_scan<true>, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
-                       idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
-                       cuts);
+    launch_scan_format<true>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
+                             nb_max, lists, cuts, chunk, n_wg, multi_query, s);
   else
-    hipLaunchKernelGGL(k_idx_scan<false>, dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
-                       idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
-                       cuts);
+    launch_scan_format<false>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores,
+                              blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, s);
   return hipGetLastError();
 }
 

@@ -135,6 +135,19 @@ csa2_status csa2_index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales, i
                             const float* head_w, const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k,
                             void* workspace, size_t ws_bytes, void* stream);
+
+/* csa2_index_scan with another block score for the pool (the block-score variants a study of
+ * the hierarchical indexer's recall compares; alphalab.site sec."2. CSA2" names pool misses,
+ * the candidates the first Full layer's pool leaves out, as the method's risk).  block_score:
+ * 0 = the largest visible score of the block (csa2_index_scan), 1 = the sum of its visible
+ * scores, 2 = the mean of its two largest visible scores (one visible position: that score).
+ * The later stages (csa2_index_pool, csa2_index_select, csa2_index_select_reindex) rank blocks by
+ * whichever score the scan left in the workspace.  With 1 or 2 the Full layer's Top-K over the
+ * pool need not equal its Top-K over every position. */
+csa2_status csa2_index_scan_blocks(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq,
+                                   const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int B,
+                                   int T, int n_max, int block_size, int pool_blocks, int top_k, int block_score,
+                                   void* workspace, size_t ws_bytes, void* stream);
 csa2_status csa2_index_pool(const int32_t* n_visible, int B, int T, int n_max,
                             int block_size, int pool_blocks, int top_k,
                             int32_t* pool_pos, int32_t* pool_len,

@@ -109,12 +109,30 @@ def ranking_scores(s: np.ndarray) -> np.ndarray:
     return np.asarray(s, dtype=np.float64).astype(np.float32) + np.float32(0.0)
 
 
-def block_scores(s32: np.ndarray, n_vis: int, block: int) -> np.ndarray:
-    """blk[j] = max of the scores of block j = positions [j*block, min((j+1)*block, n_vis))."""
+BLOCK_SCORES = ("max", "sum", "top2")
+
+
+def block_scores(s32: np.ndarray, n_vis: int, block: int, mode: str = "max") -> np.ndarray:
+    """blk[j] over the scores of block j = positions [j*block, min((j+1)*block, n_vis)):
+      max   the largest (the pool's block score, reading S4);
+      sum   the sum of the block's scores;
+      top2  the mean of its two largest scores (the score itself for a one-position block).
+    The sum and the mean are taken in float64 and rounded to float32, the ranking precision (R1).
+    The last two are variants for the recall study of the hierarchical indexer ([p5 2]: the
+    pool's misses are the method's risk)."""
     nb = -(-n_vis // block)
     blk = np.empty(nb, np.float32)
     for j in range(nb):
-        blk[j] = s32[j * block:min((j + 1) * block, n_vis)].max()
+        v = s32[j * block:min((j + 1) * block, n_vis)].astype(np.float64)
+        if mode == "max":
+            blk[j] = v.max()
+        elif mode == "sum":
+            blk[j] = np.float32(v.sum())
+        elif mode == "top2":
+            t = np.sort(v)[::-1][:2]
+            blk[j] = np.float32(t.mean())
+        else:
+            raise ValueError(mode)
     return blk
 
 
@@ -146,7 +164,7 @@ def top_k(cand: np.ndarray, s32_cand: np.ndarray, k: int) -> np.ndarray:
 
 
 def full_layer(k8_seq: np.ndarray, q_bf16: np.ndarray, w: np.ndarray, n_vis: int,
-               block: int, pool_blocks: int, k: int) -> Dict[str, np.ndarray]:
+               block: int, pool_blocks: int, k: int, block_score: str = "max") -> Dict[str, np.ndarray]:
     """One query of a Full layer: score every visible position, build the block pool
     (pool_blocks > 0) and take the Top-k over the pool ([p1 4.2], [p2 4]).  With
     pool_blocks == 0 there is no pool and the Top-k runs over every visible position."""
@@ -154,7 +172,7 @@ def full_layer(k8_seq: np.ndarray, q_bf16: np.ndarray, w: np.ndarray, n_vis: int
     s = indexer_scores(k_rows(k8_seq, slice(0, n_vis)), q8, w)
     s32 = ranking_scores(s)
     if pool_blocks > 0:
-        pool = candidate_pool(block_scores(s32, n_vis, block), n_vis, block, pool_blocks)
+        pool = candidate_pool(block_scores(s32, n_vis, block, block_score), n_vis, block, pool_blocks)
         cand = pool
     else:
         pool = None

@@ -82,6 +82,21 @@ def gpu_index_full(inp, B, T, n_max, pool_blocks, top_k, block=8):
     return out
 
 
+def gpu_index_full_blocks(inp, B, T, n_max, pool_blocks, top_k, block_score, block=8):
+    """csa2_index_scan_blocks (the given block score) followed by csa2_index_select."""
+    cap = pool_blocks * block
+    pool_pos, pool_len = empty((B, T, cap), torch.int32), empty((B, T), torch.int32)
+    idx, sc = empty((B, T, top_k), torch.int32), empty((B, T, top_k), torch.float32)
+    ws_bytes = H.csa2_index_full_workspace(B, T, n_max, block, pool_blocks, top_k)
+    ws = empty((ws_bytes,), torch.uint8)
+    k, ks, rows = keys(inp)
+    nv = dev(inp["n_visible"])
+    H.csa2_index_scan_blocks(k, ks, rows, dev(inp["idx_q"]), dev(inp["head_w"]), nv, B, T, n_max, block,
+                             pool_blocks, top_k, block_score, ws, ws_bytes)
+    H.csa2_index_select(nv, B, T, n_max, block, pool_blocks, top_k, pool_pos, pool_len, idx, sc, ws, ws_bytes)
+    return {"topk": host(idx), "topk_score": host(sc), "pool_pos": host(pool_pos), "pool_len": host(pool_len)}
+
+
 def gpu_reindex(inp, B, T, pool_pos, pool_len, top_k, L=None):
     L = inp["ri_q"].shape[0] if L is None else L
     cap = pool_pos.shape[-1]
@@ -177,7 +192,7 @@ def assert_topk_equiv(gpu_idx, ref_idx, ref_score_at, what=""):
     return len(diff)
 
 
-def assert_pool_equiv(gpu_pool, gpu_len, ref_pool, ref_s32, n_vis, block, P, what=""):
+def assert_pool_equiv(gpu_pool, gpu_len, ref_pool, ref_s32, n_vis, block, P, what="", mode="max"):
     gp = np.asarray(gpu_pool[:gpu_len])
     assert gpu_len == len(ref_pool), f"{what}: pool length {gpu_len} vs {len(ref_pool)}"
     assert np.all(np.asarray(gpu_pool[gpu_len:]) == -1), f"{what}: pool padding"
@@ -190,7 +205,7 @@ def assert_pool_equiv(gpu_pool, gpu_len, ref_pool, ref_s32, n_vis, block, P, wha
         assert np.count_nonzero(gp // block == j) == n, f"{what}: block {j} incomplete"
     diff = gb ^ rb
     if diff:
-        blk = O.block_scores(ref_s32, n_vis, block)
+        blk = O.block_scores(ref_s32, n_vis, block, mode)
         sP = min(blk[j] for j in rb)
         for j in diff:
             assert abs(float(blk[j]) - float(sP)) <= TIE_REL * abs(float(sP)), (

@@ -156,3 +156,9 @@ def test_encoder_chunk_rejects(H):
     a[15], a[12] = 0, 128                       # first chunk: no history rows
     a[24] = 8
     expect(H, 3, lambda: H.csa2_encoder_chunk(*a))
+
+
+def test_scan_blocks_rejects_unknown_block_score(H):
+    ws = H.csa2_index_full_workspace(1, 1, 4096, 8, 64, 64)
+    expect(H, 1, lambda: H.csa2_index_scan_blocks(FAKE, None, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, 64, 64, 3,
+                                                  FAKE, ws))

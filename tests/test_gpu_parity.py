@@ -219,6 +219,25 @@ def test_index_full_parity(N, P, K, nv):
         check_full(w, inp, gpu, 0, t)
 
 
+@pytest.mark.parametrize("T", [2, 9])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_pool_block_score_variants(mode, T):
+    """The pool and its Top-K with the sum (1) and top-2 mean (2) block scores, against the oracle
+    with the same block score; T = 9 runs the multi-query scan."""
+    name = {1: "sum", 2: "top2"}[mode]
+    N, P, K = 20003, 128, 256
+    w = small(T=T, N=N, pool_blocks=P, top_k=K, seed=3300 + 10 * mode + T)
+    inp = workloads.make_inputs(w, with_attention=False)
+    inp["n_visible"] = np.array([N - 3 * t for t in range(T)], np.int32).reshape(1, T)
+    gpu = G.gpu_index_full_blocks(inp, 1, T, N, P, K, mode)
+    for t in range(T):
+        n = int(inp["n_visible"][0, t])
+        ref = O.full_layer(G.host_keys(inp, 0), inp["idx_q"][0, t], inp["head_w"][0, t], n, 8, P, K, name)
+        G.assert_pool_equiv(gpu["pool_pos"][0, t], int(gpu["pool_len"][0, t]), ref["pool"], ref["scores32"], n, 8, P,
+                            f"{name} pool t{t}", mode=name)
+        G.assert_topk_equiv(gpu["topk"][0, t], ref["topk"], lambda p: ref["scores"][p], f"{name} topk t{t}")
+
+
 @pytest.mark.parametrize("P", [256, 0])
 def test_stage_entries_match_index_full(P):
     """scan, pool and Top-K called as separate stages (the Top-K on a second stream) give the

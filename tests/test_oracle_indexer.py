@@ -302,3 +302,38 @@ def test_fp4_key_workload_chain_selection_properties():
     dense = O.top_k(np.arange(w.N, dtype=np.int32), f["scores32"], w.top_k)
     assert np.array_equal(f["topk"], dense)
     assert np.isin(inp["planted_pos"], f["topk"]).all()
+
+
+# ---------------------------------------------------------------- block-score variants (recall study)
+
+def test_block_score_variants_by_hand():
+    s32 = np.array([1, 5, 3, 5, 2, 0, 4, 1, 7, 6, -1, 2, 9], np.float32)   # blocks of 4: 3 full + 1 partial
+    assert O.block_scores(s32, 13, 4, "max").tolist() == [5, 4, 7, 9]
+    assert O.block_scores(s32, 13, 4, "sum").tolist() == [14, 7, 14, 9]
+    assert O.block_scores(s32, 13, 4, "top2").tolist() == [5, 3, 6.5, 9]    # ties count twice; one position
+    assert O.block_scores(s32, 12, 4, "top2").tolist() == [5, 3, 6.5]
+
+
+def test_block_score_variants_brute_force():
+    rng = np.random.default_rng(12)
+    for n in (1, 7, 8, 9, 63):
+        s32 = rng.standard_normal(n).astype(np.float32)
+        for j, (mx, sm, t2) in enumerate(zip(O.block_scores(s32, n, 8, "max"), O.block_scores(s32, n, 8, "sum"),
+                                              O.block_scores(s32, n, 8, "top2"))):
+            blk = sorted((float(x) for x in s32[8 * j:8 * j + 8]), reverse=True)
+            assert mx == np.float32(blk[0])
+            assert sm == np.float32(sum(blk))
+            assert t2 == np.float32((blk[0] + blk[1]) / 2 if len(blk) > 1 else blk[0])
+
+
+def test_only_the_max_block_score_keeps_an_isolated_needle():
+    """One very high score alone in its block against dense blocks of moderate scores: the max
+    block score keeps the needle's block in a one-block pool (so the dense Top-1 is in the pool,
+    lemma S6), while the sum and the top-2 mean prefer a dense block and lose it."""
+    s32 = np.full(64, 1.0, np.float32)
+    s32[0:8] = 0.0
+    s32[3] = 5.0                      # the needle
+    s32[40:48] = 3.0                  # a dense block
+    for mode, keeps in (("max", True), ("sum", False), ("top2", False)):
+        pool = O.candidate_pool(O.block_scores(s32, 64, 8, mode), 64, 8, 1)
+        assert (3 in pool.tolist()) == keeps, mode

@@ -423,6 +423,64 @@ def make_encoder_chunk(w: EncoderPrefill) -> Dict[str, np.ndarray]:
     return d
 
 
+# ---------------------------------------------------------------- recall study of the hierarchical indexer
+
+RECALL_FAMILIES = ("full_isolated", "reindex_isolated", "shared_isolated", "full_clusters")
+
+
+def make_recall_context(N: int, seed: int, n_needles: int = 32, n_clusters: int = 8,
+                        sigma: float = 4.0, cluster_sigma: float = 2.0) -> Dict[str, object]:
+    """One decode query over N positions with planted needles for the hierarchical indexer's recall
+    study (alphalab.site sec."2. CSA2": the first Full layer's pool decides what the Reindex layers
+    can pick).  Keys are N(0,1) rows with, before the E4M3 cast, a shift delta added at the needle
+    positions: the minimum-norm delta with q8_h . delta = s * ||q8_h|| for every head h of the
+    target queries (the planted-cluster recipe of the 1M decode):
+      full_isolated     n_needles single positions, target the Full query, s = sigma;
+      reindex_isolated  n_needles single positions, target the Reindex query only, s = sigma;
+      shared_isolated   n_needles single positions, target both queries, s = sigma;
+      full_clusters     n_clusters aligned blocks of 8 positions, target the Full query,
+                        s = cluster_sigma (weaker alone, dense as a block).
+    Returns idx_k [1][N][128], idx_q / head_w (Full), ri_q [1][1][1][32][128] / ri_w (one Reindex
+    layer), n_visible [1][1], and families {name: sorted positions}."""
+    ss = np.random.SeedSequence(seed)
+    g = [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(5)]
+    d: Dict[str, object] = {}
+    d["idx_q"] = to_bf16_bits(draw_normal_f32(g[0], (1, 1, IDX_HEADS, IDX_DIM)))
+    d["head_w"] = g[1].random(size=(1, 1, IDX_HEADS), dtype=np.float32)
+    d["ri_q"] = to_bf16_bits(draw_normal_f32(g[0], (1, 1, 1, IDX_HEADS, IDX_DIM)))
+    d["ri_w"] = g[1].random(size=(1, 1, 1, IDX_HEADS), dtype=np.float32)
+    qf = e4m3_bytes_as_float(to_e4m3_bytes(bf16_bits_as_float(d["idx_q"][0, 0]))).astype(np.float64)
+    qr = e4m3_bytes_as_float(to_e4m3_bytes(bf16_bits_as_float(d["ri_q"][0, 0, 0]))).astype(np.float64)
+
+    def shift(a, s):
+        return np.linalg.lstsq(a, s * np.linalg.norm(a, axis=1), rcond=None)[0].astype(np.float32)
+
+    deltas = {"full_isolated": shift(qf, sigma), "reindex_isolated": shift(qr, sigma),
+              "shared_isolated": shift(np.concatenate([qf, qr]), sigma), "full_clusters": shift(qf, cluster_sigma)}
+    nb = N // 8
+    blocks = g[2].choice(nb, size=3 * n_needles + n_clusters, replace=False)
+    fam: Dict[str, np.ndarray] = {}
+    off = g[3].integers(0, 8, size=3 * n_needles)
+    for i, name in enumerate(RECALL_FAMILIES[:3]):
+        b = blocks[i * n_needles:(i + 1) * n_needles]
+        fam[name] = np.sort(8 * b + off[i * n_needles:(i + 1) * n_needles]).astype(np.int32)
+    cb = blocks[3 * n_needles:]
+    fam["full_clusters"] = np.sort((8 * cb[:, None] + np.arange(8)[None, :]).reshape(-1)).astype(np.int32)
+    idx_k = np.empty((1, N, IDX_DIM), np.uint8)
+    chunk = 1 << 17
+    for r0 in range(0, N, chunk):
+        r1 = min(N, r0 + chunk)
+        x = draw_normal_f32(g[4], (r1 - r0, IDX_DIM))
+        for name, pos in fam.items():
+            sel = pos[(pos >= r0) & (pos < r1)] - r0
+            x[sel] += deltas[name]
+        idx_k[0, r0:r1] = to_e4m3_bytes(x)
+    d["idx_k"] = idx_k
+    d["n_visible"] = np.full((1, 1), N, np.int32)
+    d["families"] = fam
+    return d
+
+
 def small_variant(w: Workload, **changes) -> Workload:
     """A copy of a workload with some fields changed (for parity cases at reduced size)."""
     return dataclasses.replace(w, **changes)
