@@ -62,7 +62,7 @@ struct Carver {
 };
 
 struct FullPlan {
-  int Q, nb_max, nb_stride, chunk, n_wg, n_units, blocks_per_unit, P, cap;
+  int Q, nb_max, nb_stride, chunk, n_wg, upw, n_units, blocks_per_unit, P, cap;
   bool internal_pool, multi_query;
 };
 
@@ -76,8 +76,16 @@ FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
   p.multi_query = csa2::scan_multi_query(T, n_max);
   p.chunk = p.multi_query ? csa2::scan_mq_chunk(n_max, B, T) : csa2::scan_chunk_positions(n_max, p.Q);
   p.n_wg = n_max > 0 ? (n_max + p.chunk - 1) / p.chunk : 1;
-  p.n_units = p.n_wg * csa2::kScanUnitsPerWg;
-  p.blocks_per_unit = p.chunk / (csa2::kBlock * csa2::kScanUnitsPerWg);
+  // Each wave of the scan lists the five best blocks of upw units of its range.  Units are made as
+  // small as the pool takes (at most 4096 units of at least 8 blocks): with a pool holding a large
+  // share of the blocks, big units often have more than four selected blocks and must be re-read.
+  const int bpw = p.chunk / (csa2::kBlock * csa2::kScanUnitsPerWg);
+  p.upw = 1;
+  while (bpw / (2 * p.upw) >= 8 && (int64_t)p.n_wg * csa2::kScanUnitsPerWg * 2 * p.upw <= 4096 &&
+         (!p.multi_query || 2 * p.upw <= 4))
+    p.upw *= 2;
+  p.n_units = p.n_wg * csa2::kScanUnitsPerWg * p.upw;
+  p.blocks_per_unit = bpw / p.upw;
   p.internal_pool = pool_blocks == 0;
   p.P = p.internal_pool ? top_k : pool_blocks;
   p.cap = p.P * csa2::kBlock;
@@ -162,7 +170,7 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   const FullPlan p = plan_full(B, T, n_max, 1, 1);
   st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                        scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg, p.multi_query,
-                                       csa2::kBlockMax, (hipStream_t)stream),
+                                       csa2::kBlockMax, p.upw, (hipStream_t)stream),
                  "index scan launch");
   return st == CSA2_OK ? ok() : st;
 }
@@ -211,7 +219,7 @@ static csa2_status index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   if (n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg,
-                                         p.multi_query, block_score, (hipStream_t)stream),
+                                         p.multi_query, block_score, p.upw, (hipStream_t)stream),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }
@@ -451,7 +459,7 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   if (do_scan && n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query,
-                                         csa2::kBlockMax, s),
+                                         csa2::kBlockMax, p.upw, s),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }
@@ -579,10 +587,14 @@ size_t carve_encoder(void* ws, int B, int T, int64_t k_rows, int layers, int H, 
 }  // namespace
 
 size_t csa2_encoder_chunk_workspace(int B, int T, int64_t k_rows, int layers, int H, int top_k, int swa_window) {
-  if (B < 1 || T < 1 || k_rows < 0 || k_rows > csa2::kMaxFullPositions || layers < 1 || layers > csa2::kMaxLayers ||
-      H < 16 || H % 16 != 0 || top_k < 1 || top_k > csa2::kMaxTopK || swa_window < 0)
+  if (B < 1 || T < 1 || T > 65535 || k_rows < 0 || k_rows > csa2::kMaxFullPositions || layers < 1 ||
+      layers > csa2::kMaxLayers || H < 16 || H % 16 != 0 || top_k < 1 || top_k > csa2::kMaxTopK || swa_window < 0)
     return 0;
-  return carve_encoder(nullptr, B, T, k_rows, layers, H, top_k, swa_window, nullptr);
+  // enough for every chunk of at most T tokens: the attention's split plan, and so its partial
+  // states, does not grow monotonically with T
+  size_t need = 0;
+  for (int t = 1; t <= T; ++t) need = std::max(need, carve_encoder(nullptr, B, t, k_rows, layers, H, top_k, swa_window, nullptr));
+  return need;
 }
 
 csa2_status csa2_encoder_chunk(int G, int layers, const uint16_t* new_idx_k, const uint16_t* new_latent,

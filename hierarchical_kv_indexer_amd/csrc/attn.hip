@@ -13,6 +13,8 @@
 // raw bytes are loaded into registers while the current chunk is computed.  When the (layer,
 // query, head group) count alone cannot fill the GPU, the rows are split across workgroups and
 // k_attn_combine merges the partial softmax states (max, sum, weighted rows).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -589,7 +591,11 @@ AttnPlan plan_attn(int L, int B, int T, int H, int k, int window) {
   const long long groups = (long long)L * B * T * (H / p.heads_per_wg);
   const int rows_max = k + window;
   const int max_chunks = (rows_max + kRows - 1) / kRows;
-  long long want = (512 + groups - 1) / groups;         // splits to reach ~512 workgroups
+  // splits to reach ~512 workgroups of the 16-head kernel (two fit on a CU); the 64-head kernel
+  // fits one workgroup per CU, so its splits stop at one round of ~256 workgroups: a second,
+  // partial round costs more than the longer splits (measured on the batch-8 and caller-pool
+  // workloads: 41.9 and 39.5 us with ~400 and 320 workgroups)
+  long long want = p.heads_per_wg == 64 ? std::max(1LL, 256 / groups) : (512 + groups - 1) / groups;
   int splits = (int)(want < max_chunks ? want : max_chunks);
   if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;

@@ -25,14 +25,16 @@ constexpr int kMqMaxChunk = 4096;
 constexpr int kMqMaxPositions = 256 * kMqMaxChunk;   // 4096 units per query
 bool scan_multi_query(int T, int n_max);
 int scan_mq_chunk(int n_max, int B, int T);
-constexpr int kScanUnitsPerWg = kFullThreads / 64;   // 16 units of chunk/16 positions per chunk
+constexpr int kScanUnitsPerWg = kFullThreads / 64;   // 16 waves per chunk, each with upw units of the
+                                                     // pool's unit lists (chunk/(16*upw) positions each)
 constexpr int kMaxFullPositions = 1 << 21;           // 256 chunks of 8192 per query: 4096 units
 // Indexer keys: idx_ks == null: E4M3 idx_k [rows][128]; otherwise FP4 codes idx_k [rows][64] and
 // E4M3 scales idx_ks [rows][8] (one per 16 channels).
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, hipStream_t s);
+                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, int upw,
+                           hipStream_t s);
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
                            int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s);

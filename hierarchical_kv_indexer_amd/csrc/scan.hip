@@ -305,11 +305,56 @@ size_t scan_lds_bytes(int chunk) {
 // Best ranking key (score key, block) of a wave's blocks (one per lane), removed from the
 // set.  Entries are (key, block) with key 0 / block 0xffffffff meaning "none"; returns
 // rank_key or 0.
-__device__ __forceinline__ uint64_t wave_pop_best(uint32_t& key, uint32_t& blk) {
-  const uint32_t m = wave_max_u32(key);
-  const uint32_t jm = wave_min_u32(key == m ? blk : 0xffffffffu);
+// Max / min over aligned groups of LANES lanes (8, 16, 32 or 64); every lane of a group gets
+// its group's value.
+template <int LANES>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t x) {
+  if constexpr (LANES == 64) return wave_max_u32(x);
+  x = max(x, dpp_mov<0xB1>(x));                          // quad_perm [1,0,3,2]
+  x = max(x, dpp_mov<0x4E>(x));                          // quad_perm [2,3,0,1]
+  x = max(x, dpp_mov<0x141>(x));                         // row_half_mirror
+  if constexpr (LANES >= 16) x = max(x, dpp_mov<0x140>(x));   // row_mirror
+  if constexpr (LANES >= 32) x = max(x, swap16(x));
+  return x;
+}
+template <int LANES>
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t x) {
+  if constexpr (LANES == 64) return wave_min_u32(x);
+  x = min(x, dpp_mov<0xB1>(x));
+  x = min(x, dpp_mov<0x4E>(x));
+  x = min(x, dpp_mov<0x141>(x));
+  if constexpr (LANES >= 16) x = min(x, dpp_mov<0x140>(x));
+  if constexpr (LANES >= 32) x = min(x, swap16(x));
+  return x;
+}
+
+// Best ranking key (score key, block) of a group's blocks (one per lane), removed from the
+// set.  Entries are (key, block) with key 0 / block 0xffffffff meaning "none"; returns
+// rank_key or 0.
+template <int LANES>
+__device__ __forceinline__ uint64_t group_pop_best(uint32_t& key, uint32_t& blk) {
+  const uint32_t m = group_max_u32<LANES>(key);
+  const uint32_t jm = group_min_u32<LANES>(key == m ? blk : 0xffffffffu);
   if (key == m && blk == jm) { key = 0u; blk = 0xffffffffu; }
   return (m == 0u && jm == 0xffffffffu) ? 0ull : rank_key(m, jm);
+}
+
+// The five best blocks of each group of LANES lanes (lane i of a group holds one block); the
+// first lane of group s writes unit unit0 + s.
+template <int LANES>
+__device__ __forceinline__ void write_unit_lists(uint32_t key, uint32_t blk, int n_groups, size_t unit0,
+                                                 uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
+  uint64_t best[5];
+#pragma unroll
+  for (int r = 0; r < 5; ++r) best[r] = group_pop_best<LANES>(key, blk);
+  const int lane = threadIdx.x & 63;
+  if (lane % LANES == 0 && lane / LANES < n_groups) {
+    const size_t unit = unit0 + lane / LANES;
+    u32x4* lp = (u32x4*)(lists + unit * 4);
+    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
+    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
+    cuts[unit] = best[4];
+  }
 }
 
 // grid (n_wg, Q), one workgroup of 16 waves per chunk of positions (sized so the grid is about
@@ -331,7 +376,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     const uint16_t* __restrict__ idx_q,
     const float* __restrict__ head_w, const int32_t* __restrict__ n_visible, int T, int n_max,
     int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
-    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
+    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts, int upw) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   uint16_t* qlds = (uint16_t*)lds;
   float* sbuf = (float*)(lds + kIdxHeads * kIdxDim * 2);
@@ -415,21 +460,19 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     for (int i = threadIdx.x; i < nblk; i += kFullThreads) brow[i] = wkeys[i];
   }
   if (!lists) return;
-  // five best blocks of unit `wave` (bpu <= 64 blocks: one per lane)
+  // the wave's blocks (bpu <= 64: one per lane), split into upw units of bpu/upw blocks; each
+  // unit lists its five best
   const int bpu = chunk / (kBlock * kFullWaves);
   const int ub = wave * bpu;
   const bool ok = lane < bpu && ub + lane < nblk;
-  uint32_t key = ok ? wkeys[ub + lane] : 0u;
-  uint32_t blk = ok ? (uint32_t)(p_begin / kBlock + ub + lane) : 0xffffffffu;
-  uint64_t best[5];
-#pragma unroll
-  for (int r = 0; r < 5; ++r) best[r] = wave_pop_best(key, blk);
-  if (lane == 0) {
-    const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kFullWaves + wave;
-    u32x4* lp = (u32x4*)(lists + unit * 4);
-    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
-    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
-    cuts[unit] = best[4];
+  const uint32_t key = ok ? wkeys[ub + lane] : 0u;
+  const uint32_t blk = ok ? (uint32_t)(p_begin / kBlock + ub + lane) : 0xffffffffu;
+  const size_t unit0 = (((size_t)q * gridDim.x + blockIdx.x) * kFullWaves + wave) * upw;
+  switch (bpu / upw) {
+    case 8: write_unit_lists<8>(key, blk, upw, unit0, lists, cuts); break;
+    case 16: write_unit_lists<16>(key, blk, upw, unit0, lists, cuts); break;
+    case 32: write_unit_lists<32>(key, blk, upw, unit0, lists, cuts); break;
+    default: write_unit_lists<64>(key, blk, upw, unit0, lists, cuts); break;
   }
 }
 
@@ -509,7 +552,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
     const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w, const int32_t* __restrict__ n_visible,
     int T, int n_max, int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
-    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
+    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts, int upw) {
   __shared__ __attribute__((aligned(16))) unsigned char stage[2][kMqRows * kMqStride];
   __shared__ __attribute__((aligned(16))) float sstage[2][kMqQueries][kMqRows];   // scores of a step
   __shared__ uint32_t wkeys[kMqQueries][kMqMaxChunk / kBlock];
@@ -620,11 +663,11 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
     for (int i = lane; i < nblk; i += 64) brow[i] = wk[i];
   }
   if (!lists) return;
-  // lane u < 16 keeps the five best ranking keys of unit u, inserted one block at a time (the
-  // keys are distinct, so the visiting order does not matter; it is rotated per lane to spread
-  // the LDS reads over the banks)
-  const int bpu = chunk / (kBlock * kScanUnitsPerWg);
-  if (lane < kScanUnitsPerWg) {
+  // lane u < 16*upw keeps the five best ranking keys of unit u (bpu blocks), inserted one block at
+  // a time (the keys are distinct, so the visiting order does not matter; it is rotated per lane
+  // to spread the LDS reads over the banks)
+  const int bpu = chunk / (kBlock * kScanUnitsPerWg * upw);
+  if (lane < kScanUnitsPerWg * upw) {
     const int ub = lane * bpu;
     uint64_t best[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
     const int rot = lane % bpu;
@@ -638,7 +681,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
         best[r] = hi;
       }
     }
-    const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kScanUnitsPerWg + lane;
+    const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kScanUnitsPerWg * upw + lane;
     u32x4* lp = (u32x4*)(lists + unit * 4);
     lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
     lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
@@ -673,15 +716,15 @@ template <bool kFp4, int kBS>
 static void launch_scan_variant(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                                 const float* head_w, const int32_t* n_visible, int Q, int T, int n_max, float* scores,
                                 uint32_t* blkkey, int nb_max, uint64_t* lists, uint64_t* cuts, int chunk, int n_wg,
-                                bool multi_query, hipStream_t s) {
+                                bool multi_query, int upw, hipStream_t s) {
   if (multi_query) {
     const int groups = (Q / T) * ((T + kMqQueries - 1) / kMqQueries);
     hipLaunchKernelGGL((k_idx_scan_mq<kFp4, kBS>), dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts);
+                       idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts, upw);
   } else {
     hipLaunchKernelGGL((k_idx_scan<kFp4, kBS>), dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
                        idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
-                       cuts);
+                       cuts, upw);
   }
 }
 
@@ -689,30 +732,33 @@ template <bool kFp4>
 static void launch_scan_format(int block_score, const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows,
                                const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int Q, int T,
                                int n_max, float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                               uint64_t* cuts, int chunk, int n_wg, bool multi_query, hipStream_t s) {
+                               uint64_t* cuts, int chunk, int n_wg, bool multi_query, int upw, hipStream_t s) {
   if (block_score == kBlockSum)
     launch_scan_variant<kFp4, kBlockSum>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
-                                         nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+                                         nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
   else if (block_score == kBlockTop2)
     launch_scan_variant<kFp4, kBlockTop2>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores,
-                                          blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+                                          blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
   else
     launch_scan_variant<kFp4, kBlockMax>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
-                                         nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+                                         nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
 }
 
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, hipStream_t s) {
+                           uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, int upw,
+                           hipStream_t s) {
   if (block_score < kBlockMax || block_score > kBlockTop2) return hipErrorInvalidValue;
+  const int bpw = chunk / (kBlock * kFullWaves);       // blocks per wave
+  if (upw < 1 || bpw % upw != 0 || bpw / upw < 8 || (bpw / upw & (bpw / upw - 1)) != 0) return hipErrorInvalidValue;
   if (multi_query && (chunk % 1024 != 0 || chunk > kMqMaxChunk || Q % T != 0)) return hipErrorInvalidValue;
   if (idx_ks)
     launch_scan_format<true>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
-                             nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+                             nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
   else
     launch_scan_format<false>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores,
-                              blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, s);
+                              blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
   return hipGetLastError();
 }
 

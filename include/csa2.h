@@ -259,7 +259,8 @@ csa2_status csa2_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales, 
  *               p0 - hist + r, hist = min(p0, swa_window - 1), swa_rows = hist + T
  *   out         [G][layers][B][T][H][512] bf16 out
  *   topk_idx    [G][B][T][top_k] int32 out (each group's index set, ascending, -1 padded) or NULL
- *   workspace   device scratch of csa2_encoder_chunk_workspace(...) bytes, 16-byte aligned
+ *   workspace   device scratch of csa2_encoder_chunk_workspace(...) bytes, 16-byte aligned; a size
+ *               queried for T tokens serves every chunk of at most T tokens
  * Work is enqueued on `stream` in group order; the caches must not be read or written by other
  * work in the meantime.  Supported: m >= 1, floor((p0+T)/m) <= k_rows <= 2^21,
  * layers*B*T <= 65535, H % 16 == 0, 1 <= top_k <= 2048, 0 <= swa_window <= 4096. */
