@@ -43,6 +43,14 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// gfx950 LDS transpose read of 16-bit elements: within each 16-lane group, lane 4a+b receives
+// element b of the 8 bytes addressed by lanes a, a+4, a+8 and a+12 (in that order).
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 struct RawRow {          // this thread's quarter (128 channels) of one chunk row
   u32x4 d[8];            // main: d[0..3] = 64 code bytes; SWA: d[0..7] = 128 E4M3 bytes
   u32x2 sc;              // main: 8 scale bytes
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
 
   // Accumulators start as MFMA results (of zero operands), so the compiler keeps them in the
   // accumulation registers across the loop.
-  f32x4 o[16];                                       // tile 8*blk + t: dims 256*hf + 128*blk + 8j + t
+  f32x4 o[16];                                       // tile u: dims 256*hf + 16u + j
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -484,60 +492,61 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
         pos_c = c + 3 < nchunks ? row_index(c + 3) : -1;
       }
     }
-    // O[head 4g+v][dim 256*hf + 128*blk + 8j + t] += sum_r P[head][r] X[r][dim]
+    // O[head 4g+v][dim 256*hf + 16*u + j] += sum_r P[head][r] X[r][dim].  The B operand of tile u
+    // (rows 32kk + 8g .. +7 of dim 256hf + 16u + j in lane (j, g)) comes straight from row-major X
+    // by two LDS transpose reads: in each 16-lane group, lane 4a+b receives element b of the
+    // 8 bytes addressed by lanes a, a+4, a+8 and a+12, so lane j = 4a+i addresses row
+    // 32kk + 8g + i (+4 for the second read), dims 256hf + 16u + 4a .. +3.
 #pragma unroll
     for (int kk = 0; kk < kRows / 32; ++kk) {
       const u32x4 pa = *(const u32x4*)(Pg + j * kPStride + 32 * kk + 8 * g);
+      const uint16_t* xt = Xc + (32 * kk + 8 * g + (j >> 2)) * kXStride + 256 * hf + 4 * (j & 3);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const uint16_t* xc = Xc + (32 * kk + 8 * g) * kXStride + 256 * hf + 128 * blk + 8 * j;
-        u32x4 xv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[e] = *(const u32x4*)(xc + e * kXStride);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x4 lo, hi;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lo[e] = __builtin_amdgcn_perm(xv[2 * e + 1][i], xv[2 * e][i], 0x05040100u);
-            hi[e] = __builtin_amdgcn_perm(xv[2 * e + 1][i], xv[2 * e][i], 0x07060302u);
-          }
-          o[8 * blk + 2 * i] = mfma16x16x32(pa, lo, o[8 * blk + 2 * i]);
-          o[8 * blk + 2 * i + 1] = mfma16x16x32(pa, hi, o[8 * blk + 2 * i + 1]);
-        }
+      for (int u = 0; u < 16; ++u) {
+        const u32x2 lo = ds_read_tr16(xt + 16 * u);
+        const u32x2 hi = ds_read_tr16(xt + 4 * kXStride + 16 * u);
+        o[u] = mfma16x16x32(pa, u32x4{lo.x, lo.y, hi.x, hi.y}, o[u]);
       }
     }
     if (c + 1 < nchunks) __syncthreads();            // next chunk's X and rowok written; P, red_* free
   }
 
+  // O leaves through LDS (the chunk tiles are free once every wave has finished its last
+  // O += P X): tile u of a lane holds dims 256hf + 16u + j, and each lane then stores four
+  // consecutive dims of one head at a time.
+  constexpr int kOStride = kKvDim + 4;                // floats per staged head row
+  static_assert(64 * kOStride * 4 <= (int)sizeof(X), "the staged output fits in the chunk tiles");
+  float* Os = reinterpret_cast<float*>(&X[0][0]);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Os[(16 * hg + 4 * g + v) * kOStride + 256 * hf + 16 * u + j] = o[u][v];
+  if (hf == 0 && j == 0) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      red_m[0][16 * hg + 4 * g + v] = m_run[v];
+      red_l[0][16 * hg + 4 * g + v] = l_run[v];
+    }
+  }
+  __syncthreads();
   const size_t hrow = (size_t)lq * H;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int h = hbase + 4 * g + v;
+  for (int hh = 0; hh < 16; ++hh) {
+    const int head = 16 * hg + hh, h = 64 * hq + head;
+    const f32x4 ov = *(const f32x4*)(Os + head * kOStride + 256 * hf + 4 * lane);
+    const float mh = red_m[0][head], lh = red_l[0][head];
     if (n_splits == 1) {
-      const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        u32x4 pk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pk[i] = f32_to_bf16_rne(o[8 * blk + 2 * i][v] * inv) |
-                  (f32_to_bf16_rne(o[8 * blk + 2 * i + 1][v] * inv) << 16);
-        *(u32x4*)(out + (hrow + h) * kKvDim + 256 * hf + 128 * blk + 8 * j) = pk;
-      }
-      if (lse && hf == 0 && j == 0)
-        lse[hrow + h] = l_run[v] > 0.f ? (m_run[v] + log2f(l_run[v])) * 0.69314718055994531f : -INFINITY;
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      const u32x2 pk = {f32_to_bf16_rne(ov.x * inv) | (f32_to_bf16_rne(ov.y * inv) << 16),
+                        f32_to_bf16_rne(ov.z * inv) | (f32_to_bf16_rne(ov.w * inv) << 16)};
+      *(u32x2*)(out + (hrow + h) * kKvDim + 256 * hf + 4 * lane) = pk;
+      if (lse && hf == 0 && lane == 0) lse[hrow + h] = lh > 0.f ? (mh + log2f(lh)) * 0.69314718055994531f : -INFINITY;
     } else {
       const size_t pr = (hrow + h) * n_splits + split;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        f32x4* po = (f32x4*)(part_o + pr * kKvDim + 256 * hf + 128 * blk + 8 * j);
-        po[0] = f32x4{o[8 * blk][v], o[8 * blk + 1][v], o[8 * blk + 2][v], o[8 * blk + 3][v]};
-        po[1] = f32x4{o[8 * blk + 4][v], o[8 * blk + 5][v], o[8 * blk + 6][v], o[8 * blk + 7][v]};
-      }
-      if (hf == 0 && j == 0) {
-        part_ml[pr * 2] = m_run[v];
-        part_ml[pr * 2 + 1] = l_run[v];
+      *(f32x4*)(part_o + pr * kKvDim + 256 * hf + 4 * lane) = ov;
+      if (hf == 0 && lane == 0) {
+        part_ml[pr * 2] = mh;
+        part_ml[pr * 2 + 1] = lh;
       }
     }
   }
