@@ -21,7 +21,8 @@
 namespace csa2 {
 
 constexpr int kRows = 64;                    // rows per chunk
-constexpr int kXStride = kKvDim + 8;         // bf16 elements per LDS row (pad: 16 bytes)
+constexpr int kXStride = kKvDim + 16;        // bf16 elements per LDS row (pad: 32 bytes; measured
+                                             // against 16: faster S = Q X^T reads, slower stores)
 constexpr int kPStride = kRows + 8;          // bf16 elements per P row
 constexpr int kMaxSplitRows = 4096 + kMaxTopK;   // a split never exceeds k + window rows
 constexpr float kLazyLog2 = 8.f;             // slack of the softmax reference point (log2 units)
