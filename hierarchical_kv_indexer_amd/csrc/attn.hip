@@ -44,6 +44,11 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Two floats to bf16 with one round-to-nearest-even conversion (low half first).
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // gfx950 LDS transpose read of 16-bit elements: within each 16-lane group, lane 4a+b receives
 // element b of the 8 bytes addressed by lanes a, a+4, a+8 and a+12 (in that order).
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
@@ -214,8 +219,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
       const int h = 4 * g + v;
       const float mc = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
       mnew[v] = fmaxf(m_run[v], mc);
-      alpha[v] = mnew[v] == -INFINITY ? 1.f : exp2f(m_run[v] - mnew[v]);
-      const float p = mnew[v] == -INFINITY ? 0.f : exp2f(sv[v] - mnew[v]);
+      alpha[v] = mnew[v] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[v] - mnew[v]);
+      const float p = mnew[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[v] - mnew[v]);
       const uint32_t pb = f32_to_bf16_rne(p);
       P[h * kPStride + 16 * wave + j] = (uint16_t)pb;
       psum[v] = row16_sum(bf16_bits_to_f32(pb));
@@ -457,16 +462,17 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       const float m = fmaxf(red_m[0][hh], red_m[1][hh]);
       const bool mv = m > m_run[v] + kLazyLog2;      // true from -inf to finite
       const float mnew = mv ? m : m_run[v];
-      alpha[v] = (mv && m_run[v] != -INFINITY) ? exp2f(m_run[v] - mnew) : 1.f;
+      alpha[v] = (mv && m_run[v] != -INFINITY) ? __builtin_amdgcn_exp2f(m_run[v] - mnew) : 1.f;
       moved |= mv && m_run[v] != -INFINITY;
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const float p = mnew == -INFINITY ? 0.f : exp2f(sv[r][v] - mnew);
-        const uint32_t pb = f32_to_bf16_rne(p);
-        Pg[(4 * g + v) * kPStride + 32 * hf + 16 * r + j] = (uint16_t)pb;
-        ps += bf16_bits_to_f32(pb);
-      }
+      // exponents are at most kLazyLog2 (no overflow); results below 2^-126 may flush to zero,
+      // far below the rounding of the weights that matter
+      const float p0 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[0][v] - mnew);
+      const float p1 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[1][v] - mnew);
+      const uint32_t pk = bf16x2_rne(p0, p1);
+      Pg[(4 * g + v) * kPStride + 32 * hf + j] = (uint16_t)pk;
+      Pg[(4 * g + v) * kPStride + 32 * hf + 16 + j] = (uint16_t)(pk >> 16);
+      float ps = __uint_as_float(pk << 16);
+      ps += __uint_as_float(pk & 0xffff0000u);
       ps = row16_sum(ps);
       if (j == 0) red_l[hf][hh] = ps;
       m_run[v] = mnew;
