@@ -42,31 +42,19 @@ hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hi
   return hipGetLastError();
 }
 
-// The E4M3 value nearest to x (ties to the even code), saturating at +-448, without branches:
-// the E4M3 grid spacing at |x| is 2^(e-3) for |x| in [2^e, 2^(e+1)), e >= -6, and 2^-9 below
-// 2^-6, so rounding |x| / spacing to an integer (ties to even) and scaling back is the encoding
-// followed by the decoding.  Both scalings are exact.  NaN stays NaN.
-__device__ __forceinline__ float round_e4m3(float x) {
-  const float a = fabsf(x);
-  const int e = max((int)(__float_as_uint(a) >> 23) - 127, -6);
-  const float step = __uint_as_float((uint32_t)(e - 3 + 127) << 23);
-  const float inv = __uint_as_float((uint32_t)(127 - (e - 3)) << 23);   // 1 / step, exact
-  float r = __builtin_rintf(a * inv) * step;
-  r = r > 448.f ? 448.f : r;
-  return __builtin_copysignf(r, x);
-}
-
-// Two bf16 query values (low half first) rounded to E4M3 and returned as a bf16 pair, or an fp16
-// pair with kF16 (E4M3 values are exact in both).
+// Two bf16 query values (low half first) rounded to E4M3 (nearest, ties to even, saturating at
+// +-448) and returned as a bf16 pair, or an fp16 pair with kF16 (E4M3 values are exact in both):
+// clamp, the hardware conversion to E4M3 bytes, and its exact conversion back.
 template <bool kF16>
 __device__ __forceinline__ uint32_t q8_pair(uint32_t w) {
-  const float lo = round_e4m3(bf16_bits_to_f32(w & 0xffffu));
-  const float hi = round_e4m3(bf16_bits_to_f32(w >> 16));
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const float lo = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w & 0xffffu), -448.f, 448.f);
+  const float hi = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w >> 16), -448.f, 448.f);
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, lo, hi, 1.0f, false));
   if constexpr (kF16)
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
   else
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false));
 }
 
 // The 32x128 query of one indexer head set, rounded to E4M3 and held as bf16 in LDS.
