@@ -510,33 +510,49 @@ __device__ __forceinline__ void load_ctx32(Ctx32& cx, const uint16_t* __restrict
   for (int v = 0; v < 16; ++v) cx.w[v] = w[8 * (v >> 2) + 4 * h + (v & 3)];
 }
 
-// Score of position l % 32 of a 32-row group of the staged step (row pointer `row`: this lane's
-// row); lanes l and l ^ 32 return the same value.
-template <bool kF16>
-__device__ __forceinline__ float score32(const Ctx32& cx, const unsigned char* row) {
+// This lane's key operands of a 32-row group of the staged step (row pointer `row`: this lane's
+// row, l % 32): channels 16c + 8(l/32) .. +7 in bk[c].
+__device__ __forceinline__ void load_bk32(const unsigned char* row, u32x4 (&bk)[8]) {
   const int h = (threadIdx.x >> 5) & 1;
-  u32x4 bk[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) bk[c] = *(const u32x4*)(row + 32 * c + 16 * h);
-  f32x16 acc;
+}
+
+// Two queries' MFMA chains over the same key operands of a 32-row group: a0/a1 receive the
+// per-head logits of position l % 32 (heads as in Ctx32::w).
+template <bool kF16>
+__device__ __forceinline__ void mfma_chains32(const Ctx32& c0, const Ctx32& c1, const u32x4 (&bk)[8], f32x16& a0,
+                                              f32x16& a1) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int v = 0; v < 16; ++v) a0[v] = a1[v] = 0.f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc = mfma32x32x16<kF16>(cx.qa[c], bk[c], acc);
+  for (int c = 0; c < 8; ++c) {
+    a0 = mfma32x32x16<kF16>(c0.qa[c], bk[c], a0);
+    a1 = mfma32x32x16<kF16>(c1.qa[c], bk[c], a1);
+  }
+}
+
+// Score of position l % 32 from its logits: sum over heads of w * relu(logit); lanes l and l ^ 32
+// return the same value.
+__device__ __forceinline__ float reduce32(const Ctx32& cx, const f32x16& a) {
   float p = 0.f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) p = fmaf(cx.w[v], relu_bits(acc[v]), p);
+  for (int v = 0; v < 16; ++v) p = fmaf(cx.w[v], relu_bits(a[v]), p);
   return sum_xor32(p);
 }
 
-// grid (n_wg, B * ceil(T/16)).  Step s of the chunk stages key rows p_begin + 128s .. +127 (rows
-// past the group's last visible position are clamped to it and never scored), double-buffered:
-// step s+1 is converted into the other buffer while step s is scored, and the loads of step s+2
-// are then in flight.  Staging: E4M3, thread t converts bytes 16*(t%8) .. +15 of row t/8 (channels
-// 16*(t%8) .. +15); FP4 (threads below 512), the 16 code bytes of row t/4 holding channels
-// 32*(t%4) .. +31 and the two scales of their groups.
+// grid (n_wg, B * ceil(T/16)), 8 waves; wave w scores queries 2w and 2w+1 of the group, so each
+// key operand read from LDS feeds two queries' MFMAs.  Step s of the chunk stages key rows
+// p_begin + 128s .. +127 (rows past the group's last visible position are clamped to it and never
+// scored), double-buffered: step s+1 is converted into the other buffer while step s is scored,
+// and the loads of step s+2 are then in flight.  Staging: E4M3, thread t converts bytes
+// 16*(t%8) .. +15 of rows t/8 and t/8 + 64 (channels 16*(t%8) .. +15); FP4, the 16 code bytes of
+// row t/4 holding channels 32*(t%4) .. +31 and the two scales of their groups.
+constexpr int kMqThreads = 512;
+constexpr int kMqWaves = kMqThreads / 64;
+constexpr int kMqPerWave = kMqQueries / kMqWaves;     // 2 queries per wave
 template <bool kFp4, int kBS>
-__global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
+__global__ __launch_bounds__(kMqThreads) void k_idx_scan_mq(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
     const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w, const int32_t* __restrict__ n_visible,
     int T, int n_max, int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
@@ -555,9 +571,15 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
   };
   int nv_max = 0;                             // the group's visible range
   for (int i = 0; i < nq; ++i) nv_max = max(nv_max, visible(i));
-  const bool has_q = wave < nq;
-  const int q = b * T + t0 + (has_q ? wave : 0);
-  const int p_end_q = has_q ? min(p_begin + chunk, visible(wave)) : p_begin;   // this wave's query
+  bool has_q[kMqPerWave];
+  int q[kMqPerWave], p_end_q[kMqPerWave];
+#pragma unroll
+  for (int i = 0; i < kMqPerWave; ++i) {
+    const int qi = kMqPerWave * wave + i;
+    has_q[i] = qi < nq;
+    q[i] = b * T + t0 + (has_q[i] ? qi : 0);
+    p_end_q[i] = has_q[i] ? min(p_begin + chunk, visible(qi)) : p_begin;
+  }
   const int p_end = min(p_begin + chunk, nv_max);
   const int npos = max(0, p_end - p_begin);
   const int nsteps = (npos + kMqRows - 1) / kMqRows;
@@ -566,56 +588,63 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
   const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
   const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
 
+  constexpr int kReps = kFp4 ? 1 : 2;          // staged pieces per thread
   const int srow = kFp4 ? tid >> 2 : tid >> 3, piece = kFp4 ? tid & 3 : tid & 7;
-  const bool stager = !kFp4 || tid < 4 * kMqRows;
-  u32x4 pre = {0u, 0u, 0u, 0u};
+  u32x4 pre[kReps];
   uint32_t pre_sc = 0u;
   auto load_step = [&](int st) {
-    const int64_t p = min(p_begin + kMqRows * st + srow, plast);
-    if constexpr (kFp4) {
-      if (stager) {
-        pre = *(const u32x4*)(kseq + p * (kIdxDim / 2) + 16 * piece);
+#pragma unroll
+    for (int rep = 0; rep < kReps; ++rep) {
+      const int64_t p = min(p_begin + kMqRows * st + srow + 64 * rep, plast);
+      if constexpr (kFp4) {
+        pre[rep] = *(const u32x4*)(kseq + p * (kIdxDim / 2) + 16 * piece);
         pre_sc = *(const uint16_t*)(sseq + p * (kIdxDim / 16) + 2 * piece);
+      } else {
+        pre[rep] = *(const u32x4*)(kseq + p * kIdxDim + 16 * piece);
       }
-    } else {
-      pre = *(const u32x4*)(kseq + p * kIdxDim + 16 * piece);
     }
   };
   auto store_step = [&](int buf) {
-    unsigned char* d = stage[buf] + srow * kMqStride;
-    if constexpr (kFp4) {
-      if (stager) {
+#pragma unroll
+    for (int rep = 0; rep < kReps; ++rep) {
+      unsigned char* d = stage[buf] + (srow + 64 * rep) * kMqStride;
+      if constexpr (kFp4) {
         u32x4 o[4];
-        fp4_operands(pre, pre_sc, o);
+        fp4_operands(pre[rep], pre_sc, o);
 #pragma unroll
         for (int c = 0; c < 4; ++c) *(u32x4*)(d + 64 * piece + 16 * c) = o[c];
+      } else {
+        *(u32x4*)(d + 32 * piece) = e4m3x8_to_bf16x8(pre[rep].x, pre[rep].y);
+        *(u32x4*)(d + 32 * piece + 16) = e4m3x8_to_bf16x8(pre[rep].z, pre[rep].w);
       }
-    } else {
-      *(u32x4*)(d + 32 * piece) = e4m3x8_to_bf16x8(pre.x, pre.y);
-      *(u32x4*)(d + 32 * piece + 16) = e4m3x8_to_bf16x8(pre.z, pre.w);
     }
   };
 
   // Scores of step s go to sstage[s & 1] and are written to global memory, coalesced, during step
-  // s+1 (by every thread: query tid / 64, two positions each), so the stores have a whole step to
+  // s+1 (by every thread: query tid / 32, four positions each), so the stores have a whole step to
   // complete before the next wait on the staged key loads.
-  const int oq = tid >> 6, opos = 2 * (tid & 63);
+  const int oq = tid >> 5, opos = 4 * (tid & 31);
   const int oq_end = oq < nq ? min(p_begin + chunk, visible(oq)) : p_begin;
   float* oscores = scores + (size_t)(b * T + t0 + (oq < nq ? oq : 0)) * n_max;
   auto flush_scores = [&](int st) {
     const int p = p_begin + kMqRows * st + opos;
-    const f32x2 v = *(const f32x2*)&sstage[st & 1][oq][opos];
-    if (p + 1 < oq_end) {
-      __builtin_nontemporal_store(v, (f32x2*)(oscores + p));
-    } else if (p < oq_end) {
-      __builtin_nontemporal_store(v.x, oscores + p);
+    const f32x4 v = *(const f32x4*)&sstage[st & 1][oq][opos];
+    if (p + 3 < oq_end) {
+      __builtin_nontemporal_store(v, (f32x4*)(oscores + p));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p + e < oq_end) __builtin_nontemporal_store(v[e], oscores + p + e);
     }
   };
-  uint32_t* wk = wkeys[wave];
   if (nsteps > 0) {
+    // The query operands are loaded before the first keys, so waiting for those keys also covers
+    // them and no wait for an operand load is left inside the step loop.
+    Ctx32 cx[kMqPerWave];
+#pragma unroll
+    for (int i = 0; i < kMqPerWave; ++i)      // a missing query scores the group's first one
+      load_ctx32<kFp4>(cx[i], idx_q + (size_t)q[i] * kIdxHeads * kIdxDim, head_w + (size_t)q[i] * kIdxHeads);
     load_step(0);
-    Ctx32 cx;
-    if (has_q) load_ctx32<kFp4>(cx, idx_q + (size_t)q * kIdxHeads * kIdxDim, head_w + (size_t)q * kIdxHeads);
     store_step(0);
     if (nsteps > 1) load_step(1);
     __syncthreads();
@@ -623,16 +652,41 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
     for (int st = 0; st < nsteps; ++st) {
       if (st > 0) flush_scores(st - 1);
       const unsigned char* d = stage[st & 1] + r32 * kMqStride;
-      float* so = sstage[st & 1][wave];
-      if (has_q && p_begin + kMqRows * st < p_end_q) {
-#pragma unroll 2
-        for (int m = 0; m < kMqRows / 32; ++m) {
-          const float sc = score32<kFp4>(cx, d + 32 * m * kMqStride);
+      bool act[kMqPerWave];
+#pragma unroll
+      for (int i = 0; i < kMqPerWave; ++i) act[i] = has_q[i] && p_begin + kMqRows * st < p_end_q[i];
+      if (act[0] || act[1]) {
+        // Software-pipelined over the step's 32-row groups: the MFMAs of group m+1 are issued
+        // before the reductions of group m, so the two overlap within the wave.  Both queries are
+        // scored; the LDS scores and keys of an inactive one lie past its visible range, where they
+        // are never read.
+        f32x16 acc[2][kMqPerWave];
+        auto issue = [&](int m, f32x16 (&a)[kMqPerWave]) {
+          u32x4 bk[8];
+          load_bk32(d + 32 * m * kMqStride, bk);
+          mfma_chains32<kFp4>(cx[0], cx[1], bk, a[0], a[1]);
+        };
+        auto finish = [&](int m, const f32x16 (&a)[kMqPerWave]) {
           const int pl = kMqRows * st + 32 * m + r32;               // position within the chunk
-          const bool valid = p_begin + pl < p_end_q;
-          const uint32_t key = block_key<kBS>(sc, valid);
-          if (lane < 32) so[32 * m + r32] = sc;
-          if ((lane & 0x27) == 0 && pl < 8 * nblk_g) wk[pl >> 3] = key;   // lanes 0, 8, 16, 24
+          float sc[kMqPerWave];
+          uint32_t key[kMqPerWave];
+#pragma unroll
+          for (int i = 0; i < kMqPerWave; ++i) {
+            sc[i] = reduce32(cx[i], a[i]);
+            key[i] = block_key<kBS>(sc[i], p_begin + pl < p_end_q[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < kMqPerWave; ++i) {
+            const int qi = kMqPerWave * wave + i;
+            if (lane < 32) sstage[st & 1][qi][32 * m + r32] = sc[i];
+            if ((lane & 0x27) == 0 && pl < 8 * nblk_g) wkeys[qi][pl >> 3] = key[i];   // lanes 0, 8, 16, 24
+          }
+        };
+        issue(0, acc[0]);
+#pragma unroll
+        for (int m = 0; m < kMqRows / 32; ++m) {
+          if (m + 1 < kMqRows / 32) issue(m + 1, acc[(m + 1) & 1]);
+          finish(m, acc[m & 1]);
         }
       }
       if (st + 1 < nsteps) {
@@ -643,37 +697,43 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan_mq(
     }
     flush_scores(nsteps - 1);
   }
-  if (!has_q) return;
-  // block keys and unit lists of this wave's query (its own LDS keys: no barrier needed)
-  const int nblk = (max(0, p_end_q - p_begin) + kBlock - 1) / kBlock;
-  if (blkkey) {
-    uint32_t* brow = blkkey + (size_t)q * nb_max + p_begin / kBlock;
-    for (int i = lane; i < nblk; i += 64) brow[i] = wk[i];
-  }
-  if (!lists) return;
-  // lane u < 16*upw keeps the five best ranking keys of unit u (bpu blocks), inserted one block at
-  // a time (the keys are distinct, so the visiting order does not matter; it is rotated per lane
-  // to spread the LDS reads over the banks)
+  // block keys and unit lists of this wave's queries (its own LDS keys: no barrier needed)
   const int bpu = chunk / (kBlock * kScanUnitsPerWg * upw);
-  if (lane < kScanUnitsPerWg * upw) {
-    const int ub = lane * bpu;
-    uint64_t best[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
-    const int rot = lane % bpu;
-    for (int i = 0; i < bpu; ++i) {
-      const int o = i + rot < bpu ? i + rot : i + rot - bpu;
-      uint64_t x = ub + o < nblk ? rank_key(wk[ub + o], (uint32_t)(p_begin / kBlock + ub + o)) : 0ull;
-#pragma unroll
-      for (int r = 0; r < 5; ++r) {
-        const uint64_t hi = x > best[r] ? x : best[r];
-        x = x > best[r] ? best[r] : x;
-        best[r] = hi;
-      }
+#pragma unroll 1
+  for (int i = 0; i < kMqPerWave; ++i) {
+    const int qi = kMqPerWave * wave + i;     // (recomputed: no dynamically indexed register arrays)
+    if (qi >= nq) break;
+    const int qg = b * T + t0 + qi;
+    const uint32_t* wk = wkeys[qi];
+    const int nblk = (max(0, min(p_begin + chunk, visible(qi)) - p_begin) + kBlock - 1) / kBlock;
+    if (blkkey) {
+      uint32_t* brow = blkkey + (size_t)qg * nb_max + p_begin / kBlock;
+      for (int e = lane; e < nblk; e += 64) brow[e] = wk[e];
     }
-    const size_t unit = ((size_t)q * gridDim.x + blockIdx.x) * kScanUnitsPerWg * upw + lane;
-    u32x4* lp = (u32x4*)(lists + unit * 4);
-    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
-    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
-    cuts[unit] = best[4];
+    if (!lists) continue;
+    // lane u < 16*upw keeps the five best ranking keys of unit u (bpu blocks), inserted one block
+    // at a time (the keys are distinct, so the visiting order does not matter; it is rotated per
+    // lane to spread the LDS reads over the banks)
+    if (lane < kScanUnitsPerWg * upw) {
+      const int ub = lane * bpu;
+      uint64_t best[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
+      const int rot = lane % bpu;
+      for (int e = 0; e < bpu; ++e) {
+        const int o = e + rot < bpu ? e + rot : e + rot - bpu;
+        uint64_t x = ub + o < nblk ? rank_key(wk[ub + o], (uint32_t)(p_begin / kBlock + ub + o)) : 0ull;
+#pragma unroll
+        for (int r = 0; r < 5; ++r) {
+          const uint64_t hi = x > best[r] ? x : best[r];
+          x = x > best[r] ? best[r] : x;
+          best[r] = hi;
+        }
+      }
+      const size_t unit = ((size_t)qg * gridDim.x + blockIdx.x) * kScanUnitsPerWg * upw + lane;
+      u32x4* lp = (u32x4*)(lists + unit * 4);
+      lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
+      lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
+      cuts[unit] = best[4];
+    }
   }
 }
 
@@ -707,7 +767,7 @@ static void launch_scan_variant(const uint8_t* idx_k, const uint8_t* idx_ks, int
                                 bool multi_query, int upw, hipStream_t s) {
   if (multi_query) {
     const int groups = (Q / T) * ((T + kMqQueries - 1) / kMqQueries);
-    hipLaunchKernelGGL((k_idx_scan_mq<kFp4, kBS>), dim3(n_wg, groups), dim3(kFullThreads), 0, s, idx_k, idx_ks, k_rows,
+    hipLaunchKernelGGL((k_idx_scan_mq<kFp4, kBS>), dim3(n_wg, groups), dim3(kMqThreads), 0, s, idx_k, idx_ks, k_rows,
                        idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists, cuts, upw);
   } else {
     hipLaunchKernelGGL((k_idx_scan<kFp4, kBS>), dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
