@@ -42,6 +42,7 @@ struct __attribute__((aligned(16))) SelectSmem {
   uint32_t hist[kBins + 64];             // all zero between passes; bins kBins.. take strays
   uint64_t rankbuf[kRankMax];
   uint32_t rankpart[3][kRankMax];        // partial ranks from quarters 1..3
+  uint32_t eqpart[3][kRankMax];          // partial counts of equal keys from quarters 1..3
   u32x4 wred[2][kWaves];                 // per-wave partials of block reductions
   uint32_t ecnt[2][kE * kWaves];         // per-(element, wave) totals of ordered_offsets
   uint64_t result;
@@ -173,8 +174,9 @@ __device__ __forceinline__ void find_bin(uint32_t need, Block& bk) {
 __device__ __forceinline__ uint64_t key_lo(uint32_t mn32) { return (uint64_t)mn32 << 32; }
 __device__ __forceinline__ uint64_t key_hi(uint32_t mx32) { return ((uint64_t)mx32 << 32) | 0xffffffffull; }
 
-// The need-th largest of a set of distinct 64-bit keys, all inside [lo, hi] (1 <= need <= the
-// number of keys).  for_each(f) calls f(key) for every key this thread holds (0 = none; keys
+// The need-th largest of a set of 64-bit keys, counted with repeats, all inside [lo, hi]
+// (1 <= need <= the number of keys).  Keys are distinct except when a caller's pool lists a
+// position more than once.  for_each(f) calls f(key) for every key this thread holds (0 = none; keys
 // outside [lo, hi] are ignored).  If `cand` is non-null, the keys of a bin with at most
 // kCandCap keys are copied there once and later passes read only the copy.
 // Requires a clear histogram (smem_init); leaves it clear.
@@ -242,17 +244,26 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
       const uint32_t i = threadIdx.x % kRankMax, part = threadIdx.x / kRankMax;
       const uint64_t x = sm.rankbuf[i];
       const uint32_t m0 = part * kPart, m1 = min(cnt, m0 + kPart);
-      uint32_t r = 0, m = m0;
+      uint32_t r = 0, eq = 0, m = m0;
       for (; m + 2 <= m1; m += 2) {
         const u64x2 v = *(const u64x2*)(sm.rankbuf + m);
         r += (v.x > x ? 1u : 0u) + (v.y > x ? 1u : 0u);
+        eq += (v.x == x ? 1u : 0u) + (v.y == x ? 1u : 0u);
       }
-      if (m < m1) r += sm.rankbuf[m] > x ? 1u : 0u;
-      if (part) sm.rankpart[part - 1][i] = r;
+      if (m < m1) {
+        r += sm.rankbuf[m] > x ? 1u : 0u;
+        eq += sm.rankbuf[m] == x ? 1u : 0u;
+      }
+      if (part) {
+        sm.rankpart[part - 1][i] = r;
+        sm.eqpart[part - 1][i] = eq;
+      }
       __syncthreads();
       if (part == 0 && i < cnt) {
         r += sm.rankpart[0][i] + sm.rankpart[1][i] + sm.rankpart[2][i];
-        if (r == need - 1) sm.result = x;
+        eq += sm.eqpart[0][i] + sm.eqpart[1][i] + sm.eqpart[2][i];
+        // fewer than need keys above x, at least need at or above it (every copy of x agrees)
+        if (r < need && need <= r + eq) sm.result = x;
       }
       __syncthreads();
       return sm.result;
@@ -285,10 +296,22 @@ __device__ __forceinline__ void topk_out(const uint64_t (&key)[kE], uint32_t nva
   uint32_t c[kE], off[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) c[e] = key[e] >= thr ? 1u : 0u;
-  const uint32_t total = ordered_offsets<true>(c, off, bk);
+  uint32_t total = ordered_offsets<true>(c, off, bk);
+  if (total > (uint32_t)k) {
+    // a position listed more than once ties with itself at the threshold: every key above thr
+    // stays, and copies of thr fill the remaining places in slot order
+    uint32_t g[kE], goff[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) g[e] = key[e] == thr ? 1u : 0u;
+    const uint32_t n_eq = ordered_offsets<true>(g, goff, bk);
+    const uint32_t room = (uint32_t)k - (total - n_eq);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) c[e] = (key[e] > thr || (g[e] && goff[e] < room)) ? 1u : 0u;
+    total = ordered_offsets<true>(c, off, bk);
+  }
 #pragma unroll
   for (int e = 0; e < kE; ++e) {
-    if (c[e] && off[e] < (uint32_t)k) {   // duplicate positions in a caller pool can tie
+    if (c[e] && off[e] < (uint32_t)k) {
       oi[off[e]] = (int32_t)rank_key_index(key[e]);
       if (os) os[off[e]] = key_score((uint32_t)(key[e] >> 32));
     }

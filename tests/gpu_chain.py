@@ -192,6 +192,25 @@ def assert_topk_equiv(gpu_idx, ref_idx, ref_score_at, what=""):
     return len(diff)
 
 
+def assert_topk_multiset_equiv(gpu_idx, ref_idx, ref_score_at, what=""):
+    """As assert_topk_equiv, for pools that list a position more than once: outputs are
+    non-decreasing, and copies count (multiset comparison)."""
+    from collections import Counter
+    g = np.asarray(gpu_idx)
+    r = np.asarray(ref_idx)
+    gv, rv = g[g >= 0], r[r >= 0]
+    assert np.all(g[len(gv):] == -1) and np.all(np.diff(gv) >= 0), f"{what}: GPU output not sorted/padded"
+    assert len(gv) == len(rv), f"{what}: {len(gv)} selected vs {len(rv)}"
+    cg, cr = Counter(gv.tolist()), Counter(rv.tolist())
+    diff = list((cg - cr).elements()) + list((cr - cg).elements())
+    if diff:
+        sK = min(ref_score_at(p) for p in rv.tolist())
+        for p in diff:
+            assert abs(ref_score_at(p) - sK) <= TIE_REL * abs(sK), (
+                f"{what}: position {p} (score {ref_score_at(p)}) differs beyond the tie band of s_K={sK}")
+    return len(diff)
+
+
 def assert_pool_equiv(gpu_pool, gpu_len, ref_pool, ref_s32, n_vis, block, P, what="", mode="max"):
     gp = np.asarray(gpu_pool[:gpu_len])
     assert gpu_len == len(ref_pool), f"{what}: pool length {gpu_len} vs {len(ref_pool)}"

@@ -350,6 +350,34 @@ def test_reindex_user_pools_with_invalid_entries():
         G.assert_topk_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"user pool t{t}")
 
 
+def test_reindex_user_pool_with_repeated_positions():
+    """A caller pool listing some positions two or three times: copies rank like the position
+    (score desc, position asc, counted with repeats), as the oracle's stable ranking orders them,
+    including copies that straddle the K-th place."""
+    K = 512
+    w = small("reindex_pool_256k", T=2, N=50000, user_pool=3000, top_k=K, seed=67)
+    inp = workloads.make_inputs(w, with_attention=False)
+    pp = inp["pool_pos"].copy()
+    pl = inp["pool_len"].copy()
+    for t in range(2):
+        pool = pp[0, t, :pl[0, t]].astype(np.int64)
+        base = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][0, 0, t], inp["ri_w"][0, 0, t], pool, len(pool))
+        order = O.rank_order(O.ranking_scores(base["scores"]), pool)
+        picks = pool[order[[0, 10, 508, 509, 510, 511, 700]]]
+        extra = np.concatenate([picks, picks[[1, 4]]])        # two positions three times
+        keep = np.setdiff1d(pool, pool[order[-len(extra):]])   # drop the lowest-ranked to fit
+        new = np.sort(np.concatenate([keep, extra]))
+        assert len(new) == pl[0, t]
+        pp[0, t, :len(new)] = new
+    gpu = G.gpu_reindex(inp, 1, 2, pp, pl, K)
+    for t in range(2):
+        pool = pp[0, t, :pl[0, t]]
+        r = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][0, 0, t], inp["ri_w"][0, 0, t], pool, K)
+        assert len(r["topk"][r["topk"] >= 0]) != len(set(r["topk"][r["topk"] >= 0].tolist()))  # repeats kept
+        sc = dict(zip(pool.tolist(), r["scores"].tolist()))
+        G.assert_topk_multiset_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"repeated t{t}")
+
+
 # ------------------------------------------------------------------ attention
 
 @pytest.mark.parametrize("H", [32, 64, 128])
