@@ -491,29 +491,42 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     }
     // the next chunk into the other buffer (last read before the previous barrier), then the
     // raw rows of the chunk after it
-    if (c + 1 < nchunks) {
-      store_row8(raw, X[(c + 1) & 1] + my_row * kXStride, eighth);
-      if (eighth == 0) rowok[(c + 1) & 1][my_row] = raw.kind != 0;
-      if (c + 2 < nchunks) {
-        load_chunk(raw, c + 2, pos_c);
-        pos_c = c + 3 < nchunks ? row_index(c + 3) : -1;
+    auto dequant_next = [&]() {
+      if (c + 1 < nchunks) {
+        store_row8(raw, X[(c + 1) & 1] + my_row * kXStride, eighth);
+        if (eighth == 0) rowok[(c + 1) & 1][my_row] = raw.kind != 0;
+        if (c + 2 < nchunks) {
+          load_chunk(raw, c + 2, pos_c);
+          pos_c = c + 3 < nchunks ? row_index(c + 3) : -1;
+        }
       }
-    }
+    };
     // O[head 4g+v][dim 256*hf + 16*u + j] += sum_r P[head][r] X[r][dim].  The B operand of tile u
     // (rows 32kk + 8g .. +7 of dim 256hf + 16u + j in lane (j, g)) comes straight from row-major X
     // by two LDS transpose reads: in each 16-lane group, lane 4a+b receives element b of the
     // 8 bytes addressed by lanes a, a+4, a+8 and a+12, so lane j = 4a+i addresses row
     // 32kk + 8g + i (+4 for the second read), dims 256hf + 16u + 4a .. +3.
+    auto accumulate = [&]() {
 #pragma unroll
-    for (int kk = 0; kk < kRows / 32; ++kk) {
-      const u32x4 pa = *(const u32x4*)(Pg + j * kPStride + 32 * kk + 8 * g);
-      const uint16_t* xt = Xc + (32 * kk + 8 * g + (j >> 2)) * kXStride + 256 * hf + 4 * (j & 3);
+      for (int kk = 0; kk < kRows / 32; ++kk) {
+        const u32x4 pa = *(const u32x4*)(Pg + j * kPStride + 32 * kk + 8 * g);
+        const uint16_t* xt = Xc + (32 * kk + 8 * g + (j >> 2)) * kXStride + 256 * hf + 4 * (j & 3);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const u32x2 lo = ds_read_tr16(xt + 16 * u);
-        const u32x2 hi = ds_read_tr16(xt + 4 * kXStride + 16 * u);
-        o[u] = mfma16x16x32(pa, u32x4{lo.x, lo.y, hi.x, hi.y}, o[u]);
+        for (int u = 0; u < 16; ++u) {
+          const u32x2 lo = ds_read_tr16(xt + 16 * u);
+          const u32x2 hi = ds_read_tr16(xt + 4 * kXStride + 16 * u);
+          o[u] = mfma16x16x32(pa, u32x4{lo.x, lo.y, hi.x, hi.y}, o[u]);
+        }
       }
+    };
+    // Waves w and w + 4 share a SIMD (one of each half): one dequantises while the other runs its
+    // MFMAs, then they swap, so the VALU and matrix work of the pair overlap.
+    if (hf == 0) {
+      accumulate();
+      dequant_next();
+    } else {
+      dequant_next();
+      accumulate();
     }
     if (c + 1 < nchunks) __syncthreads();            // next chunk's X and rowok written; P, red_* free
   }
