@@ -10,6 +10,7 @@ oracle checks sampled queries.
   encoder_1m       the last 256-token chunk of a 1M-token prompt (512K entries) through 3 encoder
                    groups of Full + 5 Reuse, 64 heads (csa2_encoder_chunk)
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -17,8 +18,9 @@ import pytest
 import torch
 
 import workloads
+from oracle import csa2 as O
 from tests import gpu_chain as G
-from tests.test_gpu_parity import run_chain_and_check
+from tests.test_gpu_parity import check_full, run_chain_and_check
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +131,50 @@ def test_encoder_1m_chunk_sampled():
                                     w.swa_window)
             o, _ = O.attention(inp["q"][g, l, 0, t], rows, 1.0 / math.sqrt(512))
             G.assert_attention_close(out[g, l, 0, t], o, f"encoder g{g} l{l} t{t}")
+
+
+def test_index_chain_at_the_largest_full_context():
+    """The Full layer at its largest context, 2^21 positions (256 chunks of 8192 positions: the
+    largest LDS staging, and units of 64 blocks), through the chain entries: pool, Full Top-K and
+    the 4 Reindex Top-Ks against the oracle, and the planted cluster recalled."""
+    w = dataclasses.replace(workloads.WORKLOADS["decode_1m"], name="decode_2m", N=1 << 21, seed=1011)
+    inp = workloads.make_inputs(w, with_attention=False)
+    _announce(w.name, [(0, 0)])
+    c = G.gpu_index_chain(inp, 1, 1, w.N, w.pool_blocks, w.top_k, w.n_reindex, split=True)
+    check_full(w, inp, c, 0, 0)
+    assert np.isin(inp["planted_pos"], c["topk"][0, 0]).all(), "planted cluster not recalled"
+    pool = c["pool_pos"][0, 0, :c["pool_len"][0, 0]]
+    for r in range(w.n_reindex):
+        ref = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][r, 0, 0], inp["ri_w"][r, 0, 0], pool, w.top_k)
+        sc = dict(zip(pool.tolist(), ref["scores"].tolist()))
+        G.assert_topk_equiv(c["ri_topk"][r, 0, 0], ref["topk"], lambda p: sc[p], f"ri{r}")
+
+
+@pytest.mark.parametrize("T,N", [(1, 1 << 23), (16, 1 << 20)])
+def test_index_scores_at_the_largest_context(T, N):
+    """Scores at the largest contexts the scans take: 2^23 positions for one query (1024
+    workgroups of 8192 positions) and 2^20 positions for 16 queries of one sequence in the
+    multi-query scan (its limit), with the last queries' visibility ragged.  Keys are random
+    E4M3 codes (every finite value); sampled positions (both ends, every chunk boundary, random
+    ones) against the oracle, and nothing written past a query's visible range."""
+    rng = np.random.default_rng(1013 + T)
+    k8 = rng.integers(0, 256, size=(1, N, 128), dtype=np.uint8)
+    k8[(k8 & 0x7F) == 0x7F] ^= 1                                  # no NaN codes
+    inp = {"idx_k": k8,
+           "idx_q": workloads.to_bf16_bits(rng.standard_normal((1, T, 32, 128), dtype=np.float32)),
+           "head_w": rng.random((1, T, 32), dtype=np.float32),
+           "n_visible": np.array([[N - 3 * t for t in range(T)]], np.int32)}
+    _announce(f"scores over {N} positions", [(0, t) for t in range(T)])
+    s = G.gpu_index_scores(inp, 1, T, N)
+    edges = np.arange(1024, N, 1024)                               # every chunk boundary
+    for t in sorted({0, T - 1, T // 2}):
+        n = int(inp["n_visible"][0, t])
+        pos = np.unique(np.concatenate([np.arange(2048), np.arange(n - 2048, n), edges - 1, edges,
+                                        rng.integers(0, n, 4096)]))
+        pos = pos[pos < n]
+        q8 = O.quantize_query(inp["idx_q"][0, t])
+        keys = O.k_rows(k8[0], pos)
+        ref = O.indexer_scores(keys, q8, inp["head_w"][0, t])
+        bound = G.score_abs_bound(keys, inp["idx_q"][0, t], inp["head_w"][0, t])
+        G.assert_scores_close(s[0, t, pos], ref, bound, f"t{t}")
+        assert np.all(np.isnan(s[0, t, n:])), "scores beyond n_visible must be untouched"

@@ -433,6 +433,29 @@ def test_attention_rescales_when_logits_grow_by_chunk(NH):
         assert np.allclose(lse[l, 0, t], ls, rtol=1e-3, atol=1e-3)
 
 
+@pytest.mark.parametrize("H", [16, 64])
+def test_attention_at_the_largest_sets_and_window(H):
+    """The attention's limits: Top-2048 index sets merged with a 4096-row window (6144 rows, split
+    over the most workgroups the plan takes), positions up to the last main-KV row; one query with
+    full sets and window, one with a partial set and window."""
+    K, W, N = 2048, 4096, 9000
+    w = small(B=1, T=2, N=N, H=H, layer_set=(0,), n_reindex=0, pool_blocks=0, top_k=K, swa_window=W,
+              seed=107 + H)
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(11)
+    sets = np.full((1, 1, 2, K), -1, np.int32)
+    sets[0, 0, 0] = np.sort(np.concatenate([rng.choice(N - 1, K - 1, replace=False), [N - 1]]))
+    sets[0, 0, 1, :1500] = np.sort(rng.choice(N, 1500, replace=False))
+    inp["swa_end"] = np.array([[W, 1000]], np.int32)
+    out, lse = G.gpu_attention(inp, w, sets)
+    for t in range(2):
+        rows = O.attention_rows(inp["kv_codes"][0], inp["kv_scales"][0], sets[0, 0, t], inp["swa"][0, 0],
+                                int(inp["swa_end"][0, t]), W)
+        o, ls = O.attention(inp["q"][0, 0, t], rows, 1 / math.sqrt(512))
+        G.assert_attention_close(out[0, 0, t], o, f"t{t}")
+        assert np.allclose(lse[0, 0, t], ls, rtol=1e-3, atol=1e-3)
+
+
 # ------------------------------------------------------------------ whole chain
 
 def run_chain_and_check(w, inp, queries):
