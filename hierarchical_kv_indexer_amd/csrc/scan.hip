@@ -626,10 +626,11 @@ __global__ __launch_bounds__(kMqThreads) void k_idx_scan_mq(
   const int oq = tid >> 5, opos = 4 * (tid & 31);
   const int oq_end = oq < nq ? min(p_begin + chunk, visible(oq)) : p_begin;
   float* oscores = scores + (size_t)(b * T + t0 + (oq < nq ? oq : 0)) * n_max;
+  const bool rows16 = (n_max & 3) == 0;       // score rows 16-byte aligned (p is a multiple of 4)
   auto flush_scores = [&](int st) {
     const int p = p_begin + kMqRows * st + opos;
     const f32x4 v = *(const f32x4*)&sstage[st & 1][oq][opos];
-    if (p + 3 < oq_end) {
+    if (rows16 && p + 3 < oq_end) {
       __builtin_nontemporal_store(v, (f32x4*)(oscores + p));
     } else {
 #pragma unroll

@@ -159,10 +159,11 @@ def ragged_visibility(B, T, N, seed):
 
 @pytest.mark.parametrize("fp4", [False, True])
 @pytest.mark.parametrize("B,T,N,nv", [(1, 1, 4096, None), (2, 3, 4093, [4093, 4000, 17, 0, 8, 1]),
-                                      (2, 37, 9000, "ragged")])
+                                      (2, 37, 9000, "ragged"), (1, 20, 9003, "ragged")])
 def test_index_scores_parity(B, T, N, nv, fp4):
     """Scores of every visible position, E4M3 keys and FP4 keys; T = 37 runs the multi-query scan
-    (groups of 16, 16 and 5 queries) over ragged causal visibility."""
+    (groups of 16, 16 and 5 queries) over ragged causal visibility, and T = 20 over score rows
+    that are not 16-byte aligned (N = 9003)."""
     w = small(B=B, T=T, N=N, seed=2000 + N, idx_k_fp4=fp4)
     inp = workloads.make_inputs(w, with_attention=False)
     if isinstance(nv, str):
