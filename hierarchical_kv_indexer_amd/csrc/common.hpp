@@ -89,6 +89,18 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | code;
 }
 
+// E2M1 magnitude code (0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6) of |x| / s for an E4M3 scale s > 0:
+// the number of decision points passed, 0.25, 1.25, 2.5 and 5 strictly (their ties go down to
+// the even code) and 0.75, 1.75 and 3.5 inclusively (their ties go up), compared with the exact
+// products t * s.  For a bf16 |x| this equals nearest-even rounding of the binary32 quotient:
+// x has 8 significant bits and t * s at most 7, so when |x| != t * s they differ by at least
+// ~2^-9 relative, far more than the quotient's rounding.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a, float s) {
+  return (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) + (uint32_t)(a > 1.25f * s) +
+         (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) +
+         (uint32_t)(a > 5.0f * s);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // float -> bf16 bits, round to nearest even (finite inputs).

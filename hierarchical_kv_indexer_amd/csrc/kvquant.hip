@@ -40,10 +40,7 @@ constexpr int kLutN = 768;
 // Code magnitude of the bf16 magnitude pattern `bits` for the scale 1 + m/8 (exponent 0), from
 // the decision points (exact products).
 __device__ __forceinline__ uint32_t e2m1_code_at(uint32_t bits, int m) {
-  const float a = bf16_bits_to_f32(bits), s = 1.0f + 0.125f * (float)m;
-  return (uint32_t)(a > 0.25f * s) + (uint32_t)(a >= 0.75f * s) + (uint32_t)(a > 1.25f * s) +
-         (uint32_t)(a >= 1.75f * s) + (uint32_t)(a > 2.5f * s) + (uint32_t)(a >= 3.5f * s) +
-         (uint32_t)(a > 5.0f * s);
+  return e2m1_mag_code(bf16_bits_to_f32(bits), 1.0f + 0.125f * (float)m);
 }
 
 constexpr int kQuantThreads = 256;

@@ -16,11 +16,13 @@
 // order inside an MFMA does not matter as long as the query operands use the same order,
 // which they do (both are read with the same byte offsets).
 //
-// FP4 indexer K (the variant the V4 indexer used; blog.4sapi.com sec.4): a position's key is 64
-// bytes of E2M1 codes (channel 2i in the low nibble of byte i) and 8 E4M3 scales, one per 16
-// channels, stored as two arrays.  code x scale is exact in fp16, and so is the E4M3 query, so
-// that contraction runs on the fp16 MFMA, again with exact products.  Lane (j, g) then takes channels [32g, 32g+32) of row j: its 16
-// code bytes and the row's 8 scale bytes (two of which it uses), and MFMA chunk c covers its
+// FP4 indexer (the V4 indexer stored its queries and keys in FP4; animattoys.com, FP4 section):
+// a position's key is 64 bytes of E2M1 codes (channel 2i in the low nibble of byte i) and 8 E4M3
+// scales, one per 16 channels, stored as two arrays.  With such keys the query is rounded to the
+// same format (per head and 16 channels: scale E4M3(amax/6), codes E2M1), instead of to E4M3.
+// Both code x scale values are exact in fp16, so that contraction runs on the fp16 MFMA, again
+// with exact products.  Lane (j, g) then takes channels [32g, 32g+32) of row j: its 16 code
+// bytes and the row's 8 scale bytes (two of which it uses), and MFMA chunk c covers its
 // channels 32g + 8c .. +7 on both operands.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -43,24 +45,57 @@ hipError_t launch_quantize_query(const uint16_t* in, uint8_t* out, int64_t n, hi
 }
 
 // Two bf16 query values (low half first) rounded to E4M3 (nearest, ties to even, saturating at
-// +-448) and returned as a bf16 pair, or an fp16 pair with kF16 (E4M3 values are exact in both):
-// clamp, the hardware conversion to E4M3 bytes, and its exact conversion back.
-template <bool kF16>
+// +-448) and returned as a bf16 pair (E4M3 values are exact in bf16): clamp, the hardware
+// conversion to E4M3 bytes, and its exact conversion back.
 __device__ __forceinline__ uint32_t q8_pair(uint32_t w) {
   typedef short v2s __attribute__((ext_vector_type(2)));
   const float lo = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w & 0xffffu), -448.f, 448.f);
   const float hi = __builtin_amdgcn_fmed3f(bf16_bits_to_f32(w >> 16), -448.f, 448.f);
   const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, lo, hi, 1.0f, false));
-  if constexpr (kF16)
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false));
-  else
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false));
 }
 
-// The 32x128 query of one indexer head set, rounded to E4M3 and held as bf16 in LDS.
-// NT threads, 4096/NT consecutive values each, loaded with 16-byte (or 8-byte) loads.
-// kF16: the values are held as fp16 instead of bf16 (exact either way: E4M3 fits both).
-template <int NT, bool kF16 = false>
+// FP4 rounding of the query for FP4 keys, in the keys' own format: per head and 16-channel
+// group, scale = E4M3(amax / 6) with a binary32 division, each value E2M1(x / scale) (nearest,
+// ties to the even code, saturating at 6, sign kept), all zero when the scale is 0.  The code is
+// the number of decision points passed (see e2m1_mag_code), compared with the group's exact
+// products t * scale; the value code x scale is exact in fp16 (at most 6 significant bits within
+// [2^-10, 2688]).
+struct Q4Group {
+  float lim[7];   // decision points x scale: 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (ties down / up)
+  float val[7];   // magnitudes x scale above each point: 0.5, 1, 1.5, 2, 3, 4, 6
+};
+__device__ __forceinline__ Q4Group q4_group(uint32_t amax_bits) {
+  const float s = e4m3_to_f32(f32_to_e4m3(bf16_bits_to_f32(amax_bits) / 6.0f));
+  constexpr float kLim[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  constexpr float kVal[7] = {0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  Q4Group g;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    g.lim[i] = s > 0.f ? kLim[i] * s : INFINITY;     // a zero scale keeps every value at 0
+    g.val[i] = kVal[i] * s;
+  }
+  return g;
+}
+// Two bf16 query values (low half first) of one group -> fp16 pair of code x scale.
+__device__ __forceinline__ uint32_t q4_pair(uint32_t w, const Q4Group& g) {
+  auto one = [&](uint32_t b) {
+    const float a = fabsf(bf16_bits_to_f32(b));
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) v = ((i & 1) ? a >= g.lim[i] : a > g.lim[i]) ? g.val[i] : v;
+    return (b & 0x8000u) ? -v : v;
+  };
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(one(w & 0xffffu), one(w >> 16)));
+}
+// Largest magnitude bit pattern of the bf16 pair w (patterns order like magnitudes).
+__device__ __forceinline__ uint32_t amax_bits2(uint32_t w) { return max(w & 0x7fffu, (w >> 16) & 0x7fffu); }
+
+// The 32x128 query of one indexer head set, held in LDS as MFMA operands: rounded to E4M3 and held
+// as bf16 for E4M3 keys; rounded to FP4 (q4_group) and held as fp16 for FP4 keys.
+// NT threads, 4096/NT consecutive values each, loaded with 16-byte (or 8-byte) loads; for FP4 keys
+// each thread loads the whole 16-channel group its values belong to.
+template <int NT, bool kFp4 = false>
 __device__ __forceinline__ void stage_query(const uint16_t* __restrict__ q, uint16_t* qlds) {
   constexpr int kPer = kIdxHeads * kIdxDim / NT;      // values per thread (16 or 4)
   static_assert(kPer == 16 || kPer == 4, "query staging assumes 256 or 1024 threads");
@@ -75,8 +110,22 @@ __device__ __forceinline__ void stage_query(const uint16_t* __restrict__ q, uint
     w[0] = a.x; w[1] = a.y;
   }
   uint32_t o[kPer / 2];
+  if constexpr (kFp4) {
+    // a group is this thread's 16 values, or those of 4 consecutive lanes (amax over the quad)
+    uint32_t m = 0u;
 #pragma unroll
-  for (int i = 0; i < kPer / 2; ++i) o[i] = q8_pair<kF16>(w[i]);
+    for (int i = 0; i < kPer / 2; ++i) m = max(m, amax_bits2(w[i]));
+    if constexpr (kPer == 4) {
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+      m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    }
+    const Q4Group g = q4_group(m);
+#pragma unroll
+    for (int i = 0; i < kPer / 2; ++i) o[i] = q4_pair(w[i], g);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer / 2; ++i) o[i] = q8_pair(w[i]);
+  }
   if constexpr (kPer == 16) {
     *(u32x4*)(qlds + base) = u32x4{o[0], o[1], o[2], o[3]};
     *(u32x4*)(qlds + base + 8) = u32x4{o[4], o[5], o[6], o[7]};
@@ -491,7 +540,8 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // A wave's query for 32x32x16 MFMAs: lane l holds head l % 32, channels 16c + 8(l/32) .. +7 in
-// qa[c] (rounded to E4M3, as bf16 or fp16), and the weights of the heads its outputs hold:
+// qa[c] (rounded to E4M3 as bf16 for E4M3 keys, to FP4 as fp16 for FP4 keys), and the weights
+// of the heads its outputs hold:
 // output v of lane l is head 8(v/4) + 4(l/32) + v%4.
 struct Ctx32 {
   u32x4 qa[8];
@@ -504,7 +554,15 @@ __device__ __forceinline__ void load_ctx32(Ctx32& cx, const uint16_t* __restrict
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const u32x4 v = *(const u32x4*)(q + r * kIdxDim + 16 * c + 8 * h);
-    cx.qa[c] = u32x4{q8_pair<kF16>(v.x), q8_pair<kF16>(v.y), q8_pair<kF16>(v.z), q8_pair<kF16>(v.w)};
+    if constexpr (kF16) {          // FP4 keys: group c of head r is split between lanes l and l ^ 32
+      uint32_t m = max(max(amax_bits2(v.x), amax_bits2(v.y)), max(amax_bits2(v.z), amax_bits2(v.w)));
+      const auto sw = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+      m = max(sw[0], sw[1]);
+      const Q4Group g = q4_group(m);
+      cx.qa[c] = u32x4{q4_pair(v.x, g), q4_pair(v.y, g), q4_pair(v.z, g), q4_pair(v.w, g)};
+    } else {
+      cx.qa[c] = u32x4{q8_pair(v.x), q8_pair(v.y), q8_pair(v.z), q8_pair(v.w)};
+    }
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) cx.w[v] = w[8 * (v >> 2) + 4 * h + (v & 3)];

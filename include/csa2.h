@@ -27,10 +27,13 @@
  *
  * Indexer keys, in every call that reads them (idx_k, idx_k_scales):
  *   - idx_k_scales == NULL: idx_k is [B][k_rows_per_seq][128] E4M3 bytes;
- *   - otherwise the FP4 variant (blog.4sapi.com sec.4: the V4 indexer used FP4 keys): idx_k is
- *     [B][k_rows_per_seq][64] E2M1 code bytes (channel 2i in the low nibble of byte i) and
- *     idx_k_scales [B][k_rows_per_seq][8] E4M3 scales, scale g covering channels 16g..16g+15;
- *     a key is code x scale (exact), 72 bytes per position instead of 128.
+ *   - otherwise the FP4 variant (animattoys.com, FP4 section: the V4 indexer kept its queries
+ *     and keys in FP4): idx_k is [B][k_rows_per_seq][64] E2M1 code bytes (channel 2i in the
+ *     low nibble of byte i) and idx_k_scales [B][k_rows_per_seq][8] E4M3 scales, scale g
+ *     covering channels 16g..16g+15; a key is code x scale (exact), 72 bytes per position
+ *     instead of 128.  With FP4 keys the bf16 indexer query is rounded to FP4 in the same
+ *     format instead of to E4M3: per head and 16-channel group, scale = E4M3(amax / 6) and
+ *     code = E2M1(x / scale) (the rule of csa2_quantize_kv_fp4).
  *
  * Conventions for every call:
  *   - tensor arguments are DEVICE pointers owned by the caller (except where marked host),

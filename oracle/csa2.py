@@ -19,13 +19,16 @@ Sources (DeepSeek-V4.1-Flash pages):
   [p2 3]    blog.4sapi.com, section 3 (how CSA2 is laid out): the encoder's layers 3-20 form three
             groups of six, one Full and five Reuse layers, over a sequence compressed m = 2
             tokens per entry.
+  [p3 FP4]  animattoys.com, FP4 section: V4 already stored the indexer's queries and keys in
+            FP4; the main KV now too, as E2M1 with one E4M3 scale per 16 channels.
   [p3 modes] animattoys.com, the mode configuration: encoder groups of one Full then five Reuse
             layers; decoder groups with Reindex layers.
 
 Readings where the pages are silent (each one is listed in the design notes):
   * indexer score  s[p] = sum_h w_h * ReLU(q_h . k_p), with one 128-dim key per position
     shared by the 32 query heads, and the query rounded to E4M3 (round to nearest even,
-    saturating, unit scale) before the product;
+    saturating, unit scale) before the product; with FP4 keys the query is rounded to FP4 in
+    the keys' format instead (E2M1 codes, one E4M3 scale per 16 channels);
   * block score = max of the block's scores; blocks are 8 consecutive positions aligned
     at 0, the last one may be partial;
   * ranking ties: (score descending, index ascending), for blocks and for positions;
@@ -61,6 +64,31 @@ def quantize_query(q_bf16: np.ndarray) -> np.ndarray:
     return e4m3_from_value(bf16_value(q_bf16))
 
 
+def quantize_query_fp4(q_bf16: np.ndarray):
+    """Indexer query prep for FP4 keys ([p3 FP4]: the V4 indexer kept its queries and keys in
+    FP4): bf16 [..., 32, 128] -> (E2M1 codes [..., 32, 64], E4M3 scales [..., 32, 8]) in the
+    keys' format, each head's 16-channel group quantised as a main-KV group is (scale
+    E4M3(amax/6), codes E2M1 of x/scale; `formats.kv_quantize_rows`)."""
+    bits = np.asarray(q_bf16, dtype=np.uint16)
+    lead = bits.shape[:-2]
+    rows = bits.reshape(lead + (IDX_HEADS * IDX_DIM // KV_DIM, KV_DIM))   # 4 heads per 512-wide row
+    codes, scales = kv_quantize_rows(rows)
+    return (codes.reshape(lead + (IDX_HEADS, IDX_DIM // 2)), scales.reshape(lead + (IDX_HEADS, IDX_DIM // 16)))
+
+
+def query_for_keys(q_bf16: np.ndarray, k):
+    """The query prep that goes with the indexer K's storage form: E4M3 bytes for E4M3 keys, the
+    FP4 pair for FP4 keys (see k_values)."""
+    return quantize_query_fp4(q_bf16) if isinstance(k, tuple) else quantize_query(q_bf16)
+
+
+def query_values(q8) -> np.ndarray:
+    """Prepared query -> float64 [32][128]: E4M3 bytes, or the FP4 pair (code x scale, exact)."""
+    if isinstance(q8, tuple):
+        return kv_row_values(q8[0], q8[1])
+    return e4m3_value(q8)
+
+
 def k_rows(k, sel):
     """Rows `sel` (a slice or index array) of an indexer K in either storage form: E4M3 bytes
     [n][128], or the FP4 variant (codes [n][64], scales [n][8])."""
@@ -86,13 +114,13 @@ def k_values(k) -> np.ndarray:
 def indexer_scores(k8, q8: np.ndarray, w: np.ndarray) -> np.ndarray:
     """s[p] = sum_h w[h] * max(0, q8[h] . k[p])  in float64, for every row p of k.
 
-    k: indexer K rows, E4M3 bytes [n][128] or the FP4 pair (see k_values); q8 [32][128] E4M3
-    bytes, w [32] head weights.  [p1 4.2], [p2 2]: Full and Reindex layers score indexer K
-    with their own indexer Q.  Rows are processed in independent chunks only to bound memory.
-    Every product q8 * k is exact in float64 (at most 10 significant bits) and so is the
-    128-term sum.
+    k: indexer K rows, E4M3 bytes [n][128] or the FP4 pair (see k_values); q8 the prepared
+    query (query_values: E4M3 bytes [32][128] or the FP4 pair), w [32] head weights.  [p1 4.2],
+    [p2 2]: Full and Reindex layers score indexer K with their own indexer Q.  Rows are
+    processed in independent chunks only to bound memory.  Every product q8 * k is exact in
+    float64 (at most 12 significant bits) and so is the 128-term sum.
     """
-    qv = e4m3_value(q8)                                   # [32][128] float64
+    qv = query_values(q8)                                 # [32][128] float64
     wv = np.asarray(w, dtype=np.float32).astype(np.float64)
     n = k_count(k8)
     out = np.empty(n, np.float64)
@@ -168,7 +196,7 @@ def full_layer(k8_seq: np.ndarray, q_bf16: np.ndarray, w: np.ndarray, n_vis: int
     """One query of a Full layer: score every visible position, build the block pool
     (pool_blocks > 0) and take the Top-k over the pool ([p1 4.2], [p2 4]).  With
     pool_blocks == 0 there is no pool and the Top-k runs over every visible position."""
-    q8 = quantize_query(q_bf16)
+    q8 = query_for_keys(q_bf16, k8_seq)
     s = indexer_scores(k_rows(k8_seq, slice(0, n_vis)), q8, w)
     s32 = ranking_scores(s)
     if pool_blocks > 0:
@@ -188,7 +216,7 @@ def reindex_layer(k8_seq: np.ndarray, q_bf16: np.ndarray, w: np.ndarray,
     """One query of a Reindex layer: re-score only the pool positions with the layer's own
     indexer query and weights, then take its own Top-k ([p1 4.2], [p2 4], [p5 2])."""
     pool = np.asarray(pool, dtype=np.int64)
-    q8 = quantize_query(q_bf16)
+    q8 = query_for_keys(q_bf16, k8_seq)
     s = indexer_scores(k_rows(k8_seq, pool), q8, w)
     s32 = ranking_scores(s)
     idx = top_k(pool, s32, k)

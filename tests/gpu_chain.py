@@ -162,7 +162,7 @@ def host_keys(inp, b):
 
 def score_abs_bound(k8_rows, q_bf16: np.ndarray, w: np.ndarray) -> np.ndarray:
     """A = sum_h |w_h| sum_c |q8_hc| |k_pc| for each row (keys in either storage form)."""
-    qa = np.abs(F.e4m3_value(O.quantize_query(q_bf16)))
+    qa = np.abs(O.query_values(O.query_for_keys(q_bf16, k8_rows)))
     ka = np.abs(O.k_values(k8_rows))
     return ka @ qa.T @ np.abs(w.astype(np.float64))
 

@@ -172,8 +172,8 @@ def test_index_scores_at_the_largest_context(T, N):
         pos = np.unique(np.concatenate([np.arange(2048), np.arange(n - 2048, n), edges - 1, edges,
                                         rng.integers(0, n, 4096)]))
         pos = pos[pos < n]
-        q8 = O.quantize_query(inp["idx_q"][0, t])
         keys = O.k_rows(k8[0], pos)
+        q8 = O.query_for_keys(inp["idx_q"][0, t], keys)
         ref = O.indexer_scores(keys, q8, inp["head_w"][0, t])
         bound = G.score_abs_bound(keys, inp["idx_q"][0, t], inp["head_w"][0, t])
         G.assert_scores_close(s[0, t, pos], ref, bound, f"t{t}")

@@ -61,7 +61,8 @@ def test_scan_every_e4m3_code_exact():
 def test_scan_every_fp4_key_code_and_scale_exact():
     """FP4 keys: row r holds code r % 16 in channel c(r) with scale byte r // 16 in that channel's
     group (every code x every finite positive scale, channels spread over all lanes and groups);
-    queries +1 / -1 on that channel give ReLU(+-code x scale) exactly."""
+    queries +1.5 / -1.5 on that channel (exact in FP4: code 6 x scale 0.25) give
+    ReLU(+-1.5 x code x scale) exactly."""
     sc_bytes = np.arange(1, 127, dtype=np.uint8)                 # every finite positive E4M3 scale
     n = 16 * len(sc_bytes)
     codes = np.zeros((1, n, 64), np.uint8)
@@ -76,14 +77,15 @@ def test_scan_every_fp4_key_code_and_scale_exact():
         rows_by_ch.setdefault(int(c), []).append(i)
     for c, rows in sorted(rows_by_ch.items())[:128]:
         qf = np.zeros((1, 2, 32, 128), np.float32)
-        qf[0, 0, 0, c], qf[0, 1, 0, c] = 1.0, -1.0
+        qf[0, 0, 0, c], qf[0, 1, 0, c] = 1.5, -1.5
+        assert O.query_values(O.quantize_query_fp4(workloads.to_bf16_bits(qf[0, 0])))[0, c] == 1.5
         w = np.zeros((1, 2, 32), np.float32)
         w[:, :, 0] = 1.0
         sel = np.array(rows)
         inp = {"idx_k_codes": codes[:, sel], "idx_k_scales": scales[:, sel], "idx_q": workloads.to_bf16_bits(qf),
                "head_w": w, "n_visible": np.full((1, 2), len(sel), np.int32)}
         s = G.gpu_index_scores(inp, 1, 2, len(sel))
-        v = F.e2m1_value(code[sel]) * F.e4m3_value(sb[sel])
+        v = 1.5 * F.e2m1_value(code[sel]) * F.e4m3_value(sb[sel])
         assert np.array_equal(s[0, 0], np.maximum(v, 0).astype(np.float32)), c
         assert np.array_equal(s[0, 1], np.maximum(-v, 0).astype(np.float32)), c
 
@@ -91,10 +93,11 @@ def test_scan_every_fp4_key_code_and_scale_exact():
 @pytest.mark.parametrize("fp4", [False, True])
 @pytest.mark.parametrize("multi_query", [False, True])
 def test_scan_query_rounding_every_bf16(multi_query, fp4):
-    """The scan's E4M3 rounding of the query, for every bf16 pattern, in both scan kernels (one
-    query per workgroup, and 16 queries of a sequence per workgroup).  Key rows 2c / 2c+1 hold
-    +1 / -1 in channel c and query t weights only head t % 32, so its scores are
-    ReLU(+-q8[t % 32][c]) exactly: 512 queries reveal all 65536 rounded values."""
+    """The scans' rounding of the query, for every bf16 pattern, in both scan kernels (one query
+    per workgroup, and 16 queries of a sequence per workgroup): to E4M3 for E4M3 keys, to FP4 per
+    16-channel group for FP4 keys (each group holds 16 consecutive patterns).  Key rows 2c / 2c+1
+    hold +1 / -1 in channel c and query t weights only head t % 32, so its scores are
+    ReLU(+-q[t % 32][c]) exactly: 512 queries reveal all 65536 rounded values."""
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     bits[np.isnan(F.bf16_value(bits))] = 0
     vals = bits.reshape(16, 32, 128)
@@ -116,8 +119,11 @@ def test_scan_query_rounding_every_bf16(multi_query, fp4):
     inp.update(idx_q=q.reshape(B, T, 32, 128), head_w=w.reshape(B, T, 32),
                n_visible=np.full((B, T), 256, np.int32))
     s = G.gpu_index_scores(inp, B, T, 256).reshape(512, 256)
-    q8 = F.e4m3_value(O.quantize_query(bits)).reshape(16, 32, 128)
-    ref = q8[np.arange(512) // 32, np.arange(512) % 32]             # [512][128]
+    if fp4:
+        qv = O.query_values(O.quantize_query_fp4(vals))              # [16][32][128]
+    else:
+        qv = F.e4m3_value(O.quantize_query(bits)).reshape(16, 32, 128)
+    ref = qv[np.arange(512) // 32, np.arange(512) % 32]             # [512][128]
     assert np.array_equal(s[:, 0::2], np.maximum(ref, 0).astype(np.float32))
     assert np.array_equal(s[:, 1::2], np.maximum(-ref, 0).astype(np.float32))
 
@@ -174,8 +180,8 @@ def test_index_scores_parity(B, T, N, nv, fp4):
     for b in range(B):
         for t in range(T):
             n = int(inp["n_visible"][b, t])
-            q8 = O.quantize_query(inp["idx_q"][b, t])
             keys = O.k_rows(G.host_keys(inp, b), slice(0, n))
+            q8 = O.query_for_keys(inp["idx_q"][b, t], keys)
             ref = O.indexer_scores(keys, q8, inp["head_w"][b, t])
             bound = G.score_abs_bound(keys, inp["idx_q"][b, t], inp["head_w"][b, t])
             G.assert_scores_close(s[b, t, :n], ref, bound, f"b{b} t{t}")

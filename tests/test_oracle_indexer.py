@@ -337,3 +337,81 @@ def test_only_the_max_block_score_keeps_an_isolated_needle():
     for mode, keeps in (("max", True), ("sum", False), ("top2", False)):
         pool = O.candidate_pool(O.block_scores(s32, 64, 8, mode), 64, 8, 1)
         assert (3 in pool.tolist()) == keeps, mode
+
+
+# ------------------------------------------------------------------ FP4 query (with FP4 keys)
+
+E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _fp4_group_brute_force(x: np.ndarray) -> np.ndarray:
+    """One 16-value group rounded to FP4 by brute force, independently of the oracle's codecs:
+    scale = torch's E4M3 cast of float32(amax / 6); each |x| / scale goes to the nearest E2M1
+    magnitude (exact rational distances, ties to the even code), saturating at 6."""
+    from fractions import Fraction
+    amax = np.float32(np.max(np.abs(x)))
+    s32 = np.float32(amax / np.float32(6.0))
+    s = float(torch.tensor(s32).to(torch.float8_e4m3fn).to(torch.float64))
+    out = np.zeros(16)
+    if s == 0.0:
+        return out
+    for i, v in enumerate(x.astype(np.float64)):
+        q = Fraction(abs(v)) / Fraction(s)
+        d = [abs(q - Fraction(m)) for m in E2M1_MAGS]
+        best = min(range(8), key=lambda c: (d[c], c % 2))            # ties: even code
+        out[i] = np.copysign(E2M1_MAGS[best] * s, v)
+    return out
+
+
+def test_fp4_query_matches_a_brute_force_per_head_group():
+    """[p3 FP4]: with FP4 keys the query is rounded to FP4 per head and 16-channel group.  Random
+    queries of several magnitudes (and one group of zeros) against a brute force over each group."""
+    rng = np.random.default_rng(71)
+    for scale in (1.0, 1e-3, 37.0):
+        qf = (rng.standard_normal((32, 128)) * scale).astype(np.float32)
+        qf[5, 32:48] = 0.0
+        q = workloads.to_bf16_bits(qf)
+        got = O.query_values(O.quantize_query_fp4(q))
+        x = F.bf16_value(q)
+        for h in range(32):
+            for g in range(8):
+                ref = _fp4_group_brute_force(x[h, 16 * g:16 * g + 16])
+                assert np.array_equal(got[h, 16 * g:16 * g + 16], ref), (scale, h, g)
+
+
+def test_fp4_query_round_trips_fp4_values_and_groups_are_independent():
+    """A query whose every group is code x scale with a +-6 code already is returned unchanged; a
+    change inside one group leaves every other group's values alone."""
+    rng = np.random.default_rng(72)
+    codes = rng.integers(0, 16, size=(32, 128))
+    codes[:, ::16] = rng.choice([7, 15], size=(32, 8))                # a +-6 code in every group
+    sc = 2.0 ** rng.integers(-6, 4, size=(32, 8)) * (1 + rng.integers(0, 8, size=(32, 8)) / 8)
+    vals = np.where(codes >= 8, -1, 1) * E2M1_MAGS[codes % 8] * np.repeat(sc, 16, axis=1)
+    q = workloads.to_bf16_bits(vals.astype(np.float32))
+    assert np.array_equal(F.bf16_value(q), vals)                      # exact in bf16
+    v1 = O.query_values(O.quantize_query_fp4(q))
+    assert np.array_equal(v1, vals)
+    q2 = q.copy()
+    q2[3, 20] = workloads.to_bf16_bits(np.float32([1000.0]))[0]       # group (3, 1) only
+    v2 = O.query_values(O.quantize_query_fp4(q2))
+    mask = np.ones((32, 128), bool)
+    mask[3, 16:32] = False
+    assert np.array_equal(v2[mask], v1[mask]) and not np.array_equal(v2[3, 16:32], v1[3, 16:32])
+
+
+def test_fp4_keys_score_with_the_fp4_query():
+    """The Full layer with FP4 keys scores with the FP4 query: its scores equal indexer_scores with
+    that query, and a one-hot key reads back one rounded query value."""
+    rng = np.random.default_rng(73)
+    codes = rng.integers(0, 256, size=(100, 64), dtype=np.uint8)
+    scales = rng.integers(0x30, 0x48, size=(100, 8), dtype=np.uint8)
+    q = workloads.to_bf16_bits(rng.standard_normal((32, 128)).astype(np.float32))
+    w = rng.random(32, dtype=np.float32)
+    r = O.full_layer((codes, scales), q, w, 100, 8, 0, 10)
+    assert np.array_equal(r["scores"], O.indexer_scores((codes, scales), O.quantize_query_fp4(q), w))
+    one = np.zeros((1, 64), np.uint8)
+    one[0, 9] = 0x2 << 4                                              # channel 19: E2M1 1.0
+    w1 = np.zeros(32, np.float32)
+    w1[7] = 1.0
+    s = O.indexer_scores((one, np.full((1, 8), 0x38, np.uint8)), O.quantize_query_fp4(q), w1)
+    assert s[0] == max(0.0, O.query_values(O.quantize_query_fp4(q))[7, 19])
