@@ -685,6 +685,7 @@ def main() -> int:
                    "top_k": K, "full_layer": w.has_full, "reindex_layers": w.n_reindex,
                    "attention_layers": L, "attention_heads": Hh, "indexer_heads": 32, "indexer_dim": 128,
                    "indexer_keys": "fp4 (E2M1 + E4M3/16)" if w.idx_k_fp4 else "e4m3",
+                   "indexer_query": "fp4 (E2M1 + E4M3/16)" if w.idx_k_fp4 else "e4m3",
                    "swa_window": w.swa_window, "context_replicas": R,
                    "launch": "first stage direct + hipgraph" if args.graph else "direct launches",
                    "step_algorithmic_bytes": step_bytes,
