@@ -135,7 +135,8 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_1m": Workload("decode_1m", 1003, B=1, T=1, N=1 << 20, H=16,
                           layer_set=_decode_sets([(0, 4), (1, 4), (2, 4), (3, 4), (4, 4)]),
                           n_reindex=4, planted=True),
-    # the same decode with the FP4 indexer-K variant (72 B per position instead of 128 B)
+    # the same decode with the FP4 indexer variant (keys 72 B per position instead of 128 B; the
+    # query rounded to FP4 by the library)
     "decode_1m_fp4k": Workload("decode_1m_fp4k", 1006, B=1, T=1, N=1 << 20, H=16,
                                layer_set=_decode_sets([(0, 4), (1, 4), (2, 4), (3, 4), (4, 4)]),
                                n_reindex=4, planted=True, idx_k_fp4=True),
