@@ -176,7 +176,9 @@ csa2_status csa2_index_full(const uint8_t* idx_k, const uint8_t* idx_k_scales, i
  *   idx_q      [L][B][T][32][128] bf16;  head_w [L][B][T][32] float
  *   pool_pos   [B][T][pool_cap] int32 distinct positions in ascending order (as csa2_index_full
  *              writes them; the Top-K output keeps the pool's order); entries >= pool_len and
- *              negative or out-of-range entries are ignored; pool_len [B][T] int32
+ *              negative or out-of-range entries are ignored; a position listed more than once
+ *              ranks with its copies counted, so it can be selected more than once (copies at
+ *              the top_k-th place fill the remaining places in slot order); pool_len [B][T] int32
  *   topk_idx   [L][B][T][top_k] int32 out; topk_score [L][B][T][top_k] float out or NULL
  * Supported: 1 <= top_k <= 2048, top_k <= pool_cap <= 16384. */
 size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k);
