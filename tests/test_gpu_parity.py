@@ -573,3 +573,69 @@ def test_attention_split_merge_repeats_and_graph_replays(NH):
         assert np.array_equal(G.host(out), out_ref), f"replay {i}"
         call()                                                            # eager work between replays
         assert np.array_equal(G.host(out), out_ref)
+
+
+def test_index_chain_graph_replays_and_concurrent_streams():
+    """The decode indexer (csa2_index_chain: scan, pool, Full and Reindex Top-K) captured in a HIP
+    graph replays to the eager result, with other eager calls on the same workspace in between and
+    the workspace starting from arbitrary bytes; and two chains on two streams at once, each with
+    its own workspace and outputs, give their serial results (the calls hold no global state)."""
+    import hierarchical_kv_indexer_amd as H
+    N, P, K, L = 30000, 128, 256, 2
+
+    class Chain:
+        def __init__(self, seed):
+            w = small(N=N, pool_blocks=P, top_k=K, n_reindex=L, seed=seed)
+            self.inp = workloads.make_inputs(w, with_attention=False)
+            self.ref = G.gpu_index_chain(self.inp, 1, 1, N, P, K, L)
+            self.k, self.ks, self.rows = G.keys(self.inp)
+            self.q, self.hw, self.nv = (G.dev(self.inp[n]) for n in ("idx_q", "head_w", "n_visible"))
+            self.rq, self.rw = G.dev(self.inp["ri_q"][:L]), G.dev(self.inp["ri_w"][:L])
+            self.pool_pos, self.pool_len = G.empty((1, 1, P * 8), torch.int32), G.empty((1, 1), torch.int32)
+            self.idx, self.ri_idx = G.empty((1, 1, K), torch.int32), G.empty((L, 1, 1, K), torch.int32)
+            self.wsb = H.csa2_index_chain_workspace(1, 1, N, 8, P, K, L)
+            self.ws = torch.full((self.wsb,), 0xA5, dtype=torch.uint8, device=G.DEV)
+
+        def call(self, stream=None):
+            H.csa2_index_chain(self.k, self.ks, self.rows, self.q, self.hw, self.nv, 1, 1, N, 8, P, K, self.rq,
+                               self.rw, L, self.pool_pos, self.pool_len, self.idx, None, self.ri_idx, None, self.ws,
+                               self.wsb, stream)
+
+        def check(self, what):
+            assert np.array_equal(G.host(self.idx), self.ref["topk"]), what
+            assert np.array_equal(G.host(self.ri_idx), self.ref["ri_topk"]), what
+            assert np.array_equal(G.host(self.pool_pos), self.ref["pool_pos"]), what
+            assert np.array_equal(G.host(self.pool_len), self.ref["pool_len"]), what
+
+        def clear(self):
+            for t in (self.idx, self.ri_idx, self.pool_pos, self.pool_len):
+                t.fill_(-7)
+
+    a, b = Chain(3401), Chain(3402)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        a.call(s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        a.clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a.check(f"replay {i}")
+        a.clear()
+        a.call()                                                          # eager, same workspace
+        a.check(f"eager after replay {i}")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for i in range(3):
+        a.clear()
+        b.clear()
+        torch.cuda.synchronize()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        a.call(s1)
+        b.call(s2)
+        torch.cuda.synchronize()
+        a.check(f"stream 1, round {i}")
+        b.check(f"stream 2, round {i}")
