@@ -12,7 +12,9 @@
 // and O += P X run on bf16 MFMA (16x16x32) with an online softmax in fp32, and the next chunk's
 // raw bytes are loaded into registers while the current chunk is computed.  When the (layer,
 // query, head group) count alone cannot fill the GPU, the rows are split across workgroups and
-// k_attn_combine merges the partial softmax states (max, sum, weighted rows).
+// k_attn_combine merges the partial softmax states (max, sum, weighted rows).  With H a multiple
+// of 64, k_sparse_attn_wide covers 64 heads of a (layer, query) per workgroup instead, so each
+// gathered row is dequantised once for all of them.
 #include <algorithm>
 
 #include "common.hpp"

@@ -333,7 +333,7 @@ __device__ __forceinline__ uint32_t block_key(float sc, bool valid) {
 // its instruction issue, not by the bytes in flight).
 template <bool kFp4> constexpr int kScanU = 3;
 constexpr int kFullWaves = kFullThreads / 64;   // 16
-static_assert(kFullWaves == kScanUnitsPerWg, "one unit per wave in the epilogue");
+static_assert(kFullWaves == kScanUnitsPerWg, "each wave lists the units of its own range");
 
 size_t scan_lds_bytes(int chunk) {
   return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)chunk * 4 + (size_t)(chunk / kBlock) * 4 + 16;
@@ -402,8 +402,8 @@ __device__ __forceinline__ void write_unit_lists(uint32_t key, uint32_t blk, int
 // every tile is done).
 //
 // Writes scores[q][p] for p < n_visible and, when `blkkey` is non-null, the order key of
-// each block's max score.  When `lists` is non-null, each of the chunk's 16 units (equal,
-// contiguous ranges of chunk/16 positions) writes its five best blocks as ranking keys
+// each block's max score.  When `lists` is non-null, each of the chunk's 16*upw units (equal,
+// contiguous ranges of chunk/(16*upw) positions) writes its five best blocks as ranking keys
 // (score key << 32 | ~block): lists[q][unit][0..3] = the four best (0 = none) and
 // cuts[q][unit] = the fifth best (0 = none), so every block of the unit that is not listed
 // ranks at or below cuts[q][unit].  Requires chunk % 1024 == 0 and chunk <= 8192.
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
 // ---------------------------------------------------------------------------- multi-query Full scan
 
 // When many queries of one sequence scan the same keys (a prefill chunk), a workgroup scores a
-// chunk of positions for 16 consecutive queries of the sequence, one per wave.  Each step stages
+// chunk of positions for 16 consecutive queries of the sequence, two per wave.  Each step stages
 // 128 key rows in LDS already converted to MFMA operands (bf16 for E4M3 keys, fp16 for FP4 keys,
 // both exact, channels in their natural order), so the key stream is read and converted once per
 // 16 queries.  A wave scores 32 positions at a time with 32x32x16 MFMAs (32 heads x 32 positions):
@@ -524,8 +524,8 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
 // one exchange with lane l ^ 32, and the block maxima of the 32 positions come from one 8-lane
 // reduction.  Products are exact and accumulated in fp32, as in k_idx_scan, though in a different
 // order.  Outputs are those of k_idx_scan for every query of the group (unit u of a chunk covers
-// its positions [u*chunk/16, (u+1)*chunk/16)).
-constexpr int kMqQueries = kFullWaves;        // 16 queries per workgroup, one per wave
+// its positions [u*chunk/(16*upw), (u+1)*chunk/(16*upw))).
+constexpr int kMqQueries = 16;                // queries per workgroup
 constexpr int kMqRows = 128;                  // key rows per staged step
 constexpr int kMqStride = 2 * kIdxDim + 16;   // LDS bytes per staged row: 128 16-bit operands + pad
 typedef float f32x16 __attribute__((ext_vector_type(16)));
