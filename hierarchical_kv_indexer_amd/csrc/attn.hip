@@ -29,6 +29,13 @@ constexpr int kPStride = kRows + 8;          // bf16 elements per P row
 constexpr int kMaxSplitRows = 4096 + kMaxTopK;   // a split never exceeds k + window rows
 constexpr float kLazyLog2 = 8.f;             // slack of the softmax reference point (log2 units)
 
+// Two floats -> fp16 pair (round to nearest even), low half first.  Partial rows are stored
+// normalised by their own softmax sums, so they lie within the rows' range (|x| <= 2688).
+__device__ __forceinline__ uint32_t f16x2_rne(float lo, float hi) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
+}
+
 // Max / sum over the 16 lanes of a DPP row; every lane of the row gets the same value (the
 // pairwise steps are symmetric, so the sum is rounded identically in each lane).
 __device__ __forceinline__ float row16_max(float x) {
@@ -107,14 +114,14 @@ __device__ __forceinline__ void store_row(const RawRow& r, uint16_t* xrow, int q
 // Rows of a (layer, query) are numbered: main slots 0 .. k-1 (index set order), then the window's
 // SWA rows.  grid (n_splits, H/16, L*Q): split s covers row slots [s*split_rows, (s+1)*split_rows)
 // for 16 heads.  With one split the normalised bf16 output and lse are written directly;
-// otherwise the split writes its partial state (running max m and sum l in log2 units, and the
-// unnormalised sum of p*x) for k_attn_combine.
+// otherwise the split writes its partial state (running max m in log2 units and sum l in fp32,
+// and its output row sum(p*x) / l in fp16) for k_attn_combine.
 __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     const uint8_t* __restrict__ kv_codes, const uint8_t* __restrict__ kv_scales, int64_t kv_rows,
     const uint16_t* __restrict__ qg, const int32_t* __restrict__ idx_sets, LayerSets sets,
     const uint8_t* __restrict__ swa, int swa_rows, const int32_t* __restrict__ swa_end, int window,
     int Q, int B, int T, int H, int k, float scale_log2, int split_rows, int n_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t X[kRows * kXStride];
   __shared__ __attribute__((aligned(16))) uint16_t P[16 * kPStride];
@@ -287,9 +294,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
       const size_t pr = (hrow + h) * n_splits + split;
-      f32x4* po = (f32x4*)(part_o + pr * kKvDim + 128 * wave + 8 * j);
-      po[0] = f32x4{o[0][v], o[1][v], o[2][v], o[3][v]};
-      po[1] = f32x4{o[4][v], o[5][v], o[6][v], o[7][v]};
+      const float inv = l_run[v] > 0.f ? 1.f / l_run[v] : 0.f;
+      *(u32x4*)(part_o + pr * kKvDim + 128 * wave + 8 * j) =
+          u32x4{f16x2_rne(o[0][v] * inv, o[1][v] * inv), f16x2_rne(o[2][v] * inv, o[3][v] * inv),
+                f16x2_rne(o[4][v] * inv, o[5][v] * inv), f16x2_rne(o[6][v] * inv, o[7][v] * inv)};
       if (wave == 0 && j == 0) {
         part_ml[pr * 2] = m_run[v];
         part_ml[pr * 2 + 1] = l_run[v];
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     const uint16_t* __restrict__ qg, const int32_t* __restrict__ idx_sets, LayerSets sets,
     const uint8_t* __restrict__ swa, int swa_rows, const int32_t* __restrict__ swa_end, int window,
     int Q, int B, int T, int H, int k, float scale_log2, int split_rows, int n_splits,
-    float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(16))) uint16_t X[2][kRows * kXStride];   // chunk c in X[c & 1]
   __shared__ __attribute__((aligned(16))) uint16_t P[4 * 16 * kPStride];
@@ -565,7 +573,9 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       if (lse && hf == 0 && lane == 0) lse[hrow + h] = lh > 0.f ? (mh + log2f(lh)) * 0.69314718055994531f : -INFINITY;
     } else {
       const size_t pr = (hrow + h) * n_splits + split;
-      *(f32x4*)(part_o + pr * kKvDim + 256 * hf + 4 * lane) = ov;
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      *(u32x2*)(part_o + pr * kKvDim + 256 * hf + 4 * lane) =
+          u32x2{f16x2_rne(ov.x * inv, ov.y * inv), f16x2_rne(ov.z * inv, ov.w * inv)};
       if (hf == 0 && lane == 0) {
         part_ml[pr * 2] = mh;
         part_ml[pr * 2 + 1] = lh;
@@ -579,33 +589,34 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
 // split and get weight zero), so the loads of a lane are all in flight together.
 constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(64) void k_attn_combine(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml, int n_splits, int H,
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int n_splits, int H,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
   const size_t hrow = (size_t)blockIdx.y * H + blockIdx.x;
   const int lane = threadIdx.x;
   const float* ml = part_ml + hrow * n_splits * 2;
   float m[kMaxSplits], l[kMaxSplits];
-  f32x4 a[kMaxSplits], c[kMaxSplits];
+  u32x4 a[kMaxSplits];                               // 8 fp16 dims of the split's normalised row
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
     const int sc = s < n_splits ? s : n_splits - 1;
     m[s] = ml[2 * sc];
     l[s] = ml[2 * sc + 1];
-    const f32x4* po = (const f32x4*)(part_o + (hrow * n_splits + sc) * kKvDim + 8 * lane);
-    a[s] = po[0];
-    c[s] = po[1];
+    a[s] = *(const u32x4*)(part_o + (hrow * n_splits + sc) * kKvDim + 8 * lane);
   }
   float M = -INFINITY;
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, s < n_splits ? m[s] : -INFINITY);
+  // split s holds O_s / l_s, so it enters with weight 2^(m_s - M) * l_s
   float L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSplits; ++s) {
-    const float w = (s < n_splits && m[s] != -INFINITY) ? exp2f(m[s] - M) : 0.f;
-    L += w * l[s];
+    const float w = (s < n_splits && m[s] != -INFINITY) ? exp2f(m[s] - M) * l[s] : 0.f;
+    L += w;
+    const h8 v = __builtin_bit_cast(h8, a[s]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { acc[i] += w * a[s][i]; acc[4 + i] += w * c[s][i]; }
+    for (int i = 0; i < 8; ++i) acc[i] += w * (float)v[i];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint32_t pk[4];
@@ -636,7 +647,7 @@ AttnPlan plan_attn(int L, int B, int T, int H, int k, int window) {
   p.n_splits = (rows_max + p.split_rows - 1) / p.split_rows;
   if (p.n_splits < 1) p.n_splits = 1;
   const size_t heads = (size_t)L * B * T * H;
-  p.ws_bytes = p.n_splits > 1 ? heads * p.n_splits * (kKvDim + 2) * sizeof(float) : 0;
+  p.ws_bytes = p.n_splits > 1 ? heads * p.n_splits * (kKvDim * sizeof(uint16_t) + 2 * sizeof(float)) : 0;
   return p;
 }
 
@@ -648,8 +659,8 @@ hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales,
   const int Q = B * T;
   const float scale_log2 = scale * 1.4426950408889634f;
   const AttnPlan p = plan_attn(L, B, T, H, k, window);
-  float* part_o = (float*)workspace;
-  float* part_ml = part_o ? part_o + (size_t)L * Q * H * p.n_splits * kKvDim : nullptr;
+  uint16_t* part_o = (uint16_t*)workspace;          // fp16 normalised rows, then fp32 (m, l) pairs
+  float* part_ml = part_o ? (float*)(part_o + (size_t)L * Q * H * p.n_splits * kKvDim) : nullptr;
   if (p.heads_per_wg == 64)
     hipLaunchKernelGGL(k_sparse_attn_wide, dim3(p.n_splits, H / 64, L * Q), dim3(kWideThreads), 0, s,
                        kv_codes, kv_scales, kv_rows, q, idx_sets, sets, swa, swa_rows, swa_end, window, Q,
