@@ -609,6 +609,7 @@ __device__ __forceinline__ float reduce32(const Ctx32& cx, const f32x16& a) {
 constexpr int kMqThreads = 512;
 constexpr int kMqWaves = kMqThreads / 64;
 constexpr int kMqPerWave = kMqQueries / kMqWaves;     // 2 queries per wave
+static_assert(kMqPerWave == 2, "the step loop scores two queries per wave (mfma_chains32)");
 template <bool kFp4, int kBS>
 __global__ __launch_bounds__(kMqThreads) void k_idx_scan_mq(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
