@@ -88,6 +88,18 @@ def test_reindex_and_attention_reject(H):
     expect(H, 2, lambda: H.csa2_sparse_attn(*a))
     a = list(base); a[19] = None; a[20] = 0                          # split rows need a workspace
     expect(H, 3, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[10] = 4097                                     # window beyond 4096
+    expect(H, 2, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[15] = 2049                                     # top_k beyond 2048
+    expect(H, 2, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[14] = 1040                                     # more than 1024 heads
+    expect(H, 2, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[12] = 65536                                    # L*B*T beyond 65535
+    expect(H, 2, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[18] = FAKE + 4                                 # lse not 16-byte aligned
+    expect(H, 1, lambda: H.csa2_sparse_attn(*a))
+    a = list(base); a[2] = 0                                         # no main-KV rows
+    expect(H, 1, lambda: H.csa2_sparse_attn(*a))
 
 
 def test_stage_entries_reject(H):
