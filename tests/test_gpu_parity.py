@@ -639,3 +639,16 @@ def test_index_chain_graph_replays_and_concurrent_streams():
         torch.cuda.synchronize()
         a.check(f"stream 1, round {i}")
         b.check(f"stream 2, round {i}")
+
+
+def test_chain_over_allocated_caches():
+    """Caches with more rows per sequence than the visible range (k_rows_per_seq = kv_rows = 6000,
+    n_max = 5000, n_visible 5000 and 4321 for two sequences): the per-sequence row strides are
+    the allocation's, and nothing past a query's visible range is scored or gathered."""
+    import dataclasses
+    w_alloc = small("decode_1m", B=2, N=6000, pool_blocks=64, top_k=128, seed=3501)
+    inp = workloads.make_inputs(w_alloc)
+    inp["n_visible"] = np.array([[5000], [4321]], np.int32)
+    w = dataclasses.replace(w_alloc, N=5000)
+    out = run_chain_and_check(w, inp, [(0, 0), (1, 0)])
+    assert out.shape[1] == 2
