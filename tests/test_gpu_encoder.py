@@ -72,12 +72,12 @@ def check_chunk(w, prompt, gpu_out, gpu_topk, ref, caches_after, p0, T, what):
                     G.assert_attention_close(gpu_out[g, l, b, t], o, f"{what} g{g} l{l} t{t}")
 
 
-@pytest.mark.parametrize("sizes,m", [((128,), 2), ((33, 64, 95), 3)])
-def test_encoder_chunks_match_oracle(sizes, m):
+@pytest.mark.parametrize("sizes,m,B", [((128,), 2, 1), ((33, 64, 95), 3, 1), ((96, 160), 2, 2)])
+def test_encoder_chunks_match_oracle(sizes, m, B):
     """Every chunk of a 512-token prompt: index sets, attention of every layer, and the caches
     the chunks append (bytes equal to the oracle's).  Ragged chunk sizes with m = 3 put entry
-    boundaries inside chunks."""
-    w = enc(m=m)
+    boundaries inside chunks; B = 2 runs two prompts side by side."""
+    w = enc(m=m, B=B)
     prompt = workloads.make_encoder_prompt(w)
     chunks = chunk_list(w.prompt, sizes)
     ref, caches = oracle_run(w, prompt, chunks)
