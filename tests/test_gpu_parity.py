@@ -652,3 +652,23 @@ def test_chain_over_allocated_caches():
     w = dataclasses.replace(w_alloc, N=5000)
     out = run_chain_and_check(w, inp, [(0, 0), (1, 0)])
     assert out.shape[1] == 2
+
+
+def test_attention_at_the_most_layers():
+    """64 attention layers (the limit) over 3 index sets in a Reuse pattern, two queries: every
+    layer reads its own set, query and window."""
+    L = 64
+    layer_set = tuple((l // 3) % 3 for l in range(L))
+    w = small(B=1, T=2, N=3000, H=16, layer_set=layer_set, n_reindex=2, pool_blocks=64, top_k=96, seed=109)
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(13)
+    sets = np.stack([np.stack([np.sort(rng.choice(w.N, 96, replace=False)) for _ in range(2)])
+                     for _ in range(3)]).astype(np.int32).reshape(3, 1, 2, 96)
+    out, lse = G.gpu_attention(inp, w, sets)
+    for l in (0, 1, 31, 62, 63):
+        for t in range(2):
+            rows = O.attention_rows(inp["kv_codes"][0], inp["kv_scales"][0], sets[layer_set[l], 0, t],
+                                    inp["swa"][l, 0], int(inp["swa_end"][0, t]), w.swa_window)
+            o, ls = O.attention(inp["q"][l, 0, t], rows, 1 / math.sqrt(512))
+            G.assert_attention_close(out[l, 0, t], o, f"l{l} t{t}")
+            assert np.allclose(lse[l, 0, t], ls, rtol=1e-3, atol=1e-3)
