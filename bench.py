@@ -403,7 +403,8 @@ def study_hsi_recall(args) -> int:
     block score (max / sum / top-2 mean) and a Reindex layer's Top-512 inside that pool.  Reports,
     per (context, P, block score): the share of each needle family in the Full Top-512 and in the
     Reindex Top-512, and the share of the Reindex layer's dense Top-512 (over every position, no
-    pool) that its pool-restricted Top-512 keeps.  Prints one JSON line per configuration."""
+    pool) that its pool-restricted Top-512 keeps.  A second sweep repeats the max block score with
+    Reindex queries correlated with the Full query (rho).  Prints one JSON line per configuration."""
     import numpy as np
     import torch
 
@@ -422,9 +423,9 @@ def study_hsi_recall(args) -> int:
 
     K = 512
     modes = {0: "max", 1: "sum", 2: "top2"}
-    rows = []
-    for N, seed in ((1 << 16, 4101), (1 << 18, 4102), (1 << 20, 4103)):
-        ctx = workloads.make_recall_context(N, seed)
+
+    def sweep(N, seed, pools, block_scores, rho=None):
+        ctx = workloads.make_recall_context(N, seed, rho=rho)
         k, q, hw, nv = up(ctx["idx_k"]), up(ctx["idx_q"]), up(ctx["head_w"]), up(ctx["n_visible"])
         rq, rw = up(ctx["ri_q"]), up(ctx["ri_w"])
         # the Reindex layer's dense Top-512 (no pool)
@@ -433,27 +434,35 @@ def study_hsi_recall(args) -> int:
         dense = torch.empty((1, 1, K), dtype=torch.int32, device=dev)
         H.csa2_index_full(k, None, N, rq[0], rw[0], nv, 1, 1, N, 8, 0, K, None, None, dense, None, ws, wsd)
         dense_set = set(dense.cpu().numpy().reshape(-1).tolist()) - {-1}
-        for P in (256, 512, 1024, 2048):
+        for P in pools:
             wsb = H.csa2_index_chain_workspace(1, 1, N, 8, P, K, 1)
             ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
             pool_pos = torch.empty((1, 1, P * 8), dtype=torch.int32, device=dev)
             pool_len = torch.empty((1, 1), dtype=torch.int32, device=dev)
             ftop = torch.empty((1, 1, K), dtype=torch.int32, device=dev)
             rtop = torch.empty((1, 1, 1, K), dtype=torch.int32, device=dev)
-            for bs, name in modes.items():
+            for bs in block_scores:
                 H.csa2_index_scan_blocks(k, None, N, q, hw, nv, 1, 1, N, 8, P, K, bs, ws, wsb)
                 H.csa2_index_select_reindex(k, None, N, nv, 1, 1, N, 8, P, K, rq, rw, 1, pool_pos, pool_len, ftop,
                                             None, rtop, None, ws, wsb)
                 torch.cuda.synchronize()
                 f = ftop.cpu().numpy().reshape(-1)
                 r = rtop.cpu().numpy().reshape(-1)
-                row = {"context": N, "pool_blocks": P, "block_score": name,
-                       "full_topk": {fam: round(float(np.isin(pos, f).mean()), 4) for fam, pos in ctx["families"].items()},
-                       "reindex_topk": {fam: round(float(np.isin(pos, r).mean()), 4)
-                                        for fam, pos in ctx["families"].items()},
-                       "reindex_dense_kept": round(len(dense_set & set(r.tolist())) / max(1, len(dense_set)), 4)}
-                rows.append(row)
+                row = {"context": N, "pool_blocks": P, "block_score": modes[bs]}
+                if rho is not None:
+                    row["rho"] = rho
+                row.update({
+                    "full_topk": {fam: round(float(np.isin(pos, f).mean()), 4) for fam, pos in ctx["families"].items()},
+                    "reindex_topk": {fam: round(float(np.isin(pos, r).mean()), 4)
+                                     for fam, pos in ctx["families"].items()},
+                    "reindex_dense_kept": round(len(dense_set & set(r.tolist())) / max(1, len(dense_set)), 4)})
                 print(json.dumps(row), flush=True)
+
+    for N, seed in ((1 << 16, 4101), (1 << 18, 4102), (1 << 20, 4103)):
+        sweep(N, seed, (256, 512, 1024, 2048), tuple(modes))
+    for N, seed in ((1 << 16, 4101), (1 << 20, 4103)):
+        for rho in (0.5, 0.8, 0.9, 0.95, 0.99, 1.0):
+            sweep(N, seed, (512, 2048), (0,), rho)
     return 0
 
 

@@ -430,7 +430,8 @@ RECALL_FAMILIES = ("full_isolated", "reindex_isolated", "shared_isolated", "full
 
 
 def make_recall_context(N: int, seed: int, n_needles: int = 32, n_clusters: int = 8,
-                        sigma: float = 4.0, cluster_sigma: float = 2.0) -> Dict[str, object]:
+                        sigma: float = 4.0, cluster_sigma: float = 2.0,
+                        rho: Optional[float] = None) -> Dict[str, object]:
     """One decode query over N positions with planted needles for the hierarchical indexer's recall
     study (alphalab.site sec."2. CSA2": the first Full layer's pool decides what the Reindex layers
     can pick).  Keys are N(0,1) rows with, before the E4M3 cast, a shift delta added at the needle
@@ -441,14 +442,20 @@ def make_recall_context(N: int, seed: int, n_needles: int = 32, n_clusters: int 
       shared_isolated   n_needles single positions, target both queries, s = sigma;
       full_clusters     n_clusters aligned blocks of 8 positions, target the Full query,
                         s = cluster_sigma (weaker alone, dense as a block).
+    The Reindex query is an independent N(0,1) draw z, or with `rho` the mix rho * q + sqrt(1 -
+    rho^2) * z of the Full query q and that draw (element-wise correlation rho).
     Returns idx_k [1][N][128], idx_q / head_w (Full), ri_q [1][1][1][32][128] / ri_w (one Reindex
     layer), n_visible [1][1], and families {name: sorted positions}."""
     ss = np.random.SeedSequence(seed)
     g = [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(5)]
     d: Dict[str, object] = {}
-    d["idx_q"] = to_bf16_bits(draw_normal_f32(g[0], (1, 1, IDX_HEADS, IDX_DIM)))
+    q_full = draw_normal_f32(g[0], (1, 1, IDX_HEADS, IDX_DIM))
+    d["idx_q"] = to_bf16_bits(q_full)
     d["head_w"] = g[1].random(size=(1, 1, IDX_HEADS), dtype=np.float32)
-    d["ri_q"] = to_bf16_bits(draw_normal_f32(g[0], (1, 1, 1, IDX_HEADS, IDX_DIM)))
+    z = draw_normal_f32(g[0], (1, 1, 1, IDX_HEADS, IDX_DIM))
+    if rho is not None:
+        z = (np.float32(rho) * q_full[None] + np.float32(np.sqrt(1.0 - rho * rho)) * z).astype(np.float32)
+    d["ri_q"] = to_bf16_bits(z)
     d["ri_w"] = g[1].random(size=(1, 1, 1, IDX_HEADS), dtype=np.float32)
     qf = e4m3_bytes_as_float(to_e4m3_bytes(bf16_bits_as_float(d["idx_q"][0, 0]))).astype(np.float64)
     qr = e4m3_bytes_as_float(to_e4m3_bytes(bf16_bits_as_float(d["ri_q"][0, 0, 0]))).astype(np.float64)
