@@ -226,6 +226,25 @@ def test_index_full_parity(N, P, K, nv):
         check_full(w, inp, gpu, 0, t)
 
 
+@pytest.mark.parametrize("P,run", [(64, (1600, 3200)), (128, (4000, 4400)), (256, (8000, 8008))])
+def test_pool_with_runs_of_high_blocks(P, run):
+    """Runs of consecutive high-scoring blocks: the units inside a run hold more pool blocks than
+    the four they list, so they are re-read.  Depending on how far a run's unlisted blocks reach
+    above the P-th best listed block (runs of 200, 50 and 1 blocks against P = 64, 128, 256), the
+    P-th best block lies in that listed block's bin, which is ranked directly, or above it, where a
+    selection over every candidate finds it.  Run rows repeat the 64 best rows of the random keys."""
+    N, K = 20000, 256
+    w = small(N=N, pool_blocks=P, top_k=K, seed=3400 + P)
+    inp = workloads.make_inputs(w, with_attention=False)
+    k = inp["idx_k"]
+    s = O.indexer_scores(k[0], O.query_for_keys(inp["idx_q"][0, 0], k[0]), inp["head_w"][0, 0])
+    best = np.argsort(s, kind="stable")[-64:]
+    a, b = run
+    k[0, a:b] = k[0, best[np.arange(b - a) % 64]]
+    gpu = G.gpu_index_full(inp, 1, 1, N, P, K)
+    check_full(w, inp, gpu, 0, 0)
+
+
 @pytest.mark.parametrize("T", [2, 9])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_pool_block_score_variants(mode, T):
