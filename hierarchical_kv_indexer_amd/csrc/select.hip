@@ -174,17 +174,70 @@ __device__ __forceinline__ void find_bin(uint32_t need, Block& bk) {
 __device__ __forceinline__ uint64_t key_lo(uint32_t mn32) { return (uint64_t)mn32 << 32; }
 __device__ __forceinline__ uint64_t key_hi(uint32_t mx32) { return ((uint64_t)mx32 << 32) | 0xffffffffull; }
 
+// The need-th largest of the cnt keys in sm.rankbuf (1 <= need <= cnt <= kRankMax), collected
+// before the caller's barrier: thread t compares key t % 256 with one quarter of the keys (the
+// quarter is the same for a whole wave, so every LDS read is a broadcast).
+__device__ __forceinline__ uint64_t rank_collected(uint32_t cnt, uint32_t need, Block& bk) {
+  SelectSmem& sm = bk.sm;
+  constexpr uint32_t kPart = kRankMax / 4;
+  const uint32_t i = threadIdx.x % kRankMax, part = threadIdx.x / kRankMax;
+  const uint64_t x = sm.rankbuf[i];
+  const uint32_t m0 = part * kPart, m1 = min(cnt, m0 + kPart);
+  uint32_t r = 0, eq = 0, m = m0;
+  for (; m + 2 <= m1; m += 2) {
+    const u64x2 v = *(const u64x2*)(sm.rankbuf + m);
+    r += (v.x > x ? 1u : 0u) + (v.y > x ? 1u : 0u);
+    eq += (v.x == x ? 1u : 0u) + (v.y == x ? 1u : 0u);
+  }
+  if (m < m1) {
+    r += sm.rankbuf[m] > x ? 1u : 0u;
+    eq += sm.rankbuf[m] == x ? 1u : 0u;
+  }
+  if (part) {
+    sm.rankpart[part - 1][i] = r;
+    sm.eqpart[part - 1][i] = eq;
+  }
+  __syncthreads();
+  if (part == 0 && i < cnt) {
+    r += sm.rankpart[0][i] + sm.rankpart[1][i] + sm.rankpart[2][i];
+    eq += sm.eqpart[0][i] + sm.eqpart[1][i] + sm.eqpart[2][i];
+    // fewer than need keys above x, at least need at or above it (every copy of x agrees)
+    if (r < need && need <= r + eq) sm.result = x;
+  }
+  __syncthreads();
+  return sm.result;
+}
+
+// The first pass of a selection, kept for a later one over a related set (see k_pool).
+struct FirstPass {
+  uint64_t lo, hi;
+  int shift;
+  bool wide;
+  uint32_t bin, above;                   // the bin that held the result, keys in bins above it
+  bool valid;
+};
+
+// Bin of key k (lo <= k <= hi) in that pass; a key outside the range would go to a spare bin.
+__device__ __forceinline__ uint32_t first_pass_bin(const FirstPass& fp, uint64_t k) {
+  const uint64_t b = fp.wide ? (uint64_t)(((uint32_t)(k >> 32) - (uint32_t)(fp.lo >> 32)) >> (fp.shift - 32))
+                             : (k - fp.lo) >> fp.shift;
+  return k >= fp.lo && k <= fp.hi && b < (uint64_t)kBins ? (uint32_t)b : (uint32_t)kBins + (threadIdx.x & 63);
+}
+
 // The need-th largest of a set of 64-bit keys, counted with repeats, all inside [lo, hi]
 // (1 <= need <= the number of keys).  Keys are distinct except when a caller's pool lists a
 // position more than once.  for_each(f) calls f(key) for every key this thread holds (0 = none; keys
 // outside [lo, hi] are ignored).  If `cand` is non-null, the keys of a bin with at most
-// kCandCap keys are copied there once and later passes read only the copy.
+// kCandCap keys are copied there once and later passes read only the copy.  If `save` is
+// non-null, the first pass's histogram (kBins counts) is copied there and its range, digit and
+// outcome into *fp (fp->valid is false if no pass ran).
 // Requires a clear histogram (smem_init); leaves it clear.
 template <class ForEach>
 __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uint64_t hi, Block& bk,
-                               uint64_t* cand) {
+                               uint64_t* cand, uint32_t* save = nullptr, FirstPass* fp = nullptr) {
   SelectSmem& sm = bk.sm;
-  bool use_cand = false;
+  bool use_cand = false, first = true;
+  if (fp) fp->valid = false;
   if (lo == 0ull) lo = 1ull;             // 0 marks "no key"
   const uint32_t stray = (uint32_t)kBins + (threadIdx.x & 63);
   while (true) {
@@ -212,8 +265,11 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
       }
     }
     __syncthreads();
+    if (save && first) *(u32x4*)&save[4 * threadIdx.x] = *(const u32x4*)&sm.hist[4 * threadIdx.x];
     find_bin(need, bk);
     const uint32_t bin = sm.found_bin, above = sm.found_above, cnt = sm.found_cnt;
+    if (fp && first) *fp = FirstPass{lo, hi, shift, wide, bin, above, true};
+    first = false;
     need -= above;
     const uint64_t nlo = lo + ((uint64_t)bin << shift);
     const uint64_t nhi = shift == 0 ? nlo : min(hi, nlo + (((uint64_t)1 << shift) - 1));
@@ -240,33 +296,7 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
         }
       }
       __syncthreads();
-      constexpr uint32_t kPart = kRankMax / 4;
-      const uint32_t i = threadIdx.x % kRankMax, part = threadIdx.x / kRankMax;
-      const uint64_t x = sm.rankbuf[i];
-      const uint32_t m0 = part * kPart, m1 = min(cnt, m0 + kPart);
-      uint32_t r = 0, eq = 0, m = m0;
-      for (; m + 2 <= m1; m += 2) {
-        const u64x2 v = *(const u64x2*)(sm.rankbuf + m);
-        r += (v.x > x ? 1u : 0u) + (v.y > x ? 1u : 0u);
-        eq += (v.x == x ? 1u : 0u) + (v.y == x ? 1u : 0u);
-      }
-      if (m < m1) {
-        r += sm.rankbuf[m] > x ? 1u : 0u;
-        eq += sm.rankbuf[m] == x ? 1u : 0u;
-      }
-      if (part) {
-        sm.rankpart[part - 1][i] = r;
-        sm.eqpart[part - 1][i] = eq;
-      }
-      __syncthreads();
-      if (part == 0 && i < cnt) {
-        r += sm.rankpart[0][i] + sm.rankpart[1][i] + sm.rankpart[2][i];
-        eq += sm.eqpart[0][i] + sm.eqpart[1][i] + sm.eqpart[2][i];
-        // fewer than need keys above x, at least need at or above it (every copy of x agrees)
-        if (r < need && need <= r + eq) sm.result = x;
-      }
-      __syncthreads();
-      return sm.result;
+      return rank_collected(cnt, need, bk);
     }
     if (cand && !use_cand && cnt <= (uint32_t)kCandCap) {
       if (threadIdx.x == 0) sm.ncand = 0;
@@ -356,6 +386,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
   __shared__ uint32_t byrank[kMaxTopK];      // selected blocks, ascending
   __shared__ uint16_t satunit[kUnitsPerThread * kNT];   // unit of each re-read slot
   __shared__ uint32_t satcnt[kUnitsPerThread * kNT];    // its count, then its output offset
+  __shared__ uint32_t hsave[kBins];          // T0's first histogram pass
   Block bk{sm};
   const int q = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int nv = n_visible[q];
@@ -398,7 +429,26 @@ __global__ __launch_bounds__(kNT) void k_pool(
     };
     bk.reduce(nvalid, mn, mx);
     uint64_t t0 = 1ull;                       // T0 <= T*: the P-th best listed key
-    if (nvalid >= (uint32_t)P) t0 = select_kth(for_each_e, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
+    FirstPass fp;
+    fp.valid = false;
+    if (nvalid >= (uint32_t)P)
+      t0 = select_kth(for_each_e, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr, hsave, &fp);
+
+    // The candidates for T* are the blocks >= T0; all lie in T0's first-pass range (a unit's
+    // unlisted blocks are below its listed ones).  Their histogram over that pass's bins is the
+    // saved one with: bins below T0's bin empty; T0's bin holding the listed keys >= T0, of which
+    // there are P - (keys in bins above); re-read units' listed keys >= T0 taken out and their
+    // blocks >= T0 put in.  Restored here into the (clear) histogram, and cleared again below if
+    // no unit is re-read or the re-read keys do not fit in LDS.
+    if (fp.valid) {
+      const uint32_t b0 = 4u * (uint32_t)t;
+      u32x4 h = *(const u32x4*)&hsave[b0];
+      h.x = b0 + 0 < fp.bin ? 0u : (b0 + 0 == fp.bin ? (uint32_t)P - fp.above : h.x);
+      h.y = b0 + 1 < fp.bin ? 0u : (b0 + 1 == fp.bin ? (uint32_t)P - fp.above : h.y);
+      h.z = b0 + 2 < fp.bin ? 0u : (b0 + 2 == fp.bin ? (uint32_t)P - fp.above : h.z);
+      h.w = b0 + 3 < fp.bin ? 0u : (b0 + 3 == fp.bin ? (uint32_t)P - fp.above : h.w);
+      *(u32x4*)&sm.hist[b0] = h;
+    }
 
     // units that may hold unlisted blocks >= T0 are re-read; sidx = their slot
     int sidx[kUnitsPerThread];
@@ -411,6 +461,8 @@ __global__ __launch_bounds__(kNT) void k_pool(
     __syncthreads();
     const uint32_t nsat = sm.nsat;
     const bool dense = nsat * (uint32_t)bpu <= (uint32_t)kCandCap;   // re-read keys fit in LDS
+    const bool from_first = fp.valid && nsat > 0 && dense;
+    if (fp.valid && !from_first) *(u32x4*)&sm.hist[4 * t] = u32x4{0u, 0u, 0u, 0u};
     auto unit_key = [&](uint32_t si, int o) -> uint64_t {   // key of block o of re-read slot si
       const int jj = satunit[si] * bpu + o;
       return jj < nb ? rank_key(keys[jj], (uint32_t)jj) : 0ull;
@@ -420,6 +472,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
         for (int o = lane; o < bpu; o += 64) {
           const uint64_t k = unit_key(si, o);
           cand[si * bpu + o] = k >= t0 ? k : 0ull;
+          if (from_first && k >= t0) atomicAdd(&sm.hist[first_pass_bin(fp, k)], 1u);
         }
     }
     auto sat_key = [&](uint32_t si, int o) -> uint64_t {
@@ -429,8 +482,10 @@ __global__ __launch_bounds__(kNT) void k_pool(
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        if (from_first && sidx[i] >= 0 && e[i][r] >= t0) atomicSub(&sm.hist[first_pass_bin(fp, e[i][r])], 1u);
         if (sidx[i] >= 0 || e[i][r] < t0) e[i][r] = 0ull;
+      }
     __syncthreads();
 
     uint64_t tstar = t0;                      // no unit re-read: every block >= T0 is listed
@@ -439,15 +494,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
       mn = 0xffffffffu;
       mx = 0u;
       if (dense) {
-#pragma unroll
-        for (int i = 0; i < kUnitsPerThread; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (e[i][r]) { mn = min(mn, (uint32_t)(e[i][r] >> 32)); mx = max(mx, (uint32_t)(e[i][r] >> 32)); }
         const uint32_t nc = nsat * (uint32_t)bpu;
-        for (uint32_t i = t; i < nc; i += kNT)
-          if (cand[i]) { mn = min(mn, (uint32_t)(cand[i] >> 32)); mx = max(mx, (uint32_t)(cand[i] >> 32)); }
-        bk.reduce(dummy, mn, mx);
         auto for_each_c = [&](auto f) {
 #pragma unroll
           for (int i = 0; i < kUnitsPerThread; ++i)
@@ -455,7 +502,37 @@ __global__ __launch_bounds__(kNT) void k_pool(
             for (int r = 0; r < 4; ++r) f(e[i][r]);
           for (uint32_t i = threadIdx.x; i < nc; i += kNT) f(cand[i]);
         };
-        tstar = select_kth(for_each_c, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
+        if (from_first) {
+          // the candidates' histogram is in place: find T*'s bin, then rank it or narrow it
+          find_bin((uint32_t)P, bk);
+          const uint32_t above = sm.found_above, cnt = sm.found_cnt;
+          const uint64_t blo = fp.lo + ((uint64_t)sm.found_bin << fp.shift);
+          const uint64_t bhi = fp.shift == 0 ? blo : min(fp.hi, blo + (((uint64_t)1 << fp.shift) - 1));
+          if (fp.shift == 0) {
+            tstar = blo;
+          } else if (cnt <= (uint32_t)kRankMax) {
+            for_each_c([&](uint64_t k) {
+              if (k >= blo && k <= bhi) {
+                const uint32_t a = atomicAdd(&sm.nrank, 1u);
+                if (a < (uint32_t)kRankMax) sm.rankbuf[a] = k;
+              }
+            });
+            __syncthreads();
+            tstar = rank_collected(cnt, (uint32_t)P - above, bk);
+          } else {
+            tstar = select_kth(for_each_c, (uint32_t)P - above, blo, bhi, bk, nullptr);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kUnitsPerThread; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (e[i][r]) { mn = min(mn, (uint32_t)(e[i][r] >> 32)); mx = max(mx, (uint32_t)(e[i][r] >> 32)); }
+          for (uint32_t i = t; i < nc; i += kNT)
+            if (cand[i]) { mn = min(mn, (uint32_t)(cand[i] >> 32)); mx = max(mx, (uint32_t)(cand[i] >> 32)); }
+          bk.reduce(dummy, mn, mx);
+          tstar = select_kth(for_each_c, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
+        }
       } else {
         // many units re-read (heavy ties): select over every block directly
         for (int jj = t; jj < nb; jj += kNT) { mn = min(mn, keys[jj]); mx = max(mx, keys[jj]); }
