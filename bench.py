@@ -47,6 +47,7 @@ METRIC = "decode queries/s at 1M ctx (Full+Reindex+attn); achieved HBM GB/s vs p
 HBM_PEAK_GBS = 8000.0
 SCAN_SOURCES = ("hierarchical_kv_indexer_amd/csrc/scan.hip", "hierarchical_kv_indexer_amd/csrc/common.hpp")
 PMC_FILE = os.path.join(ROOT, "profiles", "k_idx_scan_decode_1m_pmc.json")
+KERNEL_FILE = os.path.join(ROOT, "profiles", "decode_1m_kernels.json")
 COPY_BYTES = 256 << 20          # plain device copy that calibrates the HBM byte counters
 IDX_Q_BYTES = 32 * 128 * 2      # one indexer query (bf16)
 IDX_W_BYTES = 32 * 4            # its head weights
@@ -161,26 +162,98 @@ def summarize_pmc(fetch_dir: str, write_dir: str) -> int:
     return 0
 
 
-def cpu_baseline(w, inp, seconds: float):
-    """The oracle, as it stands, on this host: the whole chain for query (0, 0), repeated."""
-    from oracle import csa2 as O
+def _median_rate(run_once, seconds: float, max_runs: int):
+    """Median over 3 timed runs of the rate of run_once(); each run repeats it for about
+    `seconds` / 3 (at least once, at most max_runs times)."""
+    rates, n_total = [], 0
+    for _ in range(3):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            run_once()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / 3 or n >= max_runs:
+                break
+        rates.append(n / el)
+        n_total += n
+    rates.sort()
+    return rates[1], n_total
+
+
+def _oracle_threads():
+    """Threads the oracle's numpy/BLAS work may use on this host: the CPUs this process may run on
+    (the BLAS pool's own limit applies on top; see _blas_threads)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+        return 1
+
+
+def cpu_baseline(w, inp, seconds: float):
+    """The oracle, as it stands, on this host: the whole chain for query (0, 0), timed with its
+    BLAS pool limited to 1 thread and then with every thread it may use (median of 3 runs each).
+    Only the oracle's matrix products run on several threads; the rest of it (block scores,
+    ranking, attention rows) is serial numpy.  `cores` is the thread count of the all-threads
+    run."""
+    from oracle import csa2 as O
+    from threadpoolctl import threadpool_limits
+
+    def once():
         O.query_chain(inp, w, 0, 0)
-        n += 1
-        el = time.perf_counter() - t0
-        if (el >= seconds and n >= 2) or n >= 50:
-            break
+
+    threads = min(_oracle_threads(), _blas_threads())
+    with threadpool_limits(limits=1):
+        r1, n1 = _median_rate(once, seconds / 2, 20)
+    with threadpool_limits(limits=threads):
+        rn, nn = _median_rate(once, seconds / 2, 20)
     what = (f"Full scan of {w.N} positions, pool, Top-{w.top_k}, " if w.has_full else "caller pool, ")
-    return {"value": n / el, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} runs of the whole chain ({what}{w.n_reindex} Reindex layers, {w.L} attention "
-                      f"layers) for one query of {w.name}, {el:.1f} s"}
+    return {"value": rn, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "value_1_thread": r1,
+            "sample": f"the whole chain ({what}{w.n_reindex} Reindex layers, {w.L} attention layers) for one "
+                      f"query of {w.name}; median of 3 runs at {threads} BLAS threads ({nn} chains) and at 1 "
+                      f"thread ({n1} chains), {_oracle_threads()} CPUs available"}
+
+
+def measure_copy_gbps(dev, stream, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Bytes read plus written per second by a plain device-to-device copy of nbytes (torch's copy
+    kernel), timed with events on `stream`: the practical ceiling of a one-pass kernel here."""
+    import torch
+    src = torch.full((nbytes,), 1, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        dst.copy_(src)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+        torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
+def kernel_duration_from_profile(kernel: str, workload: str):
+    """Average duration (us) of `kernel` at `workload` from the committed rocprofv3 kernel-trace
+    summary, or None when it is missing or the kernel's sources changed since it was taken."""
+    try:
+        with open(KERNEL_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha1") != scan_source_hash() or d.get("workload") != workload:
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("avg_us")
 
 
 QUANT_ROW_BYTES = 512 * 2 + 256 + 32      # bf16 latent row in, E2M1 codes and E4M3 scales out
@@ -362,6 +435,38 @@ def bench_encoder(args, w) -> int:
     return 0
 
 
+KERNEL_NAMES = ("k_idx_scan", "k_pool", "k_ri_score", "k_topk", "k_sparse_attn", "k_attn_combine")
+
+
+def summarize_trace(trace_dir: str, workload: str, steps: int) -> int:
+    """Turns a rocprofv3 --kernel-trace --stats run of this script into the kernel-duration summary
+    later runs report (profiles/decode_1m_kernels.json): per kernel of the chain, its calls per
+    step and average duration, keyed to the scan's source hash."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
+    kernels = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Name", "")
+            short = next((k for k in KERNEL_NAMES if k + "<" in name or k + "(" in name or name.endswith(k)), None)
+            if short is None:
+                continue
+            calls, avg = int(r["Calls"]), float(r["AverageNs"])
+            if short in kernels:                   # template variants of one kernel: merge
+                c0, a0 = kernels[short]["calls"], kernels[short]["avg_us"] * 1e3
+                avg = (a0 * c0 + avg * calls) / (c0 + calls)
+                calls += c0
+            kernels[short] = {"calls": calls, "avg_us": round(avg / 1e3, 3)}
+    out = {"workload": workload, "source_sha1": scan_source_hash(), "profiled_steps": steps,
+           "kernels": kernels, "stats_file": os.path.relpath(files[0], trace_dir)}
+    os.makedirs(os.path.dirname(KERNEL_FILE), exist_ok=True)
+    with open(KERNEL_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+    return 0
+
+
 def cpu_baseline_encoder(w, seconds: float):
     """The oracle, as it stands, on this host: the measured chunk's tokens through the first group
     (Full layer over every visible entry, then the group's attention layers), one token after the
@@ -371,11 +476,7 @@ def cpu_baseline_encoder(w, seconds: float):
 
     import workloads
     from oracle import csa2 as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = min(_oracle_threads(), _blas_threads())
     inp = workloads.make_encoder_chunk(dataclasses.replace(w, G=1))
     h, n0 = w.hist(w.p0), w.p0 // w.m
     n = 0
@@ -476,10 +577,14 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="replay everything after the first stage from a HIP graph (measured slower here)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device-to-device copy measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of known size (for the HBM byte counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write the kernel-duration summary of a rocprofv3 --stats run of this script "
+                         "(--workload and --steps as in that run)")
     ap.add_argument("--kernel", choices=("chain", "quantize_kv"), default="chain",
                     help="quantize_kv: time the FP4 main-KV quantiser alone")
     ap.add_argument("--rows", type=int, default=1 << 20, help="latent rows per quantiser launch")
@@ -489,6 +594,8 @@ def main() -> int:
 
     if args.summarize_pmc:
         return summarize_pmc(*args.summarize_pmc)
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.workload, args.steps)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the sharding plan is written up with the design notes).", file=sys.stderr)
@@ -661,14 +768,29 @@ def main() -> int:
     step_bytes = step_algorithmic_bytes(w)
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    copy_gbs = measure_copy_gbps(dev, stream) if not args.no_copy else None
     roofline = None
     if w.has_full:
         scan_bytes = scan_algorithmic_bytes(w)
         achieved = scan_bytes / (first_ms * 1e-3) / 1e9
+        kernel_us = kernel_duration_from_profile("k_idx_scan", w.name)
         roofline = {"bound": "hbm", "kernel": "k_idx_scan", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic_from_profile() if w.name == "decode_1m" else None,
-                    "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(first_ms * 1e3, 3)}
+                    "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": round(first_ms * 1e3, 3),
+                    # the event-bracketed launch above includes its dispatch; the committed rocprofv3
+                    # kernel trace gives the kernel's own duration (None once the scan's sources change)
+                    "frac_event": round(achieved / HBM_PEAK_GBS, 4),
+                    "kernel_us_rocprof": kernel_us,
+                    "frac_kernel": (round(scan_bytes / (kernel_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                    if kernel_us else None),
+                    # the whole step's algorithmic bytes over its wall time
+                    "step_achieved": round(step_gbs, 1),
+                    "step_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                    # the same figures against a plain device-to-device copy measured in this run
+                    "copy_GBps": round(copy_gbs, 1) if copy_gbs else None,
+                    "frac_of_copy": round(achieved / copy_gbs, 4) if copy_gbs else None,
+                    "step_frac_of_copy": round(step_gbs / copy_gbs, 4) if copy_gbs else None}
         log(f"[bench] {args.steps} steps in {wall:.4f} s: {ms_per_step * 1e3:.2f} us/step, scan "
             f"{first_ms * 1e3:.2f} us ({achieved:.0f} GB/s algorithmic), whole step {step_gbs:.0f} GB/s algorithmic")
     else:

@@ -32,6 +32,7 @@ csa2_status ok() {
   return CSA2_OK;
 }
 
+
 csa2_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return CSA2_OK;
@@ -625,6 +626,17 @@ csa2_status csa2_encoder_chunk(int G, int layers, const uint16_t* new_idx_k, con
   REQUIRE_PTR(kv_scales);
   REQUIRE_PTR(swa_kv);
   REQUIRE(new_latent == nullptr || aligned16(new_latent), CSA2_ERR_INVALID_ARG, "new_latent must be 16-byte aligned");
+  REQUIRE(new_idx_k == nullptr || aligned16(new_idx_k), CSA2_ERR_INVALID_ARG, "new_idx_k must be 16-byte aligned");
+  // everything the nested Full-layer and attention calls check, before the appends modify the
+  // caches: a call that fails here has enqueued nothing
+  REQUIRE_PTR(idx_q);
+  REQUIRE_PTR(head_w);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(out);
+  REQUIRE(topk_idx == nullptr || aligned16(topk_idx), CSA2_ERR_INVALID_ARG, "topk_idx must be 16-byte aligned");
+  REQUIRE(H >= 16 && H % 16 == 0 && H <= 1024, CSA2_ERR_UNSUPPORTED, "H must be a multiple of 16 in [16, 1024]");
+  REQUIRE(top_k >= 1 && top_k <= csa2::kMaxTopK, CSA2_ERR_UNSUPPORTED, "top_k must be in [1, %d]", csa2::kMaxTopK);
+  REQUIRE(softmax_scale > 0.f, CSA2_ERR_INVALID_ARG, "softmax_scale must be > 0");
   const size_t need = carve_encoder(nullptr, B, T, k_rows, layers, H, top_k, swa_window, nullptr);
   REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
           "workspace of %zu bytes required (got %zu)", need, ws_bytes);

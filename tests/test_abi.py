@@ -168,6 +168,14 @@ def test_encoder_chunk_rejects(H):
     a[15], a[12] = 0, 128                       # first chunk: no history rows
     a[24] = 8
     expect(H, 3, lambda: H.csa2_encoder_chunk(*a))
+    # pointers only the nested Full-layer and attention calls use are checked before the cache
+    # appends: without a GPU any launch would fail with CSA2_ERR_HIP, so an argument error here
+    # means nothing was enqueued (the caches stay untouched)
+    for i in (8, 9, 10, 21):                    # idx_q, head_w, q, out
+        expect(H, 1, call(i, None))
+    expect(H, 1, call(22, FAKE + 4))            # topk_idx alignment
+    expect(H, 2, call(17, 40))                  # H
+    expect(H, 2, call(18, 4096))                # top_k
 
 
 def test_scan_blocks_rejects_unknown_block_score(H):

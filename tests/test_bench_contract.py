@@ -61,3 +61,36 @@ def test_decode_1m_algorithmic_bytes():
     w = workloads.WORKLOADS["decode_1m"]
     assert bench.scan_algorithmic_bytes(w) == (1 << 20) * 128 + 32 * 128 * 2 + 32 * 4
     assert bench.step_algorithmic_bytes(w) == 147942016
+
+
+def test_kernel_trace_summary_and_its_staleness(tmp_path, monkeypatch):
+    """A rocprofv3 --stats table becomes per-kernel averages (template variants merged by call
+    count); the scan's duration is reported only while its sources hash to the profiled ones."""
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    with open(d / "123_kernel_stats.csv", "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage"])
+        wr.writeheader()
+        wr.writerow({"Name": "void csa2::k_idx_scan<false, 0>(unsigned char const*, ...)", "Calls": 30,
+                     "TotalDurationNs": 30 * 25000, "AverageNs": 25000.0, "Percentage": 40})
+        wr.writerow({"Name": "csa2::k_pool(unsigned long const*, ...)", "Calls": 30, "TotalDurationNs": 300000,
+                     "AverageNs": 10000.0, "Percentage": 20})
+        wr.writerow({"Name": "void csa2::k_ri_score<false>(...)", "Calls": 10, "TotalDurationNs": 40000,
+                     "AverageNs": 4000.0, "Percentage": 5})
+        wr.writerow({"Name": "void csa2::k_ri_score<true>(...)", "Calls": 30, "TotalDurationNs": 240000,
+                     "AverageNs": 8000.0, "Percentage": 5})
+        wr.writerow({"Name": "__amd_rocclr_copyBuffer", "Calls": 3, "TotalDurationNs": 3, "AverageNs": 1.0,
+                     "Percentage": 0})
+    out = tmp_path / "kernels.json"
+    monkeypatch.setattr(bench, "KERNEL_FILE", str(out))
+    assert bench.summarize_trace(str(tmp_path / "trace"), "decode_1m", 30) == 0
+    k = json.loads(out.read_text())["kernels"]
+    assert k["k_idx_scan"] == {"calls": 30, "avg_us": 25.0}
+    assert k["k_ri_score"] == {"calls": 40, "avg_us": 7.0}
+    assert "copy" not in json.dumps(k)
+    assert bench.kernel_duration_from_profile("k_idx_scan", "decode_1m") == 25.0
+    assert bench.kernel_duration_from_profile("k_idx_scan", "decode_b8_128k") is None
+    d2 = json.loads(out.read_text())
+    d2["source_sha1"] = "0" * 40
+    out.write_text(json.dumps(d2))
+    assert bench.kernel_duration_from_profile("k_idx_scan", "decode_1m") is None

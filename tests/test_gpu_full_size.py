@@ -60,7 +60,7 @@ def test_decode_1m_fp4_keys_whole_chain():
 def test_decode_b8_128k_sampled():
     w = workloads.WORKLOADS["decode_b8_128k"]
     inp = workloads.make_inputs(w)
-    queries = [(0, 0), (5, 0), (7, 0)]
+    queries = [(b, 0) for b in range(w.B)]                     # every query of the batch
     _announce(w.name, queries)
     run_chain_and_check(w, inp, queries)
 
@@ -68,7 +68,7 @@ def test_decode_b8_128k_sampled():
 def test_reindex_pool_256k_sampled():
     w = workloads.WORKLOADS["reindex_pool_256k"]
     inp = workloads.make_inputs(w)
-    queries = [(0, 0), (0, 17), (0, 63)]
+    queries = [(0, t) for t in list(range(0, 64, 4)) + [17, 63]]   # 18 of the 64 caller pools
     _announce(w.name, queries)
     run_chain_and_check(w, inp, queries)
 
@@ -76,7 +76,12 @@ def test_reindex_pool_256k_sampled():
 def test_prefill_4k_64k_sampled():
     w = workloads.WORKLOADS["prefill_4k_64k"]
     inp = workloads.make_inputs(w)
-    queries = [(0, 0), (0, 2047), (0, 4095)]
+    # 32 tokens over the causal ramp: both ends of 16 multi-query groups of 16 tokens spread from
+    # the first to the last (t = 16g and 16g + 15), so each group's largest and smallest visible
+    # range is checked
+    groups = np.linspace(0, w.T // 16 - 1, 16).round().astype(int)
+    queries = sorted({(0, int(16 * g + d)) for g in groups for d in (0, 15)})
+    assert len(queries) == 32
     _announce(w.name, queries)
     run_chain_and_check(w, inp, queries)
 

@@ -19,10 +19,12 @@ generator per tensor, children spawned in the order of ``STREAMS``):
 
   indexer K            N(0,1) float32 -> E4M3 (torch cast, values clamped to +-448 first);
                        FP4 variant (``idx_k_fp4``): the same draws -> E2M1 codes with one
-                       power-of-two E4M3 scale per 16 channels (the smallest power of two
-                       >= amax/6, within [2^-9, 2^8]), codes the nearest E2M1 magnitude of
-                       x / scale by table lookup (this generator's own encoder; any FP4 bytes
-                       are valid input), 64 code bytes + 8 scale bytes per position
+                       E4M3 scale per 16 channels: amax/6 times U(1, 1.5) (stream
+                       ``fp4_scale``), cast to E4M3 by torch (any mantissa), negative for
+                       half the groups (sign bit drawn from the same stream); codes the
+                       nearest E2M1 magnitude of |x / scale| by table lookup, sign that of
+                       x / scale (this generator's own encoder; any FP4 bytes are valid
+                       input), 64 code bytes + 8 scale bytes per position
   indexer Q (Full/RI)  N(0,1) float32 -> bf16 (torch cast, round to nearest even)
   head weights w       U(0,1) float32
   main-KV E2M1 codes   categorical over the 16 codes (``E2M1_MAG_WEIGHTS`` / 256 per
@@ -51,7 +53,7 @@ KV_CODE_BYTES = KV_DIM // 2
 KV_SCALE_BYTES = KV_DIM // 16
 
 STREAMS = ("idx_k", "idx_q", "head_w", "ri_q", "ri_w", "kv_codes", "kv_scales",
-           "q", "swa", "planted", "user_pool")
+           "q", "swa", "planted", "user_pool", "fp4_scale")
 
 # Relative frequencies (out of 256) of the E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
 # Codes are drawn independently of the U(0.5, 2) scales (E[s^2] = 1.75); the mean
@@ -212,21 +214,26 @@ def draw_kv_codes(rng: np.random.Generator, rows: int) -> np.ndarray:
 E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
 
 
-def to_fp4_pow2(x: np.ndarray):
-    """float32 [n][d] -> (codes [n][d/2] u8, scales [n][d/16] u8): per 16 channels the smallest
-    power-of-two scale >= amax/6 (clamped to [2^-9, 2^8], exact in E4M3), each channel the
-    nearest E2M1 magnitude of x / scale (a table lookup on the midpoints), sign from x."""
+def to_fp4_keys(x: np.ndarray, rng: np.random.Generator):
+    """float32 [n][d] -> (codes [n][d/2] u8, scales [n][d/16] u8): per 16 channels an E4M3 scale
+    of amax/6 times U(1, 1.5) (within [2^-9, 448]; torch's E4M3 cast, so any mantissa), negated
+    for a random half of the groups; each channel the nearest E2M1 magnitude of |x / scale| (a
+    table lookup on the midpoints), with the sign of x / scale."""
     n, dch = x.shape
     g = x.reshape(n, dch // 16, 16).astype(np.float32)
     amax = np.abs(g).max(-1)
-    e = np.ceil(np.log2(np.maximum(amax / 6.0, 2.0 ** -9))).clip(-9, 8)
-    scale = np.exp2(e).astype(np.float32)
-    q = np.abs(g) / scale[..., None]                        # exact: division by a power of two
+    jitter = rng.uniform(1.0, 1.5, size=amax.shape).astype(np.float32)
+    neg = rng.random(size=amax.shape) < 0.5
+    mag = np.clip(amax / 6.0 * jitter, 2.0 ** -9, 448.0).astype(np.float32)
+    sbytes = to_e4m3_bytes(mag) | (neg.astype(np.uint8) << 7)
+    scale = e4m3_bytes_as_float(sbytes)                     # the stored (signed) scale
+    q = np.abs(g) / np.abs(scale)[..., None]
     mid = (E2M1_MAGS[1:] + E2M1_MAGS[:-1]) / 2
-    mag = np.searchsorted(mid, q, side="left").astype(np.uint8)
-    c = (mag | (np.signbit(g).astype(np.uint8) << 3)).reshape(n, dch)
+    code_mag = np.searchsorted(mid, q, side="left").astype(np.uint8)
+    sign = np.signbit(g) ^ np.signbit(scale)[..., None]
+    c = (code_mag | (sign.astype(np.uint8) << 3)).reshape(n, dch)
     codes = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
-    return codes, to_e4m3_bytes(scale)
+    return codes, sbytes
 
 
 def draw_normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
@@ -276,7 +283,7 @@ def make_inputs(w: Workload, with_attention: bool = True) -> Dict[str, np.ndarra
                 if lo < hi:
                     x[lo - r0:hi - r0] += delta
             if w.idx_k_fp4:
-                idx_k[b, r0:r1], idx_k_scales[b, r0:r1] = to_fp4_pow2(x)
+                idx_k[b, r0:r1], idx_k_scales[b, r0:r1] = to_fp4_keys(x, gens["fp4_scale"])
             else:
                 idx_k[b, r0:r1] = to_e4m3_bytes(x)
     if w.idx_k_fp4:
