@@ -37,6 +37,9 @@ EXPORTS = (
                               _P, _SZ, _P)),
     ("csa2_index_select_reindex", _I, (_P, _P, _I64, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P,
                                        _P, _SZ, _P)),
+    ("csa2_noalloc_scratch_bytes", _SZ, ()),
+    ("csa2_index_chain_noalloc", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P,
+                                      _P, _P, _P)),
     ("csa2_reindex_workspace", _SZ, (_I, _I, _I, _I, _I)),
     ("csa2_reindex", _I, (_P, _P, _I64, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
     ("csa2_sparse_attn_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
@@ -182,6 +185,21 @@ def csa2_index_chain(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_
                                   _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx), _ptr(topk_score),
                                   _ptr(ri_topk_idx), _ptr(ri_topk_score), _ptr(workspace), ws_bytes,
                                   _stream(stream, idx_k)))
+
+
+def csa2_noalloc_scratch_bytes() -> int:
+    return lib().csa2_noalloc_scratch_bytes()
+
+
+def csa2_index_chain_noalloc(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,
+                             n_max: int, block_size: int, pool_blocks: int, top_k: int, ri_q, ri_w, L: int,
+                             pool_pos, pool_len, topk_idx, topk_score, ri_topk_idx, ri_topk_score,
+                             stream=None) -> None:
+    _check(lib().csa2_index_chain_noalloc(_ptr(idx_k), _ptr(idx_k_scales), k_rows_per_seq, _ptr(idx_q), _ptr(head_w),
+                                          _ptr(n_visible), B, T, n_max, block_size, pool_blocks, top_k, _ptr(ri_q),
+                                          _ptr(ri_w), L, _ptr(pool_pos), _ptr(pool_len), _ptr(topk_idx),
+                                          _ptr(topk_score), _ptr(ri_topk_idx), _ptr(ri_topk_score),
+                                          _stream(stream, idx_k)))
 
 
 def csa2_index_select_reindex(idx_k, idx_k_scales, k_rows_per_seq: int, n_visible, B: int, T: int, n_max: int,

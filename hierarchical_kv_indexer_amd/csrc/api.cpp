@@ -8,6 +8,7 @@
 #include <cstring>
 #include <string>
 
+#include "api_internal.hpp"
 #include "csa2.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -32,6 +33,19 @@ csa2_status ok() {
   return CSA2_OK;
 }
 
+}  // namespace
+
+csa2_status csa2::api_fail(csa2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+namespace {
 
 csa2_status hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));

@@ -217,6 +217,28 @@ csa2_status csa2_index_select_reindex(const uint8_t* idx_k, const uint8_t* idx_k
                                       int32_t* ri_topk_idx, float* ri_topk_score, void* workspace,
                                       size_t ws_bytes, void* stream);
 
+/* csa2_index_chain for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops and harnesses that forbid hipMalloc.  The same arguments and
+ * results as csa2_index_chain without the workspace: its scratch is a fixed array of this library
+ * in device memory, CSA2_NOALLOC_SCRATCH_BYTES (16 MiB) on every GPU it runs on, held until the
+ * process ends; the call itself allocates nothing (the first call on a device looks up the
+ * address of that device's array; callers that capture graphs make one call before capturing).
+ *   - a shape whose csa2_index_chain_workspace(...) exceeds CSA2_NOALLOC_SCRATCH_BYTES returns
+ *     CSA2_ERR_UNSUPPORTED before anything is enqueued (the 1M-position decode of one query and
+ *     8 queries over 128K positions, each with 4 Reindex layers, need about 5 and 7 MiB);
+ *   - argument errors are those of csa2_index_chain;
+ *   - every call on one GPU uses that GPU's one array, so calls that may overlap on a GPU
+ *     (another stream, another thread) race on it and must be serialised by the caller.
+ * csa2_noalloc_scratch_bytes() returns CSA2_NOALLOC_SCRATCH_BYTES. */
+#define CSA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+size_t csa2_noalloc_scratch_bytes(void);
+csa2_status csa2_index_chain_noalloc(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq,
+                                     const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int B,
+                                     int T, int n_max, int block_size, int pool_blocks, int top_k,
+                                     const uint16_t* ri_q, const float* ri_w, int L, int32_t* pool_pos,
+                                     int32_t* pool_len, int32_t* topk_idx, float* topk_score, int32_t* ri_topk_idx,
+                                     float* ri_topk_score, void* stream);
+
 /* Sparse attention of L layers (blog.4sapi.com sec.2 and sec.5; alphalab.site sec."3. FP4"):
  * layer l attends, per query and head, over the main-KV rows of index set layer_set[l]
  * (FP4 E2M1 codes x E4M3 per-16-channel scales, dequantised exactly) followed by its own SWA

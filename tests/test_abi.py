@@ -178,6 +178,30 @@ def test_encoder_chunk_rejects(H):
     expect(H, 2, call(18, 4096))                # top_k
 
 
+def test_noalloc_chain_rejects(H):
+    """csa2_index_chain_noalloc: the chain's argument errors, then shapes beyond its fixed scratch,
+    all before anything is enqueued (without a GPU a launch or the scratch lookup would fail with
+    CSA2_ERR_HIP)."""
+    cap = H.csa2_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    for B, N in ((1, 1 << 20), (8, 131072), (1, 1 << 21)):
+        assert H.csa2_index_chain_workspace(B, 1, N, 8, 2048, 512, 4) <= cap, (B, N)
+    assert H.csa2_index_chain_workspace(16, 1, 1 << 21, 8, 2048, 512, 4) > cap
+    # idx_k, ks, rows, idx_q, head_w, nvis, B, T, n_max, block, P, K, ri_q, ri_w, L, pool_pos, pool_len,
+    # topk_idx, topk_score, ri_topk_idx, ri_topk_score
+    ok = [FAKE, None, 1 << 21, FAKE, FAKE, FAKE, 16, 1, 1 << 21, 8, 2048, 512, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None,
+          FAKE, None]
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return lambda: H.csa2_index_chain_noalloc(*a)
+    expect(H, 2, call(6, 16))                   # 16 queries at 2^21 positions: beyond the scratch
+    expect(H, 1, call(6, 0))                    # B
+    expect(H, 1, call(3, None))                 # idx_q
+    expect(H, 2, call(10, 4096))                # pool beyond 16384 positions
+    expect(H, 1, call(12, None))                # ri_q with L > 0
+
+
 def test_scan_blocks_rejects_unknown_block_score(H):
     ws = H.csa2_index_full_workspace(1, 1, 4096, 8, 64, 64)
     expect(H, 1, lambda: H.csa2_index_scan_blocks(FAKE, None, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, 64, 64, 3,
