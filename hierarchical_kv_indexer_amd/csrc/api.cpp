@@ -79,6 +79,7 @@ struct Carver {
 struct FullPlan {
   int Q, nb_max, nb_stride, chunk, n_wg, upw, n_units, blocks_per_unit, P, cap;
   bool internal_pool, multi_query;
+  bool chunk_lists;   // the scan also leaves chunk lists and the pool selects from them first
 };
 
 constexpr int kMaxPositions = 1 << 23;   // scores only: 1024 chunks of 8192 positions per query
@@ -104,6 +105,12 @@ FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
   p.internal_pool = pool_blocks == 0;
   p.P = p.internal_pool ? top_k : pool_blocks;
   p.cap = p.P * csa2::kBlock;
+  // Chunk lists (16 blocks and a cut per chunk of the one-query scan) pay off when a chunk is
+  // expected to hold few pool blocks: at most 8 on average, so that few chunks have more than 16
+  // and must be re-read.  The 1M decode (chunks of 512 blocks, 1/64 of the blocks pooled) expects 8.
+  const int bpc = p.chunk / csa2::kBlock;
+  p.chunk_lists = !p.multi_query && p.upw == 1 && p.n_wg <= 256 && p.nb_max > p.P &&
+                  (int64_t)p.P * bpc <= (int64_t)8 * p.nb_max;
   return p;
 }
 
@@ -113,6 +120,8 @@ struct FullWs {
   uint32_t* blkkey;
   uint64_t* lists;
   uint64_t* cuts;
+  uint64_t* clists;    // chunk lists (chunk_lists only)
+  uint64_t* ccuts;
   int32_t* pool_pos;   // internal pool (pool_blocks == 0 only)
   int32_t* pool_len;
 };
@@ -124,6 +133,8 @@ size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
   w.blkkey = c.take<uint32_t>((size_t)p.Q * p.nb_stride + 64);   // + tail read by unit batches
   w.lists = c.take<uint64_t>((size_t)p.Q * p.n_units * 4);
   w.cuts = c.take<uint64_t>((size_t)p.Q * p.n_units);
+  w.clists = p.chunk_lists ? c.take<uint64_t>((size_t)p.Q * p.n_wg * csa2::kListLen) : nullptr;
+  w.ccuts = p.chunk_lists ? c.take<uint64_t>((size_t)p.Q * p.n_wg) : nullptr;
   w.pool_pos = p.internal_pool ? c.take<int32_t>((size_t)p.Q * p.cap) : nullptr;
   w.pool_len = p.internal_pool ? c.take<int32_t>((size_t)p.Q) : nullptr;
   if (out) *out = w;
@@ -185,7 +196,7 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   const FullPlan p = plan_full(B, T, n_max, 1, 1);
   st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                        scores, nullptr, p.nb_max, nullptr, nullptr, p.chunk, p.n_wg, p.multi_query,
-                                       csa2::kBlockMax, p.upw, (hipStream_t)stream),
+                                       csa2::kBlockMax, p.upw, nullptr, nullptr, (hipStream_t)stream),
                  "index scan launch");
   return st == CSA2_OK ? ok() : st;
 }
@@ -234,7 +245,7 @@ static csa2_status index_scan(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   if (n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg,
-                                         p.multi_query, block_score, p.upw, (hipStream_t)stream),
+                                         p.multi_query, block_score, p.upw, w.clists, w.ccuts, (hipStream_t)stream),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }
@@ -275,7 +286,8 @@ static csa2_status check_topk_args(int32_t* topk_idx, float* topk_score) {
 static csa2_status launch_pool_stage(const FullPlan& p, const FullWs& w, const int32_t* n_visible, int n_max,
                                      int32_t* pool_pos, int32_t* pool_len, int top_k, int32_t* topk_idx,
                                      float* topk_score, hipStream_t s) {
-  return hip_check(csa2::launch_pool(w.lists, w.cuts, p.n_units, p.blocks_per_unit, w.blkkey, p.nb_stride,
+  return hip_check(csa2::launch_pool(w.lists, w.cuts, p.n_units, p.blocks_per_unit, w.clists, w.ccuts, p.n_wg,
+                                     p.chunk / csa2::kBlock, w.blkkey, p.nb_stride,
                                      n_visible, n_max, p.P, p.internal_pool ? w.pool_pos : pool_pos, p.cap,
                                      p.internal_pool ? w.pool_len : pool_len, w.scores, topk_idx ? top_k : 0,
                                      topk_idx, topk_score, p.Q, s),
@@ -373,10 +385,36 @@ csa2_status csa2_index_full(const uint8_t* idx_k, const uint8_t* idx_k_scales, i
                            topk_score, workspace, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scores by slot of `items` scored pools and their unit lists (see k_ri_score).
+struct ListWs {
+  float* slot_scores;
+  uint64_t* lists;
+  uint64_t* cuts;
+};
+
+size_t carve_lists(void* ws, int items, int cap, ListWs* out) {
+  Carver c{(char*)ws};
+  ListWs w;
+  const size_t nu = (size_t)csa2::ri_units(cap);
+  w.slot_scores = c.take<float>((size_t)items * cap);
+  w.lists = c.take<uint64_t>((size_t)items * nu * csa2::kRiUnitList);
+  w.cuts = c.take<uint64_t>((size_t)items * nu);
+  if (out) *out = w;
+  return c.off;
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k) {
   (void)top_k;
-  if (L < 1 || B < 1 || T < 1 || pool_cap < 1) return 0;
-  return align_up((size_t)L * B * T * pool_cap * sizeof(float));
+  if (L < 1 || B < 1 || T < 1 || pool_cap < 1 || pool_cap > csa2::kMaxPool) return 0;
+  return carve_lists(nullptr, L * B * T, pool_cap, nullptr);
 }
 
 csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
@@ -404,29 +442,34 @@ csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int6
           "workspace of %zu bytes required (got %zu)", need, ws_bytes);
   const int Q = B * T;
   hipStream_t s = (hipStream_t)stream;
-  float* ri = (float*)workspace;
-  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, pool_pos, pool_len,
-                                                   pool_cap, L, Q, T, ri, s),
+  ListWs lw;
+  carve_lists(workspace, L * Q, pool_cap, &lw);
+  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, nullptr, 0, 0,
+                                                   pool_pos, pool_len, pool_cap, L, Q, T, lw.slot_scores, lw.lists,
+                                                   lw.cuts, s),
                              "reindex score launch");
   if (st != CSA2_OK) return st;
-  csa2::TopkJob j{};
-  j.scores = ri;
-  j.score_stride = pool_cap;
-  j.n_rows = k_rows_per_seq;
-  j.by_position = 0;
-  j.items = L * Q;
-  j.out_idx = topk_idx;
-  j.out_score = topk_score;
-  st = hip_check(csa2::launch_topk(pool_pos, pool_len, pool_cap, Q, top_k, j, csa2::TopkJob{}, s), "top-k launch");
+  st = hip_check(csa2::launch_topk_lists(lw.lists, lw.cuts, lw.slot_scores, pool_pos, pool_len, pool_cap, Q, top_k,
+                                         k_rows_per_seq, k_rows_per_seq, 0, nullptr, nullptr, L * Q, topk_idx,
+                                         topk_score, s),
+                 "top-k launch");
   return st == CSA2_OK ? ok() : st;
 }
 
-// Full layer plus L Reindex layers over its pool: the Full workspace, then the Reindex scores.
-static size_t carve_chain(void* ws, const FullPlan& p, int n_max, int L, FullWs* fw, float** ri) {
+}  // extern "C"
+
+namespace {
+
+// Full layer plus L Reindex layers over its pool: the Full workspace, then the slot scores and
+// chunk lists of the Full layer's Top-K item and the L Reindex items.
+size_t carve_chain(void* ws, const FullPlan& p, int n_max, int L, FullWs* fw, ListWs* lw) {
   const size_t full = carve_full(ws, p, n_max, fw);
-  if (ri) *ri = ws ? (float*)((char*)ws + full) : nullptr;
-  return full + (L > 0 ? align_up((size_t)L * p.Q * p.cap * sizeof(float)) : 0);
+  return full + carve_lists(ws ? (char*)ws + full : nullptr, (L + 1) * p.Q, p.cap, lw);
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t csa2_index_chain_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k, int L) {
   (void)block_size;
@@ -468,35 +511,28 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
           "workspace of %zu bytes required (got %zu)", need, ws_bytes);
   FullWs w;
-  float* ri = nullptr;
-  carve_chain(workspace, p, n_max, L, &w, &ri);
+  ListWs lw;
+  carve_chain(workspace, p, n_max, L, &w, &lw);
   hipStream_t s = (hipStream_t)stream;
   if (do_scan && n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query,
-                                         csa2::kBlockMax, p.upw, s),
+                                         csa2::kBlockMax, p.upw, w.clists, w.ccuts, s),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }
   st = launch_pool_stage(p, w, n_visible, n_max, pool_pos, pool_len, top_k, nullptr, nullptr, s);
   if (st != CSA2_OK) return st;
-  csa2::TopkJob rj{};
-  if (L > 0) {
-    st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, ri_q, ri_w, pool_pos, pool_len, p.cap, L, p.Q, T,
-                                         ri, s),
-                   "reindex score launch");
-    if (st != CSA2_OK) return st;
-    rj.scores = ri;
-    rj.score_stride = p.cap;
-    rj.n_rows = k_rows_per_seq;
-    rj.by_position = 0;
-    rj.items = L * p.Q;
-    rj.out_idx = ri_topk_idx;
-    rj.out_score = ri_topk_score;
-  }
-  // the Reindex layers' Top-K and the Full layer's Top-K in one launch
-  st = hip_check(csa2::launch_topk(pool_pos, pool_len, p.cap, p.Q, top_k, rj,
-                                   full_topk_job(p, w, n_max, topk_idx, topk_score), s),
+  // the Full layer's pool scores (gathered from the scan's scores) and the Reindex layers'
+  // scores, each chunk with its list; then every layer's Top-K in one launch
+  st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, L ? ri_q : nullptr, L ? ri_w : nullptr,
+                                       w.scores, n_max, p.Q, pool_pos, pool_len, p.cap, L, p.Q, T, lw.slot_scores,
+                                       lw.lists, lw.cuts, s),
+                 "pool scoring launch");
+  if (st != CSA2_OK) return st;
+  st = hip_check(csa2::launch_topk_lists(lw.lists, lw.cuts, lw.slot_scores, pool_pos, pool_len, p.cap, p.Q, top_k,
+                                         n_max > 0 ? n_max : 1, k_rows_per_seq, p.Q, topk_idx, topk_score, L * p.Q,
+                                         ri_topk_idx, ri_topk_score, s),
                  "top-k launch");
   return st == CSA2_OK ? ok() : st;
 }

@@ -10,6 +10,7 @@ constexpr int kFullThreads = 1024;     // Full scan: one workgroup of 16 waves p
 constexpr int kSelectThreads = 1024;
 constexpr int kAttnThreads = 256;
 constexpr int kMaxLayers = 64;
+constexpr int kListLen = 16;           // keys of a chunk list (pool scan chunks, scored pool chunks)
 
 struct LayerSets { int32_t set[kMaxLayers]; };
 
@@ -30,19 +31,34 @@ constexpr int kScanUnitsPerWg = kFullThreads / 64;   // 16 waves per chunk, each
 constexpr int kMaxFullPositions = 1 << 21;           // 256 chunks of 8192 per query: 4096 units
 // Indexer keys: idx_ks == null: E4M3 idx_k [rows][128]; otherwise FP4 codes idx_k [rows][64] and
 // E4M3 scales idx_ks [rows][8] (one per 16 channels).
+// With clists non-null (one-query scan, one unit per wave) each chunk also leaves its 16 best
+// blocks and a cut (k_idx_scan's chunk list) in clists[q][chunk][16] and ccuts[q][chunk].
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
                            uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, int upw,
-                           hipStream_t s);
+                           uint64_t* clists, uint64_t* ccuts, hipStream_t s);
+// Reindex scoring of pool slots in chunks of kRiChunk (and, for the first full_items items, the
+// Full layer's scan scores gathered by position); with `lists` non-null each unit of kRiUnit
+// slots lists its kRiUnitList best keys and a cut (see k_ri_score).
+constexpr int kRiChunk = 128;
+constexpr int kRiUnit = 32;            // slots of a pool-scoring list unit (one wave's slots)
+constexpr int kRiUnitList = 4;         // keys a unit lists; its 5th best is its cut
+__host__ __device__ inline int ri_chunks(int pool_cap) { return (pool_cap + kRiChunk - 1) / kRiChunk; }
+__host__ __device__ inline int ri_units(int pool_cap) { return ri_chunks(pool_cap) * (kRiChunk / kRiUnit); }
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
-                           const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
-                           int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s);
+                           const float* head_w, const float* full_scores, int64_t full_stride, int full_items,
+                           const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
+                           float* slot_scores, uint64_t* lists, uint64_t* cuts, hipStream_t s);
 
 // select.hip
 // Pool of the top P blocks (positions ascending, -1 padded to cap_out), one WG per query.
 // With K > 0 the same WG then takes the Top-K of the pool from the scan's scores.
+// With clists non-null the pool is selected from the scan's chunk lists first (n_chunks chunks of
+// blocks_per_chunk blocks per query), and from the unit lists only when too many chunks would
+// have to be re-read.
 hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
+                       const uint64_t* clists, const uint64_t* ccuts, int n_chunks, int blocks_per_chunk,
                        const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max, int P,
                        int32_t* pool_pos, int cap_out, int32_t* pool_len, const float* scores, int K,
                        int32_t* topk_idx, float* topk_score, int Q, hipStream_t s);
@@ -62,6 +78,14 @@ struct TopkJob {
 // Items of job a, then items of job b (b.items may be 0), in one launch.
 hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
                        const TopkJob& a, const TopkJob& b, hipStream_t s);
+// Top-K of items scored by launch_ri_score with lists: item it (of items_a + items_b; query
+// it % Q within its group) selects from its units' lists, re-reading slot_scores only for units
+// whose cut reaches the threshold.  Outputs as launch_topk (job a's items write out_a, job b's
+// out_b; [items][k], -1 / 0 padded, ascending positions for an ascending pool).
+hipError_t launch_topk_lists(const uint64_t* lists, const uint64_t* cuts, const float* slot_scores,
+                             const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
+                             int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* out_a, float* out_sa,
+                             int items_b, int32_t* out_b, float* out_sb, hipStream_t s);
 
 // encoder.hip
 // n_visible[b][t] = floor((p0 + t + 1) / m), swa_end[b][t] = hist + t + 1.

@@ -335,8 +335,10 @@ template <bool kFp4> constexpr int kScanU = 3;
 constexpr int kFullWaves = kFullThreads / 64;   // 16
 static_assert(kFullWaves == kScanUnitsPerWg, "each wave lists the units of its own range");
 
+// LDS of k_idx_scan: the query (bf16), the chunk's scores and block keys, the stage counter, and
+// 64 words for the chunk list's ranking.
 size_t scan_lds_bytes(int chunk) {
-  return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)chunk * 4 + (size_t)(chunk / kBlock) * 4 + 16;
+  return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)chunk * 4 + (size_t)(chunk / kBlock) * 4 + 16 + 64 * 8;
 }
 
 // Best ranking key (score key, block) of a wave's blocks (one per lane), removed from the
@@ -394,6 +396,89 @@ __device__ __forceinline__ void write_unit_lists(uint32_t key, uint32_t blk, int
   }
 }
 
+// The chunk's unit lists and its chunk list, computed by one wave from the chunk's block keys in
+// LDS (used with one unit per wave: 16 units of bpu = 4*KB blocks, so lane l holds blocks
+// KB*l .. KB*l+KB-1 and each aligned quad of lanes holds one unit).
+//   unit lists: as write_unit_lists (the five best blocks of each unit);
+//   chunk list: from the 64 keys the 16 units list (in block order) and the largest unit cut mc,
+//     the keys above mc among the 16 best, in block order, into clist[0..15] (0 padded), and the
+//     cut max(mc, the 17th best listed key).  Every block of the chunk that is not in its list
+//     ranks at or below that cut: a block outside its unit's four is at or below the unit's cut,
+//     and a listed key left out is at or below mc or the 17th.
+// xch: 64 LDS words of this wave.
+template <int KB>
+__device__ __forceinline__ void wave_chunk_lists(const uint32_t* wkeys, int nblk, uint32_t blk0, size_t unit0,
+                                                 uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts,
+                                                 uint64_t* __restrict__ clist, uint64_t* __restrict__ ccut,
+                                                 uint64_t* xch) {
+  const int lane = threadIdx.x & 63;
+  uint32_t k[KB];
+#pragma unroll
+  for (int i = 0; i < KB; ++i) {
+    const int b = KB * lane + i;
+    k[i] = b < nblk ? wkeys[b] : 0u;
+  }
+  const uint32_t my0 = blk0 + (uint32_t)(KB * lane);
+  uint64_t best[5];
+#pragma unroll
+  for (int r = 0; r < 5; ++r) {
+    uint32_t lk = 0u, li = 0u;                   // this lane's best: the first of its largest keys
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (k[i] > lk) { lk = k[i]; li = (uint32_t)i; }
+    uint32_t gk = max(lk, dpp_mov<0xB1>(lk));    // quad_perm [1,0,3,2]
+    gk = max(gk, dpp_mov<0x4E>(gk));             // quad_perm [2,3,0,1]
+    uint32_t gb = (lk == gk && lk != 0u) ? my0 + li : 0xffffffffu;
+    gb = min(gb, dpp_mov<0xB1>(gb));
+    gb = min(gb, dpp_mov<0x4E>(gb));
+    best[r] = gk ? rank_key(gk, gb) : 0ull;
+    const bool mine = gk != 0u && lk == gk && my0 + li == gb;
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+      if (mine && (uint32_t)i == li) k[i] = 0u;
+  }
+  const int u = lane >> 2, rq = lane & 3;
+  if (rq == 0) {
+    u32x4* lp = (u32x4*)(lists + (unit0 + u) * 4);
+    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
+    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
+    cuts[unit0 + u] = best[4];
+  }
+  // the unit's four in block order (a larger block is a smaller low word; none sorts last)
+  auto cx = [&](int a, int b) {
+    const bool sw = (uint32_t)best[a] < (uint32_t)best[b];
+    const uint64_t x = sw ? best[b] : best[a], y = sw ? best[a] : best[b];
+    best[a] = x;
+    best[b] = y;
+  };
+  cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+  const uint64_t x = rq == 0 ? best[0] : (rq == 1 ? best[1] : (rq == 2 ? best[2] : best[3]));
+  // mc: the largest unit cut
+  const uint32_t chi = wave_max_u32((uint32_t)(best[4] >> 32));
+  const uint32_t clo = wave_max_u32((uint32_t)(best[4] >> 32) == chi ? (uint32_t)best[4] : 0u);
+  const uint64_t mc = ((uint64_t)chi << 32) | clo;
+  // rank of x among the 64 listed keys (LDS operations of a wave complete in order)
+  xch[lane] = x;
+  __builtin_amdgcn_wave_barrier();
+  uint32_t rank = 0;
+#pragma unroll 16
+  for (int m = 0; m < 64; ++m) rank += xch[m] > x ? 1u : 0u;
+  const bool flag = x != 0ull && x > mc && rank < (uint32_t)kListLen;
+  const uint64_t fm = __ballot(flag);
+  const uint32_t nflag = (uint32_t)__popcll(fm);
+  if (flag) clist[__builtin_amdgcn_mbcnt_hi((uint32_t)(fm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)fm, 0u))] = x;
+  if (lane < kListLen && (uint32_t)lane >= nflag) clist[lane] = 0ull;
+  // the cut: max(mc, the 17th best listed key), none when fewer than 17 keys are listed
+  const uint64_t m17 = __ballot(x != 0ull && rank == (uint32_t)kListLen);
+  uint64_t c17 = 0ull;
+  if (m17) {
+    const int l17 = __ffsll((unsigned long long)m17) - 1;
+    c17 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), l17) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l17);
+  }
+  if (lane == 0) *ccut = c17 > mc ? c17 : mc;
+}
+
 // grid (n_wg, Q), one workgroup of 16 waves per chunk of positions (sized so the grid is about
 // one workgroup per CU).  The waves take pipeline stages of kScanU tiles from an LDS counter,
 // so a wave that the CU's arbitration favours simply takes more stages and all waves finish
@@ -413,12 +498,14 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     const uint16_t* __restrict__ idx_q,
     const float* __restrict__ head_w, const int32_t* __restrict__ n_visible, int T, int n_max,
     int chunk, float* __restrict__ scores, uint32_t* __restrict__ blkkey, int nb_max,
-    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts, int upw) {
+    uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts, int upw, uint64_t* __restrict__ clists,
+    uint64_t* __restrict__ ccuts) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   uint16_t* qlds = (uint16_t*)lds;
   float* sbuf = (float*)(lds + kIdxHeads * kIdxDim * 2);
   uint32_t* wkeys = (uint32_t*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4);
   int* ctr = (int*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4 + (chunk / kBlock) * 4);
+  uint64_t* xch = (uint64_t*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4 + (chunk / kBlock) * 4 + 16);
   const int q = blockIdx.y, b = q / T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -497,6 +584,21 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     for (int i = threadIdx.x; i < nblk; i += kFullThreads) brow[i] = wkeys[i];
   }
   if (!lists) return;
+  if (clists) {
+    // one wave builds the chunk's unit lists and its chunk list (upw == 1)
+    if (wave != 0) return;
+    const size_t ch = (size_t)q * gridDim.x + blockIdx.x;
+    const size_t unit0 = ch * kFullWaves;
+    const uint32_t blk0 = (uint32_t)(p_begin / kBlock);
+    uint64_t* cl = clists + ch * kListLen;
+    switch (chunk / (kBlock * 64)) {             // blocks per lane
+      case 2: wave_chunk_lists<2>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
+      case 4: wave_chunk_lists<4>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
+      case 8: wave_chunk_lists<8>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
+      default: wave_chunk_lists<16>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
+    }
+    return;
+  }
   // the wave's blocks (bpu <= 64: one per lane), split into upw units of bpu/upw blocks; each
   // unit lists its five best
   const int bpu = chunk / (kBlock * kFullWaves);
@@ -809,22 +911,22 @@ int scan_mq_chunk(int n_max, int B, int T) {
 
 int scan_chunk_positions(int n_max, int queries) {
   // about one workgroup per CU (256) over all queries, at most 256 workgroups per query (the
-  // pool takes at most 4096 units); multiples of 1024 positions, at most 8192 (LDS staging)
+  // pool takes at most 4096 units); a power of two from 1024 to 8192 positions (LDS staging),
+  // so that each wave's share of blocks splits into power-of-two units
   long long total = (long long)n_max * (queries > 0 ? queries : 1);
   long long c = (total + 255) / 256;
   long long per_query = ((long long)n_max + 255) / 256;
   if (c < per_query) c = per_query;
-  c = (c + 1023) / 1024 * 1024;
-  if (c < 1024) c = 1024;
-  if (c > 8192) c = 8192;
-  return (int)c;
+  long long p = 1024;
+  while (p < c && p < 8192) p *= 2;
+  return (int)p;
 }
 
 template <bool kFp4, int kBS>
 static void launch_scan_variant(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                                 const float* head_w, const int32_t* n_visible, int Q, int T, int n_max, float* scores,
                                 uint32_t* blkkey, int nb_max, uint64_t* lists, uint64_t* cuts, int chunk, int n_wg,
-                                bool multi_query, int upw, hipStream_t s) {
+                                bool multi_query, int upw, uint64_t* clists, uint64_t* ccuts, hipStream_t s) {
   if (multi_query) {
     const int groups = (Q / T) * ((T + kMqQueries - 1) / kMqQueries);
     hipLaunchKernelGGL((k_idx_scan_mq<kFp4, kBS>), dim3(n_wg, groups), dim3(kMqThreads), 0, s, idx_k, idx_ks, k_rows,
@@ -832,7 +934,7 @@ static void launch_scan_variant(const uint8_t* idx_k, const uint8_t* idx_ks, int
   } else {
     hipLaunchKernelGGL((k_idx_scan<kFp4, kBS>), dim3(n_wg, Q), dim3(kFullThreads), scan_lds_bytes(chunk), s, idx_k,
                        idx_ks, k_rows, idx_q, head_w, n_visible, T, n_max, chunk, scores, blkkey, nb_max, lists,
-                       cuts, upw);
+                       cuts, upw, clists, ccuts);
   }
 }
 
@@ -840,105 +942,168 @@ template <bool kFp4>
 static void launch_scan_format(int block_score, const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows,
                                const uint16_t* idx_q, const float* head_w, const int32_t* n_visible, int Q, int T,
                                int n_max, float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
-                               uint64_t* cuts, int chunk, int n_wg, bool multi_query, int upw, hipStream_t s) {
+                               uint64_t* cuts, int chunk, int n_wg, bool multi_query, int upw, uint64_t* clists,
+                               uint64_t* ccuts, hipStream_t s) {
   if (block_score == kBlockSum)
     launch_scan_variant<kFp4, kBlockSum>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
-                                         nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
+                                         nb_max, lists, cuts, chunk, n_wg, multi_query, upw, clists, ccuts, s);
   else if (block_score == kBlockTop2)
     launch_scan_variant<kFp4, kBlockTop2>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores,
-                                          blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
+                                          blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, upw, clists, ccuts, s);
   else
     launch_scan_variant<kFp4, kBlockMax>(idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
-                                         nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
+                                         nb_max, lists, cuts, chunk, n_wg, multi_query, upw, clists, ccuts, s);
 }
 
 hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const int32_t* n_visible, int Q, int T, int n_max,
                            float* scores, uint32_t* blkkey, int nb_max, uint64_t* lists,
                            uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, int upw,
-                           hipStream_t s) {
+                           uint64_t* clists, uint64_t* ccuts, hipStream_t s) {
   if (block_score < kBlockMax || block_score > kBlockTop2) return hipErrorInvalidValue;
   const int bpw = chunk / (kBlock * kFullWaves);       // blocks per wave
   if (upw < 1 || bpw % upw != 0 || bpw / upw < 8 || (bpw / upw & (bpw / upw - 1)) != 0) return hipErrorInvalidValue;
   if (multi_query && (chunk % 1024 != 0 || chunk > kMqMaxChunk || Q % T != 0)) return hipErrorInvalidValue;
+  if (clists && (multi_query || upw != 1 || !lists || !ccuts)) return hipErrorInvalidValue;   // one unit per wave
   if (idx_ks)
     launch_scan_format<true>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
-                             nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
+                             nb_max, lists, cuts, chunk, n_wg, multi_query, upw, clists, ccuts, s);
   else
     launch_scan_format<false>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores,
-                              blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, upw, s);
+                              blkkey, nb_max, lists, cuts, chunk, n_wg, multi_query, upw, clists, ccuts, s);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------- Reindex scoring
 
 constexpr int kRiTilesPerWave = 2;
+static_assert(kScanThreads / 64 * kRiTilesPerWave * 16 == kRiChunk, "a workgroup scores one chunk of slots");
 
-// grid (n_chunks, L*Q).  Item it = l*Q + q scores pool slots [x*chunk, (x+1)*chunk) of query
-// q (chunk = 64 * kRiTilesPerWave) with layer l's query and weights.  Slots beyond pool_len or
-// holding positions outside [0, k_rows) are not written.
+// grid (n_chunks, items): item it scores pool slots [x*kRiChunk, (x+1)*kRiChunk) of its query.
+//   it <  full_items  the Full layer of query q = it: the scan's score of each slot's position,
+//                     full_scores[q * full_stride + pos] (no keys are read);
+//   it >= full_items  Reindex layer r / Q of query q = r % Q (r = it - full_items): the slot's
+//                     indexer key scored with that layer's query idx_q[r] and weights head_w[r].
+// Writes slot_scores[it][slot] for slots < pool_len holding a position in [0, k_rows) (others are
+// not written).  With `lists` non-null, each wave's 32 slots (one unit; unit 4x + wave) also leave
+// the pool Top-K its part: the ranking keys (score key << 32 | ~position) of the unit's 4 best
+// slots in slot order in lists[it][unit][0..3] (0 = none) and its 5th best in cuts[it][unit]
+// (0 = none), so every slot of the unit that is not listed ranks at or below the cut.  Equal keys
+// (a position listed more than once) are taken one slot at a time.
 template <bool kFp4>
 __global__ __launch_bounds__(kScanThreads) void k_ri_score(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
-    const uint16_t* __restrict__ idx_q,
-    const float* __restrict__ head_w, const int32_t* __restrict__ pool_pos,
-    const int32_t* __restrict__ pool_len, int cap, int Q, int T, float* __restrict__ ri_scores) {
+    const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
+    const float* __restrict__ full_scores, int64_t full_stride, int full_items,
+    const int32_t* __restrict__ pool_pos, const int32_t* __restrict__ pool_len, int cap, int Q, int T,
+    float* __restrict__ slot_scores, uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
   __shared__ __attribute__((aligned(16))) uint16_t qlds[kIdxHeads * kIdxDim];
-  __shared__ float sbuf[kScanThreads / 64][kRiTilesPerWave * 16];
-  const int it = blockIdx.y, q = it % Q, b = q / T;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int it = blockIdx.y;
+  const bool full = it < full_items;
+  const int r = it - full_items, q = full ? it : r % Q, b = q / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
   int len = pool_len[q];
   len = len < 0 ? 0 : (len > cap ? cap : len);
-  const int chunk = 64 * kRiTilesPerWave;
-  const int s_begin = blockIdx.x * chunk;
-  const int s_end = min(s_begin + chunk, len);
+  const int s_begin = blockIdx.x * kRiChunk;
+  const int s_end = min(s_begin + kRiChunk, len);
   if (s_end <= s_begin) return;
-  const int sw = s_begin + 16 * kRiTilesPerWave * wave;          // first slot of this wave
   const int32_t* pp = pool_pos + (size_t)q * cap;
-  int pos[kRiTilesPerWave];
+  float* out = slot_scores + (size_t)it * cap;
+  const int sw = s_begin + kRiUnit * wave;                         // first slot of this wave's unit
+  // this lane's candidate for the unit's list: slot sw + lane (lanes < 32)
+  float my_sc = 0.f;
+  int my_pos = -1;
+  if (full) {
+    const int64_t n_rows = min(k_rows, full_stride);
+    if (lane < kRiUnit) {
+      const int slot = sw + lane;
+      int pos = slot < s_end ? pp[slot] : -1;
+      pos = (pos >= 0 && (int64_t)pos < n_rows) ? pos : -1;
+      my_sc = pos >= 0 ? full_scores[(size_t)q * full_stride + pos] : 0.f;
+      my_pos = pos;
+      if (pos >= 0) out[slot] = my_sc;
+    }
+  } else {
+    int pos[kRiTilesPerWave];
 #pragma unroll
-  for (int u = 0; u < kRiTilesPerWave; ++u) {
-    const int slot = sw + 16 * u + j;
-    pos[u] = slot < s_end ? pp[slot] : -1;
+    for (int u = 0; u < kRiTilesPerWave; ++u) {
+      const int slot = sw + 16 * u + j;
+      pos[u] = slot < s_end ? pp[slot] : -1;
+    }
+    stage_query<kScanThreads, kFp4>(idx_q + (size_t)r * kIdxHeads * kIdxDim, qlds);
+    const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
+    const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
+    TileRaw<kFp4> raw[kRiTilesPerWave];
+    bool ok[kRiTilesPerWave];
+#pragma unroll
+    for (int u = 0; u < kRiTilesPerWave; ++u) {
+      ok[u] = pos[u] >= 0 && (int64_t)pos[u] < k_rows;
+      load_key<kFp4>(kseq, sseq, ok[u] ? pos[u] : 0, g, raw[u]);
+    }
+    __syncthreads();
+    TileCtx cx;
+    key_ctx<kFp4>(cx, qlds, head_w + (size_t)r * kIdxHeads);
+    float sc[kRiTilesPerWave];
+#pragma unroll
+    for (int u = 0; u < kRiTilesPerWave; ++u) {
+      sc[u] = key_score<kFp4>(cx, raw[u]);
+      if (g == 0 && ok[u]) out[sw + 16 * u + j] = sc[u];
+    }
+    // lane 16u + j (u < 2) takes tile u's slot sw + 16u + j (every lane of a column holds its score)
+    const int p0 = ok[0] ? pos[0] : -1, p1 = ok[1] ? pos[1] : -1;
+    my_sc = g == 1 ? sc[1] : sc[0];
+    my_pos = g == 0 ? p0 : (g == 1 ? p1 : -1);
   }
-  stage_query<kScanThreads, kFp4>(idx_q + (size_t)it * kIdxHeads * kIdxDim, qlds);
-  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
-  const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
-  TileRaw<kFp4> raw[kRiTilesPerWave];
-  bool ok[kRiTilesPerWave];
+  if (!lists) return;
+  // the unit's five best keys, one at a time: the largest key, and among copies of it the lowest
+  // lane (slot), leaves the set
+  uint64_t x = my_pos >= 0 ? rank_key(score_key(my_sc), (uint32_t)my_pos) : 0ull;
+  uint64_t best[kRiUnitList + 1];
+  int bslot[kRiUnitList + 1];
 #pragma unroll
-  for (int u = 0; u < kRiTilesPerWave; ++u) {
-    ok[u] = pos[u] >= 0 && (int64_t)pos[u] < k_rows;
-    load_key<kFp4>(kseq, sseq, ok[u] ? pos[u] : 0, g, raw[u]);
+  for (int n = 0; n < kRiUnitList + 1; ++n) {
+    const uint32_t hi = wave_max_u32((uint32_t)(x >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(x >> 32) == hi ? (uint32_t)x : 0u);
+    const uint64_t m = ((uint64_t)hi << 32) | lo;
+    const uint64_t at = __ballot(x == m && m != 0ull);
+    const int first = at ? __ffsll((unsigned long long)at) - 1 : 64;
+    best[n] = m;
+    bslot[n] = first;
+    if (lane == first) x = 0ull;
   }
-  __syncthreads();
-  TileCtx cx;
-  key_ctx<kFp4>(cx, qlds, head_w + (size_t)it * kIdxHeads);
-#pragma unroll
-  for (int u = 0; u < kRiTilesPerWave; ++u) {
-    const float sc = key_score<kFp4>(cx, raw[u]);
-    if (g == 0) sbuf[wave][16 * u + j] = sc;
-  }
-  float* out = ri_scores + (size_t)it * cap;
-  if (g == 0) {
-#pragma unroll
-    for (int u = 0; u < kRiTilesPerWave; ++u)
-      if (ok[u]) out[sw + 16 * u + j] = sbuf[wave][16 * u + j];
+  if (lane == 0) {
+    // the four listed in slot order (none = slot 64 sorts last)
+    auto cx = [&](int a, int c) {
+      const bool sw2 = bslot[a] > bslot[c];
+      const uint64_t ka = sw2 ? best[c] : best[a], kc = sw2 ? best[a] : best[c];
+      const int sa = sw2 ? bslot[c] : bslot[a], sc2 = sw2 ? bslot[a] : bslot[c];
+      best[a] = ka; best[c] = kc; bslot[a] = sa; bslot[c] = sc2;
+    };
+    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+    const size_t unit = (size_t)it * (gridDim.x * (kRiChunk / kRiUnit)) + blockIdx.x * (kRiChunk / kRiUnit) + wave;
+    u32x4* lp = (u32x4*)(lists + unit * kRiUnitList);
+    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
+    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
+    cuts[unit] = best[kRiUnitList];
   }
 }
 
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
-                           const float* head_w, const int32_t* pool_pos, const int32_t* pool_len,
-                           int pool_cap, int L, int Q, int T, float* ri_scores, hipStream_t s) {
-  const int chunk = 64 * kRiTilesPerWave;
-  const int n_chunks = (pool_cap + chunk - 1) / chunk;
+                           const float* head_w, const float* full_scores, int64_t full_stride, int full_items,
+                           const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
+                           float* slot_scores, uint64_t* lists, uint64_t* cuts, hipStream_t s) {
+  const int n_chunks = (pool_cap + kRiChunk - 1) / kRiChunk;
+  const int items = full_items + L * Q;
+  if (items == 0) return hipSuccess;
   if (idx_ks)
-    hipLaunchKernelGGL(k_ri_score<true>, dim3(n_chunks, L * Q), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, pool_pos, pool_len, pool_cap, Q, T, ri_scores);
+    hipLaunchKernelGGL(k_ri_score<true>, dim3(n_chunks, items), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
+                       idx_q, head_w, full_scores, full_stride, full_items, pool_pos, pool_len, pool_cap, Q, T,
+                       slot_scores, lists, cuts);
   else
-    hipLaunchKernelGGL(k_ri_score<false>, dim3(n_chunks, L * Q), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, pool_pos, pool_len, pool_cap, Q, T, ri_scores);
+    hipLaunchKernelGGL(k_ri_score<false>, dim3(n_chunks, items), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
+                       idx_q, head_w, full_scores, full_stride, full_items, pool_pos, pool_len, pool_cap, Q, T,
+                       slot_scores, lists, cuts);
   return hipGetLastError();
 }
 

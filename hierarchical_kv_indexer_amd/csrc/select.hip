@@ -364,6 +364,50 @@ __device__ __forceinline__ void sort4(uint32_t (&v)[4]) {
   cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
 }
 
+// The pool's output, shared by both pool kernels: slot s holds block byrank[s / 8] (position s
+// when all blocks are kept, `all`), ascending, -1 padded to cap_out; pool_len the count.  With
+// K > 0 it goes on to the Top-K positions of the pool by (score desc, position asc) from the scan's
+// scores of this query, written in slot (= position) order.
+__device__ __forceinline__ void pool_out(bool all, int nv, int nb, uint32_t nsel, const uint32_t* byrank,
+                                         int32_t* __restrict__ gp, int cap_out, int32_t* __restrict__ len_out,
+                                         const float* __restrict__ sc, int K, int32_t* __restrict__ oi,
+                                         float* __restrict__ os, Block& bk) {
+  const int t = threadIdx.x;
+  int total;
+  if (all) {
+    total = nv;
+  } else {
+    total = 8 * (int)nsel;
+    if (nsel > 0 && (int)byrank[nsel - 1] == nb - 1) total -= kBlock - (nv - kBlock * (nb - 1));
+  }
+  int32_t ps[kE];
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const int sl = i * kNT + t;
+    ps[i] = sl < total ? (all ? sl : kBlock * (int)byrank[sl >> 3] + (sl & 7)) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const int sl = i * kNT + t;
+    if (sl < cap_out) gp[sl] = ps[i];
+  }
+  if (t == 0) *len_out = total;
+  if (K == 0) return;
+  float sv[kE];
+#pragma unroll
+  for (int i = 0; i < kE; ++i) sv[i] = sc[ps[i] >= 0 ? ps[i] : 0];
+  uint64_t key[kE];
+  uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const uint32_t k32 = score_key(sv[i]);
+    key[i] = ps[i] >= 0 ? rank_key(k32, (uint32_t)ps[i]) : 0ull;
+    nvalid += ps[i] >= 0 ? 1u : 0u;
+    if (ps[i] >= 0) { mn = min(mn, k32); mx = max(mx, k32); }
+  }
+  topk_out(key, nvalid, mn, mx, K, oi, os, bk);
+}
+
 // One WG per query: keeps the top P blocks by (block max desc, block asc) as the pool, written
 // as positions in ascending order (all blocks if there are at most P), -1 padded to cap_out
 // (a multiple of 8).  With K > 0 it goes on to the Top-K positions of the pool by (score desc,
@@ -610,7 +654,542 @@ __global__ __launch_bounds__(kNT) void k_pool(
     __syncthreads();
   }
 
-  // pool positions: slot s holds block byrank[s / 8], or position s when all blocks are kept
+  pool_out(all, nv, nb, nsel, byrank, pool_pos + (size_t)q * cap_out, cap_out, pool_len + q,
+           scores + (size_t)q * n_max, K, topk_idx + (size_t)q * K, topk_score ? topk_score + (size_t)q * K : nullptr,
+           bk);
+}
+
+// ------------------------------------------------------------------ list selection, 512 threads
+//
+// The pool's and the Top-K's selections from lists (the scan's chunk lists, the pool scoring's
+// unit lists) take few block-wide steps, and each step of a workgroup costs about the same
+// however little data it touches, so these kernels run 512 threads (two waves per SIMD): measured
+// on this part, a scan step with a barrier takes ~0.33 us at 512 threads against ~0.60 us at 1024.
+//
+// Lists: group g (a chunk of the scan, or a unit of 32 pool slots) lists its best keys in member
+// order, and its cut bounds every member it does not list.  Let T0' be the lower edge of the
+// first-pass histogram bin that holds the P-th best listed key: T0' <= T0 <= T*, where T0 is that
+// key and T* the true P-th best of all members.  A group whose cut is below T0' has no unlisted
+// member that can be selected; the groups whose cut reaches T0' are re-read.  T*'s histogram is
+// the first pass's (left uncleared: bins below T0's bin only add to the counts below it) with the
+// re-read groups' listed keys taken out and all their members >= T0' put in.
+namespace ls {
+
+constexpr int NT = 512;
+constexpr int W = NT / 64;
+constexpr int BINS = 4096;
+constexpr int BPT = BINS / NT;              // bins per thread (8)
+constexpr int RANK_MAX = 64;                // bins this small are ranked by one wave
+constexpr int CAND = 4096;                  // re-read members held in LDS
+constexpr int MAX_SAT = 128;                // re-read groups
+constexpr int MAX_GROUPS = 512;
+static_assert(BPT == 8, "find_bin reads two 16-byte bin quads per thread");
+
+struct __attribute__((aligned(16))) Smem {
+  uint32_t hist[BINS + 64];                 // bins BINS.. take out-of-range keys and are never read
+  u32x4 wred[2][W];
+  uint32_t ecnt[2][64 * W];                 // ordered(): per-(element, wave) totals; rank_small: partials
+  uint64_t rk[RANK_MAX];
+  uint64_t cand[CAND];                      // re-read members (0 = none / below T0')
+  uint16_t satgroup[MAX_SAT];
+  uint32_t satinfo[MAX_SAT];                // selected count of a re-read group, then its offset
+  uint16_t satof[MAX_GROUPS];               // group -> 1 + its re-read slot (0: not re-read)
+  uint64_t result;
+  uint32_t bin, above, cnt, nrk, nsat;
+};
+
+__device__ __forceinline__ void init(Smem& sm) {
+  for (int i = threadIdx.x; i < BINS / 4; i += NT) *(u32x4*)&sm.hist[4 * i] = u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 0) { sm.nsat = 0; sm.nrk = 0; }
+}
+
+struct Blk {
+  Smem& sm;
+  int parity = 0;
+  __device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t inc = wave_incl_sum(v);
+    if (lane == 63) sm.wred[parity][wave].x = inc;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const uint32_t s = sm.wred[parity][w].x;
+      before += w < wave ? s : 0u;
+      tot += s;
+    }
+    parity ^= 1;
+    total = tot;
+    return before + inc - v;
+  }
+  __device__ __forceinline__ void reduce(uint32_t& cnt, uint32_t& mn, uint32_t& mx) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    cnt = wave_sum_u32(cnt);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
+    if (lane == 0) sm.wred[parity][wave] = u32x4{cnt, mn, mx, 0u};
+    __syncthreads();
+    cnt = 0u;
+    mn = 0xffffffffu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const u32x4 r = sm.wred[parity][w];
+      cnt += r.x;
+      mn = min(mn, r.y);
+      mx = max(mx, r.z);
+    }
+    parity ^= 1;
+  }
+};
+
+// Offsets in element-major order (element i of thread t is item i*NT + t), as ordered_offsets.
+template <bool FLAGS, int N>
+__device__ __forceinline__ uint32_t ordered(const uint32_t (&c)[N], uint32_t (&off)[N], Blk& bk) {
+  static_assert(N <= 16, "per-(element, wave) totals hold 16 elements");
+  Smem& sm = bk.sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* ec = sm.ecnt[bk.parity];
+  bk.parity ^= 1;
+  uint32_t pre[N], mine = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (FLAGS) {
+      const uint64_t m = __ballot(c[i] != 0u);
+      pre[i] = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (lane == i) mine = (uint32_t)__popcll(m);
+    } else {
+      const uint32_t inc = wave_incl_sum(c[i]);
+      pre[i] = inc - c[i];
+      const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      if (lane == i) mine = tot;
+    }
+  }
+  if (lane < N) ec[lane * W + wave] = mine;
+  __syncthreads();
+  uint32_t tot_i = 0u, pre_w = 0u;
+  if (lane < N) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const uint32_t v = ec[lane * W + w];
+      tot_i += v;
+      pre_w += w < wave ? v : 0u;
+    }
+  }
+  const uint32_t inc_t = wave_incl_sum(tot_i);
+  const uint32_t base = inc_t - tot_i + pre_w;
+#pragma unroll
+  for (int i = 0; i < N; ++i) off[i] = (uint32_t)__builtin_amdgcn_readlane((int)base, i) + pre[i];
+  return (uint32_t)__builtin_amdgcn_readlane((int)inc_t, N - 1);
+}
+
+// The bin b with above(b) < need <= above(b) + hist[b] (above(b): counts of bins > b) into sm.bin,
+// sm.above, sm.cnt; with `clear` the histogram is cleared as it is read.  Thread t owns bins
+// 8t .. 8t+7.  need >= 1 and at most the histogram's total.
+__device__ __forceinline__ void find_bin(uint32_t need, bool clear, Blk& bk) {
+  Smem& sm = bk.sm;
+  const int t = threadIdx.x;
+  u32x4* hp = (u32x4*)&sm.hist[BPT * t];
+  const u32x4 h0 = hp[0], h1 = hp[1];
+  if (clear) hp[0] = hp[1] = u32x4{0u, 0u, 0u, 0u};
+  const uint32_t hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mine += hv[i];
+  uint32_t total;
+  const uint32_t below = bk.excl_scan(mine, total);
+  uint32_t above = total - below - mine;
+  if (above < need && need <= above + mine) {
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (above < need && need <= above + hv[i]) {
+        sm.bin = BPT * t + i;
+        sm.above = above;
+        sm.cnt = hv[i];
+      }
+      above += hv[i];
+    }
+    sm.nrk = 0u;
+  }
+  __syncthreads();
+}
+
+// Histogram binning of one pass: keys in [lo, hi] into BINS bins of width 2^shift; while the
+// digit lies in the score half of the key (wide), on the upper 32 bits only.
+struct Pass {
+  uint64_t lo, hi;
+  int shift;
+  bool wide;
+  __device__ __forceinline__ void make(uint64_t l, uint64_t h) {
+    lo = l;
+    hi = h;
+    shift = max(0, bitlen64(hi - lo) - 12);
+    wide = shift >= 32 && (uint32_t)lo == 0u;
+  }
+  // bin of k, or BINS + lane when k lies outside [lo, hi]
+  __device__ __forceinline__ uint32_t bin(uint64_t k) const {
+    const uint32_t stray = (uint32_t)BINS + (threadIdx.x & 63);
+    if (wide) {
+      const uint32_t d = (uint32_t)(k >> 32) - (uint32_t)(lo >> 32), span = (uint32_t)((hi - lo) >> 32);
+      return d <= span ? (d >> (shift - 32)) : stray;
+    }
+    return (k >= lo && k <= hi) ? (uint32_t)((k - lo) >> shift) : stray;
+  }
+  __device__ __forceinline__ uint64_t bin_lo(uint32_t b) const { return lo + ((uint64_t)b << shift); }
+  __device__ __forceinline__ uint64_t bin_hi(uint32_t b) const {
+    return shift == 0 ? bin_lo(b) : min(hi, bin_lo(b) + (((uint64_t)1 << shift) - 1));
+  }
+};
+
+// The need-th largest key held in sm.rk (n <= RANK_MAX, counted with repeats): thread t compares
+// key t % 64 with keys 8w .. 8w+7 (w = t / 64; the eight keys are the same for a whole wave, so
+// the reads broadcast), and wave 0 adds the eight partial counts.
+__device__ __forceinline__ uint64_t rank_small(uint32_t n, uint32_t need, Blk& bk) {
+  Smem& sm = bk.sm;
+  static_assert(RANK_MAX == 8 * W, "eight keys per wave");
+  const int t = threadIdx.x, i = t & 63, w = t >> 6;
+  const uint64_t x = i < (int)n ? sm.rk[i] : 0ull;
+  uint32_t r = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = 8 * w + j;
+    const uint64_t y = sm.rk[m];
+    r += (m < (int)n && y > x) ? 1u : 0u;
+    eq += (m < (int)n && y == x) ? 1u : 0u;
+  }
+  sm.ecnt[bk.parity][w * 64 + i] = r | (eq << 16);
+  __syncthreads();
+  if (t < 64) {
+    uint32_t rt = 0, et = 0;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const uint32_t v = sm.ecnt[bk.parity][ww * 64 + t];
+      rt += v & 0xffffu;
+      et += v >> 16;
+    }
+    if (t < (int)n && rt < need && need <= rt + et) sm.result = x;
+  }
+  bk.parity ^= 1;
+  __syncthreads();
+  return sm.result;
+}
+
+// The need-th largest of a set of keys (counted with repeats) inside [lo, hi]; for_each(f) calls
+// f(key) for every key this thread holds (0 and keys outside the range are ignored).  Requires
+// a clear histogram; leaves it clear.
+template <class ForEach>
+__device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uint64_t hi, Blk& bk) {
+  Smem& sm = bk.sm;
+  if (lo == 0ull) lo = 1ull;
+  while (true) {
+    if (lo >= hi) return lo;
+    Pass ps;
+    ps.make(lo, hi);
+    for_each([&](uint64_t k) { atomicAdd(&sm.hist[ps.bin(k)], 1u); });
+    __syncthreads();
+    find_bin(need, true, bk);
+    const uint32_t b = sm.bin, cnt = sm.cnt;
+    need -= sm.above;
+    lo = ps.bin_lo(b);
+    hi = ps.bin_hi(b);
+    if (ps.shift == 0) return lo;
+    if (cnt <= (uint32_t)RANK_MAX) {
+      for_each([&](uint64_t k) {
+        if (k >= lo && k <= hi) sm.rk[atomicAdd(&sm.nrk, 1u)] = k;
+      });
+      __syncthreads();
+      return rank_small(cnt, need, bk);
+    }
+  }
+}
+
+// One list selection (see the section comment).  key[e]: element e of this thread, list entry
+// g = e*NT + t of group g / L (0 = none); cut: the cut of group t (t < n_groups, else 0).
+// reread(grp, o) -> key of member o < gsize of group grp (0 = none); emit(off, key, grp, o) writes
+// output place `off` (o = -1 for a listed entry).  Entries of a group and members are in output
+// order; groups follow each other.  Returns the number emitted (<= P), or -1 (nothing emitted)
+// when more than CAND members or MAX_SAT groups would be re-read, or when copies of one key
+// straddle the P-th place: the caller then selects densely.
+template <int L, int LPT, class Reread, class Emit>
+__device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int gsize, uint32_t P,
+                           Reread reread, Emit emit, Blk& bk) {
+  Smem& sm = bk.sm;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < LPT; ++e)
+    if (key[e]) {
+      ++nvalid;
+      mn = min(mn, (uint32_t)(key[e] >> 32));
+      mx = max(mx, (uint32_t)(key[e] >> 32));
+    }
+  bk.reduce(nvalid, mn, mx);
+  // T0': the lower edge of the first-pass bin of the P-th best listed key (1 when there are at
+  // most P listed keys: every group with a cut is then re-read)
+  Pass p0;
+  p0.make(key_lo(mn), key_hi(mx));
+  const bool hist = nvalid > P;
+  uint64_t t0 = 1ull;
+  uint32_t b0 = 0;
+  if (hist) {
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) atomicAdd(&sm.hist[p0.bin(key[e])], 1u);
+    __syncthreads();
+    find_bin(P, false, bk);
+    b0 = sm.bin;
+    t0 = p0.bin_lo(b0);
+  }
+  const int max_sat = min(MAX_SAT, CAND / gsize);
+  for (int g = t; g < MAX_GROUPS; g += NT) {
+    const uint64_t c = g == t ? cut : 0ull;
+    const bool sat = g < n_groups && c != 0ull && c >= t0;
+    uint32_t si = 0;
+    if (sat) {
+      si = atomicAdd(&sm.nsat, 1u);
+      if (si < (uint32_t)max_sat) sm.satgroup[si] = (uint16_t)g;
+    }
+    sm.satof[g] = (sat && si < (uint32_t)max_sat) ? (uint16_t)(si + 1) : (uint16_t)0;
+  }
+  __syncthreads();
+  const uint32_t nsat = sm.nsat;
+  if (nsat > (uint32_t)max_sat) {
+    if (hist) find_bin(1, true, bk);          // clear the histogram for the caller's dense path
+    return -1;
+  }
+  // re-read groups: one wave per group, members in batches of kBatch per lane whose loads are all
+  // issued before any is used
+  constexpr int kBatch = 4;
+  for (uint32_t si = wave; si < nsat; si += W) {
+    const int grp = sm.satgroup[si];
+    for (int o0 = 0; o0 < gsize; o0 += 64 * kBatch) {
+      uint64_t m[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int o = o0 + 64 * i + lane;
+        m[i] = o < gsize ? reread(grp, o) : 0ull;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int o = o0 + 64 * i + lane;
+        if (o < gsize) {
+          const uint64_t k = m[i] >= t0 ? m[i] : 0ull;
+          sm.cand[si * gsize + o] = k;
+          if (hist && k) atomicAdd(&sm.hist[p0.bin(k)], 1u);
+        }
+      }
+    }
+  }
+  // listed keys that stay candidates: >= T0', in groups that were not re-read
+#pragma unroll
+  for (int e = 0; e < LPT; ++e) {
+    const int grp = (e * NT + t) / L;
+    const bool gone = grp < n_groups && sm.satof[grp];
+    if (hist && gone && key[e] >= t0) atomicSub(&sm.hist[p0.bin(key[e])], 1u);
+    if (gone || key[e] < t0) key[e] = 0ull;
+  }
+  __syncthreads();
+  const uint32_t nc = nsat * (uint32_t)gsize;
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) f(key[e]);
+    for (uint32_t i = t; i < nc; i += NT) f(sm.cand[i]);
+  };
+  uint64_t thr;
+  if (hist) {
+    // T*: its bin in the adjusted first-pass histogram, then ranked or narrowed
+    find_bin(P, true, bk);
+    const uint32_t b = sm.bin, cnt = sm.cnt, need = P - sm.above;
+    const uint64_t lo = p0.bin_lo(b), hi = p0.bin_hi(b);
+    if (p0.shift == 0) {
+      thr = lo;
+    } else if (cnt <= (uint32_t)RANK_MAX) {
+      each([&](uint64_t k) {
+        if (k >= lo && k <= hi) sm.rk[atomicAdd(&sm.nrk, 1u)] = k;
+      });
+      __syncthreads();
+      thr = rank_small(cnt, need, bk);
+    } else {
+      thr = select_kth(each, need, lo, hi, bk);
+    }
+  } else {
+    uint32_t n = 0, cmn = 0xffffffffu, cmx = 0u;
+    each([&](uint64_t k) {
+      if (k) {
+        ++n;
+        cmn = min(cmn, (uint32_t)(k >> 32));
+        cmx = max(cmx, (uint32_t)(k >> 32));
+      }
+    });
+    bk.reduce(n, cmn, cmx);
+    thr = n > P ? select_kth(each, P, key_lo(cmn), key_hi(cmx), bk) : 1ull;
+  }
+  // selected members of each re-read group, counted by one wave (reads in batches issued first)
+  for (uint32_t si = wave; si < nsat; si += W) {
+    uint32_t c = 0;
+    for (int o0 = 0; o0 < gsize; o0 += 64 * kBatch) {
+      uint64_t mk[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int o = o0 + 64 * i + lane;
+        mk[i] = o < gsize ? sm.cand[si * gsize + o] : 0ull;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) c += (uint32_t)__popcll(__ballot(mk[i] && mk[i] >= thr));
+    }
+    if (lane == 0) sm.satinfo[si] = c;
+  }
+  __syncthreads();
+  uint32_t cnt[LPT], off[LPT];
+#pragma unroll
+  for (int e = 0; e < LPT; ++e) {
+    const int g = e * NT + t, grp = g / L;
+    const uint32_t so = grp < n_groups ? sm.satof[grp] : 0u;
+    cnt[e] = so ? ((g % L == 0) ? sm.satinfo[so - 1] : 0u) : (key[e] >= thr && key[e] ? 1u : 0u);
+  }
+  const uint32_t total = ordered<false, LPT>(cnt, off, bk);
+  if (total > P) return -1;                  // copies of one key at the P-th place
+#pragma unroll
+  for (int e = 0; e < LPT; ++e) {
+    const int g = e * NT + t, grp = g / L;
+    const uint32_t so = grp < n_groups ? sm.satof[grp] : 0u;
+    if (so) {
+      if (g % L == 0) sm.satinfo[so - 1] = off[e];
+    } else if (cnt[e]) {
+      emit(off[e], key[e], grp, -1);
+    }
+  }
+  __syncthreads();
+  for (uint32_t si = wave; si < nsat; si += W) {
+    uint32_t n = sm.satinfo[si];
+    const int grp = sm.satgroup[si];
+    for (int o0 = 0; o0 < gsize; o0 += 64 * kBatch) {
+      uint64_t mk[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int o = o0 + 64 * i + lane;
+        mk[i] = o < gsize ? sm.cand[si * gsize + o] : 0ull;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const bool sel = mk[i] && mk[i] >= thr;
+        const uint64_t m = __ballot(sel);
+        const uint32_t at = n + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+        if (sel) emit(at, mk[i], grp, o0 + 64 * i + lane);
+        n += (uint32_t)__popcll(m);
+      }
+    }
+  }
+  __syncthreads();
+  return (int)total;
+}
+
+// The P best of n keys read from global memory (key_at(j), 0 = none), emitted in index order:
+// every key above the P-th, then copies of it in index order while places remain.  Returns the
+// number emitted.  Requires a clear histogram.
+template <class KeyAt, class Emit>
+__device__ uint32_t dense_select(KeyAt key_at, int n, uint32_t P, Emit emit, Blk& bk) {
+  constexpr int kB = 16;                     // keys per thread per batch
+  const int t = threadIdx.x;
+  uint32_t nv = 0, mn = 0xffffffffu, mx = 0u;
+  for (int j = t; j < n; j += NT) {
+    const uint64_t k = key_at(j);
+    if (k) {
+      ++nv;
+      mn = min(mn, (uint32_t)(k >> 32));
+      mx = max(mx, (uint32_t)(k >> 32));
+    }
+  }
+  bk.reduce(nv, mn, mx);
+  auto each = [&](auto f) {
+    for (int base = t; base < n; base += NT * kB) {
+      uint64_t kk[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) kk[u] = base + u * NT < n ? key_at(base + u * NT) : 0ull;
+#pragma unroll
+      for (int u = 0; u < kB; ++u) f(kk[u]);
+    }
+  };
+  const uint64_t thr = nv > P ? select_kth(each, P, key_lo(mn), key_hi(mx), bk) : 1ull;
+  // keys above thr, then copies of thr in index order while places remain
+  uint32_t n_gt = 0, d0 = 0, d1 = 0;
+  for (int j = t; j < n; j += NT) n_gt += key_at(j) > thr ? 1u : 0u;
+  bk.reduce(n_gt, d0, d1);
+  const uint32_t room = P > n_gt ? P - n_gt : 0u;
+  uint32_t done = 0, eq_done = 0;
+  for (int base = 0; base < n; base += NT * kB) {
+    uint64_t kk[kB];
+    uint32_t ceq[kB], oeq[kB], sel[kB], osel[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int j = base + u * NT + t;
+      kk[u] = j < n ? key_at(j) : 0ull;
+      ceq[u] = (kk[u] && kk[u] == thr) ? 1u : 0u;
+    }
+    const uint32_t neq = ordered<true, kB>(ceq, oeq, bk);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      sel[u] = (kk[u] && (kk[u] > thr || (ceq[u] && eq_done + oeq[u] < room))) ? 1u : 0u;
+    const uint32_t ns = ordered<true, kB>(sel, osel, bk);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (sel[u] && done + osel[u] < P) emit(done + osel[u], kk[u], base + u * NT + t);
+    done += ns;
+    eq_done += neq;
+  }
+  __syncthreads();
+  return min(done, P);
+}
+
+}  // namespace ls
+
+// Pool from the scan's chunk lists (k_idx_scan: per chunk of bpc blocks, up to 16 listed blocks in
+// block order and a cut), one WG of 512 threads per query; outputs as k_pool with K = 0.  Falls
+// back to a selection over every block key when too many chunks would be re-read.
+constexpr int kPoolChunks = 256;
+constexpr int kPLE = kPoolChunks * kListLen / ls::NT;   // listed keys per thread (8)
+
+__global__ __launch_bounds__(ls::NT) void k_pool_chunks(
+    const uint64_t* __restrict__ clists, const uint64_t* __restrict__ ccuts, int n_chunks, int bpc,
+    const uint32_t* __restrict__ blkkey, int nb_max, const int32_t* __restrict__ n_visible, int n_max, int P,
+    int32_t* __restrict__ pool_pos, int cap_out, int32_t* __restrict__ pool_len) {
+  __shared__ ls::Smem sm;
+  __shared__ uint32_t byrank[kMaxTopK];      // selected blocks, ascending
+  ls::Blk bk{sm};
+  const int q = blockIdx.x, t = threadIdx.x;
+  // every load of the selection's first steps is issued here, before any is used
+  const int nv_raw = n_visible[q];
+  const uint64_t* cl = clists + (size_t)q * n_chunks * kListLen;
+  uint64_t key[kPLE];
+#pragma unroll
+  for (int e = 0; e < kPLE; ++e) {
+    const int g = e * ls::NT + t;
+    key[e] = g < n_chunks * kListLen ? cl[g] : 0ull;
+  }
+  const uint64_t cut = t < n_chunks ? ccuts[(size_t)q * n_chunks + t] : 0ull;
+  ls::init(sm);
+  const int nv = nv_raw < 0 ? 0 : (nv_raw > n_max ? n_max : nv_raw);
+  const int nb = (nv + kBlock - 1) / kBlock;
+  const uint32_t* keys = blkkey + (size_t)q * nb_max;
+  __syncthreads();
+  const bool all = nb <= P;
+  uint32_t nsel = 0;
+  if (!all) {
+    auto reread = [&](int grp, int o) -> uint64_t {
+      const int j = grp * bpc + o;
+      return j < nb ? rank_key(keys[j], (uint32_t)j) : 0ull;
+    };
+    auto emit = [&](uint32_t off, uint64_t k, int grp, int o) {
+      byrank[off] = o < 0 ? rank_key_index(k) : (uint32_t)(grp * bpc + o);
+    };
+    const int r = ls::list_select<kListLen, kPLE>(key, cut, n_chunks, bpc, (uint32_t)P, reread, emit, bk);
+    if (r >= 0) {
+      nsel = (uint32_t)r;
+    } else {
+      nsel = ls::dense_select([&](int j) -> uint64_t { return rank_key(keys[j], (uint32_t)j); }, nb, (uint32_t)P,
+                              [&](uint32_t off, uint64_t, int j) { byrank[off] = (uint32_t)j; }, bk);
+    }
+  }
+  // slot s holds block byrank[s / 8] (position s when every block is kept), -1 padded
   int total;
   if (all) {
     total = nv;
@@ -618,69 +1197,71 @@ __global__ __launch_bounds__(kNT) void k_pool(
     total = 8 * (int)nsel;
     if (nsel > 0 && (int)byrank[nsel - 1] == nb - 1) total -= kBlock - (nv - kBlock * (nb - 1));
   }
-  int32_t ps[kE];
-#pragma unroll
-  for (int i = 0; i < kE; ++i) {
-    const int sl = i * kNT + t;
-    ps[i] = sl < total ? (all ? sl : kBlock * (int)byrank[sl >> 3] + (sl & 7)) : -1;
-  }
+  // 4 slots (half a block) per 16-byte store, kMaxPool / (4 * 512) = 8 stores per thread; every
+  // byrank read is issued before the stores
   int32_t* gp = pool_pos + (size_t)q * cap_out;
+  constexpr int kSt = kMaxPool / (4 * ls::NT);
+  uint32_t blk[kSt];
 #pragma unroll
-  for (int i = 0; i < kE; ++i) {
-    const int sl = i * kNT + t;
-    if (sl < cap_out) gp[sl] = ps[i];
+  for (int i = 0; i < kSt; ++i) {
+    const int s4 = 4 * (i * ls::NT + t);
+    blk[i] = (!all && s4 < total) ? byrank[s4 >> 3] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kSt; ++i) {
+    const int s4 = 4 * (i * ls::NT + t);
+    if (s4 < cap_out) {
+      int32_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sl = s4 + e;
+        v[e] = sl < total ? (all ? sl : kBlock * (int)blk[i] + (sl & 7)) : -1;
+      }
+      *(u32x4*)(gp + s4) = u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+    }
   }
   if (t == 0) pool_len[q] = total;
-  if (K == 0) return;
-
-  // Top-K of the pool by (score desc, position asc), written in slot (= position) order
-  const float* sc = scores + (size_t)q * n_max;
-  float sv[kE];
-#pragma unroll
-  for (int i = 0; i < kE; ++i) sv[i] = sc[ps[i] >= 0 ? ps[i] : 0];
-  uint64_t key[kE];
-  uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-  for (int i = 0; i < kE; ++i) {
-    const uint32_t k32 = score_key(sv[i]);
-    key[i] = ps[i] >= 0 ? rank_key(k32, (uint32_t)ps[i]) : 0ull;
-    nvalid += ps[i] >= 0 ? 1u : 0u;
-    if (ps[i] >= 0) { mn = min(mn, k32); mx = max(mx, k32); }
-  }
-  topk_out(key, nvalid, mn, mx, K, topk_idx + (size_t)q * K, topk_score ? topk_score + (size_t)q * K : nullptr, bk);
 }
 
+
 hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
+                       const uint64_t* clists, const uint64_t* ccuts, int n_chunks, int blocks_per_chunk,
                        const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max, int P,
                        int32_t* pool_pos, int cap_out, int32_t* pool_len, const float* scores, int K,
                        int32_t* topk_idx, float* topk_score, int Q, hipStream_t s) {
-  hipLaunchKernelGGL(k_pool, dim3(Q), dim3(kNT), 0, s, lists, cuts, n_units, blocks_per_unit, blkkey,
-                     nb_max, n_visible, n_max, P, pool_pos, cap_out, pool_len, scores, K, topk_idx, topk_score);
+  if (clists) {
+    // the chunk-list pool writes the pool only; a Top-K of it is one more launch
+    if (n_chunks > kPoolChunks || blocks_per_chunk < 64 || blocks_per_chunk > 1024 || !ccuts || cap_out > kMaxPool)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_pool_chunks, dim3(Q), dim3(ls::NT), 0, s, clists, ccuts, n_chunks, blocks_per_chunk, blkkey,
+                       nb_max, n_visible, n_max, P, pool_pos, cap_out, pool_len);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || K == 0) return e;
+    TopkJob j{};
+    j.scores = scores;
+    j.score_stride = n_max;
+    j.n_rows = n_max > 0 ? n_max : 1;
+    j.by_position = 1;
+    j.items = Q;
+    j.out_idx = topk_idx;
+    j.out_score = topk_score;
+    return launch_topk(pool_pos, pool_len, cap_out, Q, K, j, TopkJob{}, s);
+  }
+  hipLaunchKernelGGL(k_pool, dim3(Q), dim3(kNT), 0, s, lists, cuts, n_units, blocks_per_unit, blkkey, nb_max,
+                     n_visible, n_max, P, pool_pos, cap_out, pool_len, scores, K, topk_idx, topk_score);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ Top-K over given pools
 
-// One WG per item: the items of job a, then those of job b (it = l*Q + q within its job).
-// Candidates: slots [0, len) of the item's query; slot i has position cand_pos[i] (ignored if
-// negative or >= the job's n_rows); its score as TopkJob states.  Output: the k best positions
-// in slot order (ascending positions for an ascending pool) with their scores, -1 / 0 padded.
-// Slot i*kNT + t belongs to thread t, so each load instruction reads consecutive slots.
-__global__ __launch_bounds__(kNT) void k_topk(const int32_t* __restrict__ cand_pos,
-                                              const int32_t* __restrict__ cand_len, int cap, int Q, int k,
-                                              TopkJob a, TopkJob b) {
-  __shared__ SelectSmem sm;
-  Block bk{sm};
-  const bool in_a = (int)blockIdx.x < a.items;
-  const TopkJob& job = in_a ? a : b;
-  const int it = in_a ? (int)blockIdx.x : (int)blockIdx.x - a.items;
-  const int q = it % Q, t = threadIdx.x;
-  smem_init(sm);
-  int len = cand_len[q];
-  len = len < 0 ? 0 : (len > cap ? cap : len);
-  const int32_t* cp = cand_pos + (size_t)q * cap;
-  const bool by_position = job.by_position != 0;
-  const float* sc = job.scores + (size_t)(by_position ? q : it) * job.score_stride;
+// Top-K of one item over all its slots (slot i*kNT + t belongs to thread t, so each load
+// instruction reads consecutive slots): slot i < len has position cp[i] (ignored if negative or
+// >= n_rows); its score is sc[position] (by_position) or sc[i].  Output as topk_out.  Requires a
+// clear histogram (smem_init).
+__device__ __forceinline__ void topk_dense(const int32_t* __restrict__ cp, int len, const float* __restrict__ sc,
+                                           bool by_position, int64_t n_rows, int k, int32_t* __restrict__ oi,
+                                           float* __restrict__ os, Block& bk) {
+  const int t = threadIdx.x;
   int32_t pos[kE];
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
@@ -692,7 +1273,7 @@ __global__ __launch_bounds__(kNT) void k_topk(const int32_t* __restrict__ cand_p
 #pragma unroll
   for (int i = 0; i < kE; ++i) {
     const int slot = i * kNT + t;
-    ok[i] = slot < len && pos[i] >= 0 && (int64_t)pos[i] < job.n_rows;
+    ok[i] = slot < len && pos[i] >= 0 && (int64_t)pos[i] < n_rows;
     s[i] = sc[by_position ? (ok[i] ? pos[i] : 0) : (slot < len ? slot : 0)];
   }
   uint64_t key[kE];
@@ -704,8 +1285,29 @@ __global__ __launch_bounds__(kNT) void k_topk(const int32_t* __restrict__ cand_p
     nvalid += ok[i] ? 1u : 0u;
     if (ok[i]) { mn = min(mn, k32); mx = max(mx, k32); }
   }
-  topk_out(key, nvalid, mn, mx, k, job.out_idx + (size_t)it * k,
-           job.out_score ? job.out_score + (size_t)it * k : nullptr, bk);
+  topk_out(key, nvalid, mn, mx, k, oi, os, bk);
+}
+
+// One WG per item: the items of job a, then those of job b (it = l*Q + q within its job).
+// Candidates: slots [0, len) of the item's query; slot i has position cand_pos[i] (ignored if
+// negative or >= the job's n_rows); its score as TopkJob states.  Output: the k best positions
+// in slot order (ascending positions for an ascending pool) with their scores, -1 / 0 padded.
+__global__ __launch_bounds__(kNT) void k_topk(const int32_t* __restrict__ cand_pos,
+                                              const int32_t* __restrict__ cand_len, int cap, int Q, int k,
+                                              TopkJob a, TopkJob b) {
+  __shared__ SelectSmem sm;
+  Block bk{sm};
+  const bool in_a = (int)blockIdx.x < a.items;
+  const TopkJob& job = in_a ? a : b;
+  const int it = in_a ? (int)blockIdx.x : (int)blockIdx.x - a.items;
+  const int q = it % Q;
+  smem_init(sm);
+  int len = cand_len[q];
+  len = len < 0 ? 0 : (len > cap ? cap : len);
+  const bool by_position = job.by_position != 0;
+  const float* sc = job.scores + (size_t)(by_position ? q : it) * job.score_stride;
+  topk_dense(cand_pos + (size_t)q * cap, len, sc, by_position, job.n_rows, k, job.out_idx + (size_t)it * k,
+             job.out_score ? job.out_score + (size_t)it * k : nullptr, bk);
 }
 
 hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
@@ -715,5 +1317,87 @@ hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap
   hipLaunchKernelGGL(k_topk, dim3(items), dim3(kNT), 0, s, cand_pos, cand_len, cap, Q, k, a, b);
   return hipGetLastError();
 }
+
+// ------------------------------------------------------------------ Top-K from unit lists
+
+// Top-K of items scored by k_ri_score with lists: unit u of an item (kRiUnit consecutive slots)
+// lists its 4 best keys in slot order and cuts at its 5th (ls::list_select, re-reading a unit's
+// slot scores when its cut reaches T0').  One WG of 512 threads per item (job a's items, then job
+// b's; query it % Q within its job).  Output as k_topk: the k best positions in slot order
+// (ascending positions for an ascending pool) with their scores, -1 / 0 padded.  Falls back to a
+// selection over every slot when too many units would be re-read or copies of one position
+// straddle the k-th place.
+constexpr int kTLE = kMaxPool / kRiUnit * kRiUnitList / ls::NT;   // listed keys per thread (4)
+
+__global__ __launch_bounds__(ls::NT) void k_topk_lists(
+    const uint64_t* __restrict__ lists, const uint64_t* __restrict__ cuts, const float* __restrict__ slot_scores,
+    const int32_t* __restrict__ cand_pos, const int32_t* __restrict__ cand_len, int cap, int Q, int k,
+    int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* __restrict__ out_a, float* __restrict__ out_sa,
+    int32_t* __restrict__ out_b, float* __restrict__ out_sb) {
+  __shared__ ls::Smem sm;
+  ls::Blk bk{sm};
+  const int it = blockIdx.x, t = threadIdx.x;
+  const bool in_a = it < items_a;
+  const int ij = in_a ? it : it - items_a;
+  const int q = ij % Q;
+  const int64_t n_rows = in_a ? n_rows_a : n_rows_b;
+  int32_t* oi = (in_a ? out_a : out_b) + (size_t)ij * k;
+  float* os_base = in_a ? out_sa : out_sb;
+  float* os = os_base ? os_base + (size_t)ij * k : nullptr;
+  const int nu = ri_units(cap);
+  // every load of the selection's first steps is issued here, before any is used
+  const int len_raw = cand_len[q];
+  const uint64_t* lrow = lists + (size_t)it * nu * kRiUnitList;
+  uint64_t key[kTLE];
+#pragma unroll
+  for (int e = 0; e < kTLE; ++e) {
+    const int g = e * ls::NT + t;
+    key[e] = g < nu * kRiUnitList ? lrow[g] : 0ull;
+  }
+  uint64_t cut = t < nu ? cuts[(size_t)it * nu + t] : 0ull;
+  ls::init(sm);
+  const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
+  const int nuse = (len + kRiUnit - 1) / kRiUnit;   // units holding slots (the others were not scored)
+#pragma unroll
+  for (int e = 0; e < kTLE; ++e)
+    if ((e * ls::NT + t) / kRiUnitList >= nuse) key[e] = 0ull;
+  if (t >= nuse) cut = 0ull;
+  __syncthreads();
+  const int32_t* cp = cand_pos + (size_t)q * cap;
+  const float* srow = slot_scores + (size_t)it * cap;
+  auto key_of_slot = [&](int slot) -> uint64_t {
+    const int pos = cp[slot];
+    return (pos >= 0 && (int64_t)pos < n_rows) ? rank_key(score_key(srow[slot]), (uint32_t)pos) : 0ull;
+  };
+  auto reread = [&](int grp, int o) -> uint64_t {
+    const int slot = grp * kRiUnit + o;
+    return slot < len ? key_of_slot(slot) : 0ull;
+  };
+  auto emit = [&](uint32_t off, uint64_t kk, int, int) {
+    oi[off] = (int32_t)rank_key_index(kk);
+    if (os) os[off] = key_score((uint32_t)(kk >> 32));
+  };
+  int total = ls::list_select<kRiUnitList, kTLE>(key, cut, nuse, kRiUnit, (uint32_t)k, reread, emit, bk);
+  if (total < 0)
+    total = (int)ls::dense_select(key_of_slot, len, (uint32_t)k,
+                                  [&](uint32_t off, uint64_t kk, int) { emit(off, kk, 0, 0); }, bk);
+  for (int i = total + t; i < k; i += ls::NT) {
+    oi[i] = -1;
+    if (os) os[i] = 0.f;
+  }
+}
+
+hipError_t launch_topk_lists(const uint64_t* lists, const uint64_t* cuts, const float* slot_scores,
+                             const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
+                             int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* out_a, float* out_sa,
+                             int items_b, int32_t* out_b, float* out_sb, hipStream_t s) {
+  const int items = items_a + items_b;
+  if (items == 0) return hipSuccess;
+  if (cap > kMaxPool || ri_units(cap) > ls::MAX_GROUPS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_topk_lists, dim3(items), dim3(ls::NT), 0, s, lists, cuts, slot_scores, cand_pos, cand_len,
+                     cap, Q, k, n_rows_a, n_rows_b, items_a, out_a, out_sa, out_b, out_sb);
+  return hipGetLastError();
+}
+
 
 }  // namespace csa2

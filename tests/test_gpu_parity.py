@@ -228,11 +228,11 @@ def test_index_full_parity(N, P, K, nv):
 
 @pytest.mark.parametrize("P,run", [(64, (1600, 3200)), (128, (4000, 4400)), (256, (8000, 8008))])
 def test_pool_with_runs_of_high_blocks(P, run):
-    """Runs of consecutive high-scoring blocks: the units inside a run hold more pool blocks than
-    the four they list, so they are re-read.  Depending on how far a run's unlisted blocks reach
-    above the P-th best listed block (runs of 200, 50 and 1 blocks against P = 64, 128, 256), the
-    P-th best block lies in that listed block's bin, which is ranked directly, or above it, where a
-    selection over every candidate finds it.  Run rows repeat the 64 best rows of the random keys."""
+    """Runs of consecutive high-scoring blocks (200, 50 and 1 blocks against P = 64, 128, 256): the
+    chunk (P = 64, 128: the scan's chunk lists of 16) or unit (P = 256: unit lists of 4) holding a
+    run has more pool blocks than it lists, so it is re-read, and the P-th best block is found
+    among the listed blocks above T0 and the re-read ones.  Run rows repeat the 64 best rows of the
+    random keys."""
     N, K = 20000, 256
     w = small(N=N, pool_blocks=P, top_k=K, seed=3400 + P)
     inp = workloads.make_inputs(w, with_attention=False)
@@ -243,6 +243,51 @@ def test_pool_with_runs_of_high_blocks(P, run):
     k[0, a:b] = k[0, best[np.arange(b - a) % 64]]
     gpu = G.gpu_index_full(inp, 1, 1, N, P, K)
     check_full(w, inp, gpu, 0, 0)
+
+
+def test_pool_tied_candidates_beyond_direct_ranking():
+    """The unit-list pool (a 131072-position context with a 2048-block pool: units of 8 blocks) with
+    the P-th best block inside a group of about 600 blocks of exactly equal score, one per unit:
+    more than 256 candidates share T*'s bin of T0's first histogram pass, so that bin is narrowed
+    by further passes instead of ranked directly.  A run of 6 high blocks inside one unit makes that
+    unit re-read, so T*'s histogram is the one derived from T0's first pass.  Equal blocks rank by
+    index on both sides: the pool and Top-K equal the oracle's exactly."""
+    N, P, K = 131072, 2048, 512
+    w = small(N=N, pool_blocks=P, top_k=K, n_reindex=1, seed=3500)
+    inp = workloads.make_inputs(w, with_attention=False)
+    k = inp["idx_k"]
+    q8 = O.query_for_keys(inp["idx_q"][0, 0], k[0])
+    s = O.ranking_scores(O.indexer_scores(k[0], q8, inp["head_w"][0, 0]))
+    blk = O.block_scores(s, N, 8)
+    target = int(np.argsort(-blk, kind="stable")[1800])        # the block ranked 1801st
+    r0 = 8 * target + int(np.argmax(s[8 * target:8 * target + 8]))
+    unit_max = blk.reshape(-1, 8).max(1)                        # units of 8 blocks (64 positions)
+    low = np.flatnonzero(unit_max < s[r0])
+    pick = low[np.linspace(2, len(low) - 1, 600).astype(int)]
+    k[0, 64 * pick] = k[0, r0]                                  # 600 blocks of score exactly s[r0]
+    run_unit = int(low[0])
+    k[0, 64 * run_unit + 8 * np.arange(6)] = k[0, int(np.argmax(s))]
+    got = G.gpu_index_chain(inp, 1, 1, N, P, K, 1, split=True)
+    ref, nd = check_full(w, inp, got, 0, 0)
+    assert nd == 0
+    gp = got["pool_pos"][0, 0, :got["pool_len"][0, 0]]
+    assert np.array_equal(gp, ref["pool"])
+
+
+def test_chain_top2048_over_a_full_pool():
+    """Top-2048 of a 16384-position pool: the chunk lists then hold exactly k keys, every chunk's cut
+    reaches T0 and the Top-K of the Full layer and of 2 Reindex layers is taken over every slot (the
+    lists' fallback); against the oracle."""
+    N, P, K, L = 131072, 2048, 2048, 2
+    w = small(N=N, pool_blocks=P, top_k=K, n_reindex=L, seed=3600)
+    inp = workloads.make_inputs(w, with_attention=False)
+    got = G.gpu_index_chain(inp, 1, 1, N, P, K, L, split=True)
+    check_full(w, inp, got, 0, 0)
+    pool = got["pool_pos"][0, 0, :got["pool_len"][0, 0]]
+    for r in range(L):
+        ref = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][r, 0, 0], inp["ri_w"][r, 0, 0], pool, K)
+        sc = dict(zip(pool.tolist(), ref["scores"].tolist()))
+        G.assert_topk_equiv(got["ri_topk"][r, 0, 0], ref["topk"], lambda p: sc[p], f"ri{r}")
 
 
 @pytest.mark.parametrize("T", [2, 9])
