@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   for (int c = 0; c < nchunks; ++c) {
     store_row(raw, X + my_row * kXStride, quarter);
     if (quarter == 0) rowok[my_row] = raw.kind != 0;
-    __syncthreads();
+    lds_barrier();
     if (c + 1 < nchunks) {
       load_chunk(raw, c + 1, pos_next);
       pos_next = c + 2 < nchunks ? row_index(c + 2) : -1;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
       for (int v = 0; v < 4; ++v) red_m[wave][4 * g + v] = mx[v];
     }
-    __syncthreads();
+    lds_barrier();
     float alpha[4], mnew[4], psum[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 #pragma unroll
       for (int v = 0; v < 4; ++v) red_l[wave][4 * g + v] = psum[v];
     }
-    __syncthreads();   // P and red_l written
+    lds_barrier();   // P and red_l written
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int h = 4 * g + v;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
         o[2 * i + 1] = mfma16x16x32(pa, hi, o[2 * i + 1]);
       }
     }
-    if (c + 1 < nchunks) __syncthreads();   // X, P, red_m and red_l are rewritten by the next chunk
+    if (c + 1 < nchunks) lds_barrier();   // X, P, red_m and red_l are rewritten by the next chunk
   }
 
   const size_t hrow = (size_t)lq * H + 16 * hg;      // (layer, query, first head of the group)
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
   }
   if (nchunks > 1) load_chunk(raw, 1, pos_b);
   int pos_c = nchunks > 2 ? row_index(2) : -1;
-  __syncthreads();
+  lds_barrier();
 
   for (int c = 0; c < nchunks; ++c) {
     const uint16_t* Xc = X[c & 1];
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       const float m = row16_max(fmaxf(sv[0][v], sv[1][v]));
       if (j == 0) red_m[hf][16 * hg + 4 * g + v] = m;
     }
-    __syncthreads();                                 // both halves' maxima
+    lds_barrier();                                 // both halves' maxima
     // The reference point of a head moves only when the chunk's max exceeds it by more than
     // kLazyLog2, so P <= 2^kLazyLog2 and O is rescaled only on such a move.  Both waves of a head
     // group take identical decisions (same maxima, same order).
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       if (j == 0) red_l[hf][hh] = ps;
       m_run[v] = mnew;
     }
-    __syncthreads();                                 // P tiles and both halves' sums
+    lds_barrier();                                 // P tiles and both halves' sums
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int hh = 16 * hg + 4 * g + v;
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       dequant_next();
       accumulate();
     }
-    if (c + 1 < nchunks) __syncthreads();            // next chunk's X and rowok written; P, red_* free
+    if (c + 1 < nchunks) lds_barrier();            // next chunk's X and rowok written; P, red_* free
   }
 
   // O leaves through LDS (the chunk tiles are free once every wave has finished its last
@@ -547,7 +547,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
   constexpr int kOStride = kKvDim + 4;                // floats per staged head row
   static_assert(64 * kOStride * 4 <= (int)sizeof(X), "the staged output fits in the chunk tiles");
   float* Os = reinterpret_cast<float*>(&X[0][0]);
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int u = 0; u < 16; ++u)
 #pragma unroll
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
       red_l[0][16 * hg + 4 * g + v] = l_run[v];
     }
   }
-  __syncthreads();
+  lds_barrier();
   const size_t hrow = (size_t)lq * H;
   for (int hh = 0; hh < 16; ++hh) {
     const int head = 16 * hg + hh, h = 64 * hq + head;

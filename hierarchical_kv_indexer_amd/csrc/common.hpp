@@ -151,6 +151,15 @@ __device__ __forceinline__ uint32_t max8_u32(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
   return x;
 }
+// Workgroup barrier that orders LDS only.  __syncthreads also orders global memory, so each
+// wave first waits for every global load and store it has in flight (a prefetch, or stores of
+// results, which take microseconds to complete while the GPU streams from HBM); kernels whose
+// waves share data only through LDS use this instead.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 // DPP wave64 primitives (no LDS traffic).
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {

@@ -333,12 +333,14 @@ __device__ __forceinline__ uint32_t block_key(float sc, bool valid) {
 // its instruction issue, not by the bytes in flight).
 template <bool kFp4> constexpr int kScanU = 3;
 constexpr int kFullWaves = kFullThreads / 64;   // 16
+constexpr int kMaxScanChunk = 8192;             // positions of a one-query scan workgroup (LDS staging)
 static_assert(kFullWaves == kScanUnitsPerWg, "each wave lists the units of its own range");
 
 // LDS of k_idx_scan: the query (bf16), the chunk's scores and block keys, the stage counter, and
-// 64 words for the chunk list's ranking.
+// the five largest packed blocks of each of the workgroup's units (for its chunk list).
 size_t scan_lds_bytes(int chunk) {
-  return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)chunk * 4 + (size_t)(chunk / kBlock) * 4 + 16 + 64 * 8;
+  return (size_t)kIdxHeads * kIdxDim * 2 + (size_t)chunk * 4 + (size_t)(chunk / kBlock) * 4 + 16 +
+         (size_t)kScanUnitsPerWg * 5 * 4;
 }
 
 // Best ranking key (score key, block) of a wave's blocks (one per lane), removed from the
@@ -378,105 +380,83 @@ __device__ __forceinline__ uint64_t group_pop_best(uint32_t& key, uint32_t& blk)
   return (m == 0u && jm == 0xffffffffu) ? 0ull : rank_key(m, jm);
 }
 
-// The five best blocks of each group of LANES lanes (lane i of a group holds one block); the
-// first lane of group s writes unit unit0 + s.
+// The five best blocks of the aligned group of LANES lanes holding this lane (lane i of a group
+// holds one block), as ranking keys (0 = none), the same in every lane of the group.
 template <int LANES>
-__device__ __forceinline__ void write_unit_lists(uint32_t key, uint32_t blk, int n_groups, size_t unit0,
-                                                 uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
-  uint64_t best[5];
+__device__ __forceinline__ void unit_best(uint32_t key, uint32_t blk, uint64_t (&best)[5]) {
 #pragma unroll
   for (int r = 0; r < 5; ++r) best[r] = group_pop_best<LANES>(key, blk);
-  const int lane = threadIdx.x & 63;
-  if (lane % LANES == 0 && lane / LANES < n_groups) {
-    const size_t unit = unit0 + lane / LANES;
-    u32x4* lp = (u32x4*)(lists + unit * 4);
-    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
-    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
-    cuts[unit] = best[4];
-  }
 }
 
-// The chunk's unit lists and its chunk list, computed by one wave from the chunk's block keys in
-// LDS (used with one unit per wave: 16 units of bpu = 4*KB blocks, so lane l holds blocks
-// KB*l .. KB*l+KB-1 and each aligned quad of lanes holds one unit).
-//   unit lists: as write_unit_lists (the five best blocks of each unit);
-//   chunk list: from the 64 keys the 16 units list (in block order) and the largest unit cut mc,
-//     the keys above mc among the 16 best, in block order, into clist[0..15] (0 padded), and the
-//     cut max(mc, the 17th best listed key).  Every block of the chunk that is not in its list
-//     ranks at or below that cut: a block outside its unit's four is at or below the unit's cut,
-//     and a listed key left out is at or below mc or the 17th.
-// xch: 64 LDS words of this wave.
-template <int KB>
-__device__ __forceinline__ void wave_chunk_lists(const uint32_t* wkeys, int nblk, uint32_t blk0, size_t unit0,
-                                                 uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts,
-                                                 uint64_t* __restrict__ clist, uint64_t* __restrict__ ccut,
-                                                 uint64_t* xch) {
+// Value of lane ^ J for J in {1, 2, 4, 8, 16, 32}.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return dpp_mov<0xB1>(v);                       // quad_perm [1,0,3,2]
+  else if constexpr (J == 2) return dpp_mov<0x4E>(v);                  // quad_perm [2,3,0,1]
+  else if constexpr (J == 4 || J == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (J << 10));
+  else if constexpr (J == 16) return swap16(v);
+  else return swap32(v);
+}
+// One compare-exchange stage of a bitonic network over the lanes of a wave (block size K,
+// distance J): the lower lane of each pair keeps the larger value where its K-block sorts
+// descending, else the smaller.
+template <int K, int J>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t x) {
   const int lane = threadIdx.x & 63;
-  uint32_t k[KB];
-#pragma unroll
-  for (int i = 0; i < KB; ++i) {
-    const int b = KB * lane + i;
-    k[i] = b < nblk ? wkeys[b] : 0u;
-  }
-  const uint32_t my0 = blk0 + (uint32_t)(KB * lane);
-  uint64_t best[5];
-#pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    uint32_t lk = 0u, li = 0u;                   // this lane's best: the first of its largest keys
-#pragma unroll
-    for (int i = 0; i < KB; ++i)
-      if (k[i] > lk) { lk = k[i]; li = (uint32_t)i; }
-    uint32_t gk = max(lk, dpp_mov<0xB1>(lk));    // quad_perm [1,0,3,2]
-    gk = max(gk, dpp_mov<0x4E>(gk));             // quad_perm [2,3,0,1]
-    uint32_t gb = (lk == gk && lk != 0u) ? my0 + li : 0xffffffffu;
-    gb = min(gb, dpp_mov<0xB1>(gb));
-    gb = min(gb, dpp_mov<0x4E>(gb));
-    best[r] = gk ? rank_key(gk, gb) : 0ull;
-    const bool mine = gk != 0u && lk == gk && my0 + li == gb;
-#pragma unroll
-    for (int i = 0; i < KB; ++i)
-      if (mine && (uint32_t)i == li) k[i] = 0u;
-  }
-  const int u = lane >> 2, rq = lane & 3;
-  if (rq == 0) {
-    u32x4* lp = (u32x4*)(lists + (unit0 + u) * 4);
-    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
-    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
-    cuts[unit0 + u] = best[4];
-  }
-  // the unit's four in block order (a larger block is a smaller low word; none sorts last)
-  auto cx = [&](int a, int b) {
-    const bool sw = (uint32_t)best[a] < (uint32_t)best[b];
-    const uint64_t x = sw ? best[b] : best[a], y = sw ? best[a] : best[b];
-    best[a] = x;
-    best[b] = y;
-  };
-  cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-  const uint64_t x = rq == 0 ? best[0] : (rq == 1 ? best[1] : (rq == 2 ? best[2] : best[3]));
-  // mc: the largest unit cut
-  const uint32_t chi = wave_max_u32((uint32_t)(best[4] >> 32));
-  const uint32_t clo = wave_max_u32((uint32_t)(best[4] >> 32) == chi ? (uint32_t)best[4] : 0u);
-  const uint64_t mc = ((uint64_t)chi << 32) | clo;
-  // rank of x among the 64 listed keys (LDS operations of a wave complete in order)
-  xch[lane] = x;
-  __builtin_amdgcn_wave_barrier();
-  uint32_t rank = 0;
-#pragma unroll 16
-  for (int m = 0; m < 64; ++m) rank += xch[m] > x ? 1u : 0u;
-  const bool flag = x != 0ull && x > mc && rank < (uint32_t)kListLen;
-  const uint64_t fm = __ballot(flag);
-  const uint32_t nflag = (uint32_t)__popcll(fm);
-  if (flag) clist[__builtin_amdgcn_mbcnt_hi((uint32_t)(fm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)fm, 0u))] = x;
-  if (lane < kListLen && (uint32_t)lane >= nflag) clist[lane] = 0ull;
-  // the cut: max(mc, the 17th best listed key), none when fewer than 17 keys are listed
-  const uint64_t m17 = __ballot(x != 0ull && rank == (uint32_t)kListLen);
-  uint64_t c17 = 0ull;
-  if (m17) {
-    const int l17 = __ffsll((unsigned long long)m17) - 1;
-    c17 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(x >> 32), l17) << 32) |
-          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l17);
-  }
-  if (lane == 0) *ccut = c17 > mc ? c17 : mc;
+  const uint32_t y = lane_xor<J>(x);
+  return (((lane & J) == 0) == ((lane & K) == 0)) ? max(x, y) : min(x, y);
+}
+// Sorts x descending over each aligned group of N lanes (N = 16 or 64).
+template <int N>
+__device__ __forceinline__ uint32_t bitonic_sort(uint32_t x) {
+#define CSA2_BSTEP(K, J) if constexpr ((K) <= N) x = bitonic_step<K, J>(x);
+  CSA2_BSTEP(2, 1)
+  CSA2_BSTEP(4, 2) CSA2_BSTEP(4, 1)
+  CSA2_BSTEP(8, 4) CSA2_BSTEP(8, 2) CSA2_BSTEP(8, 1)
+  CSA2_BSTEP(16, 8) CSA2_BSTEP(16, 4) CSA2_BSTEP(16, 2) CSA2_BSTEP(16, 1)
+  CSA2_BSTEP(32, 16) CSA2_BSTEP(32, 8) CSA2_BSTEP(32, 4) CSA2_BSTEP(32, 2) CSA2_BSTEP(32, 1)
+  CSA2_BSTEP(64, 32) CSA2_BSTEP(64, 16) CSA2_BSTEP(64, 8) CSA2_BSTEP(64, 4) CSA2_BSTEP(64, 2) CSA2_BSTEP(64, 1)
+#undef CSA2_BSTEP
+  return x;
+}
+
+// Chunk lists work on packed block keys: a block at offset o of a chunk of 2^ob blocks with key
+// k > 0 packs to max(1, (k >> ob) << ob | (2^ob - 1 - o)), an empty block to 0.  Packed values of
+// non-empty blocks are distinct and order blocks by their truncated key, then by block (lower
+// block first), so a packed bound c bounds the exact ranking key of every block whose packed
+// value is at most c by unpack_cut(c).
+__device__ __forceinline__ uint32_t pack_block(uint32_t key, int off, int ob) {
+  if (key == 0u) return 0u;
+  const uint32_t m = (1u << ob) - 1u;
+  return max(1u, (key & ~m) | (m - (uint32_t)off));
+}
+__device__ __forceinline__ uint64_t unpack_cut(uint32_t c, int ob) {
+  return c == 0u ? 0ull : ((uint64_t)(c | ((1u << ob) - 1u)) << 32) | 0xffffffffull;
+}
+
+// The chunk list, computed by wave 0 from the five best packed blocks of each of the chunk's 16
+// units in LDS (u5[5u + r], r < 4 the four best, r = 4 the fifth): of the 64 listed values and
+// the largest fifth mc, the values above mc among the 16 largest, in block order, as `entry` of
+// lanes 0..15 (exact ranking keys read from the chunk's block keys; 0 padded), and the cut
+// unpack_cut(max(mc, the 17th largest listed value)).  Every block of the chunk that is not in its
+// list is bounded by that cut: a block outside its unit's four packs at or below the unit's fifth,
+// and a listed value left out is at or below mc or the 17th.  The 64 values are sorted by a
+// bitonic network across the wave, the kept ones then by block.
+__device__ __forceinline__ void wave_chunk_list(const uint32_t* u5, const uint32_t* wkeys, uint32_t blk0, int ob,
+                                                uint64_t& entry, uint64_t& cut) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = u5[5 * (lane >> 2) + (lane & 3)];
+  const uint32_t mc = wave_max_u32(lane < kFullWaves ? u5[5 * lane + 4] : 0u);
+  x = bitonic_sort<64>(x);                                      // lane i: the i-th largest
+  const uint32_t c17 = (uint32_t)__builtin_amdgcn_readlane((int)x, kListLen);
+  const uint32_t m = (1u << ob) - 1u;
+  const bool keep = lane < kListLen && x > mc;
+  // kept values by block: 1 + (2^ob - 1 - offset), descending
+  const uint32_t z = bitonic_sort<16>(keep ? (x & m) + 1u : 0u);
+  const bool listed = lane < kListLen && z != 0u;
+  const int off = listed ? (int)(m - (z - 1u)) : 0;
+  entry = listed ? rank_key(wkeys[off], blk0 + (uint32_t)off) : 0ull;
+  cut = unpack_cut(max(mc, c17), ob);
 }
 
 // grid (n_wg, Q), one workgroup of 16 waves per chunk of positions (sized so the grid is about
@@ -491,7 +471,9 @@ __device__ __forceinline__ void wave_chunk_lists(const uint32_t* wkeys, int nblk
 // contiguous ranges of chunk/(16*upw) positions) writes its five best blocks as ranking keys
 // (score key << 32 | ~block): lists[q][unit][0..3] = the four best (0 = none) and
 // cuts[q][unit] = the fifth best (0 = none), so every block of the unit that is not listed
-// ranks at or below cuts[q][unit].  Requires chunk % 1024 == 0 and chunk <= 8192.
+// ranks at or below cuts[q][unit].  With `clists` non-null (one unit per wave) the chunk's list
+// replaces them: clists[q][chunk][0..15] and ccuts[q][chunk] as wave_chunk_list states.  Requires
+// chunk a power of two from 1024 to 8192.
 template <bool kFp4, int kBS>
 __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
@@ -505,7 +487,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   float* sbuf = (float*)(lds + kIdxHeads * kIdxDim * 2);
   uint32_t* wkeys = (uint32_t*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4);
   int* ctr = (int*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4 + (chunk / kBlock) * 4);
-  uint64_t* xch = (uint64_t*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4 + (chunk / kBlock) * 4 + 16);
+  uint32_t* u5 = (uint32_t*)(lds + kIdxHeads * kIdxDim * 2 + chunk * 4 + (chunk / kBlock) * 4 + 16);
   const int q = blockIdx.y, b = q / T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -524,7 +506,9 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   auto phys = [&](int t) { return t + rot < ntiles ? t + rot : t + rot - ntiles; };
 
   // Rows of tiles past the chunk are clamped to its last row, so every stage loads and
-  // computes unconditionally; results of such tiles are never stored.
+  // computes unconditionally; results of such tiles are never stored.  (Skipping the loads of a
+  // stage past the chunk would make the loop's load waits count conservatively across the skip,
+  // so each stage would wait for the next one's loads.)
   constexpr int kU = kScanU<kFp4>;
   TileRaw<kFp4> rA[kU], rB[kU];
   auto load_stage = [&](TileRaw<kFp4>(&r)[kU], int t0) {
@@ -541,7 +525,7 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   if (ntiles > 0) {
     stage_query<kFullThreads, kFp4>(idx_q + (size_t)q * kIdxHeads * kIdxDim, qlds);
     if (threadIdx.x == 0) *ctr = kFullWaves * kU;
-    __syncthreads();
+    lds_barrier();
     TileCtx cx;
     key_ctx<kFp4>(cx, qlds, head_w + (size_t)q * kIdxHeads);
     auto grab = [&]() {                            // next stage of this wave (monotonic)
@@ -574,44 +558,71 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
       tB = grab();
     }
   }
-  __syncthreads();
-  // coalesced stores of the chunk's scores and block keys
-  float* srow = scores + (size_t)q * n_max + p_begin;
-  for (int i = threadIdx.x; i < npos; i += kFullThreads) srow[i] = sbuf[i];
+  lds_barrier();
+  // The lists are computed before any store of the epilogue is issued: a register rewritten after
+  // a store makes the wave wait for that store to complete, which takes microseconds while the
+  // other workgroups stream keys.
   const int nblk = (npos + kBlock - 1) / kBlock;
-  if (blkkey) {
-    uint32_t* brow = blkkey + (size_t)q * nb_max + p_begin / kBlock;
-    for (int i = threadIdx.x; i < nblk; i += kFullThreads) brow[i] = wkeys[i];
-  }
-  if (!lists) return;
-  if (clists) {
-    // one wave builds the chunk's unit lists and its chunk list (upw == 1)
-    if (wave != 0) return;
-    const size_t ch = (size_t)q * gridDim.x + blockIdx.x;
-    const size_t unit0 = ch * kFullWaves;
-    const uint32_t blk0 = (uint32_t)(p_begin / kBlock);
-    uint64_t* cl = clists + ch * kListLen;
-    switch (chunk / (kBlock * 64)) {             // blocks per lane
-      case 2: wave_chunk_lists<2>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
-      case 4: wave_chunk_lists<4>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
-      case 8: wave_chunk_lists<8>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
-      default: wave_chunk_lists<16>(wkeys, nblk, blk0, unit0, lists, cuts, cl, ccuts + ch, xch); break;
-    }
-    return;
-  }
   // the wave's blocks (bpu <= 64: one per lane), split into upw units of bpu/upw blocks; each
   // unit lists its five best
-  const int bpu = chunk / (kBlock * kFullWaves);
+  const int bpu = chunk / (kBlock * kFullWaves), lanes = bpu / upw;
   const int ub = wave * bpu;
   const bool ok = lane < bpu && ub + lane < nblk;
   const uint32_t key = ok ? wkeys[ub + lane] : 0u;
-  const uint32_t blk = ok ? (uint32_t)(p_begin / kBlock + ub + lane) : 0xffffffffu;
-  const size_t unit0 = (((size_t)q * gridDim.x + blockIdx.x) * kFullWaves + wave) * upw;
-  switch (bpu / upw) {
-    case 8: write_unit_lists<8>(key, blk, upw, unit0, lists, cuts); break;
-    case 16: write_unit_lists<16>(key, blk, upw, unit0, lists, cuts); break;
-    case 32: write_unit_lists<32>(key, blk, upw, unit0, lists, cuts); break;
-    default: write_unit_lists<64>(key, blk, upw, unit0, lists, cuts); break;
+  uint64_t best[5] = {0ull, 0ull, 0ull, 0ull, 0ull};
+  uint64_t centry = 0ull, ccut = 0ull;
+  if (clists) {
+    // one unit per wave: its five largest packed blocks, then wave 0 merges the 16 units
+    const int ob = 31 - __builtin_clz((unsigned)(chunk / kBlock));
+    uint32_t pk = ok ? pack_block(key, ub + lane, ob) : 0u;
+    uint32_t top[5];
+#pragma unroll
+    for (int r = 0; r < 5; ++r) {
+      top[r] = wave_max_u32(pk);
+      if (pk == top[r]) pk = 0u;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < 5; ++r) u5[5 * wave + r] = top[r];
+    }
+    lds_barrier();
+    if (wave == 0) wave_chunk_list(u5, wkeys, (uint32_t)(p_begin / kBlock), ob, centry, ccut);
+  } else if (lists) {
+    const uint32_t blk = ok ? (uint32_t)(p_begin / kBlock + ub + lane) : 0xffffffffu;
+    switch (lanes) {
+      case 8: unit_best<8>(key, blk, best); break;
+      case 16: unit_best<16>(key, blk, best); break;
+      case 32: unit_best<32>(key, blk, best); break;
+      default: unit_best<64>(key, blk, best); break;
+    }
+  }
+  // stores: the chunk's scores and block keys (coalesced), its unit lists and its chunk list
+  constexpr int kSt = kMaxScanChunk / kFullThreads;
+  float* srow = scores + (size_t)q * n_max + p_begin;
+  float sv[kSt];
+#pragma unroll
+  for (int u = 0; u < kSt; ++u) {
+    const int i = u * kFullThreads + threadIdx.x;
+    sv[u] = i < npos ? sbuf[i] : 0.f;
+  }
+  const uint32_t bk = (int)threadIdx.x < nblk ? wkeys[threadIdx.x] : 0u;
+#pragma unroll
+  for (int u = 0; u < kSt; ++u) {
+    const int i = u * kFullThreads + threadIdx.x;
+    if (i < npos) srow[i] = sv[u];
+  }
+  if (blkkey && (int)threadIdx.x < nblk) blkkey[(size_t)q * nb_max + p_begin / kBlock + threadIdx.x] = bk;
+  if (!clists && lists && lane % lanes == 0 && lane / lanes < upw) {
+    const size_t unit = (((size_t)q * gridDim.x + blockIdx.x) * kFullWaves + wave) * upw + lane / lanes;
+    u32x4* lp = (u32x4*)(lists + unit * 4);
+    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
+    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
+    cuts[unit] = best[4];
+  }
+  if (clists && wave == 0) {
+    const size_t ch = (size_t)q * gridDim.x + blockIdx.x;
+    if (lane < kListLen) clists[ch * kListLen + lane] = centry;
+    if (lane == 0) ccuts[ch] = ccut;
   }
 }
 
@@ -809,7 +820,7 @@ __global__ __launch_bounds__(kMqThreads) void k_idx_scan_mq(
     load_step(0);
     store_step(0);
     if (nsteps > 1) load_step(1);
-    __syncthreads();
+    lds_barrier();
     const int r32 = lane & 31;
     for (int st = 0; st < nsteps; ++st) {
       if (st > 0) flush_scores(st - 1);
@@ -855,7 +866,7 @@ __global__ __launch_bounds__(kMqThreads) void k_idx_scan_mq(
         store_step((st + 1) & 1);          // that buffer was last read before the previous barrier
         if (st + 2 < nsteps) load_step(st + 2);
       }
-      __syncthreads();
+      lds_barrier();
     }
     flush_scores(nsteps - 1);
   }
@@ -918,7 +929,7 @@ int scan_chunk_positions(int n_max, int queries) {
   long long per_query = ((long long)n_max + 255) / 256;
   if (c < per_query) c = per_query;
   long long p = 1024;
-  while (p < c && p < 8192) p *= 2;
+  while (p < c && p < kMaxScanChunk) p *= 2;
   return (int)p;
 }
 
@@ -964,7 +975,8 @@ hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t 
   const int bpw = chunk / (kBlock * kFullWaves);       // blocks per wave
   if (upw < 1 || bpw % upw != 0 || bpw / upw < 8 || (bpw / upw & (bpw / upw - 1)) != 0) return hipErrorInvalidValue;
   if (multi_query && (chunk % 1024 != 0 || chunk > kMqMaxChunk || Q % T != 0)) return hipErrorInvalidValue;
-  if (clists && (multi_query || upw != 1 || !lists || !ccuts)) return hipErrorInvalidValue;   // one unit per wave
+  if (!multi_query && (chunk < 1024 || chunk > kMaxScanChunk || (chunk & (chunk - 1)) != 0)) return hipErrorInvalidValue;
+  if (clists && (multi_query || upw != 1 || !ccuts)) return hipErrorInvalidValue;   // one unit per wave
   if (idx_ks)
     launch_scan_format<true>(block_score, idx_k, idx_ks, k_rows, idx_q, head_w, n_visible, Q, T, n_max, scores, blkkey,
                              nb_max, lists, cuts, chunk, n_wg, multi_query, upw, clists, ccuts, s);
@@ -1003,11 +1015,11 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
   const int r = it - full_items, q = full ? it : r % Q, b = q / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
-  int len = pool_len[q];
-  len = len < 0 ? 0 : (len > cap ? cap : len);
+  // The pool length, the slots' positions and what they index are loaded without waiting for
+  // one another (a position is used only if it lies in range); slots at or past the length are
+  // dropped afterwards.
+  const int len_raw = pool_len[q];
   const int s_begin = blockIdx.x * kRiChunk;
-  const int s_end = min(s_begin + kRiChunk, len);
-  if (s_end <= s_begin) return;
   const int32_t* pp = pool_pos + (size_t)q * cap;
   float* out = slot_scores + (size_t)it * cap;
   const int sw = s_begin + kRiUnit * wave;                         // first slot of this wave's unit
@@ -1016,20 +1028,22 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
   int my_pos = -1;
   if (full) {
     const int64_t n_rows = min(k_rows, full_stride);
-    if (lane < kRiUnit) {
-      const int slot = sw + lane;
-      int pos = slot < s_end ? pp[slot] : -1;
-      pos = (pos >= 0 && (int64_t)pos < n_rows) ? pos : -1;
-      my_sc = pos >= 0 ? full_scores[(size_t)q * full_stride + pos] : 0.f;
+    const int slot = sw + lane;
+    int pos = (lane < kRiUnit && slot < cap) ? pp[slot] : -1;
+    pos = (pos >= 0 && (int64_t)pos < n_rows) ? pos : -1;
+    const float sc = pos >= 0 ? full_scores[(size_t)q * full_stride + pos] : 0.f;
+    const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
+    if (min(s_begin + kRiChunk, len) <= s_begin) return;
+    if (slot < len && pos >= 0) {
+      my_sc = sc;
       my_pos = pos;
-      if (pos >= 0) out[slot] = my_sc;
     }
   } else {
     int pos[kRiTilesPerWave];
 #pragma unroll
     for (int u = 0; u < kRiTilesPerWave; ++u) {
       const int slot = sw + 16 * u + j;
-      pos[u] = slot < s_end ? pp[slot] : -1;
+      pos[u] = slot < cap ? pp[slot] : -1;
     }
     stage_query<kScanThreads, kFp4>(idx_q + (size_t)r * kIdxHeads * kIdxDim, qlds);
     const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
@@ -1041,21 +1055,29 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
       ok[u] = pos[u] >= 0 && (int64_t)pos[u] < k_rows;
       load_key<kFp4>(kseq, sseq, ok[u] ? pos[u] : 0, g, raw[u]);
     }
-    __syncthreads();
+    const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
+    const int s_end = min(s_begin + kRiChunk, len);
+    if (s_end <= s_begin) return;                 // uniform across the workgroup
+#pragma unroll
+    for (int u = 0; u < kRiTilesPerWave; ++u) ok[u] = ok[u] && sw + 16 * u + j < s_end;
+    lds_barrier();
     TileCtx cx;
     key_ctx<kFp4>(cx, qlds, head_w + (size_t)r * kIdxHeads);
     float sc[kRiTilesPerWave];
 #pragma unroll
-    for (int u = 0; u < kRiTilesPerWave; ++u) {
-      sc[u] = key_score<kFp4>(cx, raw[u]);
-      if (g == 0 && ok[u]) out[sw + 16 * u + j] = sc[u];
-    }
+    for (int u = 0; u < kRiTilesPerWave; ++u) sc[u] = key_score<kFp4>(cx, raw[u]);
     // lane 16u + j (u < 2) takes tile u's slot sw + 16u + j (every lane of a column holds its score)
     const int p0 = ok[0] ? pos[0] : -1, p1 = ok[1] ? pos[1] : -1;
     my_sc = g == 1 ? sc[1] : sc[0];
     my_pos = g == 0 ? p0 : (g == 1 ? p1 : -1);
   }
-  if (!lists) return;
+  // lane i < 32 holds slot sw + i; its score is stored after the lists are computed (a register
+  // rewritten after a store makes the wave wait for the store to complete)
+  const bool store_sc = lane < kRiUnit && my_pos >= 0;
+  if (!lists) {
+    if (store_sc) out[sw + lane] = my_sc;
+    return;
+  }
   // the unit's five best keys, one at a time: the largest key, and among copies of it the lowest
   // lane (slot), leaves the set
   uint64_t x = my_pos >= 0 ? rank_key(score_key(my_sc), (uint32_t)my_pos) : 0ull;
@@ -1081,6 +1103,9 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
       best[a] = ka; best[c] = kc; bslot[a] = sa; bslot[c] = sc2;
     };
     cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+  }
+  if (store_sc) out[sw + lane] = my_sc;
+  if (lane == 0) {
     const size_t unit = (size_t)it * (gridDim.x * (kRiChunk / kRiUnit)) + blockIdx.x * (kRiChunk / kRiUnit) + wave;
     u32x4* lp = (u32x4*)(lists + unit * kRiUnitList);
     lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};

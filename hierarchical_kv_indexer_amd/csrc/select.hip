@@ -66,7 +66,7 @@ struct Block {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t inc = wave_incl_sum(v);
     if (lane == 63) sm.wred[parity][wave].x = inc;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -85,7 +85,7 @@ struct Block {
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
     if (lane == 0) sm.wred[parity][wave] = u32x4{cnt, mn, mx, 0u};
-    __syncthreads();
+    lds_barrier();
     cnt = 0u;
     mn = 0xffffffffu;
     mx = 0u;
@@ -125,7 +125,7 @@ __device__ __forceinline__ uint32_t ordered_offsets(const uint32_t (&c)[N], uint
     }
   }
   if (lane < N) ec[lane * kWaves + wave] = mine;
-  __syncthreads();
+  lds_barrier();
   uint32_t tot_i = 0u, pre_w = 0u;
   if (lane < N) {
 #pragma unroll
@@ -167,7 +167,7 @@ __device__ __forceinline__ void find_bin(uint32_t need, Block& bk) {
     }
     sm.nrank = 0u;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Bounds [lo, hi] on ranking keys whose score keys lie in [mn32, mx32].
@@ -197,14 +197,14 @@ __device__ __forceinline__ uint64_t rank_collected(uint32_t cnt, uint32_t need, 
     sm.rankpart[part - 1][i] = r;
     sm.eqpart[part - 1][i] = eq;
   }
-  __syncthreads();
+  lds_barrier();
   if (part == 0 && i < cnt) {
     r += sm.rankpart[0][i] + sm.rankpart[1][i] + sm.rankpart[2][i];
     eq += sm.eqpart[0][i] + sm.eqpart[1][i] + sm.eqpart[2][i];
     // fewer than need keys above x, at least need at or above it (every copy of x agrees)
     if (r < need && need <= r + eq) sm.result = x;
   }
-  __syncthreads();
+  lds_barrier();
   return sm.result;
 }
 
@@ -264,7 +264,7 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
         for_each(count);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (save && first) *(u32x4*)&save[4 * threadIdx.x] = *(const u32x4*)&sm.hist[4 * threadIdx.x];
     find_bin(need, bk);
     const uint32_t bin = sm.found_bin, above = sm.found_above, cnt = sm.found_cnt;
@@ -295,17 +295,17 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
           for_each(collect);
         }
       }
-      __syncthreads();
+      lds_barrier();
       return rank_collected(cnt, need, bk);
     }
     if (cand && !use_cand && cnt <= (uint32_t)kCandCap) {
       if (threadIdx.x == 0) sm.ncand = 0;
-      __syncthreads();
+      lds_barrier();
       for_each([&](uint64_t k) {
         if (k >= lo && k <= hi) cand[atomicAdd(&sm.ncand, 1u)] = k;
       });
       use_cand = true;
-      __syncthreads();
+      lds_barrier();
     }
   }
 }
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
       sidx[i] = sat ? (int)atomicAdd(&sm.nsat, 1u) : -1;
       if (sat) satunit[sidx[i]] = (uint16_t)(i * kNT + t);
     }
-    __syncthreads();
+    lds_barrier();
     const uint32_t nsat = sm.nsat;
     const bool dense = nsat * (uint32_t)bpu <= (uint32_t)kCandCap;   // re-read keys fit in LDS
     const bool from_first = fp.valid && nsat > 0 && dense;
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
         if (from_first && sidx[i] >= 0 && e[i][r] >= t0) atomicSub(&sm.hist[first_pass_bin(fp, e[i][r])], 1u);
         if (sidx[i] >= 0 || e[i][r] < t0) e[i][r] = 0ull;
       }
-    __syncthreads();
+    lds_barrier();
 
     uint64_t tstar = t0;                      // no unit re-read: every block >= T0 is listed
     if (nsat > 0) {
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
                 if (a < (uint32_t)kRankMax) sm.rankbuf[a] = k;
               }
             });
-            __syncthreads();
+            lds_barrier();
             tstar = rank_collected(cnt, (uint32_t)P - above, bk);
           } else {
             tstar = select_kth(for_each_c, (uint32_t)P - above, blo, bhi, bk, nullptr);
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
       }
       if (lane == 0) satcnt[si] = c;
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t lb[kUnitsPerThread][4], cnt[kUnitsPerThread], off[kUnitsPerThread];
 #pragma unroll
     for (int i = 0; i < kUnitsPerThread; ++i) {
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
         satcnt[sidx[i]] = off[i];
       }
     }
-    __syncthreads();
+    lds_barrier();
     for (uint32_t si = wave; si < nsat; si += kWaves) {
       uint32_t n = satcnt[si];
       const int jb = satunit[si] * bpu;
@@ -651,7 +651,7 @@ __global__ __launch_bounds__(kNT) void k_pool(
         n += (uint32_t)__popcll(m);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   pool_out(all, nv, nb, nsel, byrank, pool_pos + (size_t)q * cap_out, cap_out, pool_len + q,
@@ -680,9 +680,8 @@ constexpr int W = NT / 64;
 constexpr int BINS = 4096;
 constexpr int BPT = BINS / NT;              // bins per thread (8)
 constexpr int RANK_MAX = 64;                // bins this small are ranked by one wave
-constexpr int CAND = 4096;                  // re-read members held in LDS
 constexpr int MAX_SAT = 128;                // re-read groups
-constexpr int MAX_GROUPS = 512;
+constexpr int MAX_GROUPS = NT;              // group t's cut is held by thread t
 static_assert(BPT == 8, "find_bin reads two 16-byte bin quads per thread");
 
 struct __attribute__((aligned(16))) Smem {
@@ -690,9 +689,9 @@ struct __attribute__((aligned(16))) Smem {
   u32x4 wred[2][W];
   uint32_t ecnt[2][64 * W];                 // ordered(): per-(element, wave) totals; rank_small: partials
   uint64_t rk[RANK_MAX];
-  uint64_t cand[CAND];                      // re-read members (0 = none / below T0')
-  uint16_t satgroup[MAX_SAT];
-  uint32_t satinfo[MAX_SAT];                // selected count of a re-read group, then its offset
+  uint16_t satgroup[MAX_SAT];               // re-read slot -> group
+  uint32_t gstart[MAX_SAT + 1];             // selected members of re-read slots before this one
+  uint32_t satoff[MAX_SAT];                 // output offset of a re-read group
   uint16_t satof[MAX_GROUPS];               // group -> 1 + its re-read slot (0: not re-read)
   uint64_t result;
   uint32_t bin, above, cnt, nrk, nsat;
@@ -710,7 +709,7 @@ struct Blk {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t inc = wave_incl_sum(v);
     if (lane == 63) sm.wred[parity][wave].x = inc;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
@@ -728,7 +727,7 @@ struct Blk {
     mn = wave_min_u32(mn);
     mx = wave_max_u32(mx);
     if (lane == 0) sm.wred[parity][wave] = u32x4{cnt, mn, mx, 0u};
-    __syncthreads();
+    lds_barrier();
     cnt = 0u;
     mn = 0xffffffffu;
     mx = 0u;
@@ -766,7 +765,7 @@ __device__ __forceinline__ uint32_t ordered(const uint32_t (&c)[N], uint32_t (&o
     }
   }
   if (lane < N) ec[lane * W + wave] = mine;
-  __syncthreads();
+  lds_barrier();
   uint32_t tot_i = 0u, pre_w = 0u;
   if (lane < N) {
 #pragma unroll
@@ -811,7 +810,7 @@ __device__ __forceinline__ void find_bin(uint32_t need, bool clear, Blk& bk) {
     }
     sm.nrk = 0u;
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Histogram binning of one pass: keys in [lo, hi] into BINS bins of width 2^shift; while the
@@ -858,7 +857,7 @@ __device__ __forceinline__ uint64_t rank_small(uint32_t n, uint32_t need, Blk& b
     eq += (m < (int)n && y == x) ? 1u : 0u;
   }
   sm.ecnt[bk.parity][w * 64 + i] = r | (eq << 16);
-  __syncthreads();
+  lds_barrier();
   if (t < 64) {
     uint32_t rt = 0, et = 0;
 #pragma unroll
@@ -870,7 +869,7 @@ __device__ __forceinline__ uint64_t rank_small(uint32_t n, uint32_t need, Blk& b
     if (t < (int)n && rt < need && need <= rt + et) sm.result = x;
   }
   bk.parity ^= 1;
-  __syncthreads();
+  lds_barrier();
   return sm.result;
 }
 
@@ -886,7 +885,7 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
     Pass ps;
     ps.make(lo, hi);
     for_each([&](uint64_t k) { atomicAdd(&sm.hist[ps.bin(k)], 1u); });
-    __syncthreads();
+    lds_barrier();
     find_bin(need, true, bk);
     const uint32_t b = sm.bin, cnt = sm.cnt;
     need -= sm.above;
@@ -897,24 +896,26 @@ __device__ uint64_t select_kth(ForEach for_each, uint32_t need, uint64_t lo, uin
       for_each([&](uint64_t k) {
         if (k >= lo && k <= hi) sm.rk[atomicAdd(&sm.nrk, 1u)] = k;
       });
-      __syncthreads();
+      lds_barrier();
       return rank_small(cnt, need, bk);
     }
   }
 }
 
 // One list selection (see the section comment).  key[e]: element e of this thread, list entry
-// g = e*NT + t of group g / L (0 = none); cut: the cut of group t (t < n_groups, else 0).
-// reread(grp, o) -> key of member o < gsize of group grp (0 = none); emit(off, key, grp, o) writes
-// output place `off` (o = -1 for a listed entry).  Entries of a group and members are in output
-// order; groups follow each other.  Returns the number emitted (<= P), or -1 (nothing emitted)
-// when more than CAND members or MAX_SAT groups would be re-read, or when copies of one key
-// straddle the P-th place: the caller then selects densely.
-template <int L, int LPT, class Reread, class Emit>
+// g = e*NT + t of group g / L (0 = none); cut: the cut of group t (t < n_groups, else 0); gsize (a
+// power of two): members per group.  reread(grp, o) -> key of member o < gsize of group grp (0 =
+// none); emit(off, key, grp, o) writes output place `off` (o = -1 for a listed entry).  Entries of
+// a group and members are in output order; groups follow each other.  The members of re-read
+// groups are held in registers, MPT per thread (member o of re-read slot s is item s*gsize + o,
+// item i*NT + t in thread t's element i).  Returns the number emitted (<= P), or -1 (nothing
+// emitted) when more than MPT*NT members or MAX_SAT groups would be re-read, or when copies of
+// one key straddle the P-th place: the caller then selects densely.
+template <int L, int LPT, int MPT, class Reread, class Emit>
 __device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int gsize, uint32_t P,
                            Reread reread, Emit emit, Blk& bk) {
   Smem& sm = bk.sm;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x;
   uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
 #pragma unroll
   for (int e = 0; e < LPT; ++e)
@@ -930,54 +931,43 @@ __device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int
   p0.make(key_lo(mn), key_hi(mx));
   const bool hist = nvalid > P;
   uint64_t t0 = 1ull;
-  uint32_t b0 = 0;
   if (hist) {
 #pragma unroll
     for (int e = 0; e < LPT; ++e) atomicAdd(&sm.hist[p0.bin(key[e])], 1u);
-    __syncthreads();
+    lds_barrier();
     find_bin(P, false, bk);
-    b0 = sm.bin;
-    t0 = p0.bin_lo(b0);
+    t0 = p0.bin_lo(sm.bin);
   }
-  const int max_sat = min(MAX_SAT, CAND / gsize);
-  for (int g = t; g < MAX_GROUPS; g += NT) {
-    const uint64_t c = g == t ? cut : 0ull;
-    const bool sat = g < n_groups && c != 0ull && c >= t0;
+  const int gshift = __builtin_ctz((unsigned)gsize);
+  const int max_sat = min(MAX_SAT, (MPT * NT) >> gshift);
+  {
+    const bool sat = t < n_groups && cut != 0ull && cut >= t0;
     uint32_t si = 0;
     if (sat) {
       si = atomicAdd(&sm.nsat, 1u);
-      if (si < (uint32_t)max_sat) sm.satgroup[si] = (uint16_t)g;
+      if (si < (uint32_t)max_sat) sm.satgroup[si] = (uint16_t)t;
     }
-    sm.satof[g] = (sat && si < (uint32_t)max_sat) ? (uint16_t)(si + 1) : (uint16_t)0;
+    sm.satof[t] = (sat && si < (uint32_t)max_sat) ? (uint16_t)(si + 1) : (uint16_t)0;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t nsat = sm.nsat;
   if (nsat > (uint32_t)max_sat) {
     if (hist) find_bin(1, true, bk);          // clear the histogram for the caller's dense path
     return -1;
   }
-  // re-read groups: one wave per group, members in batches of kBatch per lane whose loads are all
-  // issued before any is used
-  constexpr int kBatch = 4;
-  for (uint32_t si = wave; si < nsat; si += W) {
-    const int grp = sm.satgroup[si];
-    for (int o0 = 0; o0 < gsize; o0 += 64 * kBatch) {
-      uint64_t m[kBatch];
+  // re-read members, all loads issued before any is used; those below T0' drop out
+  const uint32_t nc = nsat << gshift;
+  const uint32_t omask = (uint32_t)gsize - 1u;
+  uint64_t m[MPT];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int o = o0 + 64 * i + lane;
-        m[i] = o < gsize ? reread(grp, o) : 0ull;
-      }
+  for (int i = 0; i < MPT; ++i) {
+    const uint32_t idx = (uint32_t)(i * NT + t);
+    m[i] = idx < nc ? reread((int)sm.satgroup[idx >> gshift], (int)(idx & omask)) : 0ull;
+  }
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int o = o0 + 64 * i + lane;
-        if (o < gsize) {
-          const uint64_t k = m[i] >= t0 ? m[i] : 0ull;
-          sm.cand[si * gsize + o] = k;
-          if (hist && k) atomicAdd(&sm.hist[p0.bin(k)], 1u);
-        }
-      }
-    }
+  for (int i = 0; i < MPT; ++i) {
+    if (m[i] < t0) m[i] = 0ull;
+    else if (hist) atomicAdd(&sm.hist[p0.bin(m[i])], 1u);
   }
   // listed keys that stay candidates: >= T0', in groups that were not re-read
 #pragma unroll
@@ -987,12 +977,12 @@ __device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int
     if (hist && gone && key[e] >= t0) atomicSub(&sm.hist[p0.bin(key[e])], 1u);
     if (gone || key[e] < t0) key[e] = 0ull;
   }
-  __syncthreads();
-  const uint32_t nc = nsat * (uint32_t)gsize;
+  lds_barrier();
   auto each = [&](auto f) {
 #pragma unroll
     for (int e = 0; e < LPT; ++e) f(key[e]);
-    for (uint32_t i = t; i < nc; i += NT) f(sm.cand[i]);
+#pragma unroll
+    for (int i = 0; i < MPT; ++i) f(m[i]);
   };
   uint64_t thr;
   if (hist) {
@@ -1006,7 +996,7 @@ __device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int
       each([&](uint64_t k) {
         if (k >= lo && k <= hi) sm.rk[atomicAdd(&sm.nrk, 1u)] = k;
       });
-      __syncthreads();
+      lds_barrier();
       thr = rank_small(cnt, need, bk);
     } else {
       thr = select_kth(each, need, lo, hi, bk);
@@ -1023,28 +1013,25 @@ __device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int
     bk.reduce(n, cmn, cmx);
     thr = n > P ? select_kth(each, P, key_lo(cmn), key_hi(cmx), bk) : 1ull;
   }
-  // selected members of each re-read group, counted by one wave (reads in batches issued first)
-  for (uint32_t si = wave; si < nsat; si += W) {
-    uint32_t c = 0;
-    for (int o0 = 0; o0 < gsize; o0 += 64 * kBatch) {
-      uint64_t mk[kBatch];
+  // selected members: their places in item order, and each re-read slot's first place
+  uint32_t msel[MPT], moff[MPT];
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int o = o0 + 64 * i + lane;
-        mk[i] = o < gsize ? sm.cand[si * gsize + o] : 0ull;
-      }
+  for (int i = 0; i < MPT; ++i) msel[i] = (m[i] && m[i] >= thr) ? 1u : 0u;
+  const uint32_t mtotal = ordered<true, MPT>(msel, moff, bk);
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) c += (uint32_t)__popcll(__ballot(mk[i] && mk[i] >= thr));
-    }
-    if (lane == 0) sm.satinfo[si] = c;
+  for (int i = 0; i < MPT; ++i) {
+    const uint32_t idx = (uint32_t)(i * NT + t);
+    if (idx < nc && (idx & omask) == 0u) sm.gstart[idx >> gshift] = moff[i];
   }
-  __syncthreads();
+  if (t == 0) sm.gstart[nsat] = mtotal;
+  lds_barrier();
+  // output places: a re-read group takes its selected members at its first list entry
   uint32_t cnt[LPT], off[LPT];
 #pragma unroll
   for (int e = 0; e < LPT; ++e) {
     const int g = e * NT + t, grp = g / L;
     const uint32_t so = grp < n_groups ? sm.satof[grp] : 0u;
-    cnt[e] = so ? ((g % L == 0) ? sm.satinfo[so - 1] : 0u) : (key[e] >= thr && key[e] ? 1u : 0u);
+    cnt[e] = so ? ((g % L == 0) ? sm.gstart[so] - sm.gstart[so - 1] : 0u) : (key[e] >= thr && key[e] ? 1u : 0u);
   }
   const uint32_t total = ordered<false, LPT>(cnt, off, bk);
   if (total > P) return -1;                  // copies of one key at the P-th place
@@ -1053,33 +1040,20 @@ __device__ int list_select(uint64_t (&key)[LPT], uint64_t cut, int n_groups, int
     const int g = e * NT + t, grp = g / L;
     const uint32_t so = grp < n_groups ? sm.satof[grp] : 0u;
     if (so) {
-      if (g % L == 0) sm.satinfo[so - 1] = off[e];
+      if (g % L == 0) sm.satoff[so - 1] = off[e];
     } else if (cnt[e]) {
       emit(off[e], key[e], grp, -1);
     }
   }
-  __syncthreads();
-  for (uint32_t si = wave; si < nsat; si += W) {
-    uint32_t n = sm.satinfo[si];
-    const int grp = sm.satgroup[si];
-    for (int o0 = 0; o0 < gsize; o0 += 64 * kBatch) {
-      uint64_t mk[kBatch];
+  lds_barrier();
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const int o = o0 + 64 * i + lane;
-        mk[i] = o < gsize ? sm.cand[si * gsize + o] : 0ull;
-      }
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
-        const bool sel = mk[i] && mk[i] >= thr;
-        const uint64_t m = __ballot(sel);
-        const uint32_t at = n + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        if (sel) emit(at, mk[i], grp, o0 + 64 * i + lane);
-        n += (uint32_t)__popcll(m);
-      }
+  for (int i = 0; i < MPT; ++i) {
+    if (msel[i]) {
+      const uint32_t idx = (uint32_t)(i * NT + t), si = idx >> gshift;
+      emit(sm.satoff[si] + moff[i] - sm.gstart[si], m[i], (int)sm.satgroup[si], (int)(idx & omask));
     }
   }
-  __syncthreads();
+  lds_barrier();
   return (int)total;
 }
 
@@ -1136,7 +1110,7 @@ __device__ uint32_t dense_select(KeyAt key_at, int n, uint32_t P, Emit emit, Blk
     done += ns;
     eq_done += neq;
   }
-  __syncthreads();
+  lds_barrier();
   return min(done, P);
 }
 
@@ -1147,6 +1121,7 @@ __device__ uint32_t dense_select(KeyAt key_at, int n, uint32_t P, Emit emit, Blk
 // back to a selection over every block key when too many chunks would be re-read.
 constexpr int kPoolChunks = 256;
 constexpr int kPLE = kPoolChunks * kListLen / ls::NT;   // listed keys per thread (8)
+constexpr int kPLM = 8;                                    // re-read blocks per thread
 
 __global__ __launch_bounds__(ls::NT) void k_pool_chunks(
     const uint64_t* __restrict__ clists, const uint64_t* __restrict__ ccuts, int n_chunks, int bpc,
@@ -1170,7 +1145,7 @@ __global__ __launch_bounds__(ls::NT) void k_pool_chunks(
   const int nv = nv_raw < 0 ? 0 : (nv_raw > n_max ? n_max : nv_raw);
   const int nb = (nv + kBlock - 1) / kBlock;
   const uint32_t* keys = blkkey + (size_t)q * nb_max;
-  __syncthreads();
+  lds_barrier();
   const bool all = nb <= P;
   uint32_t nsel = 0;
   if (!all) {
@@ -1181,7 +1156,7 @@ __global__ __launch_bounds__(ls::NT) void k_pool_chunks(
     auto emit = [&](uint32_t off, uint64_t k, int grp, int o) {
       byrank[off] = o < 0 ? rank_key_index(k) : (uint32_t)(grp * bpc + o);
     };
-    const int r = ls::list_select<kListLen, kPLE>(key, cut, n_chunks, bpc, (uint32_t)P, reread, emit, bk);
+    const int r = ls::list_select<kListLen, kPLE, kPLM>(key, cut, n_chunks, bpc, (uint32_t)P, reread, emit, bk);
     if (r >= 0) {
       nsel = (uint32_t)r;
     } else {
@@ -1231,7 +1206,8 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
                        int32_t* topk_idx, float* topk_score, int Q, hipStream_t s) {
   if (clists) {
     // the chunk-list pool writes the pool only; a Top-K of it is one more launch
-    if (n_chunks > kPoolChunks || blocks_per_chunk < 64 || blocks_per_chunk > 1024 || !ccuts || cap_out > kMaxPool)
+    if (n_chunks > kPoolChunks || blocks_per_chunk < 64 || blocks_per_chunk > 1024 ||
+        (blocks_per_chunk & (blocks_per_chunk - 1)) != 0 || !ccuts || cap_out > kMaxPool)
       return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_pool_chunks, dim3(Q), dim3(ls::NT), 0, s, clists, ccuts, n_chunks, blocks_per_chunk, blkkey,
                        nb_max, n_visible, n_max, P, pool_pos, cap_out, pool_len);
@@ -1328,6 +1304,7 @@ hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap
 // selection over every slot when too many units would be re-read or copies of one position
 // straddle the k-th place.
 constexpr int kTLE = kMaxPool / kRiUnit * kRiUnitList / ls::NT;   // listed keys per thread (4)
+constexpr int kTLM = 8;                                            // re-read slots per thread
 
 __global__ __launch_bounds__(ls::NT) void k_topk_lists(
     const uint64_t* __restrict__ lists, const uint64_t* __restrict__ cuts, const float* __restrict__ slot_scores,
@@ -1335,6 +1312,8 @@ __global__ __launch_bounds__(ls::NT) void k_topk_lists(
     int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* __restrict__ out_a, float* __restrict__ out_sa,
     int32_t* __restrict__ out_b, float* __restrict__ out_sb) {
   __shared__ ls::Smem sm;
+  __shared__ int32_t res_i[kMaxTopK];        // the selection, written out at the end
+  __shared__ float res_s[kMaxTopK];
   ls::Blk bk{sm};
   const int it = blockIdx.x, t = threadIdx.x;
   const bool in_a = it < items_a;
@@ -1362,7 +1341,7 @@ __global__ __launch_bounds__(ls::NT) void k_topk_lists(
   for (int e = 0; e < kTLE; ++e)
     if ((e * ls::NT + t) / kRiUnitList >= nuse) key[e] = 0ull;
   if (t >= nuse) cut = 0ull;
-  __syncthreads();
+  lds_barrier();
   const int32_t* cp = cand_pos + (size_t)q * cap;
   const float* srow = slot_scores + (size_t)it * cap;
   auto key_of_slot = [&](int slot) -> uint64_t {
@@ -1374,16 +1353,31 @@ __global__ __launch_bounds__(ls::NT) void k_topk_lists(
     return slot < len ? key_of_slot(slot) : 0ull;
   };
   auto emit = [&](uint32_t off, uint64_t kk, int, int) {
-    oi[off] = (int32_t)rank_key_index(kk);
-    if (os) os[off] = key_score((uint32_t)(kk >> 32));
+    res_i[off] = (int32_t)rank_key_index(kk);
+    res_s[off] = key_score((uint32_t)(kk >> 32));
   };
-  int total = ls::list_select<kRiUnitList, kTLE>(key, cut, nuse, kRiUnit, (uint32_t)k, reread, emit, bk);
+  int total = ls::list_select<kRiUnitList, kTLE, kTLM>(key, cut, nuse, kRiUnit, (uint32_t)k, reread, emit, bk);
   if (total < 0)
     total = (int)ls::dense_select(key_of_slot, len, (uint32_t)k,
                                   [&](uint32_t off, uint64_t kk, int) { emit(off, kk, 0, 0); }, bk);
-  for (int i = total + t; i < k; i += ls::NT) {
-    oi[i] = -1;
-    if (os) os[i] = 0.f;
+  lds_barrier();
+  // every result is read before any is stored (a register rewritten after a store waits for it)
+  constexpr int kOut = kMaxTopK / ls::NT;
+  int32_t vi[kOut];
+  float vs[kOut];
+#pragma unroll
+  for (int u = 0; u < kOut; ++u) {
+    const int i = u * ls::NT + t;
+    vi[u] = i < total ? res_i[i] : -1;
+    vs[u] = i < total ? res_s[i] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kOut; ++u) {
+    const int i = u * ls::NT + t;
+    if (i < k) {
+      oi[i] = vi[u];
+      if (os) os[i] = vs[u];
+    }
   }
 }
 
@@ -1393,7 +1387,7 @@ hipError_t launch_topk_lists(const uint64_t* lists, const uint64_t* cuts, const 
                              int items_b, int32_t* out_b, float* out_sb, hipStream_t s) {
   const int items = items_a + items_b;
   if (items == 0) return hipSuccess;
-  if (cap > kMaxPool || ri_units(cap) > ls::MAX_GROUPS) return hipErrorInvalidValue;
+  if (cap > kMaxPool || ri_units(cap) > ls::MAX_GROUPS || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_topk_lists, dim3(items), dim3(ls::NT), 0, s, lists, cuts, slot_scores, cand_pos, cand_len,
                      cap, Q, k, n_rows_a, n_rows_b, items_a, out_a, out_sa, out_b, out_sb);
   return hipGetLastError();

@@ -290,6 +290,21 @@ def test_chain_top2048_over_a_full_pool():
         G.assert_topk_equiv(got["ri_topk"][r, 0, 0], ref["topk"], lambda p: sc[p], f"ri{r}")
 
 
+def test_chain_chunk_lists_over_rounded_chunks():
+    """A 600000-position context with a 256-block pool: the scan's chunk of positions rounds up to
+    4096 (147 chunks, the last one ragged), so the pool is taken from chunk lists of 512 blocks;
+    pool, Top-K and one Reindex layer against the oracle."""
+    N, P, K, L = 600000, 256, 512, 1
+    w = small(N=N, pool_blocks=P, top_k=K, n_reindex=L, seed=3700)
+    inp = workloads.make_inputs(w, with_attention=False)
+    got = G.gpu_index_chain(inp, 1, 1, N, P, K, L, split=False)
+    check_full(w, inp, got, 0, 0)
+    pool = got["pool_pos"][0, 0, :got["pool_len"][0, 0]]
+    ref = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][0, 0, 0], inp["ri_w"][0, 0, 0], pool, K)
+    sc = dict(zip(pool.tolist(), ref["scores"].tolist()))
+    G.assert_topk_equiv(got["ri_topk"][0, 0, 0], ref["topk"], lambda p: sc[p], "ri0")
+
+
 @pytest.mark.parametrize("T", [2, 9])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_pool_block_score_variants(mode, T):
