@@ -26,6 +26,7 @@ EXPORTS = (
     ("csa2_quantize_kv_fp4", _I, (_P, _I64, _P, _P, _P)),
     ("csa2_index_scores", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _P, _P)),
     ("csa2_index_full_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
+    ("csa2_index_stages_workspace", _SZ, (_I, _I, _I, _I, _I, _I)),
     ("csa2_index_scan", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
     ("csa2_index_scan_blocks", _I, (_P, _P, _I64, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P)),
     ("csa2_index_pool", _I, (_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P)),
@@ -121,6 +122,11 @@ def csa2_index_scores(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n
 def csa2_index_full_workspace(B: int, T: int, n_max: int, block_size: int, pool_blocks: int,
                               top_k: int) -> int:
     return lib().csa2_index_full_workspace(B, T, n_max, block_size, pool_blocks, top_k)
+
+
+def csa2_index_stages_workspace(B: int, T: int, n_max: int, block_size: int, pool_blocks: int,
+                                top_k: int) -> int:
+    return lib().csa2_index_stages_workspace(B, T, n_max, block_size, pool_blocks, top_k)
 
 
 def csa2_index_full(idx_k, idx_k_scales, k_rows_per_seq: int, idx_q, head_w, n_visible, B: int, T: int,

@@ -141,6 +141,78 @@ size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
   return c.off;
 }
 
+// csa2_index_full runs the scan and the selection over batches of queries, reusing one batch's
+// workspace for its intermediate data (scores, block keys, lists, internal pool): batches of tb
+// consecutive queries of one sequence when a sequence holds more than 16 queries, else of bb whole
+// sequences.  The caller's workspace decides the batches: every query at once when it holds them
+// all (fastest: the most parallel launches), else the largest batches it holds.  The smallest
+// workspace the call accepts (csa2_index_full_workspace) holds batches of kFullBatchQueries
+// queries (one selection workgroup per CU keeps the GPU busy), or everything when that is at most
+// kFullBatchBytes; past kFullSpillCap it holds 16 queries (the multi-query scan's group).
+constexpr size_t kFullBatchBytes = (size_t)64 << 20;
+constexpr size_t kFullSpillCap = (size_t)1 << 30;
+constexpr int kFullBatchQueries = 256;
+
+struct FullBatches {
+  bool by_seq;     // batches of bb whole sequences (else tb queries of one sequence)
+  int bb, tb;
+  size_t ws_bytes; // the largest batch's workspace
+};
+
+// Batches that fit `budget` bytes (ws_bytes > budget when not even the smallest batch fits).
+FullBatches plan_full_batches(int B, int T, int n_max, int pool_blocks, int top_k, size_t budget) {
+  auto need = [&](int b, int t) { return carve_full(nullptr, plan_full(b, t, n_max, pool_blocks, top_k), n_max, nullptr); };
+  FullBatches fb;
+  fb.by_seq = true;
+  fb.bb = B;
+  fb.tb = T;
+  fb.ws_bytes = need(B, T);
+  if (fb.ws_bytes <= budget) return fb;
+  if (T > 16) {
+    // a multiple of 16 queries of one sequence, as many as fit (need grows with the batch)
+    int lo = 1, hi = (T + 15) / 16;            // batches of 16*k queries, k in [lo, hi]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (need(1, std::min(T, 16 * mid)) <= budget) lo = mid; else hi = mid - 1;
+    }
+    fb.by_seq = false;
+    fb.bb = 1;
+    fb.tb = std::min(T, 16 * lo);
+    fb.ws_bytes = need(1, fb.tb);
+    if (T % fb.tb) fb.ws_bytes = std::max(fb.ws_bytes, need(1, T % fb.tb));
+  } else {
+    int lo = 1, hi = B;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (need(mid, T) <= budget) lo = mid; else hi = mid - 1;
+    }
+    fb.bb = lo;
+    fb.ws_bytes = need(lo, T);
+    if (B % lo) fb.ws_bytes = std::max(fb.ws_bytes, need(B % lo, T));
+  }
+  return fb;
+}
+
+// The smallest workspace csa2_index_full accepts (see above).
+size_t full_min_workspace(int B, int T, int n_max, int pool_blocks, int top_k) {
+  auto need = [&](int b, int t) { return carve_full(nullptr, plan_full(b, t, n_max, pool_blocks, top_k), n_max, nullptr); };
+  const size_t all = need(B, T);
+  if (all <= kFullBatchBytes) return all;
+  size_t busy;                                 // batches of about kFullBatchQueries queries
+  if (T > 16) {
+    const int tb = std::min(T, kFullBatchQueries);
+    busy = need(1, tb);
+    if (T % tb) busy = std::max(busy, need(1, T % tb));
+  } else {
+    const int bb = std::min(B, (kFullBatchQueries + T - 1) / T);
+    busy = need(bb, T);
+    if (B % bb) busy = std::max(busy, need(B % bb, T));
+  }
+  busy = std::min(busy, all);
+  if (busy <= kFullSpillCap) return busy;
+  return plan_full_batches(B, T, n_max, pool_blocks, top_k, 0).ws_bytes;   // the smallest batches
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,10 +273,16 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales,
   return st == CSA2_OK ? ok() : st;
 }
 
-size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k) {
+size_t csa2_index_stages_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k) {
   (void)block_size;
   if (B < 1 || T < 1 || n_max < 0 || pool_blocks < 0 || top_k < 1) return 0;
   return carve_full(nullptr, plan_full(B, T, n_max, pool_blocks, top_k), n_max, nullptr);
+}
+
+size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k) {
+  (void)block_size;
+  if (B < 1 || T < 1 || n_max < 0 || pool_blocks < 0 || top_k < 1) return 0;
+  return full_min_workspace(B, T, n_max, pool_blocks, top_k);
 }
 
 static csa2_status check_full_shape(int B, int T, int n_max, int block_size, int pool_blocks, int top_k) {
@@ -370,19 +448,52 @@ csa2_status csa2_index_full(const uint8_t* idx_k, const uint8_t* idx_k_scales, i
                             int block_size, int pool_blocks, int top_k, int32_t* pool_pos,
                             int32_t* pool_len, int32_t* topk_idx, float* topk_score, void* workspace,
                             size_t ws_bytes, void* stream) {
-  // check everything (both stages) before enqueueing anything
+  // check everything before enqueueing anything
   csa2_status st = check_index_common(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max);
   if (st != CSA2_OK) return st;
   if ((st = check_full_shape(B, T, n_max, block_size, pool_blocks, top_k)) != CSA2_OK) return st;
   const FullPlan p = plan_full(B, T, n_max, pool_blocks, top_k);
   if ((st = check_pool_args(p, pool_pos, pool_len)) != CSA2_OK) return st;
   if ((st = check_topk_args(topk_idx, topk_score)) != CSA2_OK) return st;
-  if ((st = check_workspace(p, n_max, workspace, ws_bytes)) != CSA2_OK) return st;
-  st = csa2_index_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, B, T, n_max, block_size, pool_blocks,
-                       top_k, workspace, ws_bytes, stream);
-  if (st != CSA2_OK) return st;
-  return csa2_index_select(n_visible, B, T, n_max, block_size, pool_blocks, top_k, pool_pos, pool_len, topk_idx,
-                           topk_score, workspace, ws_bytes, stream);
+  const size_t min_ws = full_min_workspace(B, T, n_max, pool_blocks, top_k);
+  REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= min_ws, CSA2_ERR_WORKSPACE,
+          "workspace of %zu bytes required (got %zu)", min_ws, ws_bytes);
+  const FullBatches fb = plan_full_batches(B, T, n_max, pool_blocks, top_k, ws_bytes);
+  REQUIRE(fb.ws_bytes <= ws_bytes, CSA2_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)", fb.ws_bytes,
+          ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t krow = idx_k_scales ? csa2::kIdxDim / 2 : csa2::kIdxDim;   // key bytes per row
+  const size_t srow = csa2::kIdxDim / 16;                                  // FP4 scale bytes per row
+  // one batch: queries q0 .. q0 + bb*tb - 1 (bb sequences from b0, tb queries each)
+  auto run = [&](int b0, int q0, int bb, int tb) -> csa2_status {
+    const FullPlan bp = plan_full(bb, tb, n_max, pool_blocks, top_k);
+    FullWs w;
+    carve_full(workspace, bp, n_max, &w);
+    const uint8_t* kb = idx_k + (size_t)b0 * (size_t)k_rows_per_seq * krow;
+    const uint8_t* ksb = idx_k_scales ? idx_k_scales + (size_t)b0 * (size_t)k_rows_per_seq * srow : nullptr;
+    const int32_t* nv = n_visible + q0;
+    csa2_status r = CSA2_OK;
+    if (n_max > 0) {
+      r = hip_check(csa2::launch_idx_scan(kb, ksb, k_rows_per_seq, idx_q + (size_t)q0 * csa2::kIdxHeads * csa2::kIdxDim,
+                                          head_w + (size_t)q0 * csa2::kIdxHeads, nv, bp.Q, tb, n_max, w.scores,
+                                          w.blkkey, bp.nb_stride, w.lists, w.cuts, bp.chunk, bp.n_wg, bp.multi_query,
+                                          csa2::kBlockMax, bp.upw, w.clists, w.ccuts, s),
+                    "index scan launch");
+      if (r != CSA2_OK) return r;
+    }
+    return launch_pool_stage(bp, w, nv, n_max, pool_pos ? pool_pos + (size_t)q0 * bp.cap : nullptr,
+                             pool_len ? pool_len + q0 : nullptr, top_k, topk_idx + (size_t)q0 * top_k,
+                             topk_score ? topk_score + (size_t)q0 * top_k : nullptr, s);
+  };
+  if (fb.by_seq) {
+    for (int b0 = 0; b0 < B; b0 += fb.bb)
+      if ((st = run(b0, b0 * T, std::min(fb.bb, B - b0), T)) != CSA2_OK) return st;
+  } else {
+    for (int b = 0; b < B; ++b)
+      for (int t0 = 0; t0 < T; t0 += fb.tb)
+        if ((st = run(b, b * T + t0, 1, std::min(fb.tb, T - t0))) != CSA2_OK) return st;
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -913,10 +913,13 @@ __global__ __launch_bounds__(kMqThreads) void k_idx_scan_mq(
 bool scan_multi_query(int T, int n_max) { return T >= kScanMqMinT && n_max <= kMqMaxPositions; }
 
 int scan_mq_chunk(int n_max, int B, int T) {
-  // 4096 positions, or fewer (down to 1024) while the grid is under ~1024 workgroups
+  // 4096 positions, or fewer (down to 1024) while the grid is under ~1024 workgroups, as long as
+  // a query's positions stay within 256 chunks (the pool takes at most 4096 units)
   const long long groups = (long long)B * ((T + kMqQueries - 1) / kMqQueries);
   int c = kMqMaxChunk;
-  while (c > 1024 && (long long)((n_max + c - 1) / c) * groups < 1024) c /= 2;
+  while (c > 1024 && ((long long)n_max + c / 2 - 1) / (c / 2) <= 256 &&
+         (long long)((n_max + c - 1) / c) * groups < 1024)
+    c /= 2;
   return c;
 }
 

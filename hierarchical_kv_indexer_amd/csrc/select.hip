@@ -1223,6 +1223,7 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
     j.out_score = topk_score;
     return launch_topk(pool_pos, pool_len, cap_out, Q, K, j, TopkJob{}, s);
   }
+  if (n_units > kUnitsPerThread * kNT || cap_out > kMaxPool) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_pool, dim3(Q), dim3(kNT), 0, s, lists, cuts, n_units, blocks_per_unit, blkkey, nb_max,
                      n_visible, n_max, P, pool_pos, cap_out, pool_len, scores, K, topk_idx, topk_score);
   return hipGetLastError();

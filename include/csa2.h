@@ -118,13 +118,20 @@ csa2_status csa2_index_scores(const uint8_t* idx_k, const uint8_t* idx_k_scales,
  *   workspace  device scratch of at least csa2_index_full_workspace(...) bytes
  * Supported: block_size == 8, 1 <= top_k <= 2048, top_k <= pool_blocks*block_size when
  * pool_blocks > 0, pool_blocks*block_size <= 16384, n_max <= 2^21 (2^23 for csa2_index_scores),
- * n_max <= k_rows_per_seq. */
+ * n_max <= k_rows_per_seq.
+ * csa2_index_full works through the queries in batches whose scores, block keys and lists fit in
+ * about 48 MiB (runs of a multiple of 16 queries of one sequence, or whole sequences), reusing
+ * one batch's workspace, so its workspace does not grow with the number of queries beyond one
+ * batch; the results are those of one pass over every query. */
 size_t csa2_index_full_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k);
+/* Workspace of the separate stages below, which carry every query's scores and block keys from
+ * one call to the next (the unbatched intermediates of csa2_index_full). */
+size_t csa2_index_stages_workspace(int B, int T, int n_max, int block_size, int pool_blocks, int top_k);
 
 /* The stages of csa2_index_full as separate calls.  They take the same arguments and the same
- * workspace, which carries the scan's scores and block keys (and, with pool_blocks == 0, the
- * internal pool) from one stage to the next; enqueue them in this order with identical shape
- * arguments.  csa2_index_pool and csa2_index_topk may run on different streams as long as
+ * workspace of csa2_index_stages_workspace(...) bytes, which carries the scan's scores and block
+ * keys (and, with pool_blocks == 0, the internal pool) from one stage to the next; enqueue them in
+ * this order with identical shape arguments.  csa2_index_pool and csa2_index_topk may run on different streams as long as
  * each starts after the previous stage has finished (e.g. the Top-K of the Full layer on one
  * stream while csa2_reindex scores the same pool on another).
  *   csa2_index_scan:   query preparation, the scan and the block maxima

@@ -87,7 +87,7 @@ def gpu_index_full_blocks(inp, B, T, n_max, pool_blocks, top_k, block_score, blo
     cap = pool_blocks * block
     pool_pos, pool_len = empty((B, T, cap), torch.int32), empty((B, T), torch.int32)
     idx, sc = empty((B, T, top_k), torch.int32), empty((B, T, top_k), torch.float32)
-    ws_bytes = H.csa2_index_full_workspace(B, T, n_max, block, pool_blocks, top_k)
+    ws_bytes = H.csa2_index_stages_workspace(B, T, n_max, block, pool_blocks, top_k)
     ws = empty((ws_bytes,), torch.uint8)
     k, ks, rows = keys(inp)
     nv = dev(inp["n_visible"])

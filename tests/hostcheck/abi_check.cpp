@@ -62,7 +62,7 @@ int main() {
         for (int P : Ps)
           for (int K : Ks) {
             if ((int64_t)B * T > 65535) continue;
-            acc += csa2_index_full_workspace(B, T, N, 8, P, K);
+            acc += csa2_index_full_workspace(B, T, N, 8, P, K) + csa2_index_stages_workspace(B, T, N, 8, P, K);
             for (int L = 0; L <= 4; L += 2) acc += csa2_index_chain_workspace(B, T, N, 8, P, K, L);
           }
   for (int L : {1, 4, 64})
@@ -95,7 +95,7 @@ int main() {
   // ---- Full layer and its stages
   for (int P : {0, 64, 2048}) {
     const int N = P == 2048 ? (1 << 20) : 9000, K = 64;
-    const size_t w = csa2_index_full_workspace(2, 3, N, 8, P, K);
+    const size_t w = csa2_index_stages_workspace(2, 3, N, 8, P, K);
     EXPECT(CSA2_ERR_HIP, csa2_index_full(u8, nullptr, N, u16, f32, i32, 2, 3, N, 8, P, K, o32, o32, o32, of32, ws,
                                          w, nullptr));
     EXPECT(CSA2_ERR_WORKSPACE, csa2_index_full(u8, nullptr, N, u16, f32, i32, 2, 3, N, 8, P, K, o32, o32, o32,

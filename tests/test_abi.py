@@ -36,13 +36,32 @@ def test_workspace_sizes(H):
     assert H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512) >= (1 << 20) * 4 + (1 << 17) * 4
     assert H.csa2_reindex_workspace(4, 1, 1, 16384, 512) >= 4 * 16384 * 4
     assert H.csa2_index_full_workspace(0, 1, 10, 8, 4, 4) == 0
-    full = H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512)
+    full = H.csa2_index_stages_workspace(1, 1, 1 << 20, 8, 2048, 512)
+    assert H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512) == full   # one batch
     # the chain adds, after the Full workspace, the slot scores and unit lists of the Full layer's
     # Top-K item and of each Reindex layer (16384 fp32 scores, 512 units of 32 slots x 5 keys each)
     per_item = 16384 * 4 + 512 * 4 * 8 + 512 * 8
     assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 2048, 512, 0) >= full + per_item
     assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 2048, 512, 4) >= full + 5 * per_item
     assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 0, 512, 4) == 0     # the chain needs a pool
+
+
+def test_full_workspace_is_batched(H):
+    """csa2_index_full works through the queries in batches: 4096 causal queries over 32768
+    entries (Top-512, no pool) run as 16 batches of 256 queries (one per CU) in under 64 MiB,
+    where the separate stages, which keep every query's scores, need over 512 MiB.  Batches too
+    small to fill the GPU are used only past the spill cap (1 GiB)."""
+    MiB = 1 << 20
+    assert H.csa2_index_full_workspace(1, 4096, 32768, 8, 0, 512) <= 64 * MiB
+    assert H.csa2_index_stages_workspace(1, 4096, 32768, 8, 0, 512) >= 512 * MiB
+    # 256 queries at 2^19 entries: batches of 16 would leave most CUs idle, so one batch
+    assert H.csa2_index_full_workspace(1, 256, 1 << 19, 8, 0, 512) == H.csa2_index_stages_workspace(1, 256, 1 << 19, 8, 0, 512)
+    # many short sequences: batches of whole sequences, at least 256 queries each
+    assert H.csa2_index_full_workspace(64, 8, 131072, 8, 2048, 512) < 0.6 * H.csa2_index_stages_workspace(64, 8, 131072, 8, 2048, 512)
+    # past the spill cap (2048 queries at 2^20 entries: 8 GiB of scores) batches of 16 queries
+    assert H.csa2_index_full_workspace(1, 2048, 1 << 20, 8, 0, 512) <= 96 * MiB
+    # small shapes: one batch, the stages' workspace
+    assert H.csa2_index_full_workspace(2, 3, 5000, 8, 64, 256) == H.csa2_index_stages_workspace(2, 3, 5000, 8, 64, 256)
 
 
 FAKE = 1 << 20   # a 16-byte aligned non-null value; validation fails before it is used
@@ -206,6 +225,6 @@ def test_noalloc_chain_rejects(H):
 
 
 def test_scan_blocks_rejects_unknown_block_score(H):
-    ws = H.csa2_index_full_workspace(1, 1, 4096, 8, 64, 64)
+    ws = H.csa2_index_stages_workspace(1, 1, 4096, 8, 64, 64)
     expect(H, 1, lambda: H.csa2_index_scan_blocks(FAKE, None, 4096, FAKE, FAKE, FAKE, 1, 1, 4096, 8, 64, 64, 3,
                                                   FAKE, ws))

@@ -212,6 +212,7 @@ def check_full(w, inp, gpu, b, t):
     (20003, 128, 256, None),         # ragged, several scan WGs
     (5000, 64, 512, [5000, 300, 511, 0]),   # n_vis < K, n_vis = 0, pool larger than nb
     (9000, 128, 256, 20),            # multi-query scan: 20 queries, ragged causal visibility
+    (270000, 0, 512, 16),            # one group of 16 queries over more than 256 chunks of 1024
 ])
 def test_index_full_parity(N, P, K, nv):
     T = 1 if nv is None else (nv if isinstance(nv, int) else len(nv))
@@ -223,6 +224,34 @@ def test_index_full_parity(N, P, K, nv):
         inp["n_visible"] = np.array(nv, np.int32).reshape(1, T)
     gpu = G.gpu_index_full(inp, 1, T, N, P, K)
     for t in range(T):
+        check_full(w, inp, gpu, 0, t)
+
+
+def test_index_full_batches_match_one_pass():
+    """csa2_index_full in its smallest workspace (512 causal queries over 65536 entries, no pool,
+    Top-512: two batches of 256 queries) equals the same call with room for every query at once,
+    output for output; sampled queries on both sides of the batch boundary against the oracle."""
+    import hierarchical_kv_indexer_amd as H
+    N, T, K = 65536, 512, 512
+    w = small(T=T, N=N, pool_blocks=0, top_k=K, seed=3800)
+    inp = workloads.make_inputs(w, with_attention=False)
+    inp["n_visible"] = ragged_visibility(1, T, N, 13)
+    k, ks, rows = G.keys(inp)
+    q, hw, nv = G.dev(inp["idx_q"]), G.dev(inp["head_w"]), G.dev(inp["n_visible"])
+    small_ws = H.csa2_index_full_workspace(1, T, N, 8, 0, K)
+    big_ws = H.csa2_index_stages_workspace(1, T, N, 8, 0, K)
+    assert small_ws < big_ws
+    outs = []
+    for wsb in (small_ws, big_ws):
+        ws = G.empty((wsb,), torch.uint8)
+        idx = G.empty((1, T, K), torch.int32)
+        sc = G.empty((1, T, K), torch.float32)
+        H.csa2_index_full(k, ks, rows, q, hw, nv, 1, T, N, 8, 0, K, None, None, idx, sc, ws, wsb)
+        outs.append((G.host(idx), G.host(sc)))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    gpu = {"topk": outs[0][0], "topk_score": outs[0][1]}
+    for t in (0, 255, 256, 511):
         check_full(w, inp, gpu, 0, t)
 
 
@@ -338,7 +367,7 @@ def test_stage_entries_match_index_full(P):
     pool_len = G.empty((1, T), torch.int32) if P else None
     idx = G.empty((1, T, K), torch.int32)
     sc = G.empty((1, T, K), torch.float32)
-    wsb = H.csa2_index_full_workspace(1, T, N, 8, P, K)
+    wsb = H.csa2_index_stages_workspace(1, T, N, 8, P, K)
     ws = G.empty((wsb,), torch.uint8)
     k, q, hw, nv = G.dev(inp["idx_k"]), G.dev(inp["idx_q"]), G.dev(inp["head_w"]), G.dev(inp["n_visible"])
     H.csa2_index_scan(k, None, N, q, hw, nv, 1, T, N, 8, P, K, ws, wsb)
