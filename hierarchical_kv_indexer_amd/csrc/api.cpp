@@ -556,6 +556,7 @@ csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int6
   ListWs lw;
   carve_lists(workspace, L * Q, pool_cap, &lw);
   csa2_status st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, nullptr, 0, 0,
+                                                   nullptr, nullptr,
                                                    pool_pos, pool_len, pool_cap, L, Q, T, lw.slot_scores, lw.lists,
                                                    lw.cuts, s),
                              "reindex score launch");
@@ -625,10 +626,15 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   ListWs lw;
   carve_chain(workspace, p, n_max, L, &w, &lw);
   hipStream_t s = (hipStream_t)stream;
+  // With the one-query scan in the same call, the Full layer's pool slots are scored again from
+  // their keys (the scan's own arithmetic, so the same scores) instead of storing every
+  // position's score; the split calls and the multi-query scan (another summation order) keep
+  // the stored scores.
+  const bool rescore = do_scan && !p.multi_query;
   if (do_scan && n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
-                                         w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk, p.n_wg, p.multi_query,
-                                         csa2::kBlockMax, p.upw, w.clists, w.ccuts, s),
+                                         rescore ? nullptr : w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk,
+                                         p.n_wg, p.multi_query, csa2::kBlockMax, p.upw, w.clists, w.ccuts, s),
                    "index scan launch");
     if (st != CSA2_OK) return st;
   }
@@ -637,8 +643,8 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   // the Full layer's pool scores (gathered from the scan's scores) and the Reindex layers'
   // scores, each chunk with its list; then every layer's Top-K in one launch
   st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, L ? ri_q : nullptr, L ? ri_w : nullptr,
-                                       w.scores, n_max, p.Q, pool_pos, pool_len, p.cap, L, p.Q, T, lw.slot_scores,
-                                       lw.lists, lw.cuts, s),
+                                       rescore ? nullptr : w.scores, n_max, p.Q, idx_q, head_w, pool_pos, pool_len,
+                                       p.cap, L, p.Q, T, lw.slot_scores, lw.lists, lw.cuts, s),
                  "pool scoring launch");
   if (st != CSA2_OK) return st;
   st = hip_check(csa2::launch_topk_lists(lw.lists, lw.cuts, lw.slot_scores, pool_pos, pool_len, p.cap, p.Q, top_k,

@@ -29,6 +29,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+// The same product with fp16 inputs.
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+
+// Two E2M1 codes (byte SEL of `w`, low nibble first) times a scale held twice in `s` -> two fp16.
+// With an E4M3 scale the product has at most 6 significant bits within [2^-10, 2688]: exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1x2_scaled_to_f16x2(uint32_t w, h2 s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL) * s);
+}
+// Two E4M3 bytes (the low or high 16 bits of `w`) -> two fp16 (exact).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+// 8 E4M3 bytes (two dwords) -> 8 fp16, byte order preserved.
+__device__ __forceinline__ u32x4 e4m3x8_to_f16x8(uint32_t d0, uint32_t d1) {
+  return u32x4{e4m3x2_to_f16x2<false>(d0), e4m3x2_to_f16x2<true>(d0), e4m3x2_to_f16x2<false>(d1),
+               e4m3x2_to_f16x2<true>(d1)};
+}
+
 // Two E4M3 bytes (the low or high 16 bits of `w`) -> two bf16 (exact: E4M3 has 4 significant
 // bits and its exponent range lies inside bf16's).
 template <bool HI>

@@ -48,7 +48,7 @@ __host__ __device__ inline int ri_chunks(int pool_cap) { return (pool_cap + kRiC
 __host__ __device__ inline int ri_units(int pool_cap) { return ri_chunks(pool_cap) * (kRiChunk / kRiUnit); }
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const float* full_scores, int64_t full_stride, int full_items,
-                           const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
+                           const uint16_t* full_q, const float* full_w, const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
                            float* slot_scores, uint64_t* lists, uint64_t* cuts, hipStream_t s);
 
 // select.hip

@@ -163,15 +163,6 @@ __device__ __forceinline__ void load_ctx(TileCtx& cx, const uint16_t* qlds, cons
 // canonicalisation).
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Score of this lane's row (column j of the tile); every lane of a column gets the same value.
-// The 8 heads of a lane are summed in a fixed order, then the four k-groups are combined as
-// (g0 + g1) + (g2 + g3), identically on every lane.
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
-}
-
 // Score of this lane's row from the key operands b[c] (bf16, or fp16 with kF16), laid out as the
 // query operands.  The 8 heads of a lane are summed in a fixed order, then the four k-groups are
 // combined as (g0 + g1) + (g2 + g3), identically on every lane.
@@ -247,10 +238,6 @@ __device__ __forceinline__ void load_ctx_fp4(TileCtx& cx, const uint16_t* qlds, 
 // conversion, times the E4M3 scale in packed fp16: every product has at most 6 significant bits
 // within [2^-10, 2688], so it is exact) and the query operands are fp16 too, so the contraction
 // runs on the fp16 MFMA with exact products.
-template <int SEL>
-__device__ __forceinline__ uint32_t e2m1x2_scaled_to_f16x2(uint32_t w, h2 s) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL) * s);
-}
 // 16 code bytes (channels 32g .. 32g+31) and the two scale bytes of their groups -> fp16 operands.
 __device__ __forceinline__ void fp4_operands(u32x4 codes, uint32_t sc2, u32x4 (&b)[4]) {
   const h2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc2, 1.0f, false);   // groups 2g, 2g+1 (exact)
@@ -598,18 +585,19 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   }
   // stores: the chunk's scores and block keys (coalesced), its unit lists and its chunk list
   constexpr int kSt = kMaxScanChunk / kFullThreads;
+  const int nsc = scores ? npos : 0;              // scores == nullptr: block keys and lists only
   float* srow = scores + (size_t)q * n_max + p_begin;
   float sv[kSt];
 #pragma unroll
   for (int u = 0; u < kSt; ++u) {
     const int i = u * kFullThreads + threadIdx.x;
-    sv[u] = i < npos ? sbuf[i] : 0.f;
+    sv[u] = i < nsc ? sbuf[i] : 0.f;
   }
   const uint32_t bk = (int)threadIdx.x < nblk ? wkeys[threadIdx.x] : 0u;
 #pragma unroll
   for (int u = 0; u < kSt; ++u) {
     const int i = u * kFullThreads + threadIdx.x;
-    if (i < npos) srow[i] = sv[u];
+    if (i < nsc) srow[i] = sv[u];
   }
   if (blkkey && (int)threadIdx.x < nblk) blkkey[(size_t)q * nb_max + p_begin / kBlock + threadIdx.x] = bk;
   if (!clists && lists && lane % lanes == 0 && lane / lanes < upw) {
@@ -996,7 +984,9 @@ static_assert(kScanThreads / 64 * kRiTilesPerWave * 16 == kRiChunk, "a workgroup
 
 // grid (n_chunks, items): item it scores pool slots [x*kRiChunk, (x+1)*kRiChunk) of its query.
 //   it <  full_items  the Full layer of query q = it: the scan's score of each slot's position,
-//                     full_scores[q * full_stride + pos] (no keys are read);
+//                     full_scores[q * full_stride + pos] (no keys are read), or with full_scores
+//                     null the slot's key scored with the Full layer's query full_q[q] and weights
+//                     full_w[q] (the arithmetic of k_idx_scan, so the same score);
 //   it >= full_items  Reindex layer r / Q of query q = r % Q (r = it - full_items): the slot's
 //                     indexer key scored with that layer's query idx_q[r] and weights head_w[r].
 // Writes slot_scores[it][slot] for slots < pool_len holding a position in [0, k_rows) (others are
@@ -1010,11 +1000,12 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
     const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
     const float* __restrict__ full_scores, int64_t full_stride, int full_items,
+    const uint16_t* __restrict__ full_q, const float* __restrict__ full_w,
     const int32_t* __restrict__ pool_pos, const int32_t* __restrict__ pool_len, int cap, int Q, int T,
     float* __restrict__ slot_scores, uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
   __shared__ __attribute__((aligned(16))) uint16_t qlds[kIdxHeads * kIdxDim];
   const int it = blockIdx.y;
-  const bool full = it < full_items;
+  const bool full = it < full_items, gather = full && full_scores != nullptr;
   const int r = it - full_items, q = full ? it : r % Q, b = q / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -1029,7 +1020,7 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
   // this lane's candidate for the unit's list: slot sw + lane (lanes < 32)
   float my_sc = 0.f;
   int my_pos = -1;
-  if (full) {
+  if (gather) {
     const int64_t n_rows = min(k_rows, full_stride);
     const int slot = sw + lane;
     int pos = (lane < kRiUnit && slot < cap) ? pp[slot] : -1;
@@ -1048,7 +1039,8 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
       const int slot = sw + 16 * u + j;
       pos[u] = slot < cap ? pp[slot] : -1;
     }
-    stage_query<kScanThreads, kFp4>(idx_q + (size_t)r * kIdxHeads * kIdxDim, qlds);
+    stage_query<kScanThreads, kFp4>(full ? full_q + (size_t)q * kIdxHeads * kIdxDim
+                                         : idx_q + (size_t)r * kIdxHeads * kIdxDim, qlds);
     const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
     const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
     TileRaw<kFp4> raw[kRiTilesPerWave];
@@ -1065,7 +1057,7 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
     for (int u = 0; u < kRiTilesPerWave; ++u) ok[u] = ok[u] && sw + 16 * u + j < s_end;
     lds_barrier();
     TileCtx cx;
-    key_ctx<kFp4>(cx, qlds, head_w + (size_t)r * kIdxHeads);
+    key_ctx<kFp4>(cx, qlds, full ? full_w + (size_t)q * kIdxHeads : head_w + (size_t)r * kIdxHeads);
     float sc[kRiTilesPerWave];
 #pragma unroll
     for (int u = 0; u < kRiTilesPerWave; ++u) sc[u] = key_score<kFp4>(cx, raw[u]);
@@ -1119,18 +1111,22 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
 
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
                            const float* head_w, const float* full_scores, int64_t full_stride, int full_items,
+                           const uint16_t* full_q, const float* full_w,
                            const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
                            float* slot_scores, uint64_t* lists, uint64_t* cuts, hipStream_t s) {
   const int n_chunks = (pool_cap + kRiChunk - 1) / kRiChunk;
   const int items = full_items + L * Q;
   if (items == 0) return hipSuccess;
+  if (full_items > 0 && !full_scores && (!full_q || !full_w)) return hipErrorInvalidValue;
   if (idx_ks)
     hipLaunchKernelGGL(k_ri_score<true>, dim3(n_chunks, items), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, full_scores, full_stride, full_items, pool_pos, pool_len, pool_cap, Q, T,
+                       idx_q, head_w, full_scores, full_stride, full_items, full_q, full_w, pool_pos, pool_len,
+                       pool_cap, Q, T,
                        slot_scores, lists, cuts);
   else
     hipLaunchKernelGGL(k_ri_score<false>, dim3(n_chunks, items), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, full_scores, full_stride, full_items, pool_pos, pool_len, pool_cap, Q, T,
+                       idx_q, head_w, full_scores, full_stride, full_items, full_q, full_w, pool_pos, pool_len,
+                       pool_cap, Q, T,
                        slot_scores, lists, cuts);
   return hipGetLastError();
 }
