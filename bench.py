@@ -435,7 +435,8 @@ def bench_encoder(args, w) -> int:
     return 0
 
 
-KERNEL_NAMES = ("k_idx_scan", "k_pool", "k_ri_score", "k_topk", "k_sparse_attn", "k_attn_combine")
+KERNEL_NAMES = ("k_idx_scan", "k_pool_chunks", "k_pool", "k_ri_score", "k_topk_lists", "k_topk", "k_sparse_attn",
+                "k_attn_combine")
 
 
 def summarize_trace(trace_dir: str, workload: str, steps: int) -> int:

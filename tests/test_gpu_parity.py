@@ -465,6 +465,23 @@ def test_reindex_user_pools_with_invalid_entries():
         G.assert_topk_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"user pool t{t}")
 
 
+def test_reindex_user_pool_of_odd_capacity():
+    """A caller pool of 1001 slots (rows not 16-byte aligned, a last unit of 9 slots) with
+    lengths that end inside, at and before that unit; against the oracle."""
+    w = small("reindex_pool_256k", T=3, N=30000, user_pool=1001, top_k=256, seed=67)
+    inp = workloads.make_inputs(w, with_attention=False)
+    pp = inp["pool_pos"].copy()
+    pl = inp["pool_len"].copy()
+    pl[0, :] = [1001, 995, 990]
+    gpu = G.gpu_reindex(inp, 1, 3, pp, pl, 256)
+    for t in range(3):
+        pool = pp[0, t, :pl[0, t]]
+        pool = pool[(pool >= 0) & (pool < w.N)]
+        r = O.reindex_layer(inp["idx_k"][0], inp["ri_q"][0, 0, t], inp["ri_w"][0, 0, t], pool, 256)
+        sc = dict(zip(pool.tolist(), r["scores"].tolist()))
+        G.assert_topk_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"odd pool t{t}")
+
+
 def test_reindex_user_pool_with_repeated_positions():
     """A caller pool listing some positions two or three times: copies rank like the position
     (score desc, position asc, counted with repeats), as the oracle's stable ranking orders them,
