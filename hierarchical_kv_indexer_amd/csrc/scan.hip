@@ -380,7 +380,13 @@ template <int J>
 __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   if constexpr (J == 1) return dpp_mov<0xB1>(v);                       // quad_perm [1,0,3,2]
   else if constexpr (J == 2) return dpp_mov<0x4E>(v);                  // quad_perm [2,3,0,1]
-  else if constexpr (J == 4 || J == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (J << 10));
+  else if constexpr (J == 4 || J == 8) {
+    // row_shl:J into the lanes whose bit J is clear (banks 0, 2 for J = 4; 0, 1 for J = 8), then
+    // row_shr:J into the others
+    constexpr int kLo = J == 4 ? 0x5 : 0x3;
+    const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x100 | J, 0xF, kLo, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)t, (int)v, 0x110 | J, 0xF, 0xF ^ kLo, false);
+  }
   else if constexpr (J == 16) return swap16(v);
   else return swap32(v);
 }
