@@ -626,11 +626,11 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   ListWs lw;
   carve_chain(workspace, p, n_max, L, &w, &lw);
   hipStream_t s = (hipStream_t)stream;
-  // With the one-query scan in the same call, the Full layer's pool slots are scored again from
-  // their keys (the scan's own arithmetic, so the same scores) instead of storing every
-  // position's score; the split calls and the multi-query scan (another summation order) keep
-  // the stored scores.
-  const bool rescore = do_scan && !p.multi_query;
+  // With the one-query scan over E4M3 keys in the same call, the Full layer's pool slots are
+  // scored again from their keys (the scan's own arithmetic, so the same scores) instead of
+  // storing every position's score; the split calls, FP4 keys (the scan sums 32-row tiles) and
+  // the multi-query scan (other summation orders) keep the stored scores.
+  const bool rescore = do_scan && !p.multi_query && idx_k_scales == nullptr;
   if (do_scan && n_max > 0) {
     st = hip_check(csa2::launch_idx_scan(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, n_visible, p.Q, T, n_max,
                                          rescore ? nullptr : w.scores, w.blkkey, p.nb_stride, w.lists, w.cuts, p.chunk,

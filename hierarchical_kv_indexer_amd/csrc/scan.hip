@@ -24,6 +24,8 @@
 // with exact products.  Lane (j, g) then takes channels [32g, 32g+32) of row j: its 16 code
 // bytes and the row's 8 scale bytes (two of which it uses), and MFMA chunk c covers its
 // channels 32g + 8c .. +7 on both operands.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -314,11 +316,65 @@ __device__ __forceinline__ uint32_t block_key(float sc, bool valid) {
   }
 }
 
+// ---------------------------------------------------------------------------- 32-row FP4 tiles
+
+// The one-query scan over FP4 keys scores 32 rows per tile with 32x32x16 fp16 MFMAs (32 heads x
+// 32 rows x 16 channels): lane l takes row l % 32 and the half h = l / 32 of its channels,
+// [64h, 64h + 64), so its 32 code bytes and the 4 scale bytes of its groups are contiguous, and
+// K-step c covers channels 64h + 8c .. +7 (the query operands follow the same order).  Each lane
+// then holds 16 heads of its row, so the head sum is 16 fused multiply-adds and one exchange with
+// lane l ^ 32.
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+struct TileRaw32 {
+  u32x4 c0, c1;          // code bytes 32h .. 32h+31 of the row
+  uint32_t sc;           // scale bytes 4h .. 4h+3
+};
+struct Ctx32f {
+  u32x4 qa[8];           // fp16 query operands: head l % 32, channels 64h + 8c .. +7 in qa[c]
+  float w[16];           // weights of the heads output v holds: 8(v/4) + 4h + v%4
+};
+__device__ __forceinline__ void load_row32(const uint8_t* __restrict__ kseq, const uint8_t* __restrict__ sseq,
+                                           int64_t p, TileRaw32& r) {
+  const int h = (threadIdx.x >> 5) & 1;
+  const u32x4* cp = (const u32x4*)(kseq + p * (kIdxDim / 2) + 32 * h);
+  r.c0 = cp[0];
+  r.c1 = cp[1];
+  r.sc = *(const uint32_t*)(sseq + p * (kIdxDim / 16) + 4 * h);
+}
+__device__ __forceinline__ void load_ctx32f(Ctx32f& cx, const uint16_t* qlds, const float* __restrict__ w) {
+  const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) cx.qa[c] = *(const u32x4*)(qlds + r * kIdxDim + 64 * h + 8 * c);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) cx.w[v] = w[8 * (v >> 2) + 4 * h + (v & 3)];
+}
+__device__ __forceinline__ float score32f(const Ctx32f& cx, const TileRaw32& r) {
+  const h2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, false);   // groups 4h, 4h+1
+  const h2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, true);    // groups 4h+2, 4h+3
+  const uint32_t wd[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+  f32x16_t a;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) a[v] = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {                       // word c: channels 64h + 8c .. +7
+    const _Float16 sv = c < 2 ? s01.x : (c < 4 ? s01.y : (c < 6 ? s23.x : s23.y));
+    const h2 sc = h2{sv, sv};
+    const u32x4 bk = {e2m1x2_scaled_to_f16x2<0>(wd[c], sc), e2m1x2_scaled_to_f16x2<1>(wd[c], sc),
+                      e2m1x2_scaled_to_f16x2<2>(wd[c], sc), e2m1x2_scaled_to_f16x2<3>(wd[c], sc)};
+    a = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, cx.qa[c]), __builtin_bit_cast(h8, bk), a,
+                                                0, 0, 0);
+  }
+  float p = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p = fmaf(cx.w[v], relu_bits(a[v]), p);
+  return sum_xor32(p);
+}
+
 // ---------------------------------------------------------------------------- Full scan
 
-// Tiles per pipeline stage of a wave (6 FP4 tiles measured no faster than 3: the loop is bound by
-// its instruction issue, not by the bytes in flight).
-template <bool kFp4> constexpr int kScanU = 3;
+// Tiles per pipeline stage of a wave: 3 tiles of 16 rows for E4M3 keys, 2 of 32 rows for FP4 keys
+// (the register budget of 16 waves per workgroup).
+template <bool kFp4> constexpr int kScanU = kFp4 ? 2 : 3;
 constexpr int kFullWaves = kFullThreads / 64;   // 16
 constexpr int kMaxScanChunk = 8192;             // positions of a one-query scan workgroup (LDS staging)
 static_assert(kFullWaves == kScanUnitsPerWg, "each wave lists the units of its own range");
@@ -489,7 +545,9 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   const int p_begin = blockIdx.x * chunk;
   const int p_end = min(p_begin + chunk, nv);
   const int npos = max(0, p_end - p_begin);
-  const int ntiles = (npos + 15) >> 4;
+  constexpr int kTR = kFp4 ? 32 : 16;             // rows per tile
+  const int trow = kFp4 ? (lane & 31) : j;         // this lane's row of a tile
+  const int ntiles = (npos + kTR - 1) / kTR;
   const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
   const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
   const int plast = npos > 0 ? p_end - 1 : 0;
@@ -503,13 +561,15 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
   // stage past the chunk would make the loop's load waits count conservatively across the skip,
   // so each stage would wait for the next one's loads.)
   constexpr int kU = kScanU<kFp4>;
-  TileRaw<kFp4> rA[kU], rB[kU];
-  auto load_stage = [&](TileRaw<kFp4>(&r)[kU], int t0) {
+  using Raw = typename std::conditional<kFp4, TileRaw32, TileRaw<false>>::type;
+  Raw rA[kU], rB[kU];
+  auto load_stage = [&](Raw(&r)[kU], int t0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int t = t0 + u;
-      const int p = min(p_begin + 16 * (t < ntiles ? phys(t) : t) + j, plast);
-      load_key<kFp4>(kseq, sseq, p, g, r[u]);
+      const int p = min(p_begin + kTR * (t < ntiles ? phys(t) : t) + trow, plast);
+      if constexpr (kFp4) load_row32(kseq, sseq, p, r[u]);
+      else load_key<false>(kseq, sseq, p, g, r[u]);
     }
   };
   int tA = wave * kU;                              // first stage of each wave: static
@@ -519,24 +579,33 @@ __global__ __launch_bounds__(kFullThreads) void k_idx_scan(
     stage_query<kFullThreads, kFp4>(idx_q + (size_t)q * kIdxHeads * kIdxDim, qlds);
     if (threadIdx.x == 0) *ctr = kFullWaves * kU;
     lds_barrier();
-    TileCtx cx;
-    key_ctx<kFp4>(cx, qlds, head_w + (size_t)q * kIdxHeads);
+    using Ctx = typename std::conditional<kFp4, Ctx32f, TileCtx>::type;
+    Ctx cx;
+    if constexpr (kFp4) load_ctx32f(cx, qlds, head_w + (size_t)q * kIdxHeads);
+    else key_ctx<false>(cx, qlds, head_w + (size_t)q * kIdxHeads);
     auto grab = [&]() {                            // next stage of this wave (monotonic)
       int v = 0;
       if (lane == 0) v = atomicAdd(ctr, kU);
       return __builtin_amdgcn_readfirstlane(v);
     };
-    auto compute_stage = [&](const TileRaw<kFp4>(&r)[kU], int t0) {
+    auto compute_stage = [&](const Raw(&r)[kU], int t0) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int t = t0 + u;
-        const float sc = key_score<kFp4>(cx, r[u]);
+        float sc;
+        if constexpr (kFp4) sc = score32f(cx, r[u]);
+        else sc = key_score<false>(cx, r[u]);
         if (t < ntiles) {
           const int tp = phys(t);
-          const bool valid = 16 * tp + j < npos;
+          const bool valid = kTR * tp + trow < npos;
           const uint32_t key = block_key<kBS>(sc, valid);
-          if (g == 0) sbuf[16 * tp + j] = sc;
-          if ((lane & 0x37) == 0) wkeys[2 * tp + (lane >> 3)] = key;   // lanes 0, 8
+          if constexpr (kFp4) {
+            if (lane < 32) sbuf[32 * tp + trow] = sc;
+            if ((lane & 0x27) == 0) wkeys[4 * tp + (lane >> 3)] = key;   // lanes 0, 8, 16, 24
+          } else {
+            if (g == 0) sbuf[16 * tp + j] = sc;
+            if ((lane & 0x37) == 0) wkeys[2 * tp + (lane >> 3)] = key;   // lanes 0, 8
+          }
         }
       }
     };
