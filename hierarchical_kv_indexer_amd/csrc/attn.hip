@@ -147,12 +147,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
   // then hold 16 different rows (one 16-byte slot each), which keeps the dequantised stores free
   // of bank conflicts (with four quarters of one row per pass they conflict four ways)
   const int my_row = 16 * (tid >> 6) + (tid & 15), quarter = (tid >> 4) & 3;
-  // main-row index of this thread's row in chunk c (-1: none), prefetched one chunk ahead
+  // index-set entry of this thread's row in chunk c (-1: none), prefetched one chunk ahead and
+  // checked only where its row is loaded, so nothing waits for it in between
   auto row_index = [&](int c) {
     const int slot = s0 + c * kRows + my_row;
-    if (slot >= s1 || slot >= k) return -1;
-    const int pos = idx[slot];
-    return (pos >= 0 && (int64_t)pos < kv_rows) ? pos : -1;
+    return (slot < s1 && slot < k) ? idx[slot] : -1;
   };
   int pos_cur = nchunks > 0 ? row_index(0) : -1;
   int pos_next = nchunks > 1 ? row_index(1) : -1;
@@ -178,7 +177,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
     r.kind = 0;
     if (slot < s1) {
       if (slot < k) {
-        if (pos >= 0) {
+        if (pos >= 0 && (int64_t)pos < kv_rows) {
           const u32x4* cp = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 64 * quarter);
 #pragma unroll
           for (int i = 0; i < 4; ++i) r.d[i] = cp[i];
@@ -379,9 +378,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
   const int my_row = 8 * (tid >> 6) + (tid & 7), eighth = (tid >> 3) & 7;
   auto row_index = [&](int c) {
     const int slot = s0 + c * kRows + my_row;
-    if (slot >= s1 || slot >= k) return -1;
-    const int pos = idx[slot];
-    return (pos >= 0 && (int64_t)pos < kv_rows) ? pos : -1;
+    return (slot < s1 && slot < k) ? idx[slot] : -1;
   };
   int pos_a = nchunks > 0 ? row_index(0) : -1;
   int pos_b = nchunks > 1 ? row_index(1) : -1;
@@ -410,7 +407,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     r.kind = 0;
     if (slot < s1) {
       if (slot < k) {
-        if (pos >= 0) {
+        if (pos >= 0 && (int64_t)pos < kv_rows) {
           const u32x4* cp = (const u32x4*)(codes_seq + (size_t)pos * kKvCodeBytes + 32 * eighth);
           r.d[0] = cp[0];
           r.d[1] = cp[1];
