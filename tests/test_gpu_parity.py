@@ -542,6 +542,36 @@ def test_attention_parity_on_oracle_sets(H):
     assert worst < 1e-2
 
 
+@pytest.mark.parametrize("H,Bq", [(16, 1), (16, 2), (64, 1), (64, 2)])
+def test_attention_skips_out_of_range_entries(H, Bq):
+    """Index-set entries past the cache's rows or negative (not only -1) are empty slots, in both
+    attention kernels, with row splits (one query per sequence) and without (two)."""
+    w = small(B=Bq, T=2, N=3000, H=H, layer_set=(0, 1), n_reindex=1, pool_blocks=64, top_k=256, seed=91)
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(11)
+    sets = np.full((2, Bq, 2, 256), -1, np.int32)
+    for s in range(2):
+        for b in range(Bq):
+            for t in range(2):
+                e = rng.choice(w.N, 256, replace=False).astype(np.int64)
+                bad = rng.random(256) < 0.3
+                e[bad] = rng.choice([w.N, w.N + 1, 10 ** 9, -2, -(2 ** 31)], bad.sum())
+                sets[s, b, t] = e.astype(np.int32)
+    out, lse = G.gpu_attention(inp, w, sets)
+    worst = 0.0
+    for l in range(w.L):
+        for b in range(Bq):
+            for t in range(2):
+                e = sets[w.layer_set[l], b, t].astype(np.int64)
+                kept = np.where((e >= 0) & (e < w.N), e, -1)       # the header's empty slots
+                rows = O.attention_rows(inp["kv_codes"][b], inp["kv_scales"][b], kept,
+                                        inp["swa"][l, b], int(inp["swa_end"][b, t]), w.swa_window)
+                o, ls = O.attention(inp["q"][l, b, t], rows, 1 / math.sqrt(512))
+                worst = max(worst, G.assert_attention_close(out[l, b, t], o, f"l{l} b{b} t{t}"))
+                assert np.allclose(lse[l, b, t], ls, rtol=1e-3, atol=1e-3)
+    print(f"attention worst rel err {worst:.3g}")
+
+
 @pytest.mark.parametrize("NH", [16, 64])
 def test_attention_rescales_when_logits_grow_by_chunk(NH):
     """Every 64-row chunk's logits exceed the previous chunk's by more than 2^8 (log2 units), so
