@@ -76,12 +76,14 @@ struct RawRow {          // this thread's quarter (128 channels) of one chunk ro
 __device__ __forceinline__ void store_row(const RawRow& r, uint16_t* xrow, int quarter) {
   u32x4* dst = (u32x4*)(xrow + 128 * quarter);
   if (r.kind == 1) {
+    // the eight scale bytes through the hardware E4M3 conversion (exact), two per instruction
     float s[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[2 * i] = e4m3_to_f32((r.sc[i >> 1] >> (16 * (i & 1))) & 0xffu);
-      s[2 * i + 1] = e4m3_to_f32((r.sc[i >> 1] >> (16 * (i & 1) + 8)) & 0xffu);
-    }
+    const f32x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.sc[0], 1.0f, false);
+    const f32x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.sc[0], 1.0f, true);
+    const f32x2 s45 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.sc[1], 1.0f, false);
+    const f32x2 s67 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.sc[1], 1.0f, true);
+    s[0] = s01.x; s[1] = s01.y; s[2] = s23.x; s[3] = s23.y;
+    s[4] = s45.x; s[5] = s45.y; s[6] = s67.x; s[7] = s67.y;
     // 64 code bytes: bytes 8i .. 8i+7 hold channels 16i .. 16i+15 (scale s[i])
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -323,9 +325,12 @@ struct RawRow8 {         // this thread's eighth (64 channels) of one chunk row
 __device__ __forceinline__ void store_row8(const RawRow8& r, uint16_t* xrow, int eighth) {
   u32x4* dst = (u32x4*)(xrow + 64 * eighth);
   if (r.kind == 1) {
+    // the four scale bytes through the hardware E4M3 conversion (exact), two per instruction
+    const f32x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.sc, 1.0f, false);
+    const f32x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.sc, 1.0f, true);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {                      // scale group i: 8 code bytes, 16 channels
-      const float s = e4m3_to_f32((r.sc >> (8 * i)) & 0xffu);
+      const float s = i == 0 ? s01.x : (i == 1 ? s01.y : (i == 2 ? s23.x : s23.y));
       const uint32_t w0 = r.d[i >> 1][(i & 1) * 2], w1 = r.d[i >> 1][(i & 1) * 2 + 1];
       dst[2 * i] = u32x4{e2m1x2_scaled_to_bf16x2<0>(w0, s), e2m1x2_scaled_to_bf16x2<1>(w0, s),
                          e2m1x2_scaled_to_bf16x2<2>(w0, s), e2m1x2_scaled_to_bf16x2<3>(w0, s)};

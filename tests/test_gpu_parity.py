@@ -128,8 +128,10 @@ def test_scan_query_rounding_every_bf16(multi_query, fp4):
     assert np.array_equal(s[:, 1::2], np.maximum(-ref, 0).astype(np.float32))
 
 
-def test_fp4_dequant_every_code_and_scale_exact():
-    # one main row per query, no window: the output is the dequantised row itself
+@pytest.mark.parametrize("H", [16, 64])
+def test_fp4_dequant_every_code_and_scale_exact(H):
+    # one main row per query, no window: the output is the dequantised row itself (H = 16: the
+    # 16-head kernel, H = 64: the 64-head kernel)
     rows = 8
     codes = np.zeros((1, rows, 256), np.uint8)
     ch = np.arange(512)
@@ -137,17 +139,17 @@ def test_fp4_dequant_every_code_and_scale_exact():
     codes[0, :] = nib[0::2] | (nib[1::2] << 4)
     sc = (np.arange(rows * 32) % 256).astype(np.uint8).reshape(1, rows, 32)
     sc[(sc & 0x7F) == 0x7F] = 0x38
-    w = workloads.Workload("dq", 1, B=1, T=rows, N=rows, H=16, layer_set=(0,), n_reindex=0,
+    w = workloads.Workload("dq", 1, B=1, T=rows, N=rows, H=H, layer_set=(0,), n_reindex=0,
                            top_k=1, swa_window=0)
     inp = {"kv_codes": codes, "kv_scales": sc,
-           "q": workloads.to_bf16_bits(np.random.default_rng(0).standard_normal((1, 1, rows, 16, 512), dtype=np.float32)),
+           "q": workloads.to_bf16_bits(np.random.default_rng(0).standard_normal((1, 1, rows, H, 512), dtype=np.float32)),
            "swa": np.zeros((1, 1, 1, 512), np.uint8), "swa_end": np.zeros((1, rows), np.int32)}
     idx = np.arange(rows, dtype=np.int32).reshape(1, 1, rows, 1)
     out, lse = G.gpu_attention(inp, w, idx)
     ref = F.kv_row_values(codes[0], sc[0])
-    got = F.bf16_value(out[0, 0])          # [rows][16][512]
+    got = F.bf16_value(out[0, 0])          # [rows][H][512]
     for r in range(rows):
-        assert np.array_equal(got[r], np.broadcast_to(ref[r], (16, 512))), f"row {r}"
+        assert np.array_equal(got[r], np.broadcast_to(ref[r], (H, 512))), f"row {r}"
 
 
 # ------------------------------------------------------------------ indexer stages
