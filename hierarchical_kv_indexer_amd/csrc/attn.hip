@@ -308,11 +308,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_sparse_attn(
 }
 
 // 64 heads per workgroup (H % 64 == 0), 8 waves, X double-buffered.  Wave w owns head group hg = w % 4 (heads
-// 64*blockIdx.y + 16*hg .. +15) and half hf = w / 4: for S = Q X^T it scores rows 32*hf .. +31 of
-// each 64-row chunk, for O += P X it accumulates dims 256*hf .. +255 over all 64 rows.  The two
-// waves of a head group exchange their row maxima and P tiles through LDS, so each gathered row is
-// dequantised once for all 64 heads and a wave holds 16 heads x 256 dims of accumulators (two
-// waves per SIMD fit).  grid (n_splits, H/64, L*Q); outputs as k_sparse_attn.
+// 64*blockIdx.y + 16*hg .. +15) and half hf = w / 4: for the scores it takes rows 32*hf .. +31 of
+// each 64-row chunk, for O += P X it accumulates dims 256*hf .. +255 over all 64 rows.  The scores
+// are computed as S^T = X Q^T (X rows as the A operand, the query as B), so lane (j, g) holds head j
+// and rows 4g .. 4g+3 of each 16-row tile: the softmax reductions of a head run inside the lane and
+// across its four 16-lane groups.  The two waves of a head group exchange their row maxima, sums
+// and P tiles through LDS, so each gathered row is dequantised once for all 64 heads and a wave
+// holds 16 heads x 256 dims of accumulators (two waves per SIMD fit).  grid (n_splits, H/64, L*Q);
+// outputs as k_sparse_attn.
 constexpr int kWideThreads = 512;
 
 struct RawRow8 {         // this thread's eighth (64 channels) of one chunk row
@@ -360,7 +363,8 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
   __shared__ __attribute__((aligned(16))) uint16_t X[2][kRows * kXStride];   // chunk c in X[c & 1]
   __shared__ __attribute__((aligned(16))) uint16_t P[4 * 16 * kPStride];
   __shared__ float red_m[2][64], red_l[2][64];           // [half][16 * head group + head]
-  __shared__ int32_t rowok[2][kRows];
+  __shared__ float alpha_s[64];                          // rescale factor of each head (rare use)
+  __shared__ __attribute__((aligned(16))) int32_t rowok[2][kRows];
 
   const int split = blockIdx.x, hq = blockIdx.y, lq = blockIdx.z;
   const int l = lq / Q, q = lq % Q, b = q / T;
@@ -402,9 +406,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
 #pragma unroll
     for (int t = 0; t < 16; ++t) o[t] = mfma16x16x32(z, z, f32x4{0.f, 0.f, 0.f, 0.f});
   }
-  float m_run[4], l_run[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) { m_run[v] = -INFINITY; l_run[v] = 0.f; }
+  float m_run = -INFINITY, l_run = 0.f;             // head j of the group (both halves agree)
   uint16_t* Pg = P + hg * 16 * kPStride;
 
   auto load_chunk = [&](RawRow8& r, int c, int pos) {
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
 
   for (int c = 0; c < nchunks; ++c) {
     const uint16_t* Xc = X[c & 1];
-    // S[head 4g+v][row 32*hf + 16r + j]
+    // S^T[row 32*hf + 16r + 4g + v][head j]
     f32x4 s[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -449,57 +451,64 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
     for (int cc = 0; cc < 16; ++cc)
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        s[r] = mfma16x16x32(qa[cc], *(const u32x4*)(Xc + (32 * hf + 16 * r + j) * kXStride + 32 * cc + 8 * g), s[r]);
-    float sv[2][4];
+        s[r] = mfma16x16x32(*(const u32x4*)(Xc + (32 * hf + 16 * r + j) * kXStride + 32 * cc + 8 * g), qa[cc], s[r]);
+    float sv[2][4], mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const bool ok = rowok[c & 1][32 * hf + 16 * r + j] != 0;
+      const int4 ok = *(const int4*)&rowok[c & 1][32 * hf + 16 * r + 4 * g];
+      const int okv[4] = {ok.x, ok.y, ok.z, ok.w};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sv[r][v] = ok ? s[r][v] * scale_log2 : -INFINITY;
+      for (int v = 0; v < 4; ++v) {
+        sv[r][v] = okv[v] != 0 ? s[r][v] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sv[r][v]);
+      }
     }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float m = row16_max(fmaxf(sv[0][v], sv[1][v]));
-      if (j == 0) red_m[hf][16 * hg + 4 * g + v] = m;
-    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) red_m[hf][16 * hg + j] = mx;
     lds_barrier();                                 // both halves' maxima
     // The reference point of a head moves only when the chunk's max exceeds it by more than
     // kLazyLog2, so P <= 2^kLazyLog2 and O is rescaled only on such a move.  Both waves of a head
     // group take identical decisions (same maxima, same order).
-    float alpha[4];
-    bool moved = false;
+    const float m = fmaxf(red_m[0][16 * hg + j], red_m[1][16 * hg + j]);
+    const bool mv = m > m_run + kLazyLog2;           // true from -inf to finite
+    const float mnew = mv ? m : m_run;
+    const bool moved = mv && m_run != -INFINITY;
+    const float alpha = moved ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.f;
+    // exponents are at most kLazyLog2 (no overflow); results below 2^-126 may flush to zero, far
+    // below the rounding of the weights that matter.  P[head j][rows 32hf + 16r + 4g .. +3] as bf16,
+    // and the sum of the rounded weights.
+    float ps = 0.f;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int hh = 16 * hg + 4 * g + v;
-      const float m = fmaxf(red_m[0][hh], red_m[1][hh]);
-      const bool mv = m > m_run[v] + kLazyLog2;      // true from -inf to finite
-      const float mnew = mv ? m : m_run[v];
-      alpha[v] = (mv && m_run[v] != -INFINITY) ? __builtin_amdgcn_exp2f(m_run[v] - mnew) : 1.f;
-      moved |= mv && m_run[v] != -INFINITY;
-      // exponents are at most kLazyLog2 (no overflow); results below 2^-126 may flush to zero,
-      // far below the rounding of the weights that matter
-      const float p0 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[0][v] - mnew);
-      const float p1 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[1][v] - mnew);
-      const uint32_t pk = bf16x2_rne(p0, p1);
-      Pg[(4 * g + v) * kPStride + 32 * hf + j] = (uint16_t)pk;
-      Pg[(4 * g + v) * kPStride + 32 * hf + 16 + j] = (uint16_t)(pk >> 16);
-      float ps = __uint_as_float(pk << 16);
-      ps += __uint_as_float(pk & 0xffff0000u);
-      ps = row16_sum(ps);
-      if (j == 0) red_l[hf][hh] = ps;
-      m_run[v] = mnew;
-    }
-    lds_barrier();                                 // P tiles and both halves' sums
+    for (int r = 0; r < 2; ++r) {
+      uint32_t pk[2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int hh = 16 * hg + 4 * g + v;
-      l_run[v] = l_run[v] * alpha[v] + (red_l[0][hh] + red_l[1][hh]);
+      for (int e = 0; e < 2; ++e) {
+        const float p0 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r][2 * e] - mnew);
+        const float p1 = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[r][2 * e + 1] - mnew);
+        pk[e] = bf16x2_rne(p0, p1);
+        ps += __uint_as_float(pk[e] << 16);
+        ps += __uint_as_float(pk[e] & 0xffff0000u);
+      }
+      *(u32x2*)(Pg + j * kPStride + 32 * hf + 16 * r + 4 * g) = u32x2{pk[0], pk[1]};
     }
+    ps += __shfl_xor(ps, 16);                        // the same sum in all four groups
+    ps += __shfl_xor(ps, 32);
+    if (g == 0) {
+      red_l[hf][16 * hg + j] = ps;
+      if (hf == 0) alpha_s[16 * hg + j] = alpha;
+    }
+    m_run = mnew;
+    lds_barrier();                                 // P tiles, both halves' sums, the factors
+    l_run = l_run * alpha + (red_l[0][16 * hg + j] + red_l[1][16 * hg + j]);
     if (__ballot(moved) != 0) {                      // wave-uniform, rare
+      float a4[4];                                   // O holds heads 4g .. 4g+3 in a lane
+#pragma unroll
+      for (int v = 0; v < 4; ++v) a4[v] = alpha_s[16 * hg + 4 * g + v];
 #pragma unroll
       for (int t = 0; t < 16; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[t][v] *= alpha[v];
+        for (int v = 0; v < 4; ++v) o[t][v] *= a4[v];
     }
     // the next chunk into the other buffer (last read before the previous barrier), then the
     // raw rows of the chunk after it
@@ -554,12 +563,9 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
   for (int u = 0; u < 16; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) Os[(16 * hg + 4 * g + v) * kOStride + 256 * hf + 16 * u + j] = o[u][v];
-  if (hf == 0 && j == 0) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      red_m[0][16 * hg + 4 * g + v] = m_run[v];
-      red_l[0][16 * hg + 4 * g + v] = l_run[v];
-    }
+  if (hf == 0 && g == 0) {
+    red_m[0][16 * hg + j] = m_run;
+    red_l[0][16 * hg + j] = l_run;
   }
   lds_barrier();
   const size_t hrow = (size_t)lq * H;
