@@ -484,6 +484,28 @@ def test_reindex_user_pool_of_odd_capacity():
         G.assert_topk_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"odd pool t{t}")
 
 
+@pytest.mark.parametrize("fp4", [False, True])
+def test_reindex_many_caller_pools_ragged_lengths(fp4):
+    """40 caller pools of 16384 slots (5120 scoring workgroups, several rounds of the chip) with
+    lengths that end inside a unit, at unit and workgroup boundaries, at zero and at the
+    capacity; E4M3 and FP4 keys, against the oracle."""
+    T, K, cap = 40, 512, 16384
+    w = small("reindex_pool_256k", T=T, N=40000, user_pool=cap, top_k=K, seed=69, idx_k_fp4=fp4)
+    inp = workloads.make_inputs(w, with_attention=False)
+    pp = inp["pool_pos"].copy()
+    pl = inp["pool_len"].copy()
+    lens = [cap, 0, 1, 127, 128, 129, 6 * 128, 6 * 128 + 1, 12 * 128 - 1, 5000, cap - 1, 513]
+    for t, n in enumerate(lens):
+        pl[0, t] = n
+    gpu = G.gpu_reindex(inp, 1, T, pp, pl, K)
+    for t in list(range(len(lens))) + [20, 39]:
+        pool = pp[0, t, :pl[0, t]]
+        pool = pool[(pool >= 0) & (pool < w.N)]
+        r = O.reindex_layer(G.host_keys(inp, 0), inp["ri_q"][0, 0, t], inp["ri_w"][0, 0, t], pool, K)
+        sc = dict(zip(pool.tolist(), r["scores"].tolist()))
+        G.assert_topk_equiv(gpu["topk"][0, 0, t], r["topk"], lambda p: sc[p], f"runs t{t} len {pl[0, t]}")
+
+
 def test_reindex_user_pool_with_repeated_positions():
     """A caller pool listing some positions two or three times: copies rank like the position
     (score desc, position asc, counted with repeats), as the oracle's stable ranking orders them,
