@@ -435,7 +435,7 @@ def bench_encoder(args, w) -> int:
     return 0
 
 
-KERNEL_NAMES = ("k_idx_scan", "k_pool_chunks", "k_pool", "k_ri_score", "k_topk_lists", "k_topk", "k_sparse_attn",
+KERNEL_NAMES = ("k_idx_scan", "k_pool_chunks", "k_pool", "k_ri_score", "k_topk", "k_sparse_attn",
                 "k_attn_combine")
 
 

@@ -500,21 +500,11 @@ csa2_status csa2_index_full(const uint8_t* idx_k, const uint8_t* idx_k_scales, i
 
 namespace {
 
-// Scores by slot of `items` scored pools and their unit lists (see k_ri_score).
-struct ListWs {
-  float* slot_scores;
-  uint64_t* lists;
-  uint64_t* cuts;
-};
-
-size_t carve_lists(void* ws, int items, int cap, ListWs* out) {
+// Scores by slot of `items` scored pools (see k_ri_score).
+size_t carve_slot_scores(void* ws, int items, int cap, float** out) {
   Carver c{(char*)ws};
-  ListWs w;
-  const size_t nu = (size_t)csa2::ri_units(cap);
-  w.slot_scores = c.take<float>((size_t)items * cap);
-  w.lists = c.take<uint64_t>((size_t)items * nu * csa2::kRiUnitList);
-  w.cuts = c.take<uint64_t>((size_t)items * nu);
-  if (out) *out = w;
+  float* sc = c.take<float>((size_t)items * cap);
+  if (out) *out = sc;
   return c.off;
 }
 
@@ -525,7 +515,7 @@ extern "C" {
 size_t csa2_reindex_workspace(int L, int B, int T, int pool_cap, int top_k) {
   (void)top_k;
   if (L < 1 || B < 1 || T < 1 || pool_cap < 1 || pool_cap > csa2::kMaxPool) return 0;
-  return carve_lists(nullptr, L * B * T, pool_cap, nullptr);
+  return carve_slot_scores(nullptr, L * B * T, pool_cap, nullptr);
 }
 
 csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int64_t k_rows_per_seq, const uint16_t* idx_q,
@@ -553,18 +543,22 @@ csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int6
           "workspace of %zu bytes required (got %zu)", need, ws_bytes);
   const int Q = B * T;
   hipStream_t s = (hipStream_t)stream;
-  ListWs lw;
-  carve_lists(workspace, L * Q, pool_cap, &lw);
-  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, nullptr, 0, 0,
-                                                   nullptr, nullptr,
-                                                   pool_pos, pool_len, pool_cap, L, Q, T, lw.slot_scores, lw.lists,
-                                                   lw.cuts, s),
+  float* slot_scores = nullptr;
+  carve_slot_scores(workspace, L * Q, pool_cap, &slot_scores);
+  csa2_status st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, idx_q, head_w, 0, nullptr,
+                                                   nullptr, pool_pos, pool_len, pool_cap, L, Q, T, slot_scores, s),
                              "reindex score launch");
   if (st != CSA2_OK) return st;
-  st = hip_check(csa2::launch_topk_lists(lw.lists, lw.cuts, lw.slot_scores, pool_pos, pool_len, pool_cap, Q, top_k,
-                                         k_rows_per_seq, k_rows_per_seq, 0, nullptr, nullptr, L * Q, topk_idx,
-                                         topk_score, s),
-                 "top-k launch");
+  // every item's Top-K over its scored slots, one workgroup per item
+  csa2::TopkJob jb{};
+  jb.scores = slot_scores;
+  jb.score_stride = pool_cap;
+  jb.n_rows = k_rows_per_seq;
+  jb.by_position = 0;
+  jb.items = L * Q;
+  jb.out_idx = topk_idx;
+  jb.out_score = topk_score;
+  st = hip_check(csa2::launch_topk(pool_pos, pool_len, pool_cap, Q, top_k, csa2::TopkJob{}, jb, s), "top-k launch");
   return st == CSA2_OK ? ok() : st;
 }
 
@@ -572,11 +566,11 @@ csa2_status csa2_reindex(const uint8_t* idx_k, const uint8_t* idx_k_scales, int6
 
 namespace {
 
-// Full layer plus L Reindex layers over its pool: the Full workspace, then the slot scores and
-// chunk lists of the Full layer's Top-K item and the L Reindex items.
-size_t carve_chain(void* ws, const FullPlan& p, int n_max, int L, FullWs* fw, ListWs* lw) {
+// Full layer plus L Reindex layers over its pool: the Full workspace, then the slot scores of
+// the Full layer's pool (when it is scored again from its keys) and of the L Reindex items.
+size_t carve_chain(void* ws, const FullPlan& p, int n_max, int L, FullWs* fw, float** slot_scores) {
   const size_t full = carve_full(ws, p, n_max, fw);
-  return full + carve_lists(ws ? (char*)ws + full : nullptr, (L + 1) * p.Q, p.cap, lw);
+  return full + carve_slot_scores(ws ? (char*)ws + full : nullptr, (L + 1) * p.Q, p.cap, slot_scores);
 }
 
 }  // namespace
@@ -623,8 +617,8 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   REQUIRE(workspace != nullptr && aligned16(workspace) && ws_bytes >= need, CSA2_ERR_WORKSPACE,
           "workspace of %zu bytes required (got %zu)", need, ws_bytes);
   FullWs w;
-  ListWs lw;
-  carve_chain(workspace, p, n_max, L, &w, &lw);
+  float* slot_scores = nullptr;
+  carve_chain(workspace, p, n_max, L, &w, &slot_scores);
   hipStream_t s = (hipStream_t)stream;
   // With the one-query scan over E4M3 keys in the same call, the Full layer's pool slots are
   // scored again from their keys (the scan's own arithmetic, so the same scores) instead of
@@ -640,17 +634,30 @@ static csa2_status index_chain(bool do_scan, const uint8_t* idx_k, const uint8_t
   }
   st = launch_pool_stage(p, w, n_visible, n_max, pool_pos, pool_len, top_k, nullptr, nullptr, s);
   if (st != CSA2_OK) return st;
-  // the Full layer's pool scores (gathered from the scan's scores) and the Reindex layers'
-  // scores, each chunk with its list; then every layer's Top-K in one launch
+  // the Reindex layers' scores of the pool's slots (and, when rescoring, the Full layer's); then
+  // every layer's Top-K in one launch, one workgroup per item: the Full items read their scores
+  // by slot, or by position from the scan's scores
+  const int fi = rescore ? p.Q : 0;
   st = hip_check(csa2::launch_ri_score(idx_k, idx_k_scales, k_rows_per_seq, L ? ri_q : nullptr, L ? ri_w : nullptr,
-                                       rescore ? nullptr : w.scores, n_max, p.Q, idx_q, head_w, pool_pos, pool_len,
-                                       p.cap, L, p.Q, T, lw.slot_scores, lw.lists, lw.cuts, s),
+                                       fi, idx_q, head_w, pool_pos, pool_len, p.cap, L, p.Q, T, slot_scores, s),
                  "pool scoring launch");
   if (st != CSA2_OK) return st;
-  st = hip_check(csa2::launch_topk_lists(lw.lists, lw.cuts, lw.slot_scores, pool_pos, pool_len, p.cap, p.Q, top_k,
-                                         n_max > 0 ? n_max : 1, k_rows_per_seq, p.Q, topk_idx, topk_score, L * p.Q,
-                                         ri_topk_idx, ri_topk_score, s),
-                 "top-k launch");
+  csa2::TopkJob ja{}, jb{};
+  ja.scores = rescore ? slot_scores : w.scores;
+  ja.score_stride = rescore ? p.cap : n_max;
+  ja.n_rows = n_max > 0 ? n_max : 1;
+  ja.by_position = rescore ? 0 : 1;
+  ja.items = p.Q;
+  ja.out_idx = topk_idx;
+  ja.out_score = topk_score;
+  jb.scores = slot_scores + (size_t)fi * p.cap;
+  jb.score_stride = p.cap;
+  jb.n_rows = k_rows_per_seq;
+  jb.by_position = 0;
+  jb.items = L * p.Q;
+  jb.out_idx = ri_topk_idx;
+  jb.out_score = ri_topk_score;
+  st = hip_check(csa2::launch_topk(pool_pos, pool_len, p.cap, p.Q, top_k, ja, jb, s), "top-k launch");
   return st == CSA2_OK ? ok() : st;
 }
 

@@ -39,17 +39,13 @@ hipError_t launch_idx_scan(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t 
                            uint64_t* cuts, int chunk, int n_wg, bool multi_query, int block_score, int upw,
                            uint64_t* clists, uint64_t* ccuts, hipStream_t s);
 // Reindex scoring of pool slots in chunks of kRiChunk (and, for the first full_items items, the
-// Full layer's scan scores gathered by position); with `lists` non-null each unit of kRiUnit
-// slots lists its kRiUnitList best keys and a cut (see k_ri_score).
+// Full layer's query over the same slots); scores by slot (see k_ri_score).
 constexpr int kRiChunk = 128;
-constexpr int kRiUnit = 32;            // slots of a pool-scoring list unit (one wave's slots)
-constexpr int kRiUnitList = 4;         // keys a unit lists; its 5th best is its cut
 __host__ __device__ inline int ri_chunks(int pool_cap) { return (pool_cap + kRiChunk - 1) / kRiChunk; }
-__host__ __device__ inline int ri_units(int pool_cap) { return ri_chunks(pool_cap) * (kRiChunk / kRiUnit); }
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
-                           const float* head_w, const float* full_scores, int64_t full_stride, int full_items,
-                           const uint16_t* full_q, const float* full_w, const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
-                           float* slot_scores, uint64_t* lists, uint64_t* cuts, hipStream_t s);
+                           const float* head_w, int full_items, const uint16_t* full_q, const float* full_w,
+                           const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
+                           float* slot_scores, hipStream_t s);
 
 // select.hip
 // Pool of the top P blocks (positions ascending, -1 padded to cap_out), one WG per query.
@@ -63,11 +59,9 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
                        int32_t* pool_pos, int cap_out, int32_t* pool_len, const float* scores, int K,
                        int32_t* topk_idx, float* topk_score, int Q, hipStream_t s);
 // Top-K over candidate lists.  Candidate slot i of item it has position cand_pos[(it % Q)*cap + i]
-// (slots >= cand_len[it % Q] are empty).  by_position: the score of a candidate is
-// scores[(it % Q)*score_stride + pos]; otherwise scores[it*score_stride + slot].
-// One kind of Top-K item over the pools cand_pos/cand_len: `items` items (it = l*Q + q); by
-// position, the score of a candidate at position p is scores[q*score_stride + p], otherwise that
-// of slot i is scores[it*score_stride + i]; positions >= n_rows are ignored.
+// (slots >= cand_len[it % Q] are empty).  One kind of Top-K item: `items` items (it = l*Q + q);
+// by position, the score of a candidate at position p is scores[q*score_stride + p], otherwise
+// that of slot i is scores[it*score_stride + i]; positions >= n_rows are ignored.
 struct TopkJob {
   const float* scores;
   int64_t score_stride, n_rows;
@@ -78,14 +72,6 @@ struct TopkJob {
 // Items of job a, then items of job b (b.items may be 0), in one launch.
 hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
                        const TopkJob& a, const TopkJob& b, hipStream_t s);
-// Top-K of items scored by launch_ri_score with lists: item it (of items_a + items_b; query
-// it % Q within its group) selects from its units' lists, re-reading slot_scores only for units
-// whose cut reaches the threshold.  Outputs as launch_topk (job a's items write out_a, job b's
-// out_b; [items][k], -1 / 0 padded, ascending positions for an ascending pool).
-hipError_t launch_topk_lists(const uint64_t* lists, const uint64_t* cuts, const float* slot_scores,
-                             const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
-                             int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* out_a, float* out_sa,
-                             int items_b, int32_t* out_b, float* out_sb, hipStream_t s);
 
 // encoder.hip
 // n_visible[b][t] = floor((p0 + t + 1) / m), swa_end[b][t] = hist + t + 1.

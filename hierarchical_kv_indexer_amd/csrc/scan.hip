@@ -1058,29 +1058,23 @@ constexpr int kRiTilesPerWave = 2;
 static_assert(kScanThreads / 64 * kRiTilesPerWave * 16 == kRiChunk, "a workgroup scores one chunk of slots");
 
 // grid (n_chunks, items): item it scores pool slots [x*kRiChunk, (x+1)*kRiChunk) of its query.
-//   it <  full_items  the Full layer of query q = it: the scan's score of each slot's position,
-//                     full_scores[q * full_stride + pos] (no keys are read), or with full_scores
-//                     null the slot's key scored with the Full layer's query full_q[q] and weights
-//                     full_w[q] (the arithmetic of k_idx_scan, so the same score);
+//   it <  full_items  the Full layer of query q = it: the slot's key scored with the Full layer's
+//                     query full_q[q] and weights full_w[q] (the arithmetic of k_idx_scan, so the
+//                     scan's own score);
 //   it >= full_items  Reindex layer r / Q of query q = r % Q (r = it - full_items): the slot's
 //                     indexer key scored with that layer's query idx_q[r] and weights head_w[r].
 // Writes slot_scores[it][slot] for slots < pool_len holding a position in [0, k_rows) (others are
-// not written).  With `lists` non-null, each wave's 32 slots (one unit; unit 4x + wave) also leave
-// the pool Top-K its part: the ranking keys (score key << 32 | ~position) of the unit's 4 best
-// slots in slot order in lists[it][unit][0..3] (0 = none) and its 5th best in cuts[it][unit]
-// (0 = none), so every slot of the unit that is not listed ranks at or below the cut.  Equal keys
-// (a position listed more than once) are taken one slot at a time.
+// not written).  Wave w takes slots 32w .. 32w+31 of the chunk as two tiles of 16.
 template <bool kFp4>
 __global__ __launch_bounds__(kScanThreads) void k_ri_score(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
-    const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w,
-    const float* __restrict__ full_scores, int64_t full_stride, int full_items,
+    const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w, int full_items,
     const uint16_t* __restrict__ full_q, const float* __restrict__ full_w,
     const int32_t* __restrict__ pool_pos, const int32_t* __restrict__ pool_len, int cap, int Q, int T,
-    float* __restrict__ slot_scores, uint64_t* __restrict__ lists, uint64_t* __restrict__ cuts) {
+    float* __restrict__ slot_scores) {
   __shared__ __attribute__((aligned(16))) uint16_t qlds[kIdxHeads * kIdxDim];
   const int it = blockIdx.y;
-  const bool full = it < full_items, gather = full && full_scores != nullptr;
+  const bool full = it < full_items;
   const int r = it - full_items, q = full ? it : r % Q, b = q / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
@@ -1090,119 +1084,54 @@ __global__ __launch_bounds__(kScanThreads) void k_ri_score(
   const int len_raw = pool_len[q];
   const int s_begin = blockIdx.x * kRiChunk;
   const int32_t* pp = pool_pos + (size_t)q * cap;
-  float* out = slot_scores + (size_t)it * cap;
-  const int sw = s_begin + kRiUnit * wave;                         // first slot of this wave's unit
-  // this lane's candidate for the unit's list: slot sw + lane (lanes < 32)
-  float my_sc = 0.f;
-  int my_pos = -1;
-  if (gather) {
-    const int64_t n_rows = min(k_rows, full_stride);
-    const int slot = sw + lane;
-    int pos = (lane < kRiUnit && slot < cap) ? pp[slot] : -1;
-    pos = (pos >= 0 && (int64_t)pos < n_rows) ? pos : -1;
-    const float sc = pos >= 0 ? full_scores[(size_t)q * full_stride + pos] : 0.f;
-    const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
-    if (min(s_begin + kRiChunk, len) <= s_begin) return;
-    if (slot < len && pos >= 0) {
-      my_sc = sc;
-      my_pos = pos;
-    }
-  } else {
-    int pos[kRiTilesPerWave];
+  const int sw = s_begin + 16 * kRiTilesPerWave * wave;          // first slot of this wave
+  int pos[kRiTilesPerWave];
 #pragma unroll
-    for (int u = 0; u < kRiTilesPerWave; ++u) {
-      const int slot = sw + 16 * u + j;
-      pos[u] = slot < cap ? pp[slot] : -1;
-    }
-    stage_query<kScanThreads, kFp4>(full ? full_q + (size_t)q * kIdxHeads * kIdxDim
-                                         : idx_q + (size_t)r * kIdxHeads * kIdxDim, qlds);
-    const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
-    const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
-    TileRaw<kFp4> raw[kRiTilesPerWave];
-    bool ok[kRiTilesPerWave];
-#pragma unroll
-    for (int u = 0; u < kRiTilesPerWave; ++u) {
-      ok[u] = pos[u] >= 0 && (int64_t)pos[u] < k_rows;
-      load_key<kFp4>(kseq, sseq, ok[u] ? pos[u] : 0, g, raw[u]);
-    }
-    const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
-    const int s_end = min(s_begin + kRiChunk, len);
-    if (s_end <= s_begin) return;                 // uniform across the workgroup
-#pragma unroll
-    for (int u = 0; u < kRiTilesPerWave; ++u) ok[u] = ok[u] && sw + 16 * u + j < s_end;
-    lds_barrier();
-    TileCtx cx;
-    key_ctx<kFp4>(cx, qlds, full ? full_w + (size_t)q * kIdxHeads : head_w + (size_t)r * kIdxHeads);
-    float sc[kRiTilesPerWave];
-#pragma unroll
-    for (int u = 0; u < kRiTilesPerWave; ++u) sc[u] = key_score<kFp4>(cx, raw[u]);
-    // lane 16u + j (u < 2) takes tile u's slot sw + 16u + j (every lane of a column holds its score)
-    const int p0 = ok[0] ? pos[0] : -1, p1 = ok[1] ? pos[1] : -1;
-    my_sc = g == 1 ? sc[1] : sc[0];
-    my_pos = g == 0 ? p0 : (g == 1 ? p1 : -1);
+  for (int u = 0; u < kRiTilesPerWave; ++u) {
+    const int slot = sw + 16 * u + j;
+    pos[u] = slot < cap ? pp[slot] : -1;
   }
-  // lane i < 32 holds slot sw + i; its score is stored after the lists are computed (a register
-  // rewritten after a store makes the wave wait for the store to complete)
-  const bool store_sc = lane < kRiUnit && my_pos >= 0;
-  if (!lists) {
-    if (store_sc) out[sw + lane] = my_sc;
-    return;
-  }
-  // the unit's five best keys, one at a time: the largest key, and among copies of it the lowest
-  // lane (slot), leaves the set
-  uint64_t x = my_pos >= 0 ? rank_key(score_key(my_sc), (uint32_t)my_pos) : 0ull;
-  uint64_t best[kRiUnitList + 1];
-  int bslot[kRiUnitList + 1];
+  stage_query<kScanThreads, kFp4>(full ? full_q + (size_t)q * kIdxHeads * kIdxDim
+                                       : idx_q + (size_t)r * kIdxHeads * kIdxDim, qlds);
+  const uint8_t* kseq = idx_k + (size_t)b * (size_t)k_rows * (kFp4 ? kIdxDim / 2 : kIdxDim);
+  const uint8_t* sseq = kFp4 ? idx_ks + (size_t)b * (size_t)k_rows * (kIdxDim / 16) : nullptr;
+  TileRaw<kFp4> raw[kRiTilesPerWave];
+  bool ok[kRiTilesPerWave];
 #pragma unroll
-  for (int n = 0; n < kRiUnitList + 1; ++n) {
-    const uint32_t hi = wave_max_u32((uint32_t)(x >> 32));
-    const uint32_t lo = wave_max_u32((uint32_t)(x >> 32) == hi ? (uint32_t)x : 0u);
-    const uint64_t m = ((uint64_t)hi << 32) | lo;
-    const uint64_t at = __ballot(x == m && m != 0ull);
-    const int first = at ? __ffsll((unsigned long long)at) - 1 : 64;
-    best[n] = m;
-    bslot[n] = first;
-    if (lane == first) x = 0ull;
+  for (int u = 0; u < kRiTilesPerWave; ++u) {
+    ok[u] = pos[u] >= 0 && (int64_t)pos[u] < k_rows;
+    load_key<kFp4>(kseq, sseq, ok[u] ? pos[u] : 0, g, raw[u]);
   }
-  if (lane == 0) {
-    // the four listed in slot order (none = slot 64 sorts last)
-    auto cx = [&](int a, int c) {
-      const bool sw2 = bslot[a] > bslot[c];
-      const uint64_t ka = sw2 ? best[c] : best[a], kc = sw2 ? best[a] : best[c];
-      const int sa = sw2 ? bslot[c] : bslot[a], sc2 = sw2 ? bslot[a] : bslot[c];
-      best[a] = ka; best[c] = kc; bslot[a] = sa; bslot[c] = sc2;
-    };
-    cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-  }
-  if (store_sc) out[sw + lane] = my_sc;
-  if (lane == 0) {
-    const size_t unit = (size_t)it * (gridDim.x * (kRiChunk / kRiUnit)) + blockIdx.x * (kRiChunk / kRiUnit) + wave;
-    u32x4* lp = (u32x4*)(lists + unit * kRiUnitList);
-    lp[0] = u32x4{(uint32_t)best[0], (uint32_t)(best[0] >> 32), (uint32_t)best[1], (uint32_t)(best[1] >> 32)};
-    lp[1] = u32x4{(uint32_t)best[2], (uint32_t)(best[2] >> 32), (uint32_t)best[3], (uint32_t)(best[3] >> 32)};
-    cuts[unit] = best[kRiUnitList];
+  const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
+  const int s_end = min(s_begin + kRiChunk, len);
+  if (s_end <= s_begin) return;                   // uniform across the workgroup
+  lds_barrier();
+  TileCtx cx;
+  key_ctx<kFp4>(cx, qlds, full ? full_w + (size_t)q * kIdxHeads : head_w + (size_t)r * kIdxHeads);
+  float sc[kRiTilesPerWave];
+#pragma unroll
+  for (int u = 0; u < kRiTilesPerWave; ++u) sc[u] = key_score<kFp4>(cx, raw[u]);
+  // every lane of column j holds row j's score; lane group g < 2 stores tile g's
+  if (g < kRiTilesPerWave) {
+    const int slot = sw + 16 * g + j;
+    if ((g == 0 ? ok[0] : ok[1]) && slot < s_end) slot_scores[(size_t)it * cap + slot] = g == 0 ? sc[0] : sc[1];
   }
 }
 
 hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t k_rows, const uint16_t* idx_q,
-                           const float* head_w, const float* full_scores, int64_t full_stride, int full_items,
-                           const uint16_t* full_q, const float* full_w,
+                           const float* head_w, int full_items, const uint16_t* full_q, const float* full_w,
                            const int32_t* pool_pos, const int32_t* pool_len, int pool_cap, int L, int Q, int T,
-                           float* slot_scores, uint64_t* lists, uint64_t* cuts, hipStream_t s) {
-  const int n_chunks = (pool_cap + kRiChunk - 1) / kRiChunk;
+                           float* slot_scores, hipStream_t s) {
+  const int n_chunks = ri_chunks(pool_cap);
   const int items = full_items + L * Q;
   if (items == 0) return hipSuccess;
-  if (full_items > 0 && !full_scores && (!full_q || !full_w)) return hipErrorInvalidValue;
+  if (full_items > 0 && (!full_q || !full_w)) return hipErrorInvalidValue;
   if (idx_ks)
     hipLaunchKernelGGL(k_ri_score<true>, dim3(n_chunks, items), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, full_scores, full_stride, full_items, full_q, full_w, pool_pos, pool_len,
-                       pool_cap, Q, T,
-                       slot_scores, lists, cuts);
+                       idx_q, head_w, full_items, full_q, full_w, pool_pos, pool_len, pool_cap, Q, T, slot_scores);
   else
     hipLaunchKernelGGL(k_ri_score<false>, dim3(n_chunks, items), dim3(kScanThreads), 0, s, idx_k, idx_ks, k_rows,
-                       idx_q, head_w, full_scores, full_stride, full_items, full_q, full_w, pool_pos, pool_len,
-                       pool_cap, Q, T,
-                       slot_scores, lists, cuts);
+                       idx_q, head_w, full_items, full_q, full_w, pool_pos, pool_len, pool_cap, Q, T, slot_scores);
   return hipGetLastError();
 }
 

@@ -661,12 +661,12 @@ __global__ __launch_bounds__(kNT) void k_pool(
 
 // ------------------------------------------------------------------ list selection, 512 threads
 //
-// The pool's and the Top-K's selections from lists (the scan's chunk lists, the pool scoring's
-// unit lists) take few block-wide steps, and each step of a workgroup costs about the same
-// however little data it touches, so these kernels run 512 threads (two waves per SIMD): measured
-// on this part, a scan step with a barrier takes ~0.33 us at 512 threads against ~0.60 us at 1024.
+// The pool's selection from the scan's chunk lists takes few block-wide steps, and each step of a
+// workgroup costs about the same however little data it touches, so it runs 512 threads (two
+// waves per SIMD): measured on this part, a scan step with a barrier takes ~0.33 us at 512
+// threads against ~0.60 us at 1024.
 //
-// Lists: group g (a chunk of the scan, or a unit of 32 pool slots) lists its best keys in member
+// Lists: group g (a chunk of the scan) lists its best keys in member
 // order, and its cut bounds every member it does not list.  Let T0' be the lower edge of the
 // first-pass histogram bin that holds the P-th best listed key: T0' <= T0 <= T*, where T0 is that
 // key and T* the true P-th best of all members.  A group whose cut is below T0' has no unlisted
@@ -1294,105 +1294,5 @@ hipError_t launch_topk(const int32_t* cand_pos, const int32_t* cand_len, int cap
   hipLaunchKernelGGL(k_topk, dim3(items), dim3(kNT), 0, s, cand_pos, cand_len, cap, Q, k, a, b);
   return hipGetLastError();
 }
-
-// ------------------------------------------------------------------ Top-K from unit lists
-
-// Top-K of items scored by k_ri_score with lists: unit u of an item (kRiUnit consecutive slots)
-// lists its 4 best keys in slot order and cuts at its 5th (ls::list_select, re-reading a unit's
-// slot scores when its cut reaches T0').  One WG of 512 threads per item (job a's items, then job
-// b's; query it % Q within its job).  Output as k_topk: the k best positions in slot order
-// (ascending positions for an ascending pool) with their scores, -1 / 0 padded.  Falls back to a
-// selection over every slot when too many units would be re-read or copies of one position
-// straddle the k-th place.
-constexpr int kTLE = kMaxPool / kRiUnit * kRiUnitList / ls::NT;   // listed keys per thread (4)
-constexpr int kTLM = 8;                                            // re-read slots per thread
-
-__global__ __launch_bounds__(ls::NT) void k_topk_lists(
-    const uint64_t* __restrict__ lists, const uint64_t* __restrict__ cuts, const float* __restrict__ slot_scores,
-    const int32_t* __restrict__ cand_pos, const int32_t* __restrict__ cand_len, int cap, int Q, int k,
-    int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* __restrict__ out_a, float* __restrict__ out_sa,
-    int32_t* __restrict__ out_b, float* __restrict__ out_sb) {
-  __shared__ ls::Smem sm;
-  __shared__ int32_t res_i[kMaxTopK];        // the selection, written out at the end
-  __shared__ float res_s[kMaxTopK];
-  ls::Blk bk{sm};
-  const int it = blockIdx.x, t = threadIdx.x;
-  const bool in_a = it < items_a;
-  const int ij = in_a ? it : it - items_a;
-  const int q = ij % Q;
-  const int64_t n_rows = in_a ? n_rows_a : n_rows_b;
-  int32_t* oi = (in_a ? out_a : out_b) + (size_t)ij * k;
-  float* os_base = in_a ? out_sa : out_sb;
-  float* os = os_base ? os_base + (size_t)ij * k : nullptr;
-  const int nu = ri_units(cap);
-  // every load of the selection's first steps is issued here, before any is used
-  const int len_raw = cand_len[q];
-  const uint64_t* lrow = lists + (size_t)it * nu * kRiUnitList;
-  uint64_t key[kTLE];
-#pragma unroll
-  for (int e = 0; e < kTLE; ++e) {
-    const int g = e * ls::NT + t;
-    key[e] = g < nu * kRiUnitList ? lrow[g] : 0ull;
-  }
-  uint64_t cut = t < nu ? cuts[(size_t)it * nu + t] : 0ull;
-  ls::init(sm);
-  const int len = len_raw < 0 ? 0 : (len_raw > cap ? cap : len_raw);
-  const int nuse = (len + kRiUnit - 1) / kRiUnit;   // units holding slots (the others were not scored)
-#pragma unroll
-  for (int e = 0; e < kTLE; ++e)
-    if ((e * ls::NT + t) / kRiUnitList >= nuse) key[e] = 0ull;
-  if (t >= nuse) cut = 0ull;
-  lds_barrier();
-  const int32_t* cp = cand_pos + (size_t)q * cap;
-  const float* srow = slot_scores + (size_t)it * cap;
-  auto key_of_slot = [&](int slot) -> uint64_t {
-    const int pos = cp[slot];
-    return (pos >= 0 && (int64_t)pos < n_rows) ? rank_key(score_key(srow[slot]), (uint32_t)pos) : 0ull;
-  };
-  auto reread = [&](int grp, int o) -> uint64_t {
-    const int slot = grp * kRiUnit + o;
-    return slot < len ? key_of_slot(slot) : 0ull;
-  };
-  auto emit = [&](uint32_t off, uint64_t kk, int, int) {
-    res_i[off] = (int32_t)rank_key_index(kk);
-    res_s[off] = key_score((uint32_t)(kk >> 32));
-  };
-  int total = ls::list_select<kRiUnitList, kTLE, kTLM>(key, cut, nuse, kRiUnit, (uint32_t)k, reread, emit, bk);
-  if (total < 0)
-    total = (int)ls::dense_select(key_of_slot, len, (uint32_t)k,
-                                  [&](uint32_t off, uint64_t kk, int) { emit(off, kk, 0, 0); }, bk);
-  lds_barrier();
-  // every result is read before any is stored (a register rewritten after a store waits for it)
-  constexpr int kOut = kMaxTopK / ls::NT;
-  int32_t vi[kOut];
-  float vs[kOut];
-#pragma unroll
-  for (int u = 0; u < kOut; ++u) {
-    const int i = u * ls::NT + t;
-    vi[u] = i < total ? res_i[i] : -1;
-    vs[u] = i < total ? res_s[i] : 0.f;
-  }
-#pragma unroll
-  for (int u = 0; u < kOut; ++u) {
-    const int i = u * ls::NT + t;
-    if (i < k) {
-      oi[i] = vi[u];
-      if (os) os[i] = vs[u];
-    }
-  }
-}
-
-hipError_t launch_topk_lists(const uint64_t* lists, const uint64_t* cuts, const float* slot_scores,
-                             const int32_t* cand_pos, const int32_t* cand_len, int cap, int Q, int k,
-                             int64_t n_rows_a, int64_t n_rows_b, int items_a, int32_t* out_a, float* out_sa,
-                             int items_b, int32_t* out_b, float* out_sb, hipStream_t s) {
-  const int items = items_a + items_b;
-  if (items == 0) return hipSuccess;
-  if (cap > kMaxPool || ri_units(cap) > ls::MAX_GROUPS || k < 1 || k > kMaxTopK) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_topk_lists, dim3(items), dim3(ls::NT), 0, s, lists, cuts, slot_scores, cand_pos, cand_len,
-                     cap, Q, k, n_rows_a, n_rows_b, items_a, out_a, out_sa, out_b, out_sb);
-  return hipGetLastError();
-}
-
 
 }  // namespace csa2

@@ -38,9 +38,9 @@ def test_workspace_sizes(H):
     assert H.csa2_index_full_workspace(0, 1, 10, 8, 4, 4) == 0
     full = H.csa2_index_stages_workspace(1, 1, 1 << 20, 8, 2048, 512)
     assert H.csa2_index_full_workspace(1, 1, 1 << 20, 8, 2048, 512) == full   # one batch
-    # the chain adds, after the Full workspace, the slot scores and unit lists of the Full layer's
-    # Top-K item and of each Reindex layer (16384 fp32 scores, 512 units of 32 slots x 5 keys each)
-    per_item = 16384 * 4 + 512 * 4 * 8 + 512 * 8
+    # the chain adds, after the Full workspace, the slot scores of the Full layer's Top-K item and
+    # of each Reindex layer (16384 fp32 scores each)
+    per_item = 16384 * 4
     assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 2048, 512, 0) >= full + per_item
     assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 2048, 512, 4) >= full + 5 * per_item
     assert H.csa2_index_chain_workspace(1, 1, 1 << 20, 8, 0, 512, 4) == 0     # the chain needs a pool
