@@ -80,6 +80,7 @@ struct FullPlan {
   int Q, nb_max, nb_stride, chunk, n_wg, upw, n_units, blocks_per_unit, P, cap;
   bool internal_pool, multi_query;
   bool chunk_lists;   // the scan also leaves chunk lists and the pool selects from them first
+  bool unit_lists;    // the scan leaves unit lists for the pool (neither chunk lists nor a dense pool)
 };
 
 constexpr int kMaxPositions = 1 << 23;   // scores only: 1024 chunks of 8192 positions per query
@@ -111,6 +112,9 @@ FullPlan plan_full(int B, int T, int n_max, int pool_blocks, int top_k) {
   const int bpc = p.chunk / csa2::kBlock;
   p.chunk_lists = !p.multi_query && p.upw == 1 && p.n_wg <= 256 && p.nb_max > p.P &&
                   (int64_t)p.P * bpc <= (int64_t)8 * p.nb_max;
+  // Otherwise queries of at most kDensePoolBlocks blocks are pooled over every block key, and
+  // longer ones from the scan's unit lists.
+  p.unit_lists = !p.chunk_lists && p.nb_stride > csa2::kDensePoolBlocks;
   return p;
 }
 
@@ -131,8 +135,8 @@ size_t carve_full(void* ws, const FullPlan& p, int n_max, FullWs* out) {
   FullWs w;
   w.scores = c.take<float>((size_t)p.Q * (n_max > 0 ? n_max : 1));
   w.blkkey = c.take<uint32_t>((size_t)p.Q * p.nb_stride + 64);   // + tail read by unit batches
-  w.lists = c.take<uint64_t>((size_t)p.Q * p.n_units * 4);
-  w.cuts = c.take<uint64_t>((size_t)p.Q * p.n_units);
+  w.lists = p.unit_lists ? c.take<uint64_t>((size_t)p.Q * p.n_units * 4) : nullptr;
+  w.cuts = p.unit_lists ? c.take<uint64_t>((size_t)p.Q * p.n_units) : nullptr;
   w.clists = p.chunk_lists ? c.take<uint64_t>((size_t)p.Q * p.n_wg * csa2::kListLen) : nullptr;
   w.ccuts = p.chunk_lists ? c.take<uint64_t>((size_t)p.Q * p.n_wg) : nullptr;
   w.pool_pos = p.internal_pool ? c.take<int32_t>((size_t)p.Q * p.cap) : nullptr;

@@ -13,6 +13,7 @@ constexpr int kKvScaleBytes = 32;
 constexpr int kBlock = 8;          // positions per pool block
 constexpr int kMaxPool = 16384;    // largest pool (2048 blocks x 8 positions)
 constexpr int kMaxTopK = 2048;
+constexpr int kDensePoolBlocks = kMaxPool;   // block keys a dense pool selection holds (16 per thread)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

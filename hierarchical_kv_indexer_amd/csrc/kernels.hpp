@@ -49,6 +49,8 @@ hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t 
 
 // select.hip
 // Pool of the top P blocks (positions ascending, -1 padded to cap_out), one WG per query.
+// Without chunk lists, queries whose block-key rows (nb_max) hold at most kDensePoolBlocks keys are
+// pooled over every block key; longer ones from the unit lists.
 // With K > 0 the same WG then takes the Top-K of the pool from the scan's scores.
 // With clists non-null the pool is selected from the scan's chunk lists first (n_chunks chunks of
 // blocks_per_chunk blocks per query), and from the unit lists only when too many chunks would

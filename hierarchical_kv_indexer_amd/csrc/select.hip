@@ -33,6 +33,7 @@ constexpr int kWaves = kNT / 64;
 constexpr int kRankMax = 256;            // bins this small are resolved by direct ranking
 constexpr int kCandCap = 4096;           // LDS candidates (re-read units, slow-path compaction)
 constexpr int kE = kMaxPool / kNT;       // slots per thread (16): slot i*kNT + t for i < kE
+static_assert(kDensePoolBlocks <= kE * kNT, "a dense pool holds every block key in registers");
 constexpr int kUnitsPerThread = 4;       // units per thread in the pool kernel (<= 4096 units)
 static_assert(kBins == 4 * kNT, "find_bin gives each thread four bins");
 static_assert(kNT == 4 * kRankMax, "ranking splits the bin into four quarters");
@@ -1199,6 +1200,62 @@ __global__ __launch_bounds__(ls::NT) void k_pool_chunks(
 }
 
 
+// Pool over every block key when a query has at most kDensePoolBlocks blocks (16 per thread:
+// block j = e*kNT + t): the P best by (key desc, block asc), then the pool and its Top-K as k_pool
+// writes them.  Block keys are distinct as ranking keys (the block index is part of the key),
+// so exactly P blocks pass the P-th best.
+__global__ __launch_bounds__(kNT) void k_pool_dense(
+    const uint32_t* __restrict__ blkkey, int nb_max, const int32_t* __restrict__ n_visible, int n_max, int P,
+    int32_t* __restrict__ pool_pos, int cap_out, int32_t* __restrict__ pool_len,
+    const float* __restrict__ scores, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_score) {
+  __shared__ SelectSmem sm;
+  __shared__ uint32_t byrank[kMaxTopK];      // selected blocks, ascending
+  Block bk{sm};
+  const int q = blockIdx.x, t = threadIdx.x;
+  int nv = n_visible[q];
+  nv = nv < 0 ? 0 : (nv > n_max ? n_max : nv);
+  const int nb = (nv + kBlock - 1) / kBlock;
+  const uint32_t* keys = blkkey + (size_t)q * nb_max;
+  smem_init(sm);
+  const bool all = nb <= P;
+  uint32_t nsel = 0;
+  if (!all) {
+    uint32_t k32[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int jb = e * kNT + t;
+      k32[e] = jb < nb ? keys[jb] : 0u;
+    }
+    uint64_t key[kE];
+    uint32_t nvalid = 0, mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      const int jb = e * kNT + t;
+      const bool ok = jb < nb;
+      key[e] = ok ? rank_key(k32[e], (uint32_t)jb) : 0ull;
+      nvalid += ok ? 1u : 0u;
+      if (ok) { mn = min(mn, k32[e]); mx = max(mx, k32[e]); }
+    }
+    bk.reduce(nvalid, mn, mx);
+    auto for_each = [&](auto f) {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) f(key[e]);
+    };
+    const uint64_t thr = select_kth(for_each, (uint32_t)P, key_lo(mn), key_hi(mx), bk, nullptr);
+    uint32_t c[kE], off[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) c[e] = key[e] >= thr ? 1u : 0u;
+    nsel = min(ordered_offsets<true>(c, off, bk), (uint32_t)P);
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+      if (c[e] && off[e] < (uint32_t)P) byrank[off[e]] = (uint32_t)(e * kNT + t);
+    lds_barrier();
+  }
+  pool_out(all, nv, nb, nsel, byrank, pool_pos + (size_t)q * cap_out, cap_out, pool_len + q,
+           scores + (size_t)q * n_max, K, topk_idx + (size_t)q * K, topk_score ? topk_score + (size_t)q * K : nullptr,
+           bk);
+}
+
 hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
                        const uint64_t* clists, const uint64_t* ccuts, int n_chunks, int blocks_per_chunk,
                        const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max, int P,
@@ -1223,7 +1280,13 @@ hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units,
     j.out_score = topk_score;
     return launch_topk(pool_pos, pool_len, cap_out, Q, K, j, TopkJob{}, s);
   }
-  if (n_units > kUnitsPerThread * kNT || cap_out > kMaxPool) return hipErrorInvalidValue;
+  if (cap_out > kMaxPool) return hipErrorInvalidValue;
+  if (nb_max <= kDensePoolBlocks) {
+    hipLaunchKernelGGL(k_pool_dense, dim3(Q), dim3(kNT), 0, s, blkkey, nb_max, n_visible, n_max, P, pool_pos,
+                       cap_out, pool_len, scores, K, topk_idx, topk_score);
+    return hipGetLastError();
+  }
+  if (n_units > kUnitsPerThread * kNT) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_pool, dim3(Q), dim3(kNT), 0, s, lists, cuts, n_units, blocks_per_unit, blkkey, nb_max,
                      n_visible, n_max, P, pool_pos, cap_out, pool_len, scores, K, topk_idx, topk_score);
   return hipGetLastError();

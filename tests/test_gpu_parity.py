@@ -259,11 +259,11 @@ def test_index_full_batches_match_one_pass():
 
 @pytest.mark.parametrize("P,run", [(64, (1600, 3200)), (128, (4000, 4400)), (256, (8000, 8008))])
 def test_pool_with_runs_of_high_blocks(P, run):
-    """Runs of consecutive high-scoring blocks (200, 50 and 1 blocks against P = 64, 128, 256): the
-    chunk (P = 64, 128: the scan's chunk lists of 16) or unit (P = 256: unit lists of 4) holding a
-    run has more pool blocks than it lists, so it is re-read, and the P-th best block is found
-    among the listed blocks above T0 and the re-read ones.  Run rows repeat the 64 best rows of the
-    random keys."""
+    """Runs of consecutive high-scoring blocks (200, 50 and 1 blocks against P = 64, 128, 256).
+    P = 64, 128: the chunk holding a run has more pool blocks than its chunk list of 16, so it is
+    re-read, and the P-th best block is found among the listed blocks above T0 and the re-read
+    ones.  P = 256: too large a share of the 2500 blocks for chunk lists, so the pool is selected
+    over every block key.  Run rows repeat the 64 best rows of the random keys."""
     N, K = 20000, 256
     w = small(N=N, pool_blocks=P, top_k=K, seed=3400 + P)
     inp = workloads.make_inputs(w, with_attention=False)
@@ -276,14 +276,16 @@ def test_pool_with_runs_of_high_blocks(P, run):
     check_full(w, inp, gpu, 0, 0)
 
 
-def test_pool_tied_candidates_beyond_direct_ranking():
-    """The unit-list pool (a 131072-position context with a 2048-block pool: units of 8 blocks) with
-    the P-th best block inside a group of about 600 blocks of exactly equal score, one per unit:
-    more than 256 candidates share T*'s bin of T0's first histogram pass, so that bin is narrowed
-    by further passes instead of ranked directly.  A run of 6 high blocks inside one unit makes that
-    unit re-read, so T*'s histogram is the one derived from T0's first pass.  Equal blocks rank by
-    index on both sides: the pool and Top-K equal the oracle's exactly."""
-    N, P, K = 131072, 2048, 512
+@pytest.mark.parametrize("N", [131072, 200000])
+def test_pool_tied_candidates_beyond_direct_ranking(N):
+    """A 2048-block pool with the P-th best block inside a group of about 600 blocks of exactly
+    equal score, one per unit of 8 blocks: more than 256 candidates share T*'s histogram bin, so
+    that bin is narrowed by further passes instead of ranked directly.  N = 131072 (16384 blocks)
+    runs the dense pool over every block key; N = 200000 (25000 blocks) the unit-list pool, where
+    a run of 6 high blocks inside one unit makes that unit re-read, so T*'s histogram is the one
+    derived from T0's first pass.  Equal blocks rank by index on both sides: the pool and Top-K
+    equal the oracle's exactly."""
+    P, K = 2048, 512
     w = small(N=N, pool_blocks=P, top_k=K, n_reindex=1, seed=3500)
     inp = workloads.make_inputs(w, with_attention=False)
     k = inp["idx_k"]
