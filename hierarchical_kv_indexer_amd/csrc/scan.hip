@@ -1064,9 +1064,10 @@ static_assert(kScanThreads / 64 * kRiTilesPerWave * 16 == kRiChunk, "a workgroup
 //   it >= full_items  Reindex layer r / Q of query q = r % Q (r = it - full_items): the slot's
 //                     indexer key scored with that layer's query idx_q[r] and weights head_w[r].
 // Writes slot_scores[it][slot] for slots < pool_len holding a position in [0, k_rows) (others are
-// not written).  Wave w takes slots 32w .. 32w+31 of the chunk as two tiles of 16.
+// not written).  Wave w takes slots 32w .. 32w+31 of the chunk as two tiles of 16.  Eight waves per
+// SIMD fit (64 registers): with many short workgroups the rate follows the waves in flight.
 template <bool kFp4>
-__global__ __launch_bounds__(kScanThreads) void k_ri_score(
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_ri_score(
     const uint8_t* __restrict__ idx_k, const uint8_t* __restrict__ idx_ks, int64_t k_rows,
     const uint16_t* __restrict__ idx_q, const float* __restrict__ head_w, int full_items,
     const uint16_t* __restrict__ full_q, const float* __restrict__ full_w,
