@@ -593,9 +593,11 @@ __global__ __launch_bounds__(kWideThreads) void k_sparse_attn_wide(
 }
 
 // grid (H, L*Q), one wave per head: lane i merges dims 8i .. 8i+7 over the head's n_splits
-// partial states.  Every split slot is loaded up front (indices past n_splits clamp to the last
-// split and get weight zero), so the loads of a lane are all in flight together.
+// partial states.  Every split slot up to kMax (a bound on n_splits chosen at launch) is
+// loaded up front (indices past n_splits clamp to the last split and get weight zero), so the
+// loads of a lane are all in flight together.
 constexpr int kMaxSplits = 16;
+template <int kMax>
 __global__ __launch_bounds__(64) void k_attn_combine(
     const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml, int n_splits, int H,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
@@ -603,10 +605,10 @@ __global__ __launch_bounds__(64) void k_attn_combine(
   const size_t hrow = (size_t)blockIdx.y * H + blockIdx.x;
   const int lane = threadIdx.x;
   const float* ml = part_ml + hrow * n_splits * 2;
-  float m[kMaxSplits], l[kMaxSplits];
-  u32x4 a[kMaxSplits];                               // 8 fp16 dims of the split's normalised row
+  float m[kMax], l[kMax];
+  u32x4 a[kMax];                               // 8 fp16 dims of the split's normalised row
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < kMax; ++s) {
     const int sc = s < n_splits ? s : n_splits - 1;
     m[s] = ml[2 * sc];
     l[s] = ml[2 * sc + 1];
@@ -614,12 +616,12 @@ __global__ __launch_bounds__(64) void k_attn_combine(
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, s < n_splits ? m[s] : -INFINITY);
+  for (int s = 0; s < kMax; ++s) M = fmaxf(M, s < n_splits ? m[s] : -INFINITY);
   // split s holds O_s / l_s, so it enters with weight 2^(m_s - M) * l_s
   float L = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
+  for (int s = 0; s < kMax; ++s) {
     const float w = (s < n_splits && m[s] != -INFINITY) ? exp2f(m[s] - M) * l[s] : 0.f;
     L += w;
     const h8 v = __builtin_bit_cast(h8, a[s]);
@@ -679,8 +681,15 @@ hipError_t launch_sparse_attn(const uint8_t* kv_codes, const uint8_t* kv_scales,
                        scale_log2, p.split_rows, p.n_splits, part_o, part_ml, out, lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(H, L * Q), dim3(64), 0, s, part_o, part_ml,
-                     p.n_splits, H, out, lse);
+  const dim3 cg(H, L * Q);
+  if (p.n_splits <= 4)
+    hipLaunchKernelGGL(k_attn_combine<4>, cg, dim3(64), 0, s, part_o, part_ml, p.n_splits, H, out, lse);
+  else if (p.n_splits <= 8)
+    hipLaunchKernelGGL(k_attn_combine<8>, cg, dim3(64), 0, s, part_o, part_ml, p.n_splits, H, out, lse);
+  else if (p.n_splits <= 12)
+    hipLaunchKernelGGL(k_attn_combine<12>, cg, dim3(64), 0, s, part_o, part_ml, p.n_splits, H, out, lse);
+  else
+    hipLaunchKernelGGL(k_attn_combine<kMaxSplits>, cg, dim3(64), 0, s, part_o, part_ml, p.n_splits, H, out, lse);
   return hipGetLastError();
 }
 
