@@ -215,6 +215,8 @@ def check_full(w, inp, gpu, b, t):
     (5000, 64, 512, [5000, 300, 511, 0]),   # n_vis < K, n_vis = 0, pool larger than nb
     (9000, 128, 256, 20),            # multi-query scan: 20 queries, ragged causal visibility
     (270000, 0, 512, 16),            # one group of 16 queries over more than 256 chunks of 1024
+    (131072, 2048, 512, [131072, 100003, 16389]),   # 16384 blocks: the pool over every block key
+    (131080, 2048, 512, [131080, 100003, 16389]),   # 16385 blocks: the unit-list pool
 ])
 def test_index_full_parity(N, P, K, nv):
     T = 1 if nv is None else (nv if isinstance(nv, int) else len(nv))
