@@ -52,9 +52,9 @@ hipError_t launch_ri_score(const uint8_t* idx_k, const uint8_t* idx_ks, int64_t 
 // Without chunk lists, queries whose block-key rows (nb_max) hold at most kDensePoolBlocks keys are
 // pooled over every block key; longer ones from the unit lists.
 // With K > 0 the same WG then takes the Top-K of the pool from the scan's scores.
-// With clists non-null the pool is selected from the scan's chunk lists first (n_chunks chunks of
-// blocks_per_chunk blocks per query), and from the unit lists only when too many chunks would
-// have to be re-read.
+// With clists non-null the pool is selected from the scan's chunk lists (n_chunks chunks of
+// blocks_per_chunk blocks per query), and over every block key when too many chunks would have
+// to be re-read; a Top-K with K > 0 then follows as a second launch.
 hipError_t launch_pool(const uint64_t* lists, const uint64_t* cuts, int n_units, int blocks_per_unit,
                        const uint64_t* clists, const uint64_t* ccuts, int n_chunks, int blocks_per_chunk,
                        const uint32_t* blkkey, int nb_max, const int32_t* n_visible, int n_max, int P,
